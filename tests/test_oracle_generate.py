@@ -1,0 +1,82 @@
+"""The oracle's block-autoregressive generation on the tiny fp32 workload:
+determinism, the selection rule at every step, a MASK-free finished canvas,
+and the cache growing by one canvas per append. CPU only."""
+import json
+import os
+
+import numpy as np
+
+from oracle import generate as G
+from oracle import model as M
+from oracle import sampler as S
+from synth import workloads as wl
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _weights(cfg):
+    return M.Weights(cfg, wl.embedding(cfg), wl.final_norm(cfg), lambda l: wl.layer_weights(cfg, l))
+
+
+def _boost(cfg):
+    def f(c):
+        tok, mag = wl.canvas_boost(cfg, c)
+        return tok.numpy(), mag.numpy()
+    return f
+
+
+def test_workload_geometry_matches_the_pages():
+    g = json.load(open(os.path.join(HERE, "golden", "geometry.json")))
+    for cfg in (wl.STACK30, wl.STACK30_FP8):
+        assert cfg.n_layers == g["layers"]
+        assert cfg.window == g["sliding_window"]
+        assert cfg.canvas == g["canvas_length"]
+        assert cfg.n_experts == g["experts_total"] and cfg.top_k == g["experts_active"]
+        assert abs(cfg.vocab - g["vocab_approx"]) / g["vocab_approx"] < 0.01
+
+
+def test_tiny_generation_end_to_end():
+    cfg = wl.TINY
+    W = _weights(cfg)
+    scfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    prompt = wl.prefix_tokens(cfg, wl.TINY_PREFIX).numpy()
+    canv, steps, kv = G.generate(W, prompt, 2, scfg, seed=0x5EED, boost_fn=_boost(cfg))
+    assert kv.length == wl.TINY_PREFIX + 2 * cfg.canvas
+    for c in canv:
+        assert c.shape == (cfg.canvas,)
+        assert not np.any(c == cfg.mask_id)
+        assert np.all((c >= 0) & (c < cfg.vocab - 1))
+    assert all(1 <= s <= 48 for s in steps)
+    # determinism
+    canv2, steps2, _ = G.generate(_weights(cfg), prompt, 2, scfg, seed=0x5EED, boost_fn=_boost(cfg))
+    assert steps == steps2 and all(np.array_equal(a, b) for a, b in zip(canv, canv2))
+    # another seed changes the draws
+    canv3, _, _ = G.generate(_weights(cfg), prompt, 1, scfg, seed=1, boost_fn=_boost(cfg))
+    assert not np.array_equal(canv3[0], canv[0])
+
+
+def test_tiny_canvas_steps_follow_the_selection_rule():
+    cfg = wl.TINY
+    W = _weights(cfg)
+    scfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    kv = M.KVCache.empty(cfg)
+    M.encoder_append(W, kv, wl.prefix_tokens(cfg, wl.TINY_PREFIX).numpy())
+    log = []
+
+    def on_step(state, rec, logits):
+        log.append((rec, state.committed.copy(), state.tokens.copy()))
+
+    state, recs = G.denoise_canvas(G.model_provider(W, kv, _boost(cfg)(0)), cfg.canvas, scfg,
+                                   0x5EED, 0, on_step)
+    prev_com = np.zeros(cfg.canvas, bool)
+    for rec, com, toks in log:
+        sel = S.eb_select(rec.H32, prev_com, scfg.bound)
+        assert np.array_equal(sel, rec.selected)
+        assert sel.sum() >= 1
+        for i, tok in rec.drawn.items():
+            assert toks[i] == tok and tok != cfg.mask_id
+        prev_com = com.copy()
+    assert state.done and state.committed.all()
+    # the boosted workload spreads the entropies: some low, some high
+    H0 = log[0][0].H
+    assert H0.min() < 1.0 and H0.max() > 5.0
