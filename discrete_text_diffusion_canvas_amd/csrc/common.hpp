@@ -1,0 +1,122 @@
+// Shared device helpers for the gfx950 kernels: storage types, conversions,
+// wavefront reductions and MFMA fragment types. CDNA4 only (wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+constexpr int WAVE = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---- bf16 <-> f32 (bf16 held as raw uint16_t in memory) ----
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// round an f32 to the nearest bf16 value, kept as f32
+__device__ __forceinline__ float round_bf(float f) { return bf2f(f2bf(f)); }
+
+// ---- OCP e4m3fn byte -> f32 (exact; NaN code 0x7f/0xff -> NaN) ----
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    uint32_t s = (b & 0x80u) << 24;
+    uint32_t e = (b >> 3) & 0xfu;
+    uint32_t m = b & 0x7u;
+    if (e == 0) {  // subnormal: m/8 * 2^-6 = m * 2^-9
+        float v = (float)m * 0.001953125f;
+        return __uint_as_float(__float_as_uint(v) | s);
+    }
+    if (e == 0xf && m == 0x7) return __uint_as_float(0x7fc00000u | s);
+    // bias 7 -> bias 127: exponent + 120
+    return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// ---- wavefront reductions ----
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+// (value, index) argmax with lowest index on equal values
+struct ArgMax {
+    float v;
+    int i;
+};
+__device__ __forceinline__ ArgMax argmax_merge(ArgMax a, ArgMax b) {
+    if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+    return a;
+}
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        ArgMax b{__shfl_xor(a.v, o, WAVE), __shfl_xor(a.i, o, WAVE)};
+        a = argmax_merge(a, b);
+    }
+    return a;
+}
+
+// Base-2 entropy partials of a set of tempered logits z2 = z * log2(e):
+// m = max z2, s = sum 2^(z2-m), t = sum 2^(z2-m) (z2-m).
+struct EntPart {
+    float m, s, t;
+};
+// merge two partials onto the larger max
+__device__ __forceinline__ EntPart ent_merge(EntPart a, EntPart b) {
+    if (b.m > a.m) { EntPart c = a; a = b; b = c; }
+    if (b.s == 0.f) return a;
+    float d = b.m - a.m;  // <= 0
+    float f = exp2f(d);
+    a.s += b.s * f;
+    a.t += f * (b.t + d * b.s);
+    return a;
+}
+__device__ __forceinline__ EntPart wave_ent(EntPart a) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        EntPart b{__shfl_xor(a.m, o, WAVE), __shfl_xor(a.s, o, WAVE), __shfl_xor(a.t, o, WAVE)};
+        a = ent_merge(a, b);
+    }
+    return a;
+}
+
+// Per-row partial written by the logit-statistics producers (LM-head epilogue
+// and the standalone statistics kernel) and merged by the merge kernel.
+struct RowPart {
+    float m2;    // max of z2 over the tile (-inf if empty)
+    float s;     // sum 2^(z2 - m2)
+    float t;     // sum 2^(z2 - m2) (z2 - m2)
+    float lmax;  // max raw (biased) logit over the tile
+    int amax;    // its lowest column index (-1 if empty)
+    int pad[3];
+};
+
+}  // namespace dg

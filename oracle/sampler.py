@@ -243,12 +243,13 @@ def mean_entropy(H32) -> float:
 
 
 def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: int,
-                 H32_override=None) -> StepRecord:
+                 H32_override=None, argmax_override=None) -> StepRecord:
     """Advance ``state`` by one denoising step on logits [N][V] (in place).
 
-    ``H32_override`` lets a parity test feed the entropies another
-    implementation computed, so that selection and stop are compared on
-    identical inputs.
+    ``H32_override`` / ``argmax_override`` let a parity test feed the
+    entropies and argmaxes another implementation computed (after checking
+    them against this oracle's), so that selection, draws, stop and fill are
+    compared on identical inputs.
     """
     if state.done:
         raise ValueError("canvas already finished")
@@ -258,6 +259,8 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
     L = np.asarray(logits, dtype=np.float64)
     H, a, _, _ = row_stats(L, tau, cfg.mask_id)
     H32 = H.astype(np.float32) if H32_override is None else np.asarray(H32_override, np.float32)
+    if argmax_override is not None:
+        a = np.asarray(argmax_override, dtype=np.int64)
     cand = ~state.committed
     sel = eb_select(H32, state.committed, cfg.bound, cfg.bound_mode)
     drawn = {}

@@ -1,0 +1,81 @@
+"""The C ABI library loads, exports every function include/dg.h declares, and
+rejects bad arguments on the host before touching the GPU. CPU only."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+LIB = os.path.join(ROOT, "discrete_text_diffusion_canvas_amd", "libdg.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(dg_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdg.so is not built (run __graft_entry__.build())")
+    return C.CDLL(LIB)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("dg_sampler_step", "dg_last_error", "dg_canvas_reset"):
+        assert must in names
+    assert len(names) >= 6
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_defaults_are_the_model_cards_values(lib):
+    from discrete_text_diffusion_canvas_amd import binding as B
+    c = B.sampler_default()
+    assert (c.max_steps, c.stable_steps, c.bound_mode) == (48, 2, 0)
+    assert abs(c.temp_start - 0.8) < 1e-7 and abs(c.temp_end - 0.4) < 1e-7
+    assert abs(c.bound - 0.1) < 1e-8 and abs(c.stop_entropy - 0.005) < 1e-9
+
+
+def test_sampler_step_validates_before_launch(lib):
+    from discrete_text_diffusion_canvas_amd import binding as B
+    L = B.lib
+    cfg = B.sampler_default()
+    fake = C.c_void_p(0x1000)            # never dereferenced: validation fails first
+    canvas = B.CanvasStruct(0x1000, 0x1000, 0x1000, 0x1000, None, None, 16, 0)
+    stats = B.StepStatsStruct(0x1000, 0x1000, 0x1000, 0x1000, None)
+
+    def call(**kw):
+        a = dict(cfg=cfg, logits=fake, dtype=B.DG_BF16, n=16, V=64, ld=64, mask=63, canvas=canvas,
+                 step=0, stats=stats, ws=fake, wsb=1 << 20)
+        a.update(kw)
+        return L.dg_sampler_step(C.byref(a["cfg"]), a["logits"], a["dtype"], a["n"], a["V"], a["ld"],
+                                 a["mask"], C.byref(a["canvas"]), a["step"], 1, C.byref(a["stats"]),
+                                 a["ws"], a["wsb"], None)
+
+    assert call(logits=None) == -1
+    assert call(dtype=7) == -5
+    assert call(V=60, ld=64) == -2                 # not a multiple of 8
+    assert call(ld=32) == -2
+    assert call(mask=64) == -1
+    assert call(n=17) == -2                        # canvas n mismatch
+    assert call(step=48) == -1
+    assert call(step=-2) == -1
+    assert call(wsb=0) == -3
+    bad = B.sampler_default()
+    bad.temp_end = 0.0
+    assert call(cfg=bad) == -1
+    bad = B.sampler_default()
+    bad.bound_mode = 9
+    assert call(cfg=bad) == -1
+    assert b"bound_mode" in L.dg_last_error()
+    half = B.CanvasStruct(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 16, 0)
+    assert call(canvas=half) == -1

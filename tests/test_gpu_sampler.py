@@ -1,0 +1,186 @@
+"""Parity of the HIP EB sampler (dg_sampler_step) with the oracle, through the
+C ABI, on seeded synthetic logits: small ragged shapes, the full 256 x 262144
+bf16 workload, float32 logits with a per-row boost, scripted stop sequences,
+edge sizes and determinism."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sampler as S
+from synth import workloads as wl
+
+from parity import ENT_TOL, argmax_ok, draw_is_near_tie
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x5EED
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from discrete_text_diffusion_canvas_amd import binding
+    return binding
+
+
+def _biased(L, bias):
+    L = np.asarray(L, np.float64).copy()
+    if bias is not None:
+        tok, mag = bias
+        L[np.arange(L.shape[0]), tok] += mag.astype(np.float64)
+    return L
+
+
+def run_and_compare(B, logits_fn, n, V, steps, bias=None, seed=SEED, canvas_idx=0,
+                    bound_mode=0, step_ids=None):
+    """Run the GPU sampler step by step and check every step against the oracle.
+
+    Returns (gpu tokens, number of steps run, list of per-step records)."""
+    dev = torch.device("cuda")
+    mask = V - 1
+    btok = bval = None
+    if bias is not None:
+        btok = torch.tensor(bias[0], dtype=torch.int32, device=dev)
+        bval = torch.tensor(bias[1], dtype=torch.float32, device=dev)
+    canvas = B.Canvas(n, mask, canvas_idx, dev, btok, bval)
+    stats = B.StepStats(n, dev)
+    ws = torch.empty(B.sampler_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
+    cfg = B.sampler_default()
+    cfg.bound_mode = bound_mode
+    ocfg = S.SamplerConfig(mask_id=mask, bound_mode=["sum", "sum_minus_max"][bound_mode])
+    st = S.CanvasState.fresh(n, mask, canvas_idx)
+    recs = []
+    ids = step_ids if step_ids is not None else range(steps)
+    for t in ids:
+        Ld = logits_fn(t)
+        B.sampler_step(cfg, Ld, mask, canvas, t, seed, stats, ws)
+        torch.cuda.synchronize()
+        L = _biased(Ld.float().cpu().numpy(), bias)
+        tau = S.temperature(t, ocfg)
+        H, a, M, Ssum = S.row_stats(L, tau, mask)
+        Hg = stats.entropy.cpu().numpy()
+        ag = stats.argmax.cpu().numpy().astype(np.int64)
+        lse = stats.lse.cpu().numpy()
+        assert np.max(np.abs(Hg - H)) < ENT_TOL, (t, np.max(np.abs(Hg - H)))
+        assert np.max(np.abs(lse - (M + np.log(Ssum)))) < 1e-4 * max(1.0, np.abs(M).max())
+        z = S.tempered(L, tau, mask)
+        for i in np.nonzero(ag != a)[0]:
+            assert argmax_ok(z[i], int(ag[i]), int(a[i])), (t, i, ag[i], a[i])
+        if step_ids is not None:
+            st.steps = t
+        rec = S.sampler_step(st, L, t, ocfg, seed, H32_override=Hg, argmax_override=ag)
+        sel_g = stats.selected.cpu().numpy().astype(bool)
+        assert np.array_equal(sel_g, rec.selected), t
+        tok_g = canvas.tokens.cpu().numpy().astype(np.int64)
+        for i in np.nonzero(tok_g != st.tokens)[0]:
+            assert rec.selected[i], (t, i)
+            u = S.draw_uniform(seed, int(i), t, canvas_idx)
+            assert draw_is_near_tie(L[i], tau, mask, u), (t, i, tok_g[i], st.tokens[i])
+            st.tokens[i] = tok_g[i]
+        assert np.array_equal(canvas.committed.cpu().numpy().astype(bool), st.committed)
+        state = canvas.state.cpu().numpy()
+        assert state[B.ST_DONE] == int(st.done)
+        assert state[B.ST_STEP] == t + 1
+        assert state[B.ST_STABLE] == st.stable
+        assert state[B.ST_STOP] == int(rec.stop)
+        assert state[B.ST_FINISHED] == int(rec.finished)
+        assert state[B.ST_SELECTED] == int(rec.selected.sum())
+        assert abs(stats.mean_entropy.item() - rec.mean_H) == 0.0
+        assert np.array_equal(canvas.prev_argmax.cpu().numpy(), ag)
+        recs.append(rec)
+        if st.done:
+            break
+    assert np.array_equal(canvas.tokens.cpu().numpy(), st.tokens)
+    return canvas.tokens.cpu().numpy(), len(recs), recs
+
+
+def test_small_bf16_trajectory(B):
+    n, V = 64, 4096
+    toks, steps, recs = run_and_compare(
+        B, lambda t: wl.sampler_logits(t, shape=(n, V), device="cuda"), n, V, 48)
+    assert sum(r.selected.sum() for r in recs) >= 1
+    assert not np.any(toks == V - 1)
+
+
+@pytest.mark.parametrize("V", [5000, 2056, 8])
+def test_ragged_vocab_f32_with_boost(B, V):
+    n = 32
+    g = torch.Generator().manual_seed(V)
+    tok = torch.randint(0, V - 1, (n,), generator=g).numpy()
+    mag = (torch.rand(n, generator=g) * 12).numpy().astype(np.float32)
+
+    def logits(t):
+        gg = torch.Generator().manual_seed(1000 * V + t)
+        return torch.randn(n, V, generator=gg).to("cuda")
+    run_and_compare(B, logits, n, V, 48, bias=(tok, mag), canvas_idx=3)
+
+
+def test_sum_minus_max_mode(B):
+    n, V = 48, 1024
+    run_and_compare(B, lambda t: wl.sampler_logits(t + 7, shape=(n, V), max_peak=30.0, device="cuda"),
+                    n, V, 48, bound_mode=1)
+
+
+def test_full_vocab_256_rows_selected_steps(B):
+    n, V = wl.SAMPLER_ONLY_SHAPE
+    buf = torch.empty((n, V), dtype=torch.bfloat16, device="cuda")
+
+    def logits(t):
+        return wl.sampler_logits(t, device="cuda", out=buf)
+    run_and_compare(B, logits, n, V, None, step_ids=[0, 1, 2, 47])
+
+
+def test_stop_rule_fires_on_device(B):
+    """Confident, stable rows: the canvas stops at t = 1 and is filled by argmax."""
+    n, V = 256, 64
+    import math
+    import scipy.optimize
+    h = 0.0049
+
+    def logits(t):
+        tau = S.temperature(t, S.SamplerConfig())
+        p = scipy.optimize.brentq(lambda q: -(q * math.log(q) + (1 - q) * math.log(1 - q)) - h,
+                                  0.5, 1 - 1e-15)
+        L = torch.full((n, V), -1e4, dtype=torch.float32)
+        ids = torch.arange(n) % 50
+        L[torch.arange(n), ids] = 0.0
+        L[torch.arange(n), ids + 1] = tau * (math.log(1 - p) - math.log(p))
+        return L.cuda()
+    toks, steps, recs = run_and_compare(B, logits, n, V, 48)
+    assert steps == 2 and recs[-1].stop
+    assert np.array_equal(toks[~(recs[0].selected | recs[1].selected)],
+                          (np.arange(n) % 50)[~(recs[0].selected | recs[1].selected)])
+
+
+@pytest.mark.parametrize("n", [1, 1024])
+def test_edge_row_counts(B, n):
+    V = 256
+    run_and_compare(B, lambda t: wl.sampler_logits(t, shape=(n, V), device="cuda"), n, V, 48)
+
+
+def test_deterministic_and_done_is_sticky(B):
+    n, V = 128, 8192
+    dev = torch.device("cuda")
+    outs = []
+    for rep in range(2):
+        canvas = B.Canvas(n, V - 1, 0, dev)
+        stats = B.StepStats(n, dev)
+        ws = torch.empty(B.sampler_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
+        ents = []
+        for t in range(48):
+            B.sampler_step(B.sampler_default(), wl.sampler_logits(t, shape=(n, V), device="cuda"),
+                           V - 1, canvas, t, SEED, stats, ws)
+            ents.append(stats.entropy.clone())
+            if canvas.state[0].item():
+                break
+        outs.append((canvas.tokens.clone(), torch.stack(ents), canvas.state.clone()))
+        # further calls on a finished canvas change nothing
+        before = canvas.tokens.clone()
+        B.sampler_step(B.sampler_default(), wl.sampler_logits(0, shape=(n, V), device="cuda"),
+                       V - 1, canvas, -1, SEED, stats, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(before, canvas.tokens)
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[0][2], outs[1][2])
