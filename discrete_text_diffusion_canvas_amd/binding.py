@@ -42,7 +42,30 @@ class CanvasStruct(C.Structure):
 
 class StepStatsStruct(C.Structure):
     _fields_ = [("entropy", C.c_void_p), ("lse", C.c_void_p), ("argmax", C.c_void_p),
-                ("selected", C.c_void_p), ("mean_entropy", C.c_void_p)]
+                ("selected", C.c_void_p), ("mean_entropy", C.c_void_p), ("logits", C.c_void_p),
+                ("logits_ld", C.c_int64)]
+
+
+class ConfigStruct(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
+        "ffn_hidden", "vocab", "mask_id", "max_canvas", "window", "global_every", "weight_dtype",
+        "act_dtype")] + [("rope_base", C.c_float), ("norm_eps", C.c_float)]
+
+
+class LayerStruct(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "attn_norm", "moe_norm", "wqkv", "wo", "router", "router_bias", "w_gate", "w_up", "w_down",
+        "wqkv_scale", "wo_scale", "gate_scale", "up_scale", "down_scale")]
+
+
+class WeightsStruct(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerStruct))]
+
+
+class KVStruct(C.Structure):
+    _fields_ = [("k", C.POINTER(C.c_void_p)), ("v", C.POINTER(C.c_void_p)), ("capacity", C.c_int64),
+                ("len", C.c_int64)]
 
 
 def _load() -> C.CDLL:
@@ -60,7 +83,22 @@ def _load() -> C.CDLL:
     lib.dg_sampler_step.argtypes = [C.POINTER(SamplerCfg), vp, i32, i32, i32, i64, i32,
                                     C.POINTER(CanvasStruct), i32, u64, C.POINTER(StepStatsStruct),
                                     vp, sz, vp]
-    for name in ("dg_canvas_reset", "dg_sampler_step"):
+    P = C.POINTER
+    lib.dg_model_create.argtypes = [P(ConfigStruct), P(WeightsStruct), P(C.c_void_p)]
+    lib.dg_model_destroy.argtypes = [vp]
+    lib.dg_model_destroy.restype = None
+    lib.dg_workspace_bytes.argtypes = [vp, i32]
+    lib.dg_workspace_bytes.restype = sz
+    lib.dg_prefill_append.argtypes = [vp, P(KVStruct), vp, i32, vp, sz, vp]
+    lib.dg_canvas_step.argtypes = [vp, P(CanvasStruct), P(KVStruct), i32, u64, P(SamplerCfg),
+                                   P(StepStatsStruct), vp, sz, vp]
+    lib.dg_generate_canvas.argtypes = [vp, P(CanvasStruct), P(KVStruct), P(SamplerCfg), u64, i32, i32,
+                                       P(StepStatsStruct), P(C.c_int32), vp, sz, vp]
+    lib.dg_embed.argtypes = [vp, vp, i32, vp, vp]
+    lib.dg_decoder_layer.argtypes = [vp, i32, vp, i32, P(KVStruct), vp, vp, vp, sz, vp]
+    lib.dg_lm_head.argtypes = [vp, vp, i32, P(SamplerCfg), i32, vp, vp, P(StepStatsStruct), vp, sz, vp]
+    for name in ("dg_canvas_reset", "dg_sampler_step", "dg_model_create", "dg_prefill_append",
+                 "dg_canvas_step", "dg_generate_canvas", "dg_embed", "dg_decoder_layer", "dg_lm_head"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -121,16 +159,20 @@ class Canvas:
 
 
 class StepStats:
-    def __init__(self, n: int, device="cuda"):
+    """Per-step outputs; ``logits`` ([n][vocab], act dtype) only for model steps."""
+
+    def __init__(self, n: int, device="cuda", vocab: int = 0, logits_dtype=torch.bfloat16):
         self.entropy = torch.zeros(n, dtype=torch.float32, device=device)
         self.lse = torch.zeros(n, dtype=torch.float32, device=device)
         self.argmax = torch.zeros(n, dtype=torch.int32, device=device)
         self.selected = torch.zeros(n, dtype=torch.uint8, device=device)
         self.mean_entropy = torch.zeros(1, dtype=torch.float64, device=device)
+        self.logits = torch.empty((n, vocab), dtype=logits_dtype, device=device) if vocab else None
 
     def struct(self) -> StepStatsStruct:
+        ld = self.logits.stride(0) if self.logits is not None else 0
         return StepStatsStruct(_ptr(self.entropy), _ptr(self.lse), _ptr(self.argmax),
-                               _ptr(self.selected), _ptr(self.mean_entropy))
+                               _ptr(self.selected), _ptr(self.mean_entropy), _ptr(self.logits), ld)
 
 
 def sampler_workspace_bytes(n: int, vocab: int) -> int:
@@ -163,3 +205,120 @@ def timing_read():
     n = C.c_int32()
     check(lib.dg_timing_read(C.byref(ms), C.byref(n)))
     return ms.value, n.value
+
+
+# ---------------------------------------------------------------------------
+# Model, KV cache, workspace
+# ---------------------------------------------------------------------------
+
+_DT = {"f32": DG_F32, "bf16": DG_BF16, "fp8": DG_FP8_E4M3}
+
+
+class Model:
+    """Borrowed device weights plus the library's model handle.
+
+    ``cfg`` is a geometry object with the fields of synth.workloads.ModelConfig;
+    ``layers`` a list of dicts of device tensors (names as in dg_layer_weights).
+    """
+
+    def __init__(self, cfg, embed, final_norm, layers):
+        self.cfg = cfg
+        self.embed, self.final_norm, self.layers = embed, final_norm, layers
+        self._cs = ConfigStruct(
+            n_layers=cfg.n_layers, d_model=cfg.d_model, n_q_heads=cfg.n_q_heads,
+            n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, n_experts=cfg.n_experts,
+            top_k=cfg.top_k, ffn_hidden=cfg.ffn_hidden, vocab=cfg.vocab, mask_id=cfg.mask_id,
+            max_canvas=cfg.canvas, window=cfg.window, global_every=cfg.global_every,
+            weight_dtype=_DT[cfg.weight_dtype], act_dtype=_DT[cfg.act_dtype],
+            rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
+        arr = (LayerStruct * cfg.n_layers)()
+        for i, L in enumerate(layers):
+            for f, _ in LayerStruct._fields_:
+                setattr(arr[i], f, _ptr(L.get(f.replace("gate_scale", "w_gate_scale")
+                                           .replace("up_scale", "w_up_scale")
+                                           .replace("down_scale", "w_down_scale"))))
+        self._layers = arr
+        self._ws = WeightsStruct(_ptr(embed), _ptr(final_norm), arr)
+        h = C.c_void_p()
+        check(lib.dg_model_create(C.byref(self._cs), C.byref(self._ws), C.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            lib.dg_model_destroy(h)
+            self.handle = None
+
+    @property
+    def act_dtype(self):
+        return torch.float32 if self.cfg.act_dtype == "f32" else torch.bfloat16
+
+    def workspace(self, max_rows: int, device="cuda") -> torch.Tensor:
+        nb = int(lib.dg_workspace_bytes(self.handle, max_rows))
+        if nb == 0:
+            raise ValueError("bad max_rows")
+        return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+class KVCache:
+    """Per-layer K/V tensors [Hkv][capacity][hd] in the activation dtype."""
+
+    def __init__(self, model: Model, capacity: int, device="cuda"):
+        c = model.cfg
+        shape = (c.n_kv_heads, capacity, c.head_dim)
+        self.k = [torch.zeros(shape, dtype=model.act_dtype, device=device) for _ in range(c.n_layers)]
+        self.v = [torch.zeros(shape, dtype=model.act_dtype, device=device) for _ in range(c.n_layers)]
+        self.capacity = capacity
+        self._kp = (C.c_void_p * c.n_layers)(*[t.data_ptr() for t in self.k])
+        self._vp = (C.c_void_p * c.n_layers)(*[t.data_ptr() for t in self.v])
+        self.struct_ = KVStruct(self._kp, self._vp, capacity, 0)
+
+    @property
+    def length(self) -> int:
+        return int(self.struct_.len)
+
+    @length.setter
+    def length(self, v: int) -> None:
+        self.struct_.len = int(v)
+
+
+def prefill_append(model: Model, kv: KVCache, tokens: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    check(lib.dg_prefill_append(model.handle, C.byref(kv.struct_), _ptr(tokens), tokens.numel(),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def canvas_step(model: Model, canvas: Canvas, kv: KVCache, step_idx: int, seed: int, scfg: SamplerCfg,
+                stats: StepStats, ws: torch.Tensor, stream=None) -> None:
+    c = canvas.struct()
+    s = stats.struct()
+    check(lib.dg_canvas_step(model.handle, C.byref(c), C.byref(kv.struct_), step_idx, seed, C.byref(scfg),
+                             C.byref(s), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def generate_canvas(model: Model, canvas: Canvas, kv: KVCache, scfg: SamplerCfg, seed: int,
+                    append_after: bool, stats: StepStats, ws: torch.Tensor, poll_every: int = 4,
+                    stream=None) -> int:
+    c = canvas.struct()
+    s = stats.struct()
+    steps = C.c_int32()
+    check(lib.dg_generate_canvas(model.handle, C.byref(c), C.byref(kv.struct_), C.byref(scfg), seed,
+                                 int(bool(append_after)), poll_every, C.byref(s), C.byref(steps),
+                                 _ptr(ws), ws.numel(), _stream(stream)))
+    return steps.value
+
+
+def embed(model: Model, tokens: torch.Tensor, X: torch.Tensor, stream=None) -> None:
+    check(lib.dg_embed(model.handle, _ptr(tokens), tokens.numel(), _ptr(X), _stream(stream)))
+
+
+def decoder_layer(model: Model, layer: int, X: torch.Tensor, kv: KVCache, ws: torch.Tensor,
+                  route_ids=None, route_gates=None, stream=None) -> None:
+    check(lib.dg_decoder_layer(model.handle, layer, _ptr(X), X.shape[0], C.byref(kv.struct_),
+                               _ptr(route_ids), _ptr(route_gates), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def lm_head(model: Model, X: torch.Tensor, scfg: SamplerCfg, step_idx: int, stats: StepStats,
+            ws: torch.Tensor, bias_tok=None, bias_val=None, stream=None) -> None:
+    s = stats.struct()
+    check(lib.dg_lm_head(model.handle, _ptr(X), X.shape[0], C.byref(scfg), step_idx, _ptr(bias_tok),
+                         _ptr(bias_val), C.byref(s), _ptr(ws), ws.numel(), _stream(stream)))

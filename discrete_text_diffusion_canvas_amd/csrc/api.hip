@@ -6,14 +6,14 @@
 #include <string>
 
 #include "../../include/dg.h"
+#include "api_util.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 
-namespace {
+namespace dgapi {
 
 thread_local std::string g_err;
 
-dg_status fail(dg_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 dg_status fail(dg_status code, const char* fmt, ...) {
     char buf[512];
     va_list ap;
@@ -28,21 +28,6 @@ dg_status hip_check(hipError_t e, const char* what) {
     if (e == hipSuccess) return DG_OK;
     return fail(DG_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Bump allocator over a caller-provided workspace.
-struct Carve {
-    char* base;
-    size_t off = 0;
-    explicit Carve(void* p) : base((char*)p) {}
-    template <typename T>
-    T* take(size_t count) {
-        T* p = (T*)(base ? base + off : nullptr);
-        off += align256(count * sizeof(T));
-        return p;
-    }
-};
 
 dg_status check_sampler_cfg(const dg_sampler_cfg* s) {
     if (!s) return fail(DG_E_INVALID, "sampler config is NULL");
@@ -106,6 +91,10 @@ struct Timing {
 };
 Timing g_timing;
 
+}  // namespace dgapi
+
+namespace dgapi {
+
 // Records the start event of the dominant kernel; returns the slot or -1.
 int timing_begin(hipStream_t st) {
     if (!g_timing.on || g_timing.used >= Timing::kMax) return -1;
@@ -116,6 +105,11 @@ int timing_begin(hipStream_t st) {
 void timing_end(int slot, hipStream_t st) {
     if (slot >= 0) hipEventRecord(g_timing.ev[2 * slot + 1], st);
 }
+
+}  // namespace dgapi
+
+namespace {
+using namespace dgapi;
 
 size_t sampler_ws(int n, int V) {
     return align256((size_t)n * dg::sampler_nsplit(V) * sizeof(dg::RowPart)) +

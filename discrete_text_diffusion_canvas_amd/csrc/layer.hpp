@@ -1,0 +1,55 @@
+// Launchers of the per-layer glue kernels (layer.hip) and attention (attention.hip).
+#pragma once
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace dg {
+
+hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, int n, float* X,
+                        const int32_t* state, hipStream_t st);
+hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
+                          const int32_t* state, hipStream_t st);
+hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, int64_t pos0,
+                               double base, void* Q, int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld,
+                               int64_t kv_off, const int32_t* state, hipStream_t st);
+hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, int k, int32_t* ids, float* gates,
+                              const int32_t* state, hipStream_t st);
+hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
+                               int32_t* slot_of, const int32_t* state, hipStream_t st);
+hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
+                          int shared_off, const int32_t* state, hipStream_t st);
+
+// Attention over up to two key segments per KV head:
+//   segment 1: K1/V1 [Hkv][ld1][hd], rows [s1, e1)  (cache), positions = row index
+//   segment 2: K2/V2 [Hkv][ld2][hd], rows [0, n2)   (canvas), positions pos2_0 + row
+// Queries Q [Hq][ldq][hd] rows [0, nq) at positions qpos0 + row; output
+// O [nq][Hq*hd]. causal: key position <= query position; window > 0: and
+// query position - key position < window (per query). Softmax scale 1/sqrt(hd).
+struct AttnArgs {
+    const void* Q;
+    int64_t ldq;
+    int nq;
+    int64_t qpos0;
+    const void* K1;
+    const void* V1;
+    int64_t ld1;
+    int64_t s1, e1;
+    const void* K2;
+    const void* V2;
+    int64_t ld2;
+    int n2;
+    int64_t pos2_0;
+    int Hq, Hkv, hd;
+    int causal;
+    int window;       // per-query window for causal attention (0 = none)
+    void* O;
+    float* part_o;    // split-KV partials [splits][nq][Hq][hd] f32
+    float* part_ml;   // [splits][nq][Hq][2]
+    int splits;
+    const int32_t* state;
+};
+hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st);
+size_t attention_partial_floats(int splits, int nq, int Hq, int hd);
+
+}  // namespace dg

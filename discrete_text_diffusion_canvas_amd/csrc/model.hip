@@ -1,0 +1,478 @@
+// The model handle and the launch order of the decoder step, the encoder
+// prefill/append and canvas generation (include/dg.h).
+//
+// DiffusionGemma model card (zh-TW), "模型總覽" (overview): the encoder
+// prefills the prompt into a KV cache; the decoder denoises a canvas with
+// bidirectional attention and cross-attention into the cache; a fully
+// denoised canvas is encoded and appended, then the next canvas starts.
+// Best practice 1 gives the sampler that ends each step.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/dg.h"
+#include "api_util.hpp"
+#include "common.hpp"
+#include "gemm.hpp"
+#include "kernels.hpp"
+#include "layer.hpp"
+
+using namespace dgapi;
+
+struct dg_model {
+    dg_config cfg;
+    const void* embed;
+    const float* final_norm;
+    std::vector<dg_layer_weights> layers;
+};
+
+namespace {
+
+constexpr int MAX_SPLITS = 16;
+constexpr int SPLIT_ROWS = 256;  // partial buffers hold MAX_SPLITS x SPLIT_ROWS query rows
+
+int lm_bn(const dg_config& c) { return c.act_dtype == DG_F32 ? 128 : 256; }
+int lm_nsplit(const dg_config& c) { return (c.vocab + lm_bn(c) - 1) / lm_bn(c); }
+size_t act_bytes(const dg_config& c) { return c.act_dtype == DG_F32 ? 4 : 2; }
+bool is_global(const dg_config& c, int l) { return c.global_every > 0 && l % c.global_every == c.global_every - 1; }
+
+struct Work {
+    float* X;          // [T][d] residual stream
+    void* A;           // [T][d] normed activations (act dtype)
+    void* QKV;         // [T][(Hq+2Hkv) hd]
+    void* Q;           // [Hq][T][hd]
+    void* Kc;          // [Hkv][T][hd]
+    void* Vc;
+    void* O;           // [T][Hq hd]
+    float* part_o;     // attention split partials
+    float* part_ml;
+    float* rlog;       // [T][E]
+    int32_t* ids;      // [T][k]
+    float* gates;      // [T][k]
+    int32_t* offsets;  // [E+2]
+    int32_t* perm;     // [T(k+1)]
+    int32_t* slot_of;  // [T k]
+    void* Hbuf;        // [T(k+1)][F]
+    float* Y;          // [T(k+1)][d]
+    dg::RowPart* parts;  // [min(T, canvas)][nsplit]
+    int32_t* sel_list;
+    double* chunk_sum;
+    size_t bytes;
+    int rows;
+};
+
+Work carve(const dg_model* m, void* base, int T) {
+    const dg_config& c = m->cfg;
+    const size_t ab = act_bytes(c);
+    const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+    const int E = c.n_experts, k = c.top_k, F = c.ffn_hidden;
+    const int Nc = std::min(T, c.max_canvas);
+    Carve cv(base);
+    Work w;
+    w.X = cv.take<float>((size_t)T * d);
+    w.A = cv.take<char>((size_t)T * d * ab);
+    w.QKV = cv.take<char>((size_t)T * (Hq + 2 * Hkv) * hd * ab);
+    w.Q = cv.take<char>((size_t)T * Hq * hd * ab);
+    w.Kc = cv.take<char>((size_t)T * Hkv * hd * ab);
+    w.Vc = cv.take<char>((size_t)T * Hkv * hd * ab);
+    w.O = cv.take<char>((size_t)T * Hq * hd * ab);
+    w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
+    w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
+    w.rlog = cv.take<float>((size_t)T * E);
+    w.ids = cv.take<int32_t>((size_t)T * k);
+    w.gates = cv.take<float>((size_t)T * k);
+    w.offsets = cv.take<int32_t>(E + 2);
+    w.perm = cv.take<int32_t>((size_t)T * (k + 1));
+    w.slot_of = cv.take<int32_t>((size_t)T * k);
+    w.Hbuf = cv.take<char>((size_t)T * (k + 1) * F * ab);
+    w.Y = cv.take<float>((size_t)T * (k + 1) * d);
+    w.parts = cv.take<dg::RowPart>((size_t)Nc * lm_nsplit(c));
+    w.sel_list = cv.take<int32_t>(Nc);
+    w.chunk_sum = cv.take<double>((size_t)Nc * dg::draw_nchunk(c.vocab));
+    w.bytes = cv.off;
+    w.rows = T;
+    return w;
+}
+
+// largest chunk (<= cap) whose workspace fits in ws_bytes
+int rows_fitting(const dg_model* m, size_t ws_bytes, int cap) {
+    int best = 0;
+    for (int T = 1; T <= cap; T *= 2)
+        if (carve(m, nullptr, T).bytes <= ws_bytes) best = T;
+    if (best && best < cap && carve(m, nullptr, cap).bytes <= ws_bytes) best = cap;
+    return best;
+}
+
+dg::GemmArgs gargs() {
+    dg::GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.step_override = -1;
+    return g;
+}
+
+#define DG_TRY(expr, what)                                        \
+    do {                                                          \
+        if (dg_status _s = hip_check((expr), what)) return _s;    \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// The MoE half of a layer on rows X[0..n): X += shared(b) + sum_j g_j expert_j(b)
+// ---------------------------------------------------------------------------
+dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_t* state, hipStream_t st) {
+    const dg_config& c = m->cfg;
+    const dg_layer_weights& L = m->layers[l];
+    const int d = c.d_model, E = c.n_experts, k = c.top_k, F = c.ffn_hidden;
+    const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
+    DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.moe_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
+    {   // router logits (router weights are never e4m3)
+        dg::GemmArgs g = gargs();
+        g.A = w.A; g.lda = d; g.W = L.router; g.ldw = d; g.M = n; g.N = E; g.K = d;
+        g.C = w.rlog; g.ldc = E; g.state = state;
+        DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
+    }
+    DG_TRY(dg::launch_router_topk(w.rlog, L.router_bias, n, E, k, w.ids, w.gates, state, st), "router topk");
+    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, state, st), "hist permute");
+    {   // gate/up with SwiGLU
+        dg::GemmArgs g = gargs();
+        g.A = w.A; g.lda = d; g.a_rows = w.perm;
+        g.W = L.w_gate; g.W2 = L.w_up; g.ldw = d; g.w_group_stride = (int64_t)F * d;
+        g.w_scale = (const uint16_t*)L.gate_scale; g.w2_scale = (const uint16_t*)L.up_scale; g.scale_group_stride = F;
+        g.N = 2 * F; g.K = d; g.group_offsets = w.offsets;
+        g.C = w.Hbuf; g.ldc = F; g.c_f32 = f32; g.state = state;
+        DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, dg::SHAPE_SMALL_M, st), "expert gate/up");
+    }
+    {   // down
+        dg::GemmArgs g = gargs();
+        g.A = w.Hbuf; g.lda = F;
+        g.W = L.w_down; g.ldw = F; g.w_group_stride = (int64_t)d * F;
+        g.w_scale = (const uint16_t*)L.down_scale; g.scale_group_stride = d;
+        g.N = d; g.K = F; g.group_offsets = w.offsets;
+        g.C = w.Y; g.ldc = d; g.c_f32 = 1; g.state = state;
+        DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_STORE_F32, E + 1, dg::SHAPE_SMALL_M, st), "expert down");
+    }
+    DG_TRY(dg::launch_combine(w.X, n, d, w.Y, w.slot_of, w.gates, k, n * k, state, st), "combine");
+    return DG_OK;
+}
+
+int attn_splits(const dg_config& c, int nq, int64_t keys) {
+    const int qtiles = (nq + 63) / 64;
+    int s = (int)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, (keys + 511) / 512));
+    // enough workgroups without splitting long query sets
+    while (s > 1 && qtiles * c.n_q_heads * (s / 2) >= 512) s /= 2;
+    while (s > 1 && (int64_t)s * nq > (int64_t)MAX_SPLITS * SPLIT_ROWS) s /= 2;
+    return s;
+}
+
+// ---------------------------------------------------------------------------
+// Decoder layer over the canvas rows X[0..n) at positions P..P+n-1.
+// ---------------------------------------------------------------------------
+dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg_kv* kv, const int32_t* state,
+                        hipStream_t st) {
+    const dg_config& c = m->cfg;
+    const dg_layer_weights& L = m->layers[l];
+    const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+    const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
+    const int64_t P = kv->len;
+    DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
+    {
+        dg::GemmArgs g = gargs();
+        g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
+        g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N; g.state = state;
+        DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
+               "qkv gemm");
+    }
+    DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows,
+                                   0, state, st),
+           "rope");
+    {
+        dg::AttnArgs a;
+        memset(&a, 0, sizeof a);
+        a.Q = w.Q; a.ldq = w.rows; a.nq = n; a.qpos0 = P;
+        a.K1 = kv->k[l]; a.V1 = kv->v[l]; a.ld1 = kv->capacity;
+        a.s1 = is_global(c, l) ? 0 : std::max<int64_t>(0, P - c.window);
+        a.e1 = P;
+        a.K2 = w.Kc; a.V2 = w.Vc; a.ld2 = w.rows; a.n2 = n; a.pos2_0 = P;
+        a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.causal = 0; a.window = 0;
+        a.O = w.O; a.part_o = w.part_o; a.part_ml = w.part_ml;
+        a.splits = attn_splits(c, n, (a.e1 - a.s1) + n);
+        a.state = state;
+        DG_TRY(dg::launch_attention(a, f32, st), "attention");
+    }
+    {
+        dg::GemmArgs g = gargs();
+        g.A = w.O; g.lda = Hq * hd; g.W = L.wo; g.ldw = Hq * hd; g.w_scale = (const uint16_t*)L.wo_scale;
+        g.M = n; g.N = d; g.K = Hq * hd; g.X = w.X; g.ldx = d; g.state = state;
+        DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_RESIDUAL, 0, dg::SHAPE_PROJ, st), "o gemm");
+    }
+    return moe_block(m, l, w, n, state, st);
+}
+
+// ---------------------------------------------------------------------------
+// Encoder over one chunk of n tokens at positions P..P+n-1 (X holds their
+// embeddings); every layer's K/V rows are written into the cache.
+// ---------------------------------------------------------------------------
+dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv, int64_t P, hipStream_t st) {
+    const dg_config& c = m->cfg;
+    const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
+    const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const dg_layer_weights& L = m->layers[l];
+        DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, nullptr, st), "rmsnorm");
+        dg::GemmArgs g = gargs();
+        g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
+        g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N;
+        DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
+               "qkv gemm");
+        DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, kv->k[l],
+                                       kv->v[l], kv->capacity, P, nullptr, st),
+               "rope");
+        if (l == c.n_layers - 1) break;  // nothing in the cache depends on the rest
+        dg::AttnArgs a;
+        memset(&a, 0, sizeof a);
+        a.Q = w.Q; a.ldq = w.rows; a.nq = n; a.qpos0 = P;
+        a.K1 = kv->k[l]; a.V1 = kv->v[l]; a.ld1 = kv->capacity; a.s1 = 0; a.e1 = P + n;
+        a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.causal = 1;
+        a.window = is_global(c, l) ? 0 : c.window;
+        a.O = w.O; a.part_o = w.part_o; a.part_ml = w.part_ml;
+        int64_t span = a.window > 0 ? std::min<int64_t>(P + n, (int64_t)a.window + 64) : P + n;
+        a.splits = attn_splits(c, n, span);
+        DG_TRY(dg::launch_attention(a, f32, st), "attention");
+        dg::GemmArgs go = gargs();
+        go.A = w.O; go.lda = Hq * hd; go.W = L.wo; go.ldw = Hq * hd; go.w_scale = (const uint16_t*)L.wo_scale;
+        go.M = n; go.N = d; go.K = Hq * hd; go.X = w.X; go.ldx = d;
+        DG_TRY(dg::gemm_launch(go, f32, fp8, dg::EPI_RESIDUAL, 0, dg::SHAPE_PROJ, st), "o gemm");
+        if (dg_status s = moe_block(m, l, w, n, nullptr, st)) return s;
+    }
+    return DG_OK;
+}
+
+dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerParams& sp, int step_override,
+                  const int32_t* state, const int32_t* bias_tok, const float* bias_val, dg_step_stats* stats,
+                  hipStream_t st) {
+    const dg_config& c = m->cfg;
+    const int f32 = c.act_dtype == DG_F32;
+    DG_TRY(dg::launch_rmsnorm(w.X, n, c.d_model, m->final_norm, c.norm_eps, w.A, f32, state, st), "final norm");
+    dg::GemmArgs g = gargs();
+    g.A = w.A; g.lda = c.d_model; g.W = m->embed; g.ldw = c.d_model;
+    g.M = n; g.N = c.vocab; g.K = c.d_model;
+    g.C = stats->logits; g.ldc = stats->logits_ld; g.c_f32 = f32;
+    g.parts = w.parts; g.nsplit = lm_nsplit(c);
+    g.state = state; g.step_override = step_override; g.sp = sp; g.mask_id = c.mask_id;
+    g.bias_tok = bias_tok; g.bias_val = bias_val;
+    int slot = timing_begin(st);
+    DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
+    timing_end(slot, st);
+    DG_TRY(dg::launch_merge_rows(w.parts, n, lm_nsplit(c), state, stats->entropy, stats->lse, stats->argmax, st),
+           "merge rows");
+    return DG_OK;
+}
+
+dg_status check_kv(const dg_model* m, const dg_kv* kv) {
+    if (!kv || !kv->k || !kv->v) return fail(DG_E_INVALID, "kv cache is NULL");
+    if (kv->len < 0 || kv->capacity < kv->len) return fail(DG_E_INVALID, "kv len/capacity inconsistent");
+    for (int l = 0; l < m->cfg.n_layers; ++l)
+        if (!kv->k[l] || !kv->v[l]) return fail(DG_E_INVALID, "kv layer %d pointer is NULL", l);
+    return DG_OK;
+}
+
+dg_status check_logits(const dg_model* m, const dg_step_stats* s, int n) {
+    if (dg_status e = check_stats(s)) return e;
+    if (!s->logits) return fail(DG_E_INVALID, "stats->logits is NULL");
+    if (s->logits_ld < m->cfg.vocab) return fail(DG_E_SHAPE, "logits_ld < vocab");
+    (void)n;
+    return DG_OK;
+}
+
+dg_status ws_for(const dg_model* m, void* ws, size_t ws_bytes, int rows, Work* out) {
+    if (!ws) return fail(DG_E_INVALID, "workspace is NULL");
+    Work w = carve(m, ws, rows);
+    if (w.bytes > ws_bytes) return fail(DG_E_CAPACITY, "workspace %zu bytes < %zu needed", ws_bytes, w.bytes);
+    *out = w;
+    return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_model_create(const dg_config* c, const dg_weights* w, dg_model** out) {
+    if (!c || !w || !out) return fail(DG_E_INVALID, "NULL argument");
+    *out = nullptr;
+    if (c->n_layers < 1 || c->d_model < 32 || c->d_model % 32) return fail(DG_E_SHAPE, "d_model must be a multiple of 32");
+    if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
+        return fail(DG_E_SHAPE, "n_q_heads must be a positive multiple of n_kv_heads");
+    if (c->act_dtype != DG_F32 && c->act_dtype != DG_BF16) return fail(DG_E_UNSUPPORTED, "act_dtype");
+    if (c->weight_dtype == DG_F32 ? c->act_dtype != DG_F32 : c->act_dtype != DG_BF16)
+        return fail(DG_E_UNSUPPORTED, "f32 weights need f32 activations; bf16/e4m3 weights need bf16");
+    if (c->weight_dtype != DG_F32 && c->weight_dtype != DG_BF16 && c->weight_dtype != DG_FP8_E4M3)
+        return fail(DG_E_UNSUPPORTED, "weight_dtype");
+    const int hd = c->head_dim;
+    if (!(hd == 64 || hd == 128 || (hd == 256 && c->act_dtype == DG_BF16)))
+        return fail(DG_E_UNSUPPORTED, "head_dim must be 64 or 128 (f32) / 64, 128 or 256 (bf16)");
+    if (c->n_experts < 1 || c->n_experts > 512) return fail(DG_E_SHAPE, "n_experts outside 1..512");
+    if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return fail(DG_E_SHAPE, "top_k outside 1..min(16, E)");
+    if (c->ffn_hidden < 32 || c->ffn_hidden % 32) return fail(DG_E_SHAPE, "ffn_hidden must be a multiple of 32");
+    if (c->vocab < 8 || c->vocab % 8) return fail(DG_E_SHAPE, "vocab must be a multiple of 8");
+    if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DG_E_INVALID, "mask_id outside the vocabulary");
+    if (c->max_canvas < 1 || c->max_canvas > 1024) return fail(DG_E_SHAPE, "max_canvas outside 1..1024");
+    if (c->window < 0 || c->global_every < 0) return fail(DG_E_INVALID, "window/global_every must be >= 0");
+    if (!(c->rope_base > 1.f) || !(c->norm_eps >= 0.f)) return fail(DG_E_INVALID, "rope_base/norm_eps");
+    if (!w->embed || !w->final_norm || !w->layers) return fail(DG_E_INVALID, "weight pointer is NULL");
+    const bool fp8 = c->weight_dtype == DG_FP8_E4M3;
+    for (int l = 0; l < c->n_layers; ++l) {
+        const dg_layer_weights& L = w->layers[l];
+        if (!L.attn_norm || !L.moe_norm || !L.wqkv || !L.wo || !L.router || !L.router_bias || !L.w_gate ||
+            !L.w_up || !L.w_down)
+            return fail(DG_E_INVALID, "layer %d: weight pointer is NULL", l);
+        if (fp8 && (!L.wqkv_scale || !L.wo_scale || !L.gate_scale || !L.up_scale || !L.down_scale))
+            return fail(DG_E_INVALID, "layer %d: e4m3 weights need scales", l);
+    }
+    dg_model* m = new (std::nothrow) dg_model;
+    if (!m) return fail(DG_E_INVALID, "out of host memory");
+    m->cfg = *c;
+    m->embed = w->embed;
+    m->final_norm = w->final_norm;
+    m->layers.assign(w->layers, w->layers + c->n_layers);
+    *out = m;
+    return DG_OK;
+}
+
+void dg_model_destroy(dg_model* m) { delete m; }
+
+size_t dg_workspace_bytes(const dg_model* m, int32_t max_rows) {
+    if (!m || max_rows < 1 || max_rows > 4096) return 0;
+    return carve(m, nullptr, max_rows).bytes;
+}
+
+dg_status dg_embed(const dg_model* m, const int32_t* tokens, int32_t n, float* X, void* stream) {
+    if (!m || !tokens || !X) return fail(DG_E_INVALID, "NULL argument");
+    if (n < 1) return fail(DG_E_SHAPE, "n must be >= 1");
+    return hip_check(dg::launch_embed(m->embed, m->cfg.act_dtype == DG_F32, m->cfg.d_model, tokens, n, X, nullptr,
+                                      (hipStream_t)stream),
+                     "embed");
+}
+
+dg_status dg_decoder_layer(const dg_model* m, int32_t layer, float* X, int32_t n, const dg_kv* kv,
+                           int32_t* route_ids, float* route_gates, void* ws, size_t ws_bytes, void* stream) {
+    if (!m || !X) return fail(DG_E_INVALID, "NULL argument");
+    if (layer < 0 || layer >= m->cfg.n_layers) return fail(DG_E_INVALID, "layer out of range");
+    if (n < 1 || n > m->cfg.max_canvas) return fail(DG_E_SHAPE, "n outside 1..max_canvas");
+    if (dg_status s = check_kv(m, kv)) return s;
+    Work w;
+    if (dg_status s = ws_for(m, ws, ws_bytes, n, &w)) return s;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t xb = (size_t)n * m->cfg.d_model * sizeof(float);
+    DG_TRY(hipMemcpyAsync(w.X, X, xb, hipMemcpyDeviceToDevice, st), "copy X in");
+    if (dg_status s = decoder_layer(m, layer, w, n, kv, nullptr, st)) return s;
+    DG_TRY(hipMemcpyAsync(X, w.X, xb, hipMemcpyDeviceToDevice, st), "copy X out");
+    const size_t kb = (size_t)n * m->cfg.top_k;
+    if (route_ids) DG_TRY(hipMemcpyAsync(route_ids, w.ids, kb * 4, hipMemcpyDeviceToDevice, st), "copy ids");
+    if (route_gates) DG_TRY(hipMemcpyAsync(route_gates, w.gates, kb * 4, hipMemcpyDeviceToDevice, st), "copy gates");
+    return DG_OK;
+}
+
+dg_status dg_lm_head(const dg_model* m, const float* X, int32_t n, const dg_sampler_cfg* scfg, int32_t step_idx,
+                     const int32_t* bias_tok, const float* bias_val, dg_step_stats* stats, void* ws,
+                     size_t ws_bytes, void* stream) {
+    if (!m || !X) return fail(DG_E_INVALID, "NULL argument");
+    if (dg_status s = check_sampler_cfg(scfg)) return s;
+    if (n < 1 || n > m->cfg.max_canvas) return fail(DG_E_SHAPE, "n outside 1..max_canvas");
+    if (step_idx < 0 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
+    if ((bias_tok == nullptr) != (bias_val == nullptr)) return fail(DG_E_INVALID, "bias pointers");
+    if (dg_status s = check_logits(m, stats, n)) return s;
+    Work w;
+    if (dg_status s = ws_for(m, ws, ws_bytes, n, &w)) return s;
+    hipStream_t st = (hipStream_t)stream;
+    DG_TRY(hipMemcpyAsync(w.X, X, (size_t)n * m->cfg.d_model * 4, hipMemcpyDeviceToDevice, st), "copy X");
+    return lm_head(m, w, n, to_params(scfg), step_idx, nullptr, bias_tok, bias_val, stats, st);
+}
+
+dg_status dg_prefill_append(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t n, void* ws,
+                            size_t ws_bytes, void* stream) {
+    if (!m || !tokens) return fail(DG_E_INVALID, "NULL argument");
+    if (dg_status s = check_kv(m, kv)) return s;
+    if (n < 0) return fail(DG_E_SHAPE, "n must be >= 0");
+    if (kv->len + n > kv->capacity) return fail(DG_E_CAPACITY, "kv cache capacity %lld < %lld", (long long)kv->capacity,
+                                                (long long)(kv->len + n));
+    if (n == 0) return DG_OK;
+    if (!ws) return fail(DG_E_INVALID, "workspace is NULL");
+    const int T = rows_fitting(m, ws_bytes, std::min(n, 4096));
+    if (T < 1) return fail(DG_E_CAPACITY, "workspace too small for one row");
+    Work w = carve(m, ws, T);
+    hipStream_t st = (hipStream_t)stream;
+    int64_t P = kv->len;
+    for (int off = 0; off < n; off += T) {
+        const int cn = std::min(T, n - off);
+        DG_TRY(dg::launch_embed(m->embed, m->cfg.act_dtype == DG_F32, m->cfg.d_model, tokens + off, cn, w.X, nullptr,
+                                st),
+               "embed");
+        if (dg_status s = encoder_chunk(m, w, cn, kv, P, st)) return s;
+        P += cn;
+    }
+    kv->len = P;
+    return DG_OK;
+}
+
+dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, int32_t step_idx, uint64_t seed,
+                         const dg_sampler_cfg* scfg, dg_step_stats* stats, void* ws, size_t ws_bytes,
+                         void* stream) {
+    if (!m) return fail(DG_E_INVALID, "model is NULL");
+    if (dg_status s = check_sampler_cfg(scfg)) return s;
+    if (!canvas) return fail(DG_E_INVALID, "canvas is NULL");
+    const int n = canvas->n;
+    if (n < 1 || n > m->cfg.max_canvas) return fail(DG_E_SHAPE, "canvas n outside 1..max_canvas");
+    if (dg_status s = check_canvas(canvas, n)) return s;
+    if (dg_status s = check_kv(m, kv)) return s;
+    if (dg_status s = check_logits(m, stats, n)) return s;
+    if (step_idx < -1 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
+    Work w;
+    if (dg_status s = ws_for(m, ws, ws_bytes, n, &w)) return s;
+    hipStream_t st = (hipStream_t)stream;
+    const dg::SamplerParams sp = to_params(scfg);
+    const dg_config& c = m->cfg;
+    DG_TRY(dg::launch_embed(m->embed, c.act_dtype == DG_F32, c.d_model, canvas->tokens, n, w.X, canvas->state, st),
+           "embed");
+    for (int l = 0; l < c.n_layers; ++l)
+        if (dg_status s = decoder_layer(m, l, w, n, kv, canvas->state, st)) return s;
+    if (dg_status s = lm_head(m, w, n, sp, step_idx, canvas->state, canvas->bias_tok, canvas->bias_val, stats, st))
+        return s;
+    return hip_check(dg::launch_sampler_tail(stats->logits, c.act_dtype == DG_F32, stats->logits_ld, n, c.vocab,
+                                             c.mask_id, canvas->bias_tok, canvas->bias_val, stats->entropy,
+                                             stats->argmax, canvas->state, step_idx, sp, seed, canvas->canvas_idx,
+                                             canvas->tokens, canvas->committed, canvas->prev_argmax, stats->selected,
+                                             w.sel_list, w.chunk_sum, stats->mean_entropy, st),
+                     "sampler tail");
+}
+
+dg_status dg_generate_canvas(const dg_model* m, dg_canvas* canvas, dg_kv* kv, const dg_sampler_cfg* scfg,
+                             uint64_t seed, int32_t append_after, int32_t poll_every, dg_step_stats* stats,
+                             int32_t* steps_taken, void* ws, size_t ws_bytes, void* stream) {
+    if (!m || !canvas || !steps_taken) return fail(DG_E_INVALID, "NULL argument");
+    if (dg_status s = check_sampler_cfg(scfg)) return s;
+    if (poll_every < 1) return fail(DG_E_INVALID, "poll_every must be >= 1");
+    if (dg_status s = check_canvas(canvas, canvas->n)) return s;
+    if (dg_status s = check_kv(m, kv)) return s;
+    if (append_after && kv->len + canvas->n > kv->capacity) return fail(DG_E_CAPACITY, "kv cache full");
+    hipStream_t st = (hipStream_t)stream;
+    if (dg_status s = dg_canvas_reset(canvas, m->cfg.mask_id, stream)) return s;
+    int32_t hstate[DG_STATE_WORDS] = {0};
+    for (int t = 0; t < scfg->max_steps; ++t) {
+        if (dg_status s = dg_canvas_step(m, canvas, kv, t, seed, scfg, stats, ws, ws_bytes, stream)) return s;
+        if ((t + 1) % poll_every == 0 || t + 1 == scfg->max_steps) {
+            DG_TRY(hipMemcpyAsync(hstate, canvas->state, sizeof hstate, hipMemcpyDeviceToHost, st), "read state");
+            DG_TRY(hipStreamSynchronize(st), "sync");
+            if (hstate[DG_ST_DONE]) break;
+        }
+    }
+    DG_TRY(hipMemcpyAsync(hstate, canvas->state, sizeof hstate, hipMemcpyDeviceToHost, st), "read state");
+    DG_TRY(hipStreamSynchronize(st), "sync");
+    *steps_taken = hstate[DG_ST_STEP];
+    if (append_after) {
+        if (dg_status s = dg_prefill_append(m, kv, canvas->tokens, canvas->n, ws, ws_bytes, stream)) return s;
+    }
+    return DG_OK;
+}
+
+}  // extern "C"

@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
     const int32_t* __restrict__ state, int step_override, SamplerParams sp, int mask_id,
     const int32_t* __restrict__ bias_tok, const float* __restrict__ bias_val,
     RowPart* __restrict__ parts, int nsplit) {
-    if (state[0]) return;
+    if (state && state[0]) return;
     constexpr int PER = 8;
     const int row = blockIdx.y;
     const int sp_i = blockIdx.x;
@@ -170,7 +170,7 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
 __global__ void __launch_bounds__(256) merge_rows_kernel(
     const RowPart* __restrict__ parts, int n, int nsplit, const int32_t* __restrict__ state,
     float* __restrict__ H, float* __restrict__ lse, int32_t* __restrict__ amax) {
-    if (state[0]) return;
+    if (state && state[0]) return;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= n) return;
@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(1024) eb_select_kernel(
     const float* __restrict__ H, const uint8_t* __restrict__ committed, int n,
     int32_t* __restrict__ state, SamplerParams sp, uint8_t* __restrict__ selected,
     int32_t* __restrict__ sel_list) {
-    if (state[0]) return;
+    if (state && state[0]) return;
     __shared__ unsigned long long key[1024];
     __shared__ float hs[1024];
     __shared__ int kstar;
@@ -326,7 +326,7 @@ __global__ void __launch_bounds__(256) draw_chunks_kernel(
     const int32_t* __restrict__ bias_tok, const float* __restrict__ bias_val,
     const int32_t* __restrict__ sel_list, const int32_t* __restrict__ amax,
     const int32_t* __restrict__ state, int step_override, SamplerParams sp, double* __restrict__ chunk_sum) {
-    if (state[0]) return;
+    if (state && state[0]) return;
     const int nchunk = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
     const int k = state[4];
     const int t = step_override >= 0 ? step_override : state[1];
@@ -356,7 +356,7 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
     const int32_t* __restrict__ state, int step_override, SamplerParams sp,
     uint32_t seed_lo, uint32_t seed_hi, int canvas_idx, const double* __restrict__ chunk_sum,
     int32_t* __restrict__ tokens, uint8_t* __restrict__ committed) {
-    if (state[0]) return;
+    if (state && state[0]) return;
     const int r = blockIdx.x;
     if (r >= state[4]) return;
     const int nchunk = (V + DRAW_CHUNK - 1) / DRAW_CHUNK;
@@ -450,7 +450,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(
     int32_t* __restrict__ state, int step_override, SamplerParams sp,
     int32_t* __restrict__ tokens, uint8_t* __restrict__ committed, int32_t* __restrict__ prev_amax,
     double* __restrict__ mean_out) {
-    if (state[0]) return;
+    if (state && state[0]) return;
     const int tid = threadIdx.x;
     const int t = step_override >= 0 ? step_override : state[1];
     __shared__ int diff, ncom;

@@ -100,6 +100,9 @@ typedef struct dg_step_stats {
     int32_t* argmax;       /* lowest id on ties, MASK excluded */
     uint8_t* selected;     /* 1 where the EB selection committed this step */
     double* mean_entropy;  /* [1] canvas-mean entropy used by the stop test */
+    void* logits;          /* dg_canvas_step: [n][logits_ld] logits of record (act dtype), written;
+                              dg_sampler_step: unused */
+    int64_t logits_ld;
 } dg_step_stats;
 
 /* Library version string. */
@@ -157,6 +160,145 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
                           int32_t n, int32_t vocab, int64_t ld, int32_t mask_id, dg_canvas* canvas,
                           int32_t step_idx, uint64_t seed, dg_step_stats* stats, void* ws,
                           size_t ws_bytes, void* stream);
+
+
+/* ------------------------------------------------------------------------
+ * Model geometry. The spec table of the model card fixes the counts (30
+ * layers, 1024-token window, 128 experts with 8 active plus 1 shared, 262K
+ * vocabulary, canvas 256); widths are configuration. Layer l is global
+ * (sees the whole cache) iff global_every > 0 and l % global_every ==
+ * global_every - 1; other layers see the last `window` cache rows.
+ * ------------------------------------------------------------------------ */
+typedef struct dg_config {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;     /* 64, 128 or 256 */
+    int32_t n_experts;    /* routed experts (<= 512); the shared expert is extra */
+    int32_t top_k;        /* <= 16 */
+    int32_t ffn_hidden;   /* SwiGLU hidden width of every expert */
+    int32_t vocab;
+    int32_t mask_id;      /* placeholder token; excluded from the output distribution */
+    int32_t max_canvas;   /* largest canvas (<= 1024) */
+    int32_t window;
+    int32_t global_every;
+    int32_t weight_dtype; /* DG_F32, DG_BF16 or DG_FP8_E4M3: projection and expert matrices */
+    int32_t act_dtype;    /* DG_F32 or DG_BF16: activations, KV cache, embedding, router, logits */
+    float rope_base;
+    float norm_eps;
+} dg_config;
+
+/* One layer's weights (device). Matrices are [out][in], `in` contiguous.
+ *   wqkv   [(Hq + 2 Hkv) hd][d]   rows: query heads, key heads, value heads
+ *   wo     [d][Hq hd]
+ *   router [E][d] (act dtype), router_bias [E] f32
+ *   w_gate, w_up [E + 1][F][d]; w_down [E + 1][d][F]; expert E is the shared one
+ *   *_scale: DG_FP8_E4M3 only, bf16 per output row ([rows] / [E + 1][rows])
+ *   attn_norm, moe_norm [d] f32 RMSNorm weights */
+typedef struct dg_layer_weights {
+    const float* attn_norm;
+    const float* moe_norm;
+    const void* wqkv;
+    const void* wo;
+    const void* router;
+    const float* router_bias;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    const void* wqkv_scale;
+    const void* wo_scale;
+    const void* gate_scale;
+    const void* up_scale;
+    const void* down_scale;
+} dg_layer_weights;
+
+/* Whole-model weights: the tied embedding / LM-head matrix [vocab][d] (act
+ * dtype), the final RMSNorm weight [d] f32, and n_layers layer records
+ * (host array, copied by dg_model_create). */
+typedef struct dg_weights {
+    const void* embed;
+    const float* final_norm;
+    const dg_layer_weights* layers;
+} dg_weights;
+
+/* KV cache: per layer (host arrays of n_layers device pointers) K and V of
+ * [n_kv_heads][capacity][head_dim] in the act dtype, keys after RoPE. Rows
+ * [0, len) are filled; dg_prefill_append advances len on the host. */
+typedef struct dg_kv {
+    void* const* k;
+    void* const* v;
+    int64_t capacity;
+    int64_t len;
+} dg_kv;
+
+typedef struct dg_model dg_model;
+
+/* Validate the configuration and weight pointers and create a host-side
+ * handle (no device memory is allocated; the weights are borrowed). */
+dg_status dg_model_create(const dg_config* cfg, const dg_weights* w, dg_model** out);
+void dg_model_destroy(dg_model* m);
+
+/* Workspace bytes for steps over up to max_rows canvas rows, or prefill
+ * chunks of max_rows tokens (1 <= max_rows <= 4096). Larger workspaces let
+ * dg_prefill_append use larger chunks. */
+size_t dg_workspace_bytes(const dg_model* m, int32_t max_rows);
+
+/*
+ * dg_prefill_append - the encoder (model card zh-TW, overview: the encoder
+ * prefills the prompt into the KV cache; a finished canvas is run through the
+ * encoder and appended). Runs n tokens (device int32, positions kv->len ..
+ * kv->len + n - 1) through the layers with causal attention (a per-query
+ * sliding window on local layers) and appends every layer's rotated K and V
+ * at rows kv->len ..; the last layer's attention output and MoE are skipped.
+ * Tokens are processed in chunks of the workspace's max_rows. Updates
+ * kv->len on the host when enqueued. DG_E_CAPACITY if len + n > capacity.
+ */
+dg_status dg_prefill_append(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t n, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
+ * dg_canvas_step - one denoising step (model card zh-TW, overview and best
+ * practice 1): the decoder over all canvas positions at once against the KV
+ * cache rows [0, kv->len) (canvas positions kv->len ..), the tied LM head
+ * with the fused tempered statistics (logits of record are written to
+ * stats->logits), then the EB sampler step exactly as dg_sampler_step.
+ * step_idx as in dg_sampler_step. The canvas K/V are not cached.
+ */
+dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, int32_t step_idx,
+                         uint64_t seed, const dg_sampler_cfg* scfg, dg_step_stats* stats, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * dg_generate_canvas - denoise one canvas to completion (model card zh-TW,
+ * overview: block-autoregressive multi-canvas sampling): reset the canvas to
+ * all-MASK, run dg_canvas_step for t = 0, 1, ... until the device marks it
+ * finished (at most max_steps), then, if append_after != 0, run the finished
+ * tokens through the encoder with dg_prefill_append. Synchronises on
+ * `stream` every `poll_every` steps (>= 1) to read the done flag; returns
+ * the number of steps taken in *steps_taken (host).
+ */
+dg_status dg_generate_canvas(const dg_model* m, dg_canvas* canvas, dg_kv* kv, const dg_sampler_cfg* scfg,
+                             uint64_t seed, int32_t append_after, int32_t poll_every, dg_step_stats* stats,
+                             int32_t* steps_taken, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Component entry points (the stages of dg_canvas_step, exposed so each can
+ * be checked on its own; same validation and ownership rules):
+ *   dg_embed:          X[i][:] = embed[tokens[i]][:]                 (X f32 [n][d])
+ *   dg_decoder_layer:  X <- decoder layer `layer` over n canvas rows at
+ *                      positions kv->len .. (X f32 [n][d], in place); if
+ *                      route_ids/route_gates are not NULL the router's top-k
+ *                      ids (int32 [n][k]) and gates (f32 [n][k]) are copied out
+ *   dg_lm_head:        logits and tempered statistics of rmsnorm(X) for step
+ *                      step_idx (no selection): stats->logits, entropy, lse, argmax
+ */
+dg_status dg_embed(const dg_model* m, const int32_t* tokens, int32_t n, float* X, void* stream);
+dg_status dg_decoder_layer(const dg_model* m, int32_t layer, float* X, int32_t n, const dg_kv* kv,
+                           int32_t* route_ids, float* route_gates, void* ws, size_t ws_bytes, void* stream);
+dg_status dg_lm_head(const dg_model* m, const float* X, int32_t n, const dg_sampler_cfg* scfg, int32_t step_idx,
+                     const int32_t* bias_tok, const float* bias_val, dg_step_stats* stats, void* ws,
+                     size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

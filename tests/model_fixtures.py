@@ -1,0 +1,71 @@
+"""Builders shared by the model parity tests: seeded weights on the device for
+the HIP path and the same tensors widened for the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import model as M
+from synth import workloads as wl
+
+# reduced bf16 geometry: windowed and global layers, GQA 2:1, several tiles
+SMALL_BF16 = wl.FULL_LAYER.replace(
+    name="small_bf16", n_layers=2, d_model=512, n_q_heads=4, n_kv_heads=2, head_dim=128,
+    n_experts=16, top_k=4, ffn_hidden=256, vocab=4096, canvas=64, window=128, global_every=2)
+
+
+def device_model(B, cfg, device="cuda"):
+    embed = wl.embedding(cfg, device=device)
+    fnorm = wl.final_norm(cfg, device=device)
+    layers = [wl.layer_weights(cfg, l, device=device) for l in range(cfg.n_layers)]
+    return B.Model(cfg, embed, fnorm, layers)
+
+
+def oracle_weights(model):
+    cfg = model.cfg
+    layers = [{k: v.cpu() for k, v in L.items()} for L in model.layers]
+    return M.Weights(cfg, model.embed.cpu(), model.final_norm.cpu(), lambda l: layers[l])
+
+
+def fill_synthetic_kv(kv, cfg, P):
+    """Cache rows [0, P) of every layer from the synthetic KV generator."""
+    for l in range(cfg.n_layers):
+        k, v = wl.synthetic_kv(cfg, l, P, device=kv.k[l].device)
+        kv.k[l][:, :P] = k
+        kv.v[l][:, :P] = v
+    kv.length = P
+
+
+def oracle_kv_from_device(kv, cfg, P):
+    okv = M.KVCache.empty(cfg)
+    for l in range(cfg.n_layers):
+        okv.K[l] = kv.k[l][:, :P].float().cpu().numpy().astype(np.float64)
+        okv.V[l] = kv.v[l][:, :P].float().cpu().numpy().astype(np.float64)
+    return okv
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def rel_l2_rows(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-30)
+
+
+def routing_near_tie_ok(r, ids_gpu, ids_ora, tol):
+    """Rows where the two top-k sets differ must have the oracle's logits of
+    the differing experts within ``tol`` of its own k-th largest logit."""
+    bad = []
+    for i in range(ids_gpu.shape[0]):
+        a, b = set(ids_gpu[i].tolist()), set(ids_ora[i].tolist())
+        if a == b:
+            continue
+        kth = np.sort(r[i])[::-1][ids_gpu.shape[1] - 1]
+        for e in a ^ b:
+            if abs(r[i, e] - kth) > tol:
+                bad.append((i, e, r[i, e], kth))
+    return bad

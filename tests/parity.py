@@ -43,3 +43,42 @@ def rel_l2_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return np.linalg.norm(a - b, axis=-1) / np.maximum(np.linalg.norm(b, axis=-1), 1e-30)
+
+
+def check_sampler_step(B, st, ocfg, L, t, seed, canvas_idx, stats, canvas, ent_tol=ENT_TOL):
+    """Compare one GPU sampler step with the oracle fed the same (biased) logits.
+
+    ``st`` is the oracle CanvasState before the step; it is advanced in place
+    (adopting the GPU's tokens only where a draw is an excused near-tie).
+    Returns the oracle's StepRecord."""
+    tau = S.temperature(t, ocfg)
+    H, a, M, Ssum = S.row_stats(L, tau, ocfg.mask_id)
+    Hg = stats.entropy.cpu().numpy()
+    ag = stats.argmax.cpu().numpy().astype(np.int64)
+    assert np.max(np.abs(Hg - H)) < ent_tol, (t, np.max(np.abs(Hg - H)))
+    lse = stats.lse.cpu().numpy()
+    assert np.max(np.abs(lse - (M + np.log(Ssum)))) < 1e-4 * max(1.0, float(np.abs(M).max()))
+    z = S.tempered(L, tau, ocfg.mask_id)
+    for i in np.nonzero(ag != a)[0]:
+        assert argmax_ok(z[i], int(ag[i]), int(a[i])), (t, i, ag[i], a[i])
+    rec = S.sampler_step(st, L, t, ocfg, seed, H32_override=Hg, argmax_override=ag)
+    sel_g = stats.selected.cpu().numpy().astype(bool)
+    assert np.array_equal(sel_g, rec.selected), t
+    tok_g = canvas.tokens.cpu().numpy().astype(np.int64)
+    for i in np.nonzero(tok_g != st.tokens)[0]:
+        assert rec.selected[i], (t, i)
+        u = S.draw_uniform(seed, int(i), t, canvas_idx)
+        assert draw_is_near_tie(L[i], tau, ocfg.mask_id, u), (t, i, tok_g[i], st.tokens[i])
+        st.tokens[i] = tok_g[i]
+    assert np.array_equal(canvas.committed.cpu().numpy().astype(bool), st.committed)
+    state = canvas.state.cpu().numpy()
+    assert state[B.ST_DONE] == int(st.done)
+    assert state[B.ST_STEP] == t + 1
+    assert state[B.ST_STABLE] == st.stable
+    assert state[B.ST_STOP] == int(rec.stop)
+    assert state[B.ST_FINISHED] == int(rec.finished)
+    assert state[B.ST_SELECTED] == int(rec.selected.sum())
+    assert stats.mean_entropy.item() == rec.mean_H
+    assert np.array_equal(canvas.prev_argmax.cpu().numpy(), ag)
+    assert np.array_equal(tok_g, st.tokens)
+    return rec
