@@ -1,12 +1,23 @@
 """Benchmark of the canvas denoising hot path on one MI355X.
 
-Prints one JSON line: denoise steps/s (value), committed tokens/s, the
-dominant kernel's roofline figures (HIP-event timed inside the run) and the
-CPU oracle timed on a bounded sample of the same workload on the host cores.
+Prints one JSON line. A step is one dg_canvas_step: the decoder over the
+256-token canvas (every layer: norm, QKV, RoPE, joint canvas+prefix
+attention, output projection, router, expert permutation, grouped SwiGLU
+experts, combine), the tied 262144-way LM head with the fused tempered
+statistics, and the EB sampler (selection, Philox draws, re-mask, stop).
+Canvases run back to back: every canvas starts all-MASK and, once finished,
+is run through the encoder and appended to the KV cache (inside the timed
+region). `value` = timed steps / timed wall time (HIP-synchronised);
+committed tokens/s = canvas tokens finalised in the timed region / its time.
 
-Workloads (synthetic, seeded):
-  sampler   EB sampler only: bf16 logits [256][262144] N(0,1) plus a per-row
-            peak U(0,16), one fresh tensor per step from 4 rotating buffers.
+Workloads (synthetic, seeded; random-init weights ~N(0, 0.02)):
+  stack30   30 layers, d=2816, 16 q / 8 kv heads of 256, 128 experts top-8 +
+            1 shared (F=704), Zipf(1.1) router bias, 262144 vocab, bf16,
+            25 local (window 1024) + 5 global layers, 8192-token prompt
+            prefilled by the encoder, 4 canvases of 256 (default)
+  one_layer the same widths with 1 layer, 4096-token prompt
+  sampler   EB sampler only on bf16 logits [256][262144]
+  tiny      2 layers, d=256, fp32, vocab 4096, canvas 32, 128-token prompt
 """
 from __future__ import annotations
 
@@ -21,17 +32,145 @@ sys.path.insert(0, ROOT)
 
 METRIC = "denoise steps/s and committed tokens/s, 256-token canvas, batch 1; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 SEED = 0x5EED
 
 
-def _events_ms(fn, torch):
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+def _cores():
+    try:
+        import threadpoolctl
+        n = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+        return int(n)
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _sync_ms(fn, torch):
     torch.cuda.synchronize()
-    s.record()
+    t0 = time.perf_counter()
     fn()
-    e.record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e)
+    return (time.perf_counter() - t0) * 1e3
+
+
+# --------------------------------------------------------------------------
+# model workloads
+# --------------------------------------------------------------------------
+
+def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
+    from synth import workloads as wl
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    embed = wl.embedding(cfg, device=dev)
+    fnorm = wl.final_norm(cfg, device=dev)
+    layers = [wl.layer_weights(cfg, l, device=dev) for l in range(cfg.n_layers)]
+    model = B.Model(cfg, embed, fnorm, layers)
+    torch.cuda.synchronize()
+    t_weights = time.perf_counter() - t0
+    n = cfg.canvas
+    steps_per_canvas = 48
+    n_canv = -(-(args.warmup + args.steps) // steps_per_canvas) + 1
+    kv = B.KVCache(model, prompt_len + n * n_canv)
+    ws = model.workspace(1024)
+    prompt = wl.prefix_tokens(cfg, prompt_len).to(dev)
+    ms_prefill = _sync_ms(lambda: B.prefill_append(model, kv, prompt, ws), torch)
+    canvas = B.Canvas(n, cfg.mask_id, 0, dev)
+    stats = B.StepStats(n, device=dev, vocab=cfg.vocab, logits_dtype=model.act_dtype)
+    scfg = B.sampler_default()
+    sched = {"t": 0, "canvas": 0, "committed": 0}
+
+    def run(K):
+        for _ in range(K):
+            if sched["t"] == 0:
+                canvas.canvas_idx = sched["canvas"]
+                canvas.reset()
+            B.canvas_step(model, canvas, kv, sched["t"], SEED, scfg, stats, ws)
+            sched["t"] += 1
+            done = bool(canvas.state[B.ST_DONE].item())
+            if done or sched["t"] == scfg.max_steps:
+                B.prefill_append(model, kv, canvas.tokens, ws)
+                sched["committed"] += n
+                sched["canvas"] += 1
+                sched["t"] = 0
+
+    run(args.warmup)
+    c0 = sched["committed"]
+    ms = _sync_ms(lambda: run(args.steps), torch)
+    committed = sched["committed"] - c0
+    # dominant-kernel timing: a second pass over the same kind of steps with
+    # HIP events bracketing the LM-head GEMM on the stream it runs on
+    B.timing_enable(1)
+    run(min(args.steps, 48))
+    torch.cuda.synchronize()
+    tot_ms, launches = B.timing_read()
+    B.timing_enable(0)
+    kern_ms = tot_ms / max(launches, 1)
+    V, d = cfg.vocab, cfg.d_model
+    eb = 2 if cfg.act_dtype == "bf16" else 4
+    lm_bytes = V * d * eb + n * d * eb                 # E once + normed activations
+    lm_flops = 2.0 * n * V * d
+    achieved_gbs = lm_bytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "ms_per_step": ms / args.steps,
+        "committed_tokens": committed,
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "lm_head (gemm_kernel EPI_LMHEAD)", "kernel_ms": round(kern_ms, 4),
+                     "algorithmic_bytes_per_launch": lm_bytes,
+                     "mfma_tflops": round(lm_flops / (kern_ms * 1e-3) / 1e12, 1),
+                     "mfma_frac": round(lm_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "extra": {"prefill_tokens": prompt_len, "prefill_ms": round(ms_prefill, 2),
+                  "prefill_tokens_per_s": round(prompt_len / ms_prefill * 1e3, 1),
+                  "weights_setup_s": round(t_weights, 1), "kv_len_end": kv.length},
+        "dtype": cfg.act_dtype,
+    }
+    return res, (model, kv, ws, canvas, stats)
+
+
+def bench_stack(args, torch, B, which):
+    from synth import workloads as wl
+    cfg = {"stack30": wl.STACK30, "one_layer": wl.FULL_LAYER, "tiny": wl.TINY}[which]
+    plen = {"stack30": 8192, "one_layer": 4096, "tiny": wl.TINY_PREFIX}[which]
+    res, handles = _model_workload(args, torch, B, cfg, plen, 8)
+    res["config"] = {"workload": f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}", "layers": cfg.n_layers,
+                     "d_model": cfg.d_model, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
+                     "experts": f"{cfg.n_experts} top-{cfg.top_k} + 1 shared, F={cfg.ffn_hidden}",
+                     "vocab": cfg.vocab, "canvas": cfg.canvas, "batch": 1, "window": cfg.window,
+                     "global_every": cfg.global_every, "prompt": plen}
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_model_step(cfg, handles, torch, B, plen)
+    return res
+
+
+def cpu_model_step(cfg, handles, torch, B, plen):
+    """The oracle on one decoder layer plus the LM head (float64 numpy), on the
+    canvas state and KV the GPU run left, extrapolated to all layers."""
+    import numpy as np
+    from oracle import model as M
+    from oracle import sampler as S
+    model, kv, ws, canvas, stats = handles
+    P = kv.length
+    n = cfg.canvas
+    W = M.Weights(cfg, model.embed.cpu(), model.final_norm.cpu(),
+                  lambda l: {k: v.cpu() for k, v in model.layers[l].items()})
+    toks = canvas.tokens.cpu().numpy()
+    X = W.E[toks].copy()
+    Kl = kv.k[0][:, :P].float().cpu().numpy().astype(np.float64)
+    Vl = kv.v[0][:, :P].float().cpu().numpy().astype(np.float64)
+    W.layer(0)
+    t0 = time.perf_counter()
+    X1 = M.decoder_layer(X, W.layer(0), Kl, Vl, 0, cfg)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    L = M.lm_logits(X1, W.final_norm, W.E, cfg.norm_eps)
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    st = S.CanvasState.fresh(n, cfg.mask_id)
+    S.sampler_step(st, L, 0, ocfg, SEED)
+    t_head = time.perf_counter() - t0
+    step_s = t_layer * cfg.n_layers + t_head
+    return {"value": round(1.0 / step_s, 5), "unit": "denoise steps/s", "cores": _cores(), "kind": "oracle",
+            "sample": (f"1 decoder layer ({t_layer:.2f} s) + LM head and sampler ({t_head:.2f} s), float64 numpy, "
+                       f"extrapolated to {cfg.n_layers} layers; canvas {n}, KV {P} rows")}
 
 
 # --------------------------------------------------------------------------
@@ -48,7 +187,6 @@ def bench_sampler(args, torch, B):
     stats = B.StepStats(n, dev)
     ws = torch.empty(B.sampler_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
     cfg = B.sampler_default()
-    committed = [0]
 
     def run(k0, K):
         for k in range(k0, k0 + K):
@@ -58,24 +196,19 @@ def bench_sampler(args, torch, B):
             B.sampler_step(cfg, bufs[k % 4], mask, canvas, t, SEED, stats, ws)
 
     run(0, args.warmup)
-    torch.cuda.synchronize()
-    c0 = 0
+    ms = _sync_ms(lambda: run(args.warmup, args.steps), torch)
     B.timing_enable(1)
-    ms = _events_ms(lambda: run(args.warmup, args.steps), torch)
+    run(args.warmup + args.steps, args.steps)
+    torch.cuda.synchronize()
     tot_ms, launches = B.timing_read()
     B.timing_enable(0)
-    # committed tokens over the timed steps: replay the count on the host side
-    # from the state words is not possible after resets, so count per canvas:
-    # every 48 steps finalise all n positions.
     full = sum(1 for k in range(args.warmup, args.warmup + args.steps) if k % 48 == 47)
-    committed_tokens = full * n
-    del c0, committed
     bytes_per_launch = n * V * 2
     kern_ms = tot_ms / max(launches, 1)
     achieved = bytes_per_launch / (kern_ms * 1e-3) / 1e9
     res = {
         "ms_per_step": ms / args.steps,
-        "committed_tokens": committed_tokens,
+        "committed_tokens": full * n,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "logit_stats_kernel", "kernel_ms": round(kern_ms, 5),
@@ -85,58 +218,46 @@ def bench_sampler(args, torch, B):
         "dtype": "bf16",
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_sampler(bufs, n, V, mask, torch)
+        import numpy as np
+        from oracle import sampler as S
+        ocfg = S.SamplerConfig(mask_id=mask)
+        Ls = [b.float().cpu().numpy() for b in bufs[:2]]
+        st = S.CanvasState.fresh(n, mask)
+        times = []
+        t_end = time.perf_counter() + 12.0
+        t = 0
+        while time.perf_counter() < t_end or len(times) < 2:
+            t0 = time.perf_counter()
+            S.sampler_step(st, Ls[t % 2], t, ocfg, SEED)
+            times.append(time.perf_counter() - t0)
+            t += 1
+            if st.done:
+                st = S.CanvasState.fresh(n, mask)
+                t = 0
+        res["cpu_baseline"] = {"value": round(1.0 / float(np.median(times)), 4), "unit": "denoise steps/s",
+                               "cores": _cores(), "kind": "oracle",
+                               "sample": f"{len(times)} sampler steps (float64 numpy) on the same logits; median"}
     return res
-
-
-def cpu_sampler(bufs, n, V, mask, torch):
-    import numpy as np
-    from oracle import sampler as S
-    cfg = S.SamplerConfig(mask_id=mask)
-    Ls = [b.float().cpu().numpy() for b in bufs[:2]]
-    st = S.CanvasState.fresh(n, mask)
-    times = []
-    t_end = time.perf_counter() + 12.0
-    t = 0
-    while time.perf_counter() < t_end or len(times) < 2:
-        t0 = time.perf_counter()
-        S.sampler_step(st, Ls[t % 2], t, cfg, SEED)
-        times.append(time.perf_counter() - t0)
-        t += 1
-        if st.done:
-            st = S.CanvasState.fresh(n, mask)
-            t = 0
-    med = float(np.median(times))
-    return {"value": round(1.0 / med, 4), "unit": "denoise steps/s", "cores": _cores(), "kind": "oracle",
-            "sample": f"{len(times)} sampler steps (float64 numpy) on 256x262144 bf16 logits; median"}
-
-
-def _cores():
-    import numpy as np  # noqa: F401
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        n = max((i.get("num_threads", 1) for i in info), default=1)
-        return int(n)
-    except Exception:
-        return len(os.sched_getaffinity(0))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=96)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="sampler", choices=["sampler"])
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the denoising step is sized for a single MI355X)", file=sys.stderr)
+        print("bench.py measures one GPU: the denoising step here is built for a single MI355X "
+              "and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
     from discrete_text_diffusion_canvas_amd import binding as B
-    res = bench_sampler(args, torch, B)
+    if args.workload == "sampler":
+        res = bench_sampler(args, torch, B)
+    else:
+        res = bench_stack(args, torch, B, args.workload)
     ms = res.pop("ms_per_step")
     committed = res.pop("committed_tokens")
     total_s = ms * args.steps / 1e3
@@ -147,7 +268,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(ms, 4),
         "committed_tokens_per_s": round(committed / total_s, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -157,9 +278,10 @@ def main():
         "config": res.pop("config"),
         "roofline": res.pop("roofline"),
     }
-    if "cpu_baseline" in res:
-        out["cpu_baseline"] = res.pop("cpu_baseline")
-    print(json.dumps(out))
+    for k in ("cpu_baseline", "extra"):
+        if k in res:
+            out[k] = res.pop(k)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

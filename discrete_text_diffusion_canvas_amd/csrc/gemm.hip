@@ -345,6 +345,9 @@ static hipError_t launch_small_m(const GemmArgs& g, int groups, hipStream_t st) 
 
 hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int shape,
                        hipStream_t st) {
+    // weight-streaming contractions: the split-K streaming kernel (g.M bounds
+    // the rows per group in grouped mode)
+    if (epi != EPI_LMHEAD && shape != SHAPE_LDS) return stream_gemm_launch(g, act_f32, w_fp8, epi, groups, g.M, st);
 #define DG_DISPATCH(EPIV)                                                                              \
     if (epi == EPIV) {                                                                                 \
         if (act_f32) return shape == SHAPE_SMALL_M ? launch_small_m<float, WK_SAME, EPIV>(g, groups, st) \
@@ -361,7 +364,7 @@ hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int g
 #undef DG_DISPATCH
     if (epi == EPI_LMHEAD) {
         if (act_f32) return launch_cfg<2, 2, 4, 4, 32, float, WK_SAME, EPI_LMHEAD>(g, 0, st);
-        return launch_cfg<2, 2, 8, 8, 32, uint16_t, WK_SAME, EPI_LMHEAD>(g, 0, st);
+        return launch_lmhead_bf16(g, st);
     }
     return hipErrorInvalidValue;
 }

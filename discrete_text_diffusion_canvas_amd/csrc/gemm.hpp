@@ -9,7 +9,7 @@ namespace dg {
 
 enum { WK_SAME = 0, WK_FP8 = 1 };
 enum { EPI_STORE_F32 = 0, EPI_STORE_BF16 = 1, EPI_RESIDUAL = 2, EPI_SWIGLU = 3, EPI_LMHEAD = 4 };
-enum { SHAPE_PROJ = 0, SHAPE_SMALL_M = 1 };
+enum { SHAPE_PROJ = 0, SHAPE_SMALL_M = 1, SHAPE_LDS = 2 };
 
 struct GemmArgs {
     // A: activations [rows][K] (f32 or bf16), row stride lda; optional gather
@@ -24,7 +24,8 @@ struct GemmArgs {
     const uint16_t* w_scale;        // fp8: bf16 scale per output row (per group)
     const uint16_t* w2_scale;
     int64_t scale_group_stride;
-    int M, N, K;                    // M: rows (non-grouped); N: output columns (SwiGLU: 2F)
+    int M, N, K;                    // M: rows (non-grouped) / bound on rows per group (grouped);
+                                    // N: output columns (SwiGLU: 2F)
     const int32_t* group_offsets;   // grouped: group g owns rows [off[g], off[g+1])
     // outputs
     void* C;                        // [rows][ldc]
@@ -46,6 +47,9 @@ struct GemmArgs {
 
 hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int shape,
                        hipStream_t st);
+hipError_t launch_lmhead_bf16(const GemmArgs& g, hipStream_t st);
+hipError_t stream_gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int max_rows,
+                              hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // LM-head epilogue: logits of record (accumulator rounded to the storage

@@ -33,7 +33,7 @@ namespace {
 constexpr int MAX_SPLITS = 16;
 constexpr int SPLIT_ROWS = 256;  // partial buffers hold MAX_SPLITS x SPLIT_ROWS query rows
 
-int lm_bn(const dg_config& c) { return c.act_dtype == DG_F32 ? 128 : 256; }
+int lm_bn(const dg_config& c) { return 128; }
 int lm_nsplit(const dg_config& c) { return (c.vocab + lm_bn(c) - 1) / lm_bn(c); }
 size_t act_bytes(const dg_config& c) { return c.act_dtype == DG_F32 ? 4 : 2; }
 bool is_global(const dg_config& c, int l) { return c.global_every > 0 && l % c.global_every == c.global_every - 1; }
@@ -139,7 +139,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         g.A = w.A; g.lda = d; g.a_rows = w.perm;
         g.W = L.w_gate; g.W2 = L.w_up; g.ldw = d; g.w_group_stride = (int64_t)F * d;
         g.w_scale = (const uint16_t*)L.gate_scale; g.w2_scale = (const uint16_t*)L.up_scale; g.scale_group_stride = F;
-        g.N = 2 * F; g.K = d; g.group_offsets = w.offsets;
+        g.M = n; g.N = 2 * F; g.K = d; g.group_offsets = w.offsets;
         g.C = w.Hbuf; g.ldc = F; g.c_f32 = f32; g.state = state;
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, dg::SHAPE_SMALL_M, st), "expert gate/up");
     }
@@ -148,7 +148,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         g.A = w.Hbuf; g.lda = F;
         g.W = L.w_down; g.ldw = F; g.w_group_stride = (int64_t)d * F;
         g.w_scale = (const uint16_t*)L.down_scale; g.scale_group_stride = d;
-        g.N = d; g.K = F; g.group_offsets = w.offsets;
+        g.M = n; g.N = d; g.K = F; g.group_offsets = w.offsets;
         g.C = w.Y; g.ldc = d; g.c_f32 = 1; g.state = state;
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_STORE_F32, E + 1, dg::SHAPE_SMALL_M, st), "expert down");
     }

@@ -1,0 +1,102 @@
+"""Parity at the full widths: one decoder layer of d=2816, 16/8 heads of 256,
+128 experts (top-8) plus the shared one, F=704, Zipf(1.1) router bias, the
+tied 262144 x 2816 LM head, a 256-token canvas and a 4096-row prefix KV built
+by the encoder. The oracle checks sampled KV rows, the layer output, the
+logits of every canvas row, the statistics and the sampler's decisions."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as M
+from oracle import sampler as S
+from synth import workloads as wl
+
+from model_fixtures import device_model, oracle_weights, rel_l2, rel_l2_rows, routing_near_tie_ok
+from parity import ENT_TOL, check_sampler_step
+
+pytestmark = pytest.mark.gpu
+
+SEED = 0x5EED
+PREFIX = 4096
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from discrete_text_diffusion_canvas_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def setup(B):
+    cfg = wl.FULL_LAYER
+    model = device_model(B, cfg)
+    kv = B.KVCache(model, PREFIX + cfg.canvas)
+    ws = model.workspace(1024)
+    prompt = wl.prefix_tokens(cfg, PREFIX).cuda()
+    B.prefill_append(model, kv, prompt, ws)
+    torch.cuda.synchronize()
+    W = oracle_weights(model)
+    return cfg, model, kv, ws, W, prompt
+
+
+def test_prefix_kv_rows_match_the_encoder(B, setup):
+    """With one layer, the cached K/V of a row depend on its token only."""
+    cfg, model, kv, ws, W, prompt = setup
+    assert kv.length == PREFIX
+    rows = np.array([0, 1, 17, 1023, 1024, 2047, 3000, PREFIX - 1])
+    toks = prompt.cpu().numpy()[rows]
+    L0 = W.layer(0)
+    a = M.rmsnorm(W.E[toks], L0["attn_norm"], cfg.norm_eps)
+    _, k, v = M.qkv(a, L0, cfg, rows)
+    kg = kv.k[0][:, rows].float().cpu().numpy().transpose(1, 0, 2)
+    vg = kv.v[0][:, rows].float().cpu().numpy().transpose(1, 0, 2)
+    assert rel_l2(kg, k) < 1e-2, rel_l2(kg, k)
+    assert rel_l2(vg, v) < 1e-2, rel_l2(vg, v)
+
+
+def test_full_width_layer_and_lm_head_step(B, setup):
+    cfg, model, kv, ws, W, prompt = setup
+    n = cfg.canvas
+    toks, com = wl.committed_canvas(cfg, 128)
+    # the layer on its own, with the router's choices checked
+    X = torch.empty(n, cfg.d_model, dtype=torch.float32, device="cuda")
+    B.embed(model, toks.cuda(), X)
+    X0 = X.cpu().numpy().astype(np.float64)
+    ids = torch.zeros(n, cfg.top_k, dtype=torch.int32, device="cuda")
+    B.decoder_layer(model, 0, X, kv, ws, ids)
+    torch.cuda.synchronize()
+    okv = M.KVCache([kv.k[0][:, :PREFIX].float().cpu().numpy().astype(np.float64)],
+                    [kv.v[0][:, :PREFIX].float().cpu().numpy().astype(np.float64)])
+    tr = {}
+    M.decoder_layer(X0, W.layer(0), okv.K[0], okv.V[0], 0, cfg, trace=tr)
+    ids_g = ids.cpu().numpy()
+    bad = routing_near_tie_ok(tr["router"], ids_g, tr["ids"], 1e-2)
+    assert not bad, bad[:5]
+    hit = len(np.unique(ids_g))
+    assert 20 < hit <= 128
+    Xo = M.decoder_layer(X0, W.layer(0), okv.K[0], okv.V[0], 0, cfg, ids_override=ids_g)
+    Xg = X.cpu().numpy()
+    assert rel_l2_rows(Xg, Xo).max() < 2e-2, rel_l2_rows(Xg, Xo).max()
+    assert rel_l2(Xg - X0, Xo - X0) < 3e-2, rel_l2(Xg - X0, Xo - X0)
+    # the whole step on the committed canvas, as the step would see it at t = 5
+    canvas = B.Canvas(n, cfg.mask_id, 0, "cuda")
+    canvas.tokens.copy_(toks.cuda())
+    canvas.committed.copy_(com.cuda())
+    stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=torch.bfloat16)
+    B.canvas_step(model, canvas, kv, 5, SEED, B.sampler_default(), stats, ws)
+    torch.cuda.synchronize()
+    Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+    Lo = M.lm_logits(Xo, W.final_norm, W.E, cfg.norm_eps)
+    err = rel_l2_rows(Lg, Lo)
+    assert err.max() < 2e-2, err.max()
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    st = S.CanvasState(tokens=toks.numpy().astype(np.int64), committed=com.numpy().astype(bool),
+                       prev_argmax=np.full(n, -1, np.int64), canvas_idx=0)
+    st.steps = 5
+    rec = check_sampler_step(B, st, ocfg, Lg, 5, SEED, 0, stats, canvas)
+    assert rec.selected.sum() >= 1
+    # entropies against the oracle's own float64 logits: the stated 1e-2 nats
+    Ho, _, _, _ = S.row_stats(Lo, S.temperature(5, ocfg), cfg.mask_id)
+    assert np.abs(stats.entropy.cpu().numpy() - Ho).max() < 1e-2
