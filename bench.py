@@ -156,7 +156,7 @@ def cpu_model_step(cfg, handles, torch, B, plen):
     toks = canvas.tokens.cpu().numpy()
     X = W.E[toks].copy()
     Kl = kv.k[0][:, :P].float().cpu().numpy().astype(np.float64)
-    Vl = kv.v[0][:, :P].float().cpu().numpy().astype(np.float64)
+    Vl = kv.v[0][:, :, :P].transpose(1, 2).float().cpu().numpy().astype(np.float64)
     W.layer(0)
     t0 = time.perf_counter()
     X1 = M.decoder_layer(X, W.layer(0), Kl, Vl, 0, cfg)

@@ -261,13 +261,16 @@ class Model:
 
 
 class KVCache:
-    """Per-layer K/V tensors [Hkv][capacity][hd] in the activation dtype."""
+    """Per-layer K [Hkv][capacity][hd] and transposed V [Hkv][hd][capacity]
+    (activation dtype, zero-filled); capacity is rounded up to a multiple of 64."""
 
     def __init__(self, model: Model, capacity: int, device="cuda"):
         c = model.cfg
-        shape = (c.n_kv_heads, capacity, c.head_dim)
-        self.k = [torch.zeros(shape, dtype=model.act_dtype, device=device) for _ in range(c.n_layers)]
-        self.v = [torch.zeros(shape, dtype=model.act_dtype, device=device) for _ in range(c.n_layers)]
+        capacity = (capacity + 63) // 64 * 64
+        kshape = (c.n_kv_heads, capacity, c.head_dim)
+        vshape = (c.n_kv_heads, c.head_dim, capacity)
+        self.k = [torch.zeros(kshape, dtype=model.act_dtype, device=device) for _ in range(c.n_layers)]
+        self.v = [torch.zeros(vshape, dtype=model.act_dtype, device=device) for _ in range(c.n_layers)]
         self.capacity = capacity
         self._kp = (C.c_void_p * c.n_layers)(*[t.data_ptr() for t in self.k])
         self._vp = (C.c_void_p * c.n_layers)(*[t.data_ptr() for t in self.v])

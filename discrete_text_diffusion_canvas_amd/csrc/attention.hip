@@ -9,12 +9,19 @@
 // [prefix rows in the window || canvas rows] is the reading taken for how the
 // two attentions combine.
 //
-// Flash-style: a workgroup (4 waves) owns 64 query rows of one head and a
-// contiguous slice of the key range (split-KV); each wave owns 16 query rows.
-// Per 64-key block: K is staged in LDS row-major, V transposed ([d][key]);
-// S = Q K^T with MFMA (Q fragments stay in registers), online softmax in f32,
-// P goes through LDS to become the A operand of O += P V. Split slices write
-// unnormalised partials (O, max, sum) that a merge kernel combines.
+// Flash-style, split-KV: a workgroup owns 64 query rows and a slice of the
+// 64-key blocks; each wave owns 16 query rows, S = Q K^T and O += P V run on
+// MFMA, the softmax is online in f32, P goes through LDS to become an A
+// operand, and split slices write unnormalised partials (O, max, sum) that a
+// merge kernel combines. V is stored transposed ([d][key]) so that the B
+// operand of P V reads contiguous keys.
+//
+// bf16 (attn_dma_kernel): the 64 query rows are the 64/R positions of all R
+// query heads of one KV group, so K/V tiles are shared by the whole group;
+// the K tile [64 keys][hd] and V^T tile [hd][64 keys] of the next block are
+// copied into XOR-swizzled LDS by global_load_lds while the current block is
+// computed. Key blocks are aligned to multiples of 64 in each segment and
+// masked outside the visible range.
 #include "common.hpp"
 #include "layer.hpp"
 
@@ -53,6 +60,53 @@ __device__ __forceinline__ void from_f(float* p, float v) { *p = v; }
 
 constexpr int KB = 64;  // keys per block
 
+// Online-softmax update of one wave's 16 rows from its S tile (4 n-tiles of
+// 16 keys, already masked and scaled); writes P (storage type) to pw
+// ([16][SP]) and rescales O.
+template <typename TL, int NT_D, int SP>
+__device__ __forceinline__ void softmax_block(f32x4 (&s)[4], float (&m_run)[4], float (&l_run)[4],
+                                              f32x4 (&o)[NT_D], TL* pw, int lr, int lg) {
+    float pmax[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        pmax[i] = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
+#pragma unroll
+        for (int o2 = 1; o2 < 16; o2 <<= 1) pmax[i] = fmaxf(pmax[i], __shfl_xor(pmax[i], o2, 64));
+    }
+    float alpha[4], mnew[4], psum[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        mnew[i] = fmaxf(m_run[i], pmax[i]);
+        alpha[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew[i]);
+        psum[i] = 0.f;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float p = (mnew[i] == -INFINITY) ? 0.f : __expf(s[nt][i] - mnew[i]);
+            TL pl;
+            from_f(&pl, p);
+            psum[i] += to_f(pl);  // the probabilities the MFMA sees
+            pw[(lg * 4 + i) * SP + nt * 16 + lr] = pl;
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int o2 = 1; o2 < 16; o2 <<= 1) psum[i] += __shfl_xor(psum[i], o2, 64);
+        l_run[i] = l_run[i] * alpha[i] + psum[i];
+        m_run[i] = mnew[i];
+    }
+#pragma unroll
+    for (int j = 0; j < NT_D; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
+}
+
+// ===========================================================================
+// Generic kernel (f32, and any head_dim): one query head per workgroup,
+// staging through registers.
+// ===========================================================================
 template <typename TL, int HD>
 __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
     if (a.state && a.state[0]) return;
@@ -60,8 +114,8 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
     constexpr int SKK = HD + PADL;       // K tile row stride
     constexpr int SVT = KB + PADL;       // V^T row stride
     constexpr int SP = KB + PADL;        // P row stride
-    constexpr int NT_D = HD / 16;        // output n-tiles over head_dim
-    constexpr int KS = HD / 32;          // k-steps over head_dim
+    constexpr int NT_D = HD / 16;
+    constexpr int KS = HD / 32;
     extern __shared__ __align__(16) unsigned char smem[];
     TL* Ks = reinterpret_cast<TL*>(smem);
     TL* Vt = Ks + KB * SKK;
@@ -72,14 +126,12 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
     const int h = blockIdx.y;
     const int g = h / (a.Hq / a.Hkv);
     const int q0 = blockIdx.x * 64;
-    const int qw0 = q0 + wave * 16;  // this wave's first query row
+    const int qw0 = q0 + wave * 16;
 
-    // virtual key range: segment 1 rows [s1, e1) then segment 2 rows [0, n2)
     const int64_t L1 = a.e1 - a.s1;
     const int64_t Ltot = L1 + a.n2;
     int64_t kbeg = 0, kend = Ltot;
     if (a.causal) {
-        // query positions in this tile: [qpos0 + q0, qpos0 + q0 + 63]
         const int64_t qlo = a.qpos0 + q0, qhi = a.qpos0 + min(q0 + 63, a.nq - 1);
         kend = min<int64_t>(Ltot, qhi - a.s1 + 1);
         if (a.window > 0) kbeg = max<int64_t>(0, qlo - a.window + 1 - a.s1);
@@ -110,43 +162,29 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
     const float scale = 1.f / sqrtf((float)HD);
 
     const TL* K1 = reinterpret_cast<const TL*>(a.K1) + (int64_t)g * a.ld1 * HD;
-    const TL* V1 = reinterpret_cast<const TL*>(a.V1) + (int64_t)g * a.ld1 * HD;
+    const TL* V1 = reinterpret_cast<const TL*>(a.V1) + (int64_t)g * HD * a.ld1;
     const TL* K2 = a.K2 ? reinterpret_cast<const TL*>(a.K2) + (int64_t)g * a.ld2 * HD : nullptr;
-    const TL* V2 = a.V2 ? reinterpret_cast<const TL*>(a.V2) + (int64_t)g * a.ld2 * HD : nullptr;
+    const TL* V2 = a.V2 ? reinterpret_cast<const TL*>(a.V2) + (int64_t)g * HD * a.ld2 : nullptr;
 
     for (int64_t kb = kb0; kb < kb1; kb += KB) {
-        // ---- stage K (row-major) and V (transposed) for keys [kb, kb+64) ----
-        constexpr int CH = KB * HD / 8;  // 8-element chunks
-        for (int c = tid; c < CH; c += 256) {
+        for (int c = tid; c < KB * HD / 8; c += 256) {   // K rows, 8 elements per chunk
             const int kr = c / (HD / 8), dc = (c % (HD / 8)) * 8;
             const int64_t j = kb + kr;
-            TL kv[8], vv[8];
-            if (j < kb1) {
-                const TL* kp;
-                const TL* vp;
-                if (j < L1) { kp = K1 + (a.s1 + j) * HD; vp = V1 + (a.s1 + j) * HD; }
-                else { kp = K2 + (j - L1) * HD; vp = V2 + (j - L1) * HD; }
-                if constexpr (sizeof(TL) == 2) {
-                    u16x8 x = *reinterpret_cast<const u16x8*>(kp + dc);
-                    u16x8 y = *reinterpret_cast<const u16x8*>(vp + dc);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) { kv[q] = x[q]; vv[q] = y[q]; }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) { kv[q] = kp[dc + q]; vv[q] = vp[dc + q]; }
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) { kv[q] = 0; vv[q] = 0; }
-            }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                Ks[kr * SKK + dc + q] = kv[q];
-                Vt[(dc + q) * SVT + kr] = vv[q];
+                TL kv = 0;
+                if (j < kb1) kv = j < L1 ? K1[(a.s1 + j) * HD + dc + q] : K2[(j - L1) * HD + dc + q];
+                Ks[kr * SKK + dc + q] = kv;
             }
         }
+        for (int c = tid; c < KB * HD; c += 256) {       // V^T: consecutive threads take consecutive keys
+            const int d = c / KB, kr = c % KB;
+            const int64_t j = kb + kr;
+            TL vv = 0;
+            if (j < kb1) vv = j < L1 ? V1[(int64_t)d * a.ld1 + a.s1 + j] : V2[(int64_t)d * a.ld2 + (j - L1)];
+            Vt[d * SVT + kr] = vv;
+        }
         __syncthreads();
-        // ---- S = Q K^T for this wave's 16 rows x 64 keys ----
         f32x4 s[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
@@ -157,61 +195,22 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
                 s[nt] = amfma(qf[ks], kf, s[nt]);
             }
         }
-        // ---- mask, online softmax ----
-        float pmax[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pmax[i] = -INFINITY;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int64_t j = kb + nt * 16 + lr;
-            int64_t kpos;
-            if (j < L1) kpos = a.s1 + j; else kpos = a.pos2_0 + (j - L1);
+            const int64_t kpos = j < L1 ? a.s1 + j : a.pos2_0 + (j - L1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int qr = qw0 + lg * 4 + i;
                 const int64_t qpos = a.qpos0 + qr;
                 bool ok = j < kb1 && qr < a.nq;
                 if (a.causal) ok = ok && kpos <= qpos && (a.window <= 0 || qpos - kpos < a.window);
-                float v = ok ? s[nt][i] * scale : -INFINITY;
-                s[nt][i] = v;
-                pmax[i] = fmaxf(pmax[i], v);
+                s[nt][i] = ok ? s[nt][i] * scale : -INFINITY;
             }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) pmax[i] = fmaxf(pmax[i], __shfl_xor(pmax[i], o2, 64));
-        float alpha[4], mnew[4], psum[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            mnew[i] = fmaxf(m_run[i], pmax[i]);
-            alpha[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew[i]);
-            psum[i] = 0.f;
         }
         TL* pw = Ps + wave * 16 * SP;
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float p = (mnew[i] == -INFINITY) ? 0.f : __expf(s[nt][i] - mnew[i]);
-                TL pl;
-                from_f(&pl, p);
-                psum[i] += to_f(pl);  // the probabilities the MFMA sees
-                pw[(lg * 4 + i) * SP + nt * 16 + lr] = pl;
-            }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) psum[i] += __shfl_xor(psum[i], o2, 64);
-            l_run[i] = l_run[i] * alpha[i] + psum[i];
-            m_run[i] = mnew[i];
-        }
-#pragma unroll
-        for (int j = 0; j < NT_D; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
-        __syncthreads();  // P visible to the wave (and K/V reads done before restaging)
-        // ---- O += P V ----
+        softmax_block<TL, NT_D, SP>(s, m_run, l_run, o, pw, lr, lg);
+        __syncthreads();
 #pragma unroll
         for (int ks2 = 0; ks2 < KB / 32; ++ks2) {
             auto pf = afrag_ld<TL>(pw + lr * SP + ks2 * 32 + lg * 8);
@@ -223,7 +222,6 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
         }
         __syncthreads();
     }
-    // ---- write out ----
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int qr = qw0 + lg * 4 + i;
@@ -239,6 +237,210 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
             for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[j][i];
             if (lr == 0) {
                 float* pm = a.part_ml + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + h) * 2;
+                pm[0] = m_run[i];
+                pm[1] = l_run[i];
+            }
+        }
+    }
+}
+
+// ===========================================================================
+// bf16 kernel with LDS-DMA double buffering and GQA-shared K/V tiles.
+// ===========================================================================
+namespace {
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_a() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// K tile rows are HD*2 bytes (>= 256): chunk c of key row r sits at c ^ (r & 15).
+__device__ __forceinline__ int kswz(int r, int c) { return c ^ (r & 15); }
+// V^T tile rows are 128 bytes (64 keys): chunk c of row d sits at c ^ ((d >> 1) & 7).
+__device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
+
+}  // namespace
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_dma_kernel(AttnArgs a, int R) {
+    if (a.state && a.state[0]) return;
+    constexpr int KROWB = HD * 2;                 // bytes per K row
+    constexpr int K_BYTES = KB * KROWB;           // K tile
+    constexpr int V_BYTES = HD * KB * 2;          // V^T tile (rows of 128 bytes)
+    constexpr int STAGE = K_BYTES + V_BYTES;
+    constexpr int K_INSTR = K_BYTES / 1024 / 4;   // per wave
+    constexpr int V_INSTR = V_BYTES / 1024 / 4;
+    constexpr int LOADS = K_INSTR + V_INSTR;
+    constexpr int NT_D = HD / 16;
+    constexpr int KS = HD / 32;
+    constexpr int SP = KB + 8;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* Ps = reinterpret_cast<uint16_t*>(smem + 2 * STAGE);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int g = blockIdx.y;
+    const int QP = 64 / R;                        // positions per workgroup
+    const int qx0 = blockIdx.x * QP;
+    // this wave's 16 rows: workgroup rows [16 wave, +16) = (head, position)
+    auto row_head = [&](int rho) { return g * R + rho / QP; };
+    auto row_pos = [&](int rho) { return qx0 + rho % QP; };
+
+    // ---- the key blocks of this workgroup ----
+    const int64_t qlo = a.qpos0 + qx0, qhi = a.qpos0 + min(qx0 + QP, a.nq) - 1;
+    int64_t b1lo, b1hi;                           // segment-1 blocks [b1lo, b1hi)
+    if (a.causal) {
+        int64_t kmin = a.s1, kmax = min<int64_t>(a.e1 - 1, qhi);
+        if (a.window > 0) kmin = max<int64_t>(kmin, qlo - a.window + 1);
+        b1lo = kmin / KB;
+        b1hi = kmax >= kmin ? kmax / KB + 1 : b1lo;
+    } else {
+        b1lo = a.s1 / KB;
+        b1hi = a.e1 > a.s1 ? (a.e1 - 1) / KB + 1 : b1lo;
+    }
+    const int64_t nb1 = b1hi - b1lo;
+    const int64_t nb2 = a.n2 > 0 ? (a.n2 + KB - 1) / KB : 0;
+    const int64_t nb = nb1 + nb2;
+    const int64_t per = (nb + a.splits - 1) / a.splits;
+    const int64_t bb0 = per * blockIdx.z, bb1 = min<int64_t>(nb, bb0 + per);
+
+    const uint16_t* K1 = reinterpret_cast<const uint16_t*>(a.K1) + (int64_t)g * a.ld1 * HD;
+    const uint16_t* V1 = reinterpret_cast<const uint16_t*>(a.V1) + (int64_t)g * HD * a.ld1;
+    const uint16_t* K2 = a.K2 ? reinterpret_cast<const uint16_t*>(a.K2) + (int64_t)g * a.ld2 * HD : nullptr;
+    const uint16_t* V2 = a.V2 ? reinterpret_cast<const uint16_t*>(a.V2) + (int64_t)g * HD * a.ld2 : nullptr;
+
+    // issue the copies of virtual block vb into stage buffer st
+    auto issue = [&](int64_t vb, int stg) {
+        unsigned char* base = smem + stg * STAGE;
+        const bool seg1 = vb < nb1;
+        const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
+        const int64_t rlim = seg1 ? a.e1 : a.n2;   // rows >= rlim: any valid row (masked)
+        const uint16_t* Kb = seg1 ? K1 : K2;
+        const uint16_t* Vb = seg1 ? V1 : V2;
+        const int64_t vld = seg1 ? a.ld1 : a.ld2;
+        constexpr int KRPI = 1024 / KROWB;           // K rows per instruction
+        constexpr int KCPR = KROWB / 16;             // chunks per K row
+#pragma unroll
+        for (int j = 0; j < K_INSTR; ++j) {
+            const int r = (wave * K_INSTR + j) * KRPI + lane / KCPR;
+            const int pos = lane % KCPR;
+            int64_t kr = row0 + r;
+            if (kr >= rlim) kr = rlim - 1;
+            if (kr < 0) kr = 0;
+            const uint16_t* src = Kb + kr * HD + 8 * kswz(r, pos);
+            __builtin_amdgcn_global_load_lds(src, base + (wave * K_INSTR + j) * 1024, 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < V_INSTR; ++j) {
+            const int d = (wave * V_INSTR + j) * 8 + lane / 8;
+            const int pos = lane % 8;
+            const uint16_t* src = Vb + (int64_t)d * vld + row0 + 8 * vswz(d, pos);
+            __builtin_amdgcn_global_load_lds(src, base + K_BYTES + (wave * V_INSTR + j) * 1024, 16, 0, 0);
+        }
+    };
+
+    // ---- Q fragments ----
+    const int rho_l = wave * 16 + lr;
+    const int hq_l = row_head(rho_l), qp_l = row_pos(rho_l);
+    const bool qok_l = qp_l < a.nq;
+    const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.Q) + ((int64_t)hq_l * a.ldq + (qok_l ? qp_l : 0)) * HD;
+    u16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = qok_l ? *reinterpret_cast<const u16x8*>(Qh + ks * 32 + lg * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+
+    f32x4 o[NT_D];
+#pragma unroll
+    for (int j = 0; j < NT_D; ++j) o[j] = f32x4{0, 0, 0, 0};
+    float m_run[4], l_run[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
+    const float scale = 1.f / sqrtf((float)HD);
+    // positions of this lane's 4 output rows
+    int64_t qpos[4];
+    bool qok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rho = wave * 16 + lg * 4 + i;
+        qpos[i] = a.qpos0 + row_pos(rho);
+        qok[i] = row_pos(rho) < a.nq;
+    }
+
+    if (bb0 < bb1) issue(bb0, 0);
+    for (int64_t vb = bb0; vb < bb1; ++vb) {
+        const int stg = (int)((vb - bb0) & 1);
+        if (vb + 1 < bb1) {
+            issue(vb + 1, stg ^ 1);
+            wait_vmcnt_a<LOADS>();
+        } else {
+            wait_vmcnt_a<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        const unsigned char* Kt = smem + stg * STAGE;
+        const unsigned char* Vt = Kt + K_BYTES;
+        const bool seg1 = vb < nb1;
+        const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
+        // ---- S = Q K^T ----
+        f32x4 s[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            s[nt] = f32x4{0, 0, 0, 0};
+            const int r = nt * 16 + lr;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u16x8 kf = *reinterpret_cast<const u16x8*>(Kt + r * KROWB + kswz(r, ks * 4 + lg) * 16);
+                s[nt] = amfma(qf[ks], kf, s[nt]);
+            }
+        }
+        // ---- mask ----
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int64_t row = row0 + nt * 16 + lr;
+            bool kin;
+            int64_t kpos;
+            if (seg1) { kin = row >= a.s1 && row < a.e1; kpos = row; }
+            else { kin = row < a.n2; kpos = a.pos2_0 + row; }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bool ok = kin && qok[i];
+                if (a.causal) ok = ok && kpos <= qpos[i] && (a.window <= 0 || qpos[i] - kpos < a.window);
+                s[nt][i] = ok ? s[nt][i] * scale : -INFINITY;
+            }
+        }
+        uint16_t* pw = Ps + wave * 16 * SP;
+        softmax_block<uint16_t, NT_D, SP>(s, m_run, l_run, o, pw, lr, lg);
+        // ---- O += P V (P rows are this wave's; V^T from LDS) ----
+#pragma unroll
+        for (int ks2 = 0; ks2 < KB / 32; ++ks2) {
+            const u16x8 pf = *reinterpret_cast<const u16x8*>(pw + lr * SP + ks2 * 32 + lg * 8);
+#pragma unroll
+            for (int j = 0; j < NT_D; ++j) {
+                const int d = j * 16 + lr;
+                const u16x8 vf = *reinterpret_cast<const u16x8*>(Vt + d * 128 + vswz(d, ks2 * 4 + lg) * 16);
+                o[j] = amfma(pf, vf, o[j]);
+            }
+        }
+        __builtin_amdgcn_s_barrier();  // the stage is refilled by the next-but-one block
+    }
+    wait_vmcnt_a<0>();
+    // ---- write out ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!qok[i]) continue;
+        const int rho = wave * 16 + lg * 4 + i;
+        const int hq = row_head(rho), qr = row_pos(rho);
+        if (a.splits == 1) {
+            const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.O) + (int64_t)qr * a.Hq * HD + (int64_t)hq * HD;
+#pragma unroll
+            for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[j][i] * inv);
+        } else {
+            float* po = a.part_o + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * HD;
+#pragma unroll
+            for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[j][i];
+            if (lr == 0) {
+                float* pm = a.part_ml + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * 2;
                 pm[0] = m_run[i];
                 pm[1] = l_run[i];
             }
@@ -290,7 +492,35 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int HD>
+static hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t st) {
+    const int R = a.Hq / a.Hkv;
+    constexpr int STAGE = 64 * HD * 2 * 2;
+    const size_t lds = (size_t)2 * STAGE + (size_t)4 * 16 * (KB + 8) * 2;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_dma_kernel<HD>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    dim3 grid((a.nq + 64 / R - 1) / (64 / R), a.Hkv, a.splits);
+    attn_dma_kernel<HD><<<grid, 256, lds, st>>>(a, R);
+    if (a.splits > 1) attn_merge_kernel<uint16_t><<<dim3(a.nq, a.Hq), 256, 0, st>>>(a, HD);
+    return hipGetLastError();
+}
+
+bool attention_uses_dma(const AttnArgs& a, int act_f32) {
+    const int R = a.Hq / a.Hkv;
+    return !act_f32 && (a.hd == 128 || a.hd == 256) && R >= 1 && R <= 64 && 64 % R == 0 &&
+           a.ld1 % 64 == 0 && (a.n2 == 0 || a.ld2 % 64 == 0);
+}
+
 hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st) {
+    if (attention_uses_dma(a, act_f32)) {
+        if (a.hd == 256) return launch_attn_dma<256>(a, st);
+        return launch_attn_dma<128>(a, st);
+    }
     if (act_f32) {
         if (a.hd == 64) return launch_attn_t<float, 64>(a, st);
         if (a.hd == 128) return launch_attn_t<float, 128>(a, st);

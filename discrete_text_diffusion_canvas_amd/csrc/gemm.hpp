@@ -27,6 +27,8 @@ struct GemmArgs {
     int M, N, K;                    // M: rows (non-grouped) / bound on rows per group (grouped);
                                     // N: output columns (SwiGLU: 2F)
     const int32_t* group_offsets;   // grouped: group g owns rows [off[g], off[g+1])
+    const int32_t* hit;             // grouped: [0] = number of groups with rows, then their ids
+    const int32_t* hit_mb;          // grouped: largest number of 64-row blocks of a group
     // outputs
     void* C;                        // [rows][ldc]
     int64_t ldc;

@@ -6,8 +6,9 @@
 // tile; its 4 waves split the K loop (wave w takes k-steps w, w+4, ...), so
 // every weight byte is loaded by exactly one wave and the 4 waves read
 // adjacent pieces of each weight row at the same time. MFMA fragments are
-// loaded from global memory straight into registers, DEPTH k-steps ahead of
-// their use, so each wave keeps DEPTH x (m-tiles + 4) loads in flight. LDS is
+// loaded from global memory straight into registers one k-step ahead of their
+// use with a branch-free loop (so the compiler keeps the loads in flight), and
+// two or more waves per SIMD hide the rest of the latency. LDS is
 // used only at the end: the 4 partial tiles are summed in a fixed order
 // (deterministic) and the epilogue (store / residual add / SwiGLU) reads the
 // summed tile with coalesced stores.
@@ -17,6 +18,11 @@
 // extra reads of a weight tile hit that XCD's L2.
 #include "common.hpp"
 #include "gemm.hpp"
+
+// build-time tunable: the waves per SIMD the register allocation must allow
+#ifndef DG_STREAM_WAVES
+#define DG_STREAM_WAVES 2
+#endif
 
 namespace dg {
 
@@ -80,158 +86,174 @@ __device__ __forceinline__ float ssilu(float x) { return x / (1.f + __expf(-x));
 
 }  // namespace
 
-template <typename TL, int WK, int EPI, int DEPTH>
-__global__ void __launch_bounds__(256) stream_gemm_kernel(GemmArgs g, int n_tiles, int units, int mb_max) {
-    if (g.state && g.state[0]) return;
-    // ---- decode the block: unit u = group * n_tiles + tile, m-block mb ----
-    const int id = blockIdx.x;
-    const int blk = id / (8 * mb_max), rem = id % (8 * mb_max);
-    const int mb = rem / 8;
-    const int u = blk * 8 + rem % 8;
-    if (u >= units) return;
-    const int grp = u / n_tiles, tile = u % n_tiles;
-    int row0, mrows;
-    if (g.group_offsets) {
-        row0 = g.group_offsets[grp];
-        mrows = g.group_offsets[grp + 1] - row0;
-    } else {
-        row0 = 0;
-        mrows = g.M;
+// The K loop for TMV live m-tiles: two register slots, loads issued one
+// k-step ahead, no branches (addresses are clamped to valid memory; a k-step
+// past this wave's range contributes zero through a select on the W frags).
+template <int TMV, typename TL, int WK>
+__device__ __forceinline__ void stream_kloop(f32x4 (&acc)[STM][STN], const TL* const (&arow)[STM],
+                                             const unsigned char* const (&wrow)[STN], int wave, int lg, int KS) {
+    constexpr int WES = (WK == WK_FP8) ? 1 : (int)sizeof(TL);
+    SFrag<TL, WK_SAME> fa[2][TMV];
+    SFrag<TL, WK> fb[2][STN];
+    const int nmax = (KS + 3) / 4;
+    auto load = [&](int d, int s) {
+        const int ks = min(wave + 4 * s, KS - 1);
+        const int k = ks * 32 + lg * 8;
+#pragma unroll
+        for (int i = 0; i < TMV; ++i) fa[d][i].load(arow[i] + k);
+#pragma unroll
+        for (int j = 0; j < STN; ++j) fb[d][j].load(wrow[j] + (int64_t)k * WES);
+    };
+    auto consume = [&](int d, int s) {
+        const bool ok = wave + 4 * s < KS;
+#pragma unroll
+        for (int j = 0; j < STN; ++j)
+            if (!ok) fb[d][j].zero();
+#pragma unroll
+        for (int i = 0; i < TMV; ++i)
+#pragma unroll
+            for (int j = 0; j < STN; ++j) acc[i][j] = smfma(fa[d][i], fb[d][j], acc[i][j]);
+    };
+    load(0, 0);
+    load(1, 1);
+    for (int s = 0; s < nmax; s += 2) {
+        consume(0, s);
+        load(0, s + 2);
+        consume(1, s + 1);
+        load(1, s + 3);
     }
-    const int m0 = mb * SBM;
-    if (m0 >= mrows) return;
-    const int mcount = min(SBM, mrows - m0);
-    const int tm_live = (mcount + 15) / 16;
+}
 
+// Work: for every unit (group, 64-column tile) the m-blocks of 64 rows. Item
+// ids place the m-blocks of one unit 8 apart, so with a persistent grid (a
+// multiple of 8) they run on one XCD. Grouped mode reads the hit groups from
+// g.hit ([0] = count, then group ids) and the largest m-block count from
+// g.hit_mb; non-grouped mode has one group of g.M rows.
+template <typename TL, int WK, int EPI>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_STREAM_WAVES)))
+stream_gemm_kernel(GemmArgs g, int n_tiles) {
+    if (g.state && g.state[0]) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     constexpr int WES = (WK == WK_FP8) ? 1 : (int)sizeof(TL);
     const int64_t wgs = g.w_group_stride * WES;  // bytes between groups' weights
+    const int ngroups = g.group_offsets ? g.hit[0] : 1;
+    const int mb_max = g.group_offsets ? *g.hit_mb : (g.M + SBM - 1) / SBM;
+    const int units = ngroups * n_tiles;
+    const int64_t items = (int64_t)((units + 7) / 8) * 8 * mb_max;
+    __shared__ float tile_s[SBM][SBN + 1];
 
-    // ---- fragment sources ----
-    // A rows: m-tile i, lane row lr
-    const TL* arow[STM];
+    for (int64_t id = blockIdx.x; id < items; id += gridDim.x) {
+        const int blk = (int)(id / (8 * mb_max)), rem = (int)(id % (8 * mb_max));
+        const int mb = rem / 8;
+        const int u = blk * 8 + rem % 8;
+        if (u >= units) continue;
+        const int gi = u / n_tiles, tile = u % n_tiles;
+        const int grp = g.group_offsets ? g.hit[1 + gi] : 0;
+        int row0, mrows;
+        if (g.group_offsets) {
+            row0 = g.group_offsets[grp];
+            mrows = g.group_offsets[grp + 1] - row0;
+        } else {
+            row0 = 0;
+            mrows = g.M;
+        }
+        const int m0 = mb * SBM;
+        if (m0 >= mrows) continue;
+        const int mcount = min(SBM, mrows - m0);
+        const int tm_live = (mcount + 15) / 16;
+
+        // A rows of the m-tiles (rows past mcount read the block's first row:
+        // their outputs are never stored)
+        const TL* arow[STM];
 #pragma unroll
-    for (int i = 0; i < STM; ++i) {
-        const int r = m0 + i * 16 + lr;
-        if (r < mcount + m0 && r < mrows) {
+        for (int i = 0; i < STM; ++i) {
+            const int r = m0 + min(i * 16 + lr, mcount - 1);
             const int ar = row0 + r;
             const int src = g.a_rows ? g.a_rows[ar] : ar;
             arow[i] = reinterpret_cast<const TL*>(g.A) + (int64_t)src * g.lda;
-        } else {
-            arow[i] = nullptr;
         }
-    }
-    // W rows: n-tile j, lane col lr
-    const unsigned char* wrow[STN];
-    const int n0 = tile * SBN;
+        // W rows of the n-tiles (past N: the last row, never stored)
+        const unsigned char* wrow[STN];
+        const int n0 = tile * SBN;
 #pragma unroll
-    for (int j = 0; j < STN; ++j) {
-        int wr;
-        const unsigned char* base;
-        int limit;
-        if (EPI == EPI_SWIGLU) {
-            // n-tiles 0,1: gate rows; 2,3: up rows (same output columns)
-            wr = tile * (SBN / 2) + (j & 1) * 16 + lr;
-            base = reinterpret_cast<const unsigned char*>(j < 2 ? g.W : g.W2);
-            limit = g.N / 2;
-        } else {
-            wr = n0 + j * 16 + lr;
-            base = reinterpret_cast<const unsigned char*>(g.W);
-            limit = g.N;
-        }
-        wrow[j] = wr < limit ? base + (int64_t)grp * wgs + (int64_t)wr * g.ldw * WES : nullptr;
-    }
-
-    SFrag<TL, WK_SAME> fa[DEPTH][STM];
-    SFrag<TL, WK> fb[DEPTH][STN];
-    f32x4 acc[STM][STN];
-#pragma unroll
-    for (int i = 0; i < STM; ++i)
-#pragma unroll
-        for (int j = 0; j < STN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int KS = g.K / 32;                  // k-steps of 32
-    const int nmine = (KS - wave + 3) / 4;    // this wave's k-steps: wave, wave+4, ...
-    auto load = [&](int d, int s) {           // s-th k-step of this wave into slot d
-        if (s < nmine) {
-            const int k = (wave + 4 * s) * 32 + lg * 8;
-#pragma unroll
-            for (int i = 0; i < STM; ++i) {
-                if (i < tm_live && arow[i]) fa[d][i].load(arow[i] + k);
-                else fa[d][i].zero();
+        for (int j = 0; j < STN; ++j) {
+            int wr;
+            const unsigned char* base;
+            int limit;
+            if (EPI == EPI_SWIGLU) {
+                // n-tiles 0,1: gate rows; 2,3: up rows (same output columns)
+                wr = tile * (SBN / 2) + (j & 1) * 16 + lr;
+                base = reinterpret_cast<const unsigned char*>(j < 2 ? g.W : g.W2);
+                limit = g.N / 2;
+            } else {
+                wr = n0 + j * 16 + lr;
+                base = reinterpret_cast<const unsigned char*>(g.W);
+                limit = g.N;
             }
-#pragma unroll
-            for (int j = 0; j < STN; ++j) {
-                if (wrow[j]) fb[d][j].load(wrow[j] + (int64_t)k * WES);
-                else fb[d][j].zero();
-            }
+            wr = min(wr, limit - 1);
+            wrow[j] = base + (int64_t)grp * wgs + (int64_t)wr * g.ldw * WES;
         }
-    };
+
+        f32x4 acc[STM][STN];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load(d, d);
-    for (int s0 = 0; s0 < nmine; s0 += DEPTH) {
+        for (int i = 0; i < STM; ++i)
 #pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            if (s0 + d < nmine) {
+            for (int j = 0; j < STN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int KS = g.K / 32;
+        if (tm_live == 1) stream_kloop<1, TL, WK>(acc, arow, wrow, wave, lg, KS);
+        else if (tm_live == 2) stream_kloop<2, TL, WK>(acc, arow, wrow, wave, lg, KS);
+        else stream_kloop<4, TL, WK>(acc, arow, wrow, wave, lg, KS);
+
+        // ---- sum the 4 waves' partial tiles in LDS, in wave order ----
+        for (int w = 0; w < 4; ++w) {
+            if (wave == w) {
 #pragma unroll
                 for (int i = 0; i < STM; ++i) {
-                    if (i < tm_live) {
+                    if (i >= tm_live) continue;
 #pragma unroll
-                        for (int j = 0; j < STN; ++j) acc[i][j] = smfma(fa[d][i], fb[d][j], acc[i][j]);
-                    }
+                    for (int j = 0; j < STN; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int r = i * 16 + lg * 4 + q, c = j * 16 + lr;
+                            if (w == 0) tile_s[r][c] = acc[i][j][q];
+                            else tile_s[r][c] += acc[i][j][q];
+                        }
                 }
-                load(d, s0 + d + DEPTH);
+            }
+            __syncthreads();
+        }
+        // ---- epilogue ----
+        if constexpr (EPI == EPI_SWIGLU) {
+            const int hn0 = tile * (SBN / 2);
+            for (int e = tid; e < SBM * (SBN / 2); e += 256) {
+                const int r = e / (SBN / 2), c = e % (SBN / 2);
+                const int n = hn0 + c;
+                if (r >= mcount || n >= g.N / 2) continue;
+                float gv = tile_s[r][c], uv = tile_s[r][c + SBN / 2];
+                if (g.w_scale) {
+                    gv *= bf2f(g.w_scale[(int64_t)grp * g.scale_group_stride + n]);
+                    uv *= bf2f(g.w2_scale[(int64_t)grp * g.scale_group_stride + n]);
+                }
+                const float h = ssilu(gv) * uv;
+                const int64_t orow = row0 + m0 + r;
+                if (g.c_f32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = h;
+                else reinterpret_cast<uint16_t*>(g.C)[orow * g.ldc + n] = f2bf(h);
+            }
+        } else {
+            for (int e = tid; e < SBM * SBN; e += 256) {
+                const int r = e / SBN, c = e % SBN;
+                const int n = n0 + c;
+                if (r >= mcount || n >= g.N) continue;
+                float v = tile_s[r][c];
+                if (g.w_scale) v *= bf2f(g.w_scale[(int64_t)grp * g.scale_group_stride + n]);
+                const int64_t orow = row0 + m0 + r;
+                if constexpr (EPI == EPI_STORE_F32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = v;
+                else if constexpr (EPI == EPI_STORE_BF16) reinterpret_cast<uint16_t*>(g.C)[orow * g.ldc + n] = f2bf(v);
+                else if constexpr (EPI == EPI_RESIDUAL) g.X[orow * g.ldx + n] += v;
             }
         }
-    }
-
-    // ---- sum the 4 waves' partial tiles in LDS, in wave order ----
-    __shared__ float tile_s[SBM][SBN + 1];
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w) {
-#pragma unroll
-            for (int i = 0; i < STM; ++i)
-#pragma unroll
-                for (int j = 0; j < STN; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r = i * 16 + lg * 4 + q, c = j * 16 + lr;
-                        if (w == 0) tile_s[r][c] = acc[i][j][q];
-                        else tile_s[r][c] += acc[i][j][q];
-                    }
-        }
-        __syncthreads();
-    }
-    // ---- epilogue ----
-    if constexpr (EPI == EPI_SWIGLU) {
-        const int hn0 = tile * (SBN / 2);
-        for (int e = tid; e < SBM * (SBN / 2); e += 256) {
-            const int r = e / (SBN / 2), c = e % (SBN / 2);
-            const int n = hn0 + c;
-            if (r >= mcount || n >= g.N / 2) continue;
-            float gv = tile_s[r][c], uv = tile_s[r][c + SBN / 2];
-            if (g.w_scale) {
-                gv *= bf2f(g.w_scale[(int64_t)grp * g.scale_group_stride + n]);
-                uv *= bf2f(g.w2_scale[(int64_t)grp * g.scale_group_stride + n]);
-            }
-            const float h = ssilu(gv) * uv;
-            const int64_t orow = row0 + m0 + r;
-            if (g.c_f32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = h;
-            else reinterpret_cast<uint16_t*>(g.C)[orow * g.ldc + n] = f2bf(h);
-        }
-    } else {
-        for (int e = tid; e < SBM * SBN; e += 256) {
-            const int r = e / SBN, c = e % SBN;
-            const int n = n0 + c;
-            if (r >= mcount || n >= g.N) continue;
-            float v = tile_s[r][c];
-            if (g.w_scale) v *= bf2f(g.w_scale[(int64_t)grp * g.scale_group_stride + n]);
-            const int64_t orow = row0 + m0 + r;
-            if constexpr (EPI == EPI_STORE_F32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = v;
-            else if constexpr (EPI == EPI_STORE_BF16) reinterpret_cast<uint16_t*>(g.C)[orow * g.ldc + n] = f2bf(v);
-            else if constexpr (EPI == EPI_RESIDUAL) g.X[orow * g.ldx + n] += v;
-        }
+        __syncthreads();  // tile_s is reused by the next item
     }
 }
 
@@ -241,10 +263,11 @@ static hipError_t launch_stream_t(const GemmArgs& g, int groups, int max_rows, h
     const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + SBN / 2 - 1) / (SBN / 2) : (g.N + SBN - 1) / SBN;
     const int units = G * n_tiles;
     const int mb_max = std::max(1, (max_rows + SBM - 1) / SBM);
-    const int64_t blocks = (int64_t)((units + 7) / 8) * 8 * mb_max;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    constexpr int DEPTH = sizeof(TL) == 4 ? 2 : 4;
-    stream_gemm_kernel<TL, WK, EPI, DEPTH><<<(unsigned)blocks, 256, 0, st>>>(g, n_tiles, units, mb_max);
+    const int64_t items = (int64_t)((units + 7) / 8) * 8 * mb_max;  // upper bound
+    // persistent grid: a multiple of 8 (one slot per XCD), at most 4 per CU
+    int64_t grid = std::min<int64_t>(items, 256 * 4);
+    grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
+    stream_gemm_kernel<TL, WK, EPI><<<(unsigned)grid, 256, 0, st>>>(g, n_tiles);
     return hipGetLastError();
 }
 

@@ -56,54 +56,64 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 // RoPE + scatter. qkv [n][(Hq+2Hkv)*hd] (row i at position pos0+i) ->
 //   Q  [Hq][q_ld][hd]        rows q_off + i   (rotated)
 //   K  [Hkv][kv_ld][hd]      rows kv_off + i  (rotated)
-//   V  [Hkv][kv_ld][hd]      rows kv_off + i
-// Rotate-half: for d < hd/2 with angle a = pos * base^(-2d/hd):
+//   V^T [Hkv][hd][kv_ld]     columns kv_off + i (V stored transposed)
+// Columns i in [n, v_zero_to) of V^T are set to 0 (the canvas V^T is read in
+// whole 64-key blocks). Rotate-half: for d < hd/2, a = pos * base^(-2d/hd):
 //   out[d] = x[d] cos a - x[d+hd/2] sin a;  out[d+hd/2] = x[d+hd/2] cos a + x[d] sin a.
 // The angle is formed and reduced modulo 2*pi in float64 (positions reach
-// 10^5), then sin/cos are taken in float32.
-// Grid (n, Hq + 2*Hkv), hd/2 threads (>= 32).
+// 10^5), then sin/cos are taken in float32. One workgroup per row i handles
+// every head; thread d owns the rotation pair (d, d + hd/2).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void rope_scatter_kernel(const T* __restrict__ qkv, int n, int Hq, int Hkv, int hd, int64_t pos0,
                                     double base, T* __restrict__ Q, int64_t q_ld, int64_t q_off,
                                     T* __restrict__ K, T* __restrict__ V, int64_t kv_ld, int64_t kv_off,
-                                    const int32_t* __restrict__ state) {
+                                    int v_zero_to, const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     const int i = blockIdx.x;
-    const int h = blockIdx.y;
     const int half = hd / 2;
-    const int dd = threadIdx.x;
-    if (dd >= half) return;
-    const int width = (Hq + 2 * Hkv) * hd;
-    const T* src = qkv + (int64_t)i * width + (int64_t)h * hd;
-    auto ld = [&](int j) -> float {
-        if constexpr (sizeof(T) == 2) return bf2f(src[j]); else return src[j];
-    };
     auto st = [&](T* p, float v) {
         if constexpr (sizeof(T) == 2) *p = f2bf(v); else *p = v;
     };
-    float x1 = ld(dd), x2 = ld(dd + half);
-    if (h < Hq + Hkv) {
+    if (i >= n) {  // zero V^T columns past the rows
+        for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x)
+            st(V + ((int64_t)(e / hd) * hd + e % hd) * kv_ld + kv_off + i, 0.f);
+        return;
+    }
+    const int width = (Hq + 2 * Hkv) * hd;
+    const T* src = qkv + (int64_t)i * width;
+    auto ld = [&](int j) -> float {
+        if constexpr (sizeof(T) == 2) return bf2f(src[j]); else return src[j];
+    };
+    for (int dd = threadIdx.x; dd < half; dd += blockDim.x) {
         const double inv = pow(base, -2.0 * (double)dd / (double)hd);
         double a = (double)(pos0 + i) * inv;
         a = fmod(a, 6.283185307179586476925286766559);
         float sa, ca;
         sincosf((float)a, &sa, &ca);
-        float y1 = x1 * ca - x2 * sa;
-        float y2 = x2 * ca + x1 * sa;
-        x1 = y1;
-        x2 = y2;
+        for (int h = 0; h < Hq + 2 * Hkv; ++h) {
+            float x1 = ld(h * hd + dd), x2 = ld(h * hd + dd + half);
+            if (h < Hq + Hkv) {
+                const float y1 = x1 * ca - x2 * sa;
+                const float y2 = x2 * ca + x1 * sa;
+                x1 = y1;
+                x2 = y2;
+            }
+            if (h < Hq) {
+                T* dst = Q + ((int64_t)h * q_ld + q_off + i) * hd;
+                st(dst + dd, x1);
+                st(dst + dd + half, x2);
+            } else if (h < Hq + Hkv) {
+                T* dst = K + ((int64_t)(h - Hq) * kv_ld + kv_off + i) * hd;
+                st(dst + dd, x1);
+                st(dst + dd + half, x2);
+            } else {
+                T* dst = V + (int64_t)(h - Hq - Hkv) * hd * kv_ld + kv_off + i;
+                st(dst + (int64_t)dd * kv_ld, x1);
+                st(dst + (int64_t)(dd + half) * kv_ld, x2);
+            }
+        }
     }
-    T* dst;
-    if (h < Hq) {
-        dst = Q + ((int64_t)h * q_ld + q_off + i) * hd;
-    } else if (h < Hq + Hkv) {
-        dst = K + ((int64_t)(h - Hq) * kv_ld + kv_off + i) * hd;
-    } else {
-        dst = V + ((int64_t)(h - Hq - Hkv) * kv_ld + kv_off + i) * hd;
-    }
-    st(dst + dd, x1);
-    st(dst + dd + half, x2);
 }
 
 // ---------------------------------------------------------------------------
@@ -164,7 +174,8 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __restrict__ ids, int n, int k, int E,
                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-                                                            int32_t* __restrict__ slot_of,
+                                                            int32_t* __restrict__ slot_of, int32_t* __restrict__ hit,
+                                                            int32_t* __restrict__ hit_mb,
                                                             const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     extern __shared__ int32_t sh[];
@@ -183,10 +194,20 @@ __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __res
     }
     __syncthreads();
     if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) { off[e] = run; run += cnt[e]; }
+        int run = 0, h = 0, mbm = n > 0 ? (n + 63) / 64 : 0;
+        for (int e = 0; e < E; ++e) {
+            off[e] = run;
+            run += cnt[e];
+            if (cnt[e] > 0) {
+                hit[1 + h++] = e;
+                mbm = max(mbm, (cnt[e] + 63) / 64);
+            }
+        }
         off[E] = run;
         off[E + 1] = run + n;
+        if (n > 0) hit[1 + h++] = E;   // the shared expert: every token
+        hit[0] = h;
+        *hit_mb = mbm;
     }
     __syncthreads();
     for (int e = tid; e <= E + 1; e += 1024) offsets[e] = off[e];
@@ -253,16 +274,17 @@ hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float ep
 
 hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, int64_t pos0,
                                double base, void* Q, int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld,
-                               int64_t kv_off, const int32_t* state, hipStream_t st) {
-    dim3 grid(n, Hq + 2 * Hkv);
-    int threads = std::max(64, hd / 2);
+                               int64_t kv_off, int v_zero_to, const int32_t* state, hipStream_t st) {
+    const int rows = std::max(n, v_zero_to);
+    const int threads = std::max(64, std::min(256, hd / 2));
     if (act_f32)
-        rope_scatter_kernel<float><<<grid, threads, 0, st>>>((const float*)qkv, n, Hq, Hkv, hd, pos0, base, (float*)Q,
-                                                             q_ld, q_off, (float*)K, (float*)V, kv_ld, kv_off, state);
+        rope_scatter_kernel<float><<<rows, threads, 0, st>>>((const float*)qkv, n, Hq, Hkv, hd, pos0, base, (float*)Q,
+                                                             q_ld, q_off, (float*)K, (float*)V, kv_ld, kv_off,
+                                                             v_zero_to, state);
     else
-        rope_scatter_kernel<uint16_t><<<grid, threads, 0, st>>>((const uint16_t*)qkv, n, Hq, Hkv, hd, pos0, base,
+        rope_scatter_kernel<uint16_t><<<rows, threads, 0, st>>>((const uint16_t*)qkv, n, Hq, Hkv, hd, pos0, base,
                                                                 (uint16_t*)Q, q_ld, q_off, (uint16_t*)K,
-                                                                (uint16_t*)V, kv_ld, kv_off, state);
+                                                                (uint16_t*)V, kv_ld, kv_off, v_zero_to, state);
     return hipGetLastError();
 }
 
@@ -273,7 +295,8 @@ hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, i
 }
 
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
-                               int32_t* slot_of, const int32_t* state, hipStream_t st) {
+                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, const int32_t* state,
+                               hipStream_t st) {
     size_t lds = (size_t)(2 * E + 3 + n * k) * sizeof(int32_t);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     static bool attr = false;
@@ -283,7 +306,7 @@ hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t*
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hist_permute_kernel<<<1, 1024, lds, st>>>(ids, n, k, E, offsets, perm, slot_of, state);
+    hist_permute_kernel<<<1, 1024, lds, st>>>(ids, n, k, E, offsets, perm, slot_of, hit, hit_mb, state);
     return hipGetLastError();
 }
 

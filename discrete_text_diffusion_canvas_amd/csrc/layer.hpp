@@ -12,17 +12,22 @@ hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float ep
                           const int32_t* state, hipStream_t st);
 hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, int64_t pos0,
                                double base, void* Q, int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld,
-                               int64_t kv_off, const int32_t* state, hipStream_t st);
+                               int64_t kv_off, int v_zero_to, const int32_t* state, hipStream_t st);
 hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, int k, int32_t* ids, float* gates,
                               const int32_t* state, hipStream_t st);
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
-                               int32_t* slot_of, const int32_t* state, hipStream_t st);
+                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, const int32_t* state,
+                               hipStream_t st);
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
                           int shared_off, const int32_t* state, hipStream_t st);
 
-// Attention over up to two key segments per KV head:
-//   segment 1: K1/V1 [Hkv][ld1][hd], rows [s1, e1)  (cache), positions = row index
-//   segment 2: K2/V2 [Hkv][ld2][hd], rows [0, n2)   (canvas), positions pos2_0 + row
+// Attention over up to two key segments per KV head (V stored transposed):
+//   segment 1: K1 [Hkv][ld1][hd], V1^T [Hkv][hd][ld1], rows [s1, e1) (cache),
+//              positions = row index
+//   segment 2: K2 [Hkv][ld2][hd], V2^T [Hkv][hd][ld2], rows [0, n2) (canvas),
+//              positions pos2_0 + row
+// ld1 and ld2 are multiples of 64; V^T columns past e1 / n2 up to the next
+// multiple of 64 hold finite values.
 // Queries Q [Hq][ldq][hd] rows [0, nq) at positions qpos0 + row; output
 // O [nq][Hq*hd]. causal: key position <= query position; window > 0: and
 // query position - key position < window (per query). Softmax scale 1/sqrt(hd).

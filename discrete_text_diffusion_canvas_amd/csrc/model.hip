@@ -43,8 +43,8 @@ struct Work {
     void* A;           // [T][d] normed activations (act dtype)
     void* QKV;         // [T][(Hq+2Hkv) hd]
     void* Q;           // [Hq][T][hd]
-    void* Kc;          // [Hkv][T][hd]
-    void* Vc;
+    void* Kc;          // [Hkv][T64][hd]
+    void* Vc;          // [Hkv][hd][T64] (transposed)
     void* O;           // [T][Hq hd]
     float* part_o;     // attention split partials
     float* part_ml;
@@ -54,6 +54,8 @@ struct Work {
     int32_t* offsets;  // [E+2]
     int32_t* perm;     // [T(k+1)]
     int32_t* slot_of;  // [T k]
+    int32_t* hit;      // [E+2]: groups with rows ([0] = count)
+    int32_t* hit_mb;   // [1]: largest 64-row block count of a group
     void* Hbuf;        // [T(k+1)][F]
     float* Y;          // [T(k+1)][d]
     dg::RowPart* parts;  // [min(T, canvas)][nsplit]
@@ -61,6 +63,7 @@ struct Work {
     double* chunk_sum;
     size_t bytes;
     int rows;
+    int rows64;        // T rounded up to a multiple of 64 (canvas K/V row stride)
 };
 
 Work carve(const dg_model* m, void* base, int T) {
@@ -75,8 +78,9 @@ Work carve(const dg_model* m, void* base, int T) {
     w.A = cv.take<char>((size_t)T * d * ab);
     w.QKV = cv.take<char>((size_t)T * (Hq + 2 * Hkv) * hd * ab);
     w.Q = cv.take<char>((size_t)T * Hq * hd * ab);
-    w.Kc = cv.take<char>((size_t)T * Hkv * hd * ab);
-    w.Vc = cv.take<char>((size_t)T * Hkv * hd * ab);
+    const int T64 = (T + 63) / 64 * 64;
+    w.Kc = cv.take<char>((size_t)T64 * Hkv * hd * ab);
+    w.Vc = cv.take<char>((size_t)T64 * Hkv * hd * ab);
     w.O = cv.take<char>((size_t)T * Hq * hd * ab);
     w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
     w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
@@ -86,6 +90,8 @@ Work carve(const dg_model* m, void* base, int T) {
     w.offsets = cv.take<int32_t>(E + 2);
     w.perm = cv.take<int32_t>((size_t)T * (k + 1));
     w.slot_of = cv.take<int32_t>((size_t)T * k);
+    w.hit = cv.take<int32_t>(E + 2);
+    w.hit_mb = cv.take<int32_t>(1);
     w.Hbuf = cv.take<char>((size_t)T * (k + 1) * F * ab);
     w.Y = cv.take<float>((size_t)T * (k + 1) * d);
     w.parts = cv.take<dg::RowPart>((size_t)Nc * lm_nsplit(c));
@@ -93,6 +99,7 @@ Work carve(const dg_model* m, void* base, int T) {
     w.chunk_sum = cv.take<double>((size_t)Nc * dg::draw_nchunk(c.vocab));
     w.bytes = cv.off;
     w.rows = T;
+    w.rows64 = T64;
     return w;
 }
 
@@ -133,13 +140,14 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
     }
     DG_TRY(dg::launch_router_topk(w.rlog, L.router_bias, n, E, k, w.ids, w.gates, state, st), "router topk");
-    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, state, st), "hist permute");
+    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, w.hit, w.hit_mb, state, st),
+           "hist permute");
     {   // gate/up with SwiGLU
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.a_rows = w.perm;
         g.W = L.w_gate; g.W2 = L.w_up; g.ldw = d; g.w_group_stride = (int64_t)F * d;
         g.w_scale = (const uint16_t*)L.gate_scale; g.w2_scale = (const uint16_t*)L.up_scale; g.scale_group_stride = F;
-        g.M = n; g.N = 2 * F; g.K = d; g.group_offsets = w.offsets;
+        g.M = n; g.N = 2 * F; g.K = d; g.group_offsets = w.offsets; g.hit = w.hit; g.hit_mb = w.hit_mb;
         g.C = w.Hbuf; g.ldc = F; g.c_f32 = f32; g.state = state;
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, dg::SHAPE_SMALL_M, st), "expert gate/up");
     }
@@ -148,7 +156,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         g.A = w.Hbuf; g.lda = F;
         g.W = L.w_down; g.ldw = F; g.w_group_stride = (int64_t)d * F;
         g.w_scale = (const uint16_t*)L.down_scale; g.scale_group_stride = d;
-        g.M = n; g.N = d; g.K = F; g.group_offsets = w.offsets;
+        g.M = n; g.N = d; g.K = F; g.group_offsets = w.offsets; g.hit = w.hit; g.hit_mb = w.hit_mb;
         g.C = w.Y; g.ldc = d; g.c_f32 = 1; g.state = state;
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_STORE_F32, E + 1, dg::SHAPE_SMALL_M, st), "expert down");
     }
@@ -183,8 +191,8 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
         DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
                "qkv gemm");
     }
-    DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows,
-                                   0, state, st),
+    DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows64,
+                                   0, w.rows64, state, st),
            "rope");
     {
         dg::AttnArgs a;
@@ -193,7 +201,7 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
         a.K1 = kv->k[l]; a.V1 = kv->v[l]; a.ld1 = kv->capacity;
         a.s1 = is_global(c, l) ? 0 : std::max<int64_t>(0, P - c.window);
         a.e1 = P;
-        a.K2 = w.Kc; a.V2 = w.Vc; a.ld2 = w.rows; a.n2 = n; a.pos2_0 = P;
+        a.K2 = w.Kc; a.V2 = w.Vc; a.ld2 = w.rows64; a.n2 = n; a.pos2_0 = P;
         a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.causal = 0; a.window = 0;
         a.O = w.O; a.part_o = w.part_o; a.part_ml = w.part_ml;
         a.splits = attn_splits(c, n, (a.e1 - a.s1) + n);
@@ -226,7 +234,7 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
                "qkv gemm");
         DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, kv->k[l],
-                                       kv->v[l], kv->capacity, P, nullptr, st),
+                                       kv->v[l], kv->capacity, P, 0, nullptr, st),
                "rope");
         if (l == c.n_layers - 1) break;  // nothing in the cache depends on the rest
         dg::AttnArgs a;
@@ -272,6 +280,7 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
 dg_status check_kv(const dg_model* m, const dg_kv* kv) {
     if (!kv || !kv->k || !kv->v) return fail(DG_E_INVALID, "kv cache is NULL");
     if (kv->len < 0 || kv->capacity < kv->len) return fail(DG_E_INVALID, "kv len/capacity inconsistent");
+    if (kv->capacity % 64) return fail(DG_E_SHAPE, "kv capacity must be a multiple of 64");
     for (int l = 0; l < m->cfg.n_layers; ++l)
         if (!kv->k[l] || !kv->v[l]) return fail(DG_E_INVALID, "kv layer %d pointer is NULL", l);
     return DG_OK;

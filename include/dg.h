@@ -222,9 +222,13 @@ typedef struct dg_weights {
     const dg_layer_weights* layers;
 } dg_weights;
 
-/* KV cache: per layer (host arrays of n_layers device pointers) K and V of
- * [n_kv_heads][capacity][head_dim] in the act dtype, keys after RoPE. Rows
- * [0, len) are filled; dg_prefill_append advances len on the host. */
+/* KV cache: per layer (host arrays of n_layers device pointers) K of
+ * [n_kv_heads][capacity][head_dim] and V transposed, [n_kv_heads][head_dim]
+ * [capacity], in the act dtype; keys after RoPE. Positions [0, len) are
+ * filled; dg_prefill_append advances len on the host. capacity must be a
+ * multiple of 64 and the cache must hold finite values beyond len (allocate
+ * it zero-filled): attention reads whole 64-key blocks and masks the keys
+ * outside the visible range. */
 typedef struct dg_kv {
     void* const* k;
     void* const* v;

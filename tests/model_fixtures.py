@@ -28,19 +28,25 @@ def oracle_weights(model):
 
 
 def fill_synthetic_kv(kv, cfg, P):
-    """Cache rows [0, P) of every layer from the synthetic KV generator."""
+    """Cache rows [0, P) of every layer from the synthetic KV generator
+    (V is stored transposed, [Hkv][hd][capacity])."""
     for l in range(cfg.n_layers):
         k, v = wl.synthetic_kv(cfg, l, P, device=kv.k[l].device)
         kv.k[l][:, :P] = k
-        kv.v[l][:, :P] = v
+        kv.v[l][:, :, :P] = v.transpose(1, 2)
     kv.length = P
+
+
+def device_v(kv, l, P):
+    """Layer l's V rows [0, P) as [Hkv][P][hd] (float32, CPU)."""
+    return kv.v[l][:, :, :P].transpose(1, 2).float().cpu()
 
 
 def oracle_kv_from_device(kv, cfg, P):
     okv = M.KVCache.empty(cfg)
     for l in range(cfg.n_layers):
         okv.K[l] = kv.k[l][:, :P].float().cpu().numpy().astype(np.float64)
-        okv.V[l] = kv.v[l][:, :P].float().cpu().numpy().astype(np.float64)
+        okv.V[l] = device_v(kv, l, P).numpy().astype(np.float64)
     return okv
 
 

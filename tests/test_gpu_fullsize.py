@@ -11,7 +11,7 @@ from oracle import model as M
 from oracle import sampler as S
 from synth import workloads as wl
 
-from model_fixtures import device_model, oracle_weights, rel_l2, rel_l2_rows, routing_near_tie_ok
+from model_fixtures import device_model, device_v, oracle_weights, rel_l2, rel_l2_rows, routing_near_tie_ok
 from parity import ENT_TOL, check_sampler_step
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +51,7 @@ def test_prefix_kv_rows_match_the_encoder(B, setup):
     a = M.rmsnorm(W.E[toks], L0["attn_norm"], cfg.norm_eps)
     _, k, v = M.qkv(a, L0, cfg, rows)
     kg = kv.k[0][:, rows].float().cpu().numpy().transpose(1, 0, 2)
-    vg = kv.v[0][:, rows].float().cpu().numpy().transpose(1, 0, 2)
+    vg = kv.v[0][:, :, rows].float().cpu().numpy().transpose(2, 0, 1)
     assert rel_l2(kg, k) < 1e-2, rel_l2(kg, k)
     assert rel_l2(vg, v) < 1e-2, rel_l2(vg, v)
 
@@ -68,7 +68,7 @@ def test_full_width_layer_and_lm_head_step(B, setup):
     B.decoder_layer(model, 0, X, kv, ws, ids)
     torch.cuda.synchronize()
     okv = M.KVCache([kv.k[0][:, :PREFIX].float().cpu().numpy().astype(np.float64)],
-                    [kv.v[0][:, :PREFIX].float().cpu().numpy().astype(np.float64)])
+                    [device_v(kv, 0, PREFIX).numpy().astype(np.float64)])
     tr = {}
     M.decoder_layer(X0, W.layer(0), okv.K[0], okv.V[0], 0, cfg, trace=tr)
     ids_g = ids.cpu().numpy()

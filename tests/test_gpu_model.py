@@ -11,7 +11,7 @@ from oracle import model as M
 from oracle import sampler as S
 from synth import workloads as wl
 
-from model_fixtures import (SMALL_BF16, device_model, fill_synthetic_kv, oracle_kv_from_device,
+from model_fixtures import (SMALL_BF16, device_model, device_v, fill_synthetic_kv, oracle_kv_from_device,
                             oracle_weights, rel_l2, rel_l2_rows, routing_near_tie_ok)
 from parity import ENT_TOL, check_sampler_step
 
@@ -129,7 +129,7 @@ def test_prefill_append_matches_oracle_encoder(B, name):
     M.encoder_append(W, okv, toks.cpu().numpy())
     for l in range(cfg.n_layers):
         kg = kv.k[l][:, :n_tok].float().cpu().numpy()
-        vg = kv.v[l][:, :n_tok].float().cpu().numpy()
+        vg = device_v(kv, l, n_tok).numpy()
         assert rel_l2(kg, okv.K[l]) < KV_TOL[name], (l, rel_l2(kg, okv.K[l]))
         assert rel_l2(vg, okv.V[l]) < KV_TOL[name], (l, rel_l2(vg, okv.V[l]))
     # one pass with a large workspace gives the same cache
@@ -144,9 +144,9 @@ def test_prefill_append_matches_oracle_encoder(B, name):
 def test_prefill_capacity_is_checked(B):
     cfg = wl.TINY
     model = device_model(B, cfg)
-    kv = B.KVCache(model, 16)
+    kv = B.KVCache(model, 64)
     with pytest.raises(B.DgError) as e:
-        B.prefill_append(model, kv, wl.prefix_tokens(cfg, 17).cuda(), model.workspace(32))
+        B.prefill_append(model, kv, wl.prefix_tokens(cfg, 65).cuda(), model.workspace(32))
     assert e.value.code == -3 and kv.length == 0
 
 
