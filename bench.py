@@ -75,18 +75,21 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     prompt = wl.prefix_tokens(cfg, prompt_len).to(dev)
     ms_prefill = _sync_ms(lambda: B.prefill_append(model, kv, prompt, ws), torch)
     canvas = B.Canvas(n, cfg.mask_id, 0, dev)
-    stats = B.StepStats(n, device=dev, vocab=cfg.vocab, logits_dtype=model.act_dtype)
+    stats = B.StepStats(n, device=dev, vocab=cfg.vocab, logits_dtype=model.act_dtype, n_layers=cfg.n_layers)
     scfg = B.sampler_default()
     sched = {"t": 0, "canvas": 0, "committed": 0}
 
-    def run(K):
+    def run(K, record=None):
         for _ in range(K):
             if sched["t"] == 0:
                 canvas.canvas_idx = sched["canvas"]
                 canvas.reset()
+            P = kv.length
             B.canvas_step(model, canvas, kv, sched["t"], SEED, scfg, stats, ws)
             sched["t"] += 1
             done = bool(canvas.state[B.ST_DONE].item())
+            if record is not None:
+                record.append((P, stats.experts_hit.cpu().tolist()))
             if done or sched["t"] == scfg.max_steps:
                 B.prefill_append(model, kv, canvas.tokens, ws)
                 sched["committed"] += n
@@ -97,34 +100,104 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     c0 = sched["committed"]
     ms = _sync_ms(lambda: run(args.steps), torch)
     committed = sched["committed"] - c0
-    # dominant-kernel timing: a second pass over the same kind of steps with
-    # HIP events bracketing the LM-head GEMM on the stream it runs on
-    B.timing_enable(1)
-    run(min(args.steps, 48))
-    torch.cuda.synchronize()
-    tot_ms, launches = B.timing_read()
-    B.timing_enable(0)
-    kern_ms = tot_ms / max(launches, 1)
-    V, d = cfg.vocab, cfg.d_model
-    eb = 2 if cfg.act_dtype == "bf16" else 4
-    lm_bytes = V * d * eb + n * d * eb                 # E once + normed activations
-    lm_flops = 2.0 * n * V * d
-    achieved_gbs = lm_bytes / (kern_ms * 1e-3) / 1e9
+    # per-kernel timing: further passes over the same kind of steps with HIP
+    # events bracketing every launch of one kernel on the stream it runs on
+    kernels = {}
+    for name, target in (("expert_gate_up", B.TIME_EXPERT_GATE_UP), ("expert_down", B.TIME_EXPERT_DOWN),
+                         ("qkv_proj", B.TIME_QKV), ("attention", B.TIME_ATTENTION), ("o_proj", B.TIME_O_PROJ),
+                         ("lm_head", B.TIME_LM_HEAD)):
+        rec = []
+        B.timing_enable(target)
+        run(min(args.steps, 16), rec)
+        torch.cuda.synchronize()
+        tot_ms, launches = B.timing_read()
+        B.timing_enable(B.TIME_OFF)
+        nbytes, flops = _algorithmic(cfg, name, rec)
+        kernels[name] = {"launches": launches, "ms_total": tot_ms, "bytes": nbytes, "flops": flops,
+                         "us_per_launch": round(tot_ms / max(launches, 1) * 1e3, 2),
+                         "ms_per_step": round(tot_ms / max(len(rec), 1), 4),
+                         "achieved_gbs": round(nbytes / (tot_ms * 1e-3) / 1e9, 1),
+                         "achieved_tflops": round(flops / (tot_ms * 1e-3) / 1e12, 1),
+                         "mean_experts_hit": round(sum(sum(h) for _, h in rec) / max(len(rec), 1) / cfg.n_layers, 2)}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
+    achieved = kd["achieved_gbs"]
     res = {
         "ms_per_step": ms / args.steps,
         "committed_tokens": committed,
-        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "lm_head (gemm_kernel EPI_LMHEAD)", "kernel_ms": round(kern_ms, 4),
-                     "algorithmic_bytes_per_launch": lm_bytes,
-                     "mfma_tflops": round(lm_flops / (kern_ms * 1e-3) / 1e12, 1),
-                     "mfma_frac": round(lm_flops / (kern_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(dom, kd),
+                     "kernel": dom, "us_per_launch": kd["us_per_launch"],
+                     "algorithmic_bytes_per_launch": round(kd["bytes"] / max(kd["launches"], 1)),
+                     "mfma_tflops": kd["achieved_tflops"],
+                     "mfma_frac": round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4)},
+        "kernels": {k: {kk: vv for kk, vv in v.items() if kk not in ("ms_total", "bytes", "flops")}
+                    for k, v in kernels.items()},
         "extra": {"prefill_tokens": prompt_len, "prefill_ms": round(ms_prefill, 2),
                   "prefill_tokens_per_s": round(prompt_len / ms_prefill * 1e3, 1),
                   "weights_setup_s": round(t_weights, 1), "kv_len_end": kv.length},
         "dtype": cfg.act_dtype,
     }
     return res, (model, kv, ws, canvas, stats)
+
+
+def _algorithmic(cfg, name, rec):
+    """Algorithmic HBM bytes and flops of every launch of kernel ``name`` over
+    the recorded steps [(prefix length P, experts hit per layer)]: each weight
+    byte of the experts actually hit once, activations in and out once."""
+    n, d, F, k = cfg.canvas, cfg.d_model, cfg.ffn_hidden, cfg.top_k
+    Hq, Hkv, hd, V, L = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.vocab, cfg.n_layers
+    wb = 1 if cfg.weight_dtype == "fp8" else (4 if cfg.weight_dtype == "f32" else 2)
+    ab = 4 if cfg.act_dtype == "f32" else 2
+    nb = fl = 0.0
+    for P, hits in rec:
+        for l in range(L):
+            h = hits[l]
+            if name == "expert_gate_up":
+                nb += (h + 1) * 2 * F * d * wb + n * d * ab + n * (k + 1) * F * ab
+                fl += 2.0 * n * (k + 1) * 2 * F * d
+            elif name == "expert_down":
+                nb += (h + 1) * d * F * wb + n * (k + 1) * F * ab + n * (k + 1) * d * 4
+                fl += 2.0 * n * (k + 1) * F * d
+            elif name == "qkv_proj":
+                nb += (Hq + 2 * Hkv) * hd * d * wb + n * d * ab + n * (Hq + 2 * Hkv) * hd * ab
+                fl += 2.0 * n * (Hq + 2 * Hkv) * hd * d
+            elif name == "o_proj":
+                nb += d * Hq * hd * wb + n * Hq * hd * ab + 2 * n * d * 4
+                fl += 2.0 * n * d * Hq * hd
+            elif name == "attention":
+                glob = cfg.global_every > 0 and l % cfg.global_every == cfg.global_every - 1
+                keys = (P if glob else min(P, cfg.window)) + n
+                nb += keys * Hkv * hd * 2 * ab + 2 * n * Hq * hd * ab
+                fl += 4.0 * n * Hq * keys * hd
+        if name == "lm_head":
+            nb += V * d * ab + n * d * ab + n * V * ab
+            fl += 2.0 * n * V * d
+    return nb, fl
+
+
+def _traffic(kernel, kd):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
+    by the same counters on a copy of known size) from the summary committed
+    under profiles/, if it was taken on the kernel source as it is now."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    src = os.path.join(ROOT, kv.get("kernel_source", ""))
+    if not os.path.isfile(src):
+        return None
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("kernel_source_sha256"):
+        return None
+    try:
+        return round(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def bench_stack(args, torch, B, which):
@@ -197,11 +270,11 @@ def bench_sampler(args, torch, B):
 
     run(0, args.warmup)
     ms = _sync_ms(lambda: run(args.warmup, args.steps), torch)
-    B.timing_enable(1)
+    B.timing_enable(B.TIME_LM_HEAD)
     run(args.warmup + args.steps, args.steps)
     torch.cuda.synchronize()
     tot_ms, launches = B.timing_read()
-    B.timing_enable(0)
+    B.timing_enable(B.TIME_OFF)
     full = sum(1 for k in range(args.warmup, args.warmup + args.steps) if k % 48 == 47)
     bytes_per_launch = n * V * 2
     kern_ms = tot_ms / max(launches, 1)
@@ -278,7 +351,7 @@ def main():
         "config": res.pop("config"),
         "roofline": res.pop("roofline"),
     }
-    for k in ("cpu_baseline", "extra"):
+    for k in ("cpu_baseline", "kernels", "extra"):
         if k in res:
             out[k] = res.pop(k)
     print(json.dumps(out), flush=True)

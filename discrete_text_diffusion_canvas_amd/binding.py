@@ -43,7 +43,7 @@ class CanvasStruct(C.Structure):
 class StepStatsStruct(C.Structure):
     _fields_ = [("entropy", C.c_void_p), ("lse", C.c_void_p), ("argmax", C.c_void_p),
                 ("selected", C.c_void_p), ("mean_entropy", C.c_void_p), ("logits", C.c_void_p),
-                ("logits_ld", C.c_int64)]
+                ("logits_ld", C.c_int64), ("experts_hit", C.c_void_p)]
 
 
 class ConfigStruct(C.Structure):
@@ -159,20 +159,24 @@ class Canvas:
 
 
 class StepStats:
-    """Per-step outputs; ``logits`` ([n][vocab], act dtype) only for model steps."""
+    """Per-step outputs; ``logits`` ([n][vocab], act dtype) only for model steps;
+    ``experts_hit`` ([n_layers] int32, routed experts hit per layer) only when
+    ``n_layers`` is given."""
 
-    def __init__(self, n: int, device="cuda", vocab: int = 0, logits_dtype=torch.bfloat16):
+    def __init__(self, n: int, device="cuda", vocab: int = 0, logits_dtype=torch.bfloat16, n_layers: int = 0):
         self.entropy = torch.zeros(n, dtype=torch.float32, device=device)
         self.lse = torch.zeros(n, dtype=torch.float32, device=device)
         self.argmax = torch.zeros(n, dtype=torch.int32, device=device)
         self.selected = torch.zeros(n, dtype=torch.uint8, device=device)
         self.mean_entropy = torch.zeros(1, dtype=torch.float64, device=device)
         self.logits = torch.empty((n, vocab), dtype=logits_dtype, device=device) if vocab else None
+        self.experts_hit = torch.zeros(n_layers, dtype=torch.int32, device=device) if n_layers else None
 
     def struct(self) -> StepStatsStruct:
         ld = self.logits.stride(0) if self.logits is not None else 0
         return StepStatsStruct(_ptr(self.entropy), _ptr(self.lse), _ptr(self.argmax),
-                               _ptr(self.selected), _ptr(self.mean_entropy), _ptr(self.logits), ld)
+                               _ptr(self.selected), _ptr(self.mean_entropy), _ptr(self.logits), ld,
+                               _ptr(self.experts_hit))
 
 
 def sampler_workspace_bytes(n: int, vocab: int) -> int:
@@ -195,12 +199,16 @@ lib.dg_timing_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int32)]
 lib.dg_timing_read.restype = C.c_int32
 
 
-def timing_enable(on: int) -> None:
-    check(lib.dg_timing_enable(int(on)))
+TIME_OFF, TIME_LM_HEAD, TIME_EXPERT_GATE_UP, TIME_EXPERT_DOWN, TIME_QKV, TIME_ATTENTION, TIME_O_PROJ = range(7)
+
+
+def timing_enable(target: int) -> None:
+    """Record HIP events around every launch of kernel ``target`` (TIME_*)."""
+    check(lib.dg_timing_enable(int(target)))
 
 
 def timing_read():
-    """(summed milliseconds, launches) of the dominant kernel since enable/read."""
+    """(summed milliseconds, launches) of the timed kernel since enable/read."""
     ms = C.c_double()
     n = C.c_int32()
     check(lib.dg_timing_read(C.byref(ms), C.byref(n)))

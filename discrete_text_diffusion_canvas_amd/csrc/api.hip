@@ -83,7 +83,7 @@ __global__ void canvas_reset_kernel(int32_t* tokens, uint8_t* committed, int32_t
 
 // ---- optional event timing of the dominant kernel of each step ----
 struct Timing {
-    bool on = false;
+    int target = DG_TIME_OFF;
     static constexpr int kMax = 8192;
     hipEvent_t ev[2 * kMax];
     int used = 0;
@@ -95,9 +95,9 @@ Timing g_timing;
 
 namespace dgapi {
 
-// Records the start event of the dominant kernel; returns the slot or -1.
-int timing_begin(hipStream_t st) {
-    if (!g_timing.on || g_timing.used >= Timing::kMax) return -1;
+// Records the start event of a launch of kernel `target`; returns the slot or -1.
+int timing_begin(hipStream_t st, int target) {
+    if (g_timing.target == DG_TIME_OFF || g_timing.target != target || g_timing.used >= Timing::kMax) return -1;
     int slot = g_timing.used++;
     hipEventRecord(g_timing.ev[2 * slot], st);
     return slot;
@@ -148,13 +148,14 @@ dg_status dg_canvas_reset(dg_canvas* c, int32_t mask_id, void* stream) {
     return hip_check(hipGetLastError(), "canvas_reset launch");
 }
 
-dg_status dg_timing_enable(int32_t on) {
-    if (on && !g_timing.created) {
+dg_status dg_timing_enable(int32_t target) {
+    if (target < DG_TIME_OFF || target > DG_TIME_O_PROJ) return fail(DG_E_INVALID, "unknown timing target %d", target);
+    if (target != DG_TIME_OFF && !g_timing.created) {
         for (int i = 0; i < 2 * Timing::kMax; ++i)
             if (dg_status s = hip_check(hipEventCreate(&g_timing.ev[i]), "hipEventCreate")) return s;
         g_timing.created = true;
     }
-    g_timing.on = on != 0;
+    g_timing.target = target;
     g_timing.used = 0;
     return DG_OK;
 }
@@ -203,7 +204,7 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
     int32_t* sel_list = cv.take<int32_t>(n);
     double* chunk_sum = cv.take<double>((size_t)n * dg::draw_nchunk(vocab));
     int f32 = logits_dtype == DG_F32;
-    int slot = timing_begin(st);
+    int slot = timing_begin(st, DG_TIME_LM_HEAD);
     if (dg_status s = hip_check(dg::launch_logit_stats(logits, f32, ld, n, vocab, canvas->state, step_idx, sp, mask_id,
                                                        canvas->bias_tok, canvas->bias_val, parts, st),
                                 "logit_stats"))

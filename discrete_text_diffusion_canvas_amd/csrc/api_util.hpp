@@ -36,7 +36,7 @@ struct Carve {
 };
 
 // event timing of the dominant kernel of a step (api.hip)
-int timing_begin(hipStream_t st);
+int timing_begin(hipStream_t st, int target);
 void timing_end(int slot, hipStream_t st);
 
 }  // namespace dgapi

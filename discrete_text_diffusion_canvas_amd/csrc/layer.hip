@@ -30,27 +30,114 @@ __global__ void __launch_bounds__(256) embed_kernel(const TE* __restrict__ E, in
 }
 
 // ---------------------------------------------------------------------------
-// y = x / sqrt(mean(x^2) + eps) * w, f32 statistics. One workgroup per row.
+// y = x / sqrt(mean(x^2) + eps) * w, f32 statistics. One workgroup of 256
+// threads per row; the row (d % 4 == 0, d <= 4096) stays in registers as up to
+// 4 float4 per thread between the sum of squares and the scaled store.
 // ---------------------------------------------------------------------------
+constexpr int NORM_V4 = 4;  // float4 per thread: d <= 4096
+
 template <typename TO>
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ X, int d, const float* __restrict__ w,
-                                                      float eps, TO* __restrict__ Y, const int32_t* __restrict__ state) {
-    if (state && state[0]) return;
-    const int i = blockIdx.x;
-    const float* x = X + (int64_t)i * d;
+__device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int nv, const float* __restrict__ w,
+                                               float eps, int d, TO* __restrict__ y) {
     float ss = 0.f;
-    for (int k = threadIdx.x; k < d; k += 256) ss += x[k] * x[k];
+#pragma unroll
+    for (int j = 0; j < NORM_V4; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        if (c < nv) ss += (x[j].x * x[j].x + x[j].y * x[j].y) + (x[j].z * x[j].z + x[j].w * x[j].w);
+    }
     ss = wave_sum(ss);
     __shared__ float red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float rs = 1.f / sqrtf(tot / (float)d + eps);
-    for (int k = threadIdx.x; k < d; k += 256) {
-        float v = x[k] * rs * w[k];
-        if constexpr (sizeof(TO) == 2) Y[(int64_t)i * d + k] = f2bf(v); else Y[(int64_t)i * d + k] = v;
+    const float4* w4 = reinterpret_cast<const float4*>(w);
+#pragma unroll
+    for (int j = 0; j < NORM_V4; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        if (c >= nv) continue;
+        const float4 g = w4[c];
+        const float v[4] = {x[j].x * rs * g.x, x[j].y * rs * g.y, x[j].z * rs * g.z, x[j].w * rs * g.w};
+        if constexpr (sizeof(TO) == 2) {
+            uint2 o;
+            o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            reinterpret_cast<uint2*>(y)[c] = o;
+        } else {
+            reinterpret_cast<float4*>(y)[c] = make_float4(v[0], v[1], v[2], v[3]);
+        }
     }
 }
+
+template <typename TO>
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ X, int d, const float* __restrict__ w,
+                                                      float eps, TO* __restrict__ Y, const int32_t* __restrict__ state) {
+    if (state && state[0]) return;
+    const int i = blockIdx.x, nv = d / 4;
+    const float4* x4 = reinterpret_cast<const float4*>(X + (int64_t)i * d);
+    float4 x[NORM_V4];
+#pragma unroll
+    for (int j = 0; j < NORM_V4; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        x[j] = c < nv ? x4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    norm_row_store<TO>(x, nv, w, eps, d, Y + (int64_t)i * d);
+}
+
+// ---------------------------------------------------------------------------
+// RoPE angles of the rows i in [0, n) at positions pos0 + i: cs[i][d] =
+// (cos a, sin a) with a = pos * base^(-2d/hd), d < hd/2 (rotate-half pairs).
+// The angle is formed and reduced modulo 2*pi in float64 (positions reach
+// 10^5), then sin/cos are taken in float32. Computed once per call and shared
+// by every layer, whose rows sit at the same positions.
+// ---------------------------------------------------------------------------
+__global__ void rope_table_kernel(int hd, int64_t pos0, double base, float* __restrict__ cs,
+                                  const int32_t* __restrict__ state) {
+    if (state && state[0]) return;
+    const int i = blockIdx.x;
+    const int half = hd / 2;
+    for (int dd = threadIdx.x; dd < half; dd += blockDim.x) {
+        const double inv = pow(base, -2.0 * (double)dd / (double)hd);
+        double a = (double)(pos0 + i) * inv;
+        a = fmod(a, 6.283185307179586476925286766559);
+        float sa, ca;
+        sincosf((float)a, &sa, &ca);
+        cs[((int64_t)i * half + dd) * 2] = ca;
+        cs[((int64_t)i * half + dd) * 2 + 1] = sa;
+    }
+}
+
+// 8 consecutive elements of T <-> float (16 bytes of bf16, 32 of f32)
+template <typename T> struct Vec8;
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float* p, float (&v)[8]) {
+        const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float (&v)[8]) {
+        reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+};
+template <> struct Vec8<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&v)[8]) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            v[2 * j] = bf2f((uint16_t)(w[j] & 0xffff));
+            v[2 * j + 1] = bf2f((uint16_t)(w[j] >> 16));
+        }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
+        uint4 x;
+        x.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+        x.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+        x.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+        x.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+        *reinterpret_cast<uint4*>(p) = x;
+    }
+};
 
 // ---------------------------------------------------------------------------
 // RoPE + scatter. qkv [n][(Hq+2Hkv)*hd] (row i at position pos0+i) ->
@@ -58,59 +145,88 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
 //   K  [Hkv][kv_ld][hd]      rows kv_off + i  (rotated)
 //   V^T [Hkv][hd][kv_ld]     columns kv_off + i (V stored transposed)
 // Columns i in [n, v_zero_to) of V^T are set to 0 (the canvas V^T is read in
-// whole 64-key blocks). Rotate-half: for d < hd/2, a = pos * base^(-2d/hd):
+// whole 64-key blocks). Rotate-half with the angles of rope_table_kernel:
 //   out[d] = x[d] cos a - x[d+hd/2] sin a;  out[d+hd/2] = x[d+hd/2] cos a + x[d] sin a.
-// The angle is formed and reduced modulo 2*pi in float64 (positions reach
-// 10^5), then sin/cos are taken in float32. One workgroup per row i handles
-// every head; thread d owns the rotation pair (d, d + hd/2).
+// Grid: (16-row tiles, heads), 256 threads. A Q/K workgroup rotates its 16
+// rows in 8-element chunks (one chunk pair per thread for hd = 256). A V
+// workgroup (x < 64-row tile count) transposes a 64 x hd tile through LDS:
+// all of its loads are issued before the first LDS write, and each V^T row
+// segment leaves as 16-byte stores of 8 consecutive columns.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void rope_scatter_kernel(const T* __restrict__ qkv, int n, int Hq, int Hkv, int hd, int64_t pos0,
-                                    double base, T* __restrict__ Q, int64_t q_ld, int64_t q_off,
-                                    T* __restrict__ K, T* __restrict__ V, int64_t kv_ld, int64_t kv_off,
-                                    int v_zero_to, const int32_t* __restrict__ state) {
+__global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__ qkv, int n, int Hq, int Hkv, int hd,
+                                                           const float* __restrict__ cs, T* __restrict__ Q,
+                                                           int64_t q_ld, int64_t q_off, T* __restrict__ K,
+                                                           T* __restrict__ V, int64_t kv_ld, int64_t kv_off,
+                                                           int v_zero_to, const int32_t* __restrict__ state) {
     if (state && state[0]) return;
-    const int i = blockIdx.x;
-    const int half = hd / 2;
-    auto st = [&](T* p, float v) {
-        if constexpr (sizeof(T) == 2) *p = f2bf(v); else *p = v;
-    };
-    if (i >= n) {  // zero V^T columns past the rows
-        for (int e = threadIdx.x; e < Hkv * hd; e += blockDim.x)
-            st(V + ((int64_t)(e / hd) * hd + e % hd) * kv_ld + kv_off + i, 0.f);
-        return;
-    }
-    const int width = (Hq + 2 * Hkv) * hd;
-    const T* src = qkv + (int64_t)i * width;
-    auto ld = [&](int j) -> float {
-        if constexpr (sizeof(T) == 2) return bf2f(src[j]); else return src[j];
-    };
-    for (int dd = threadIdx.x; dd < half; dd += blockDim.x) {
-        const double inv = pow(base, -2.0 * (double)dd / (double)hd);
-        double a = (double)(pos0 + i) * inv;
-        a = fmod(a, 6.283185307179586476925286766559);
-        float sa, ca;
-        sincosf((float)a, &sa, &ca);
-        for (int h = 0; h < Hq + 2 * Hkv; ++h) {
-            float x1 = ld(h * hd + dd), x2 = ld(h * hd + dd + half);
-            if (h < Hq + Hkv) {
-                const float y1 = x1 * ca - x2 * sa;
-                const float y2 = x2 * ca + x1 * sa;
-                x1 = y1;
-                x2 = y2;
+    const int h = blockIdx.y;
+    const int half = hd / 2, width = (Hq + 2 * Hkv) * hd;
+    if (h < Hq + Hkv) {
+        const int r0 = blockIdx.x * 16;
+        const int cpr = half / 8;  // 8-element chunks per half row
+        const int rows = min(16, n - r0);
+        for (int u = threadIdx.x; u < rows * cpr; u += 256) {
+            const int i = r0 + u / cpr, d0 = (u % cpr) * 8;
+            const T* src = qkv + (int64_t)i * width + h * hd;
+            float x1[8], x2[8], y1[8], y2[8];
+            Vec8<T>::load(src + d0, x1);
+            Vec8<T>::load(src + half + d0, x2);
+            const float4* c4 = reinterpret_cast<const float4*>(cs + ((int64_t)i * half + d0) * 2);
+            const float4 c[4] = {c4[0], c4[1], c4[2], c4[3]};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y1[2 * j] = x1[2 * j] * c[j].x - x2[2 * j] * c[j].y;
+                y2[2 * j] = x2[2 * j] * c[j].x + x1[2 * j] * c[j].y;
+                y1[2 * j + 1] = x1[2 * j + 1] * c[j].z - x2[2 * j + 1] * c[j].w;
+                y2[2 * j + 1] = x2[2 * j + 1] * c[j].z + x1[2 * j + 1] * c[j].w;
             }
-            if (h < Hq) {
-                T* dst = Q + ((int64_t)h * q_ld + q_off + i) * hd;
-                st(dst + dd, x1);
-                st(dst + dd + half, x2);
-            } else if (h < Hq + Hkv) {
-                T* dst = K + ((int64_t)(h - Hq) * kv_ld + kv_off + i) * hd;
-                st(dst + dd, x1);
-                st(dst + dd + half, x2);
+            T* dst = h < Hq ? Q + ((int64_t)h * q_ld + q_off + i) * hd
+                            : K + ((int64_t)(h - Hq) * kv_ld + kv_off + i) * hd;
+            Vec8<T>::store(dst + d0, y1);
+            Vec8<T>::store(dst + half + d0, y2);
+        }
+    } else {
+        extern __shared__ float vt[];  // [64][hd + 1]
+        const int r0 = blockIdx.x * 64;
+        const int rows = min(64, max(n, v_zero_to) - r0);
+        if (rows <= 0) return;
+        const int hv = h - Hq - Hkv;
+        const int cpr = hd / 8;      // 8-element chunks per row
+        constexpr int MAXU = 8;      // 64 rows x 32 chunks (hd 256) / 256 threads
+        float v[MAXU][8];
+#pragma unroll
+        for (int j = 0; j < MAXU; ++j) {
+            const int u = threadIdx.x + 256 * j;
+            const int r = u / cpr, i = r0 + r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+            if (r < rows && i < n) Vec8<T>::load(qkv + (int64_t)i * width + h * hd + (u % cpr) * 8, v[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < MAXU; ++j) {
+            const int u = threadIdx.x + 256 * j;
+            const int r = u / cpr, c = (u % cpr) * 8;
+            if (r < rows)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vt[r * (hd + 1) + c + e] = v[j][e];
+        }
+        __syncthreads();
+        // output unit: (dim d, 8 consecutive columns)
+        const int cgs = (rows + 7) / 8;
+        const bool vec = ((kv_off + r0) % 8) == 0 && rows % 8 == 0;
+        for (int u = threadIdx.x; u < hd * cgs; u += 256) {
+            const int d = u / cgs, c0 = (u % cgs) * 8;
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = c0 + e < rows ? vt[(c0 + e) * (hd + 1) + d] : 0.f;
+            T* dst = V + ((int64_t)hv * hd + d) * kv_ld + kv_off + r0 + c0;
+            if (vec) {
+                Vec8<T>::store(dst, o);
             } else {
-                T* dst = V + (int64_t)(h - Hq - Hkv) * hd * kv_ld + kv_off + i;
-                st(dst + (int64_t)dd * kv_ld, x1);
-                st(dst + (int64_t)(dd + half) * kv_ld, x2);
+                for (int e = 0; e < 8 && c0 + e < rows; ++e) {
+                    if constexpr (sizeof(T) == 2) dst[e] = f2bf(o[e]); else dst[e] = o[e];
+                }
             }
         }
     }
@@ -168,78 +284,123 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
 // order (token-major); then the shared expert's n slots in token order.
 // offsets has E+2 entries (group g = [offsets[g], offsets[g+1]), g = E is the
 // shared expert); perm[slot] = token; slot_of[token*k + j] = slot of its j-th
-// expert. Counts come from LDS atomics; placement is deterministic: wave w
-// handles experts w, w+16, ... and walks the assignments in chunks of 64 with
-// a ballot, so the rank inside a group is a popcount.
+// expert; hit = [count, hit groups in increasing id..., E]; hit_mb = the
+// largest number of 64-row blocks of a group.
+//
+// A stable counting sort without serial scans: the assignments are cut into
+// chunks of 64 (one wavefront each). Inside a chunk the lanes holding the
+// same expert id are found with one ballot per id bit, so a lane's rank among
+// them is a popcount and the chunk's count per expert is written by its first
+// lane. A scan over the chunks per expert and one over the experts then give
+// every assignment its slot: offset(expert) + earlier chunks + rank.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __restrict__ ids, int n, int k, int E,
                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ slot_of, int32_t* __restrict__ hit,
                                                             int32_t* __restrict__ hit_mb,
+                                                            int32_t* __restrict__ hit_out,
                                                             const int32_t* __restrict__ state) {
     if (state && state[0]) return;
-    extern __shared__ int32_t sh[];
+    extern __shared__ __align__(16) unsigned char shraw[];
     const int total = n * k;
-    int32_t* cnt = sh;               // [E + 1]
-    int32_t* off = sh + E + 1;       // [E + 2]
-    int32_t* sid = off + E + 2;      // [total]
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e <= E; e += 1024) cnt[e] = 0;
+    const int nch = (total + 63) / 64;
+    int32_t* off = reinterpret_cast<int32_t*>(shraw);            // [E + 2]
+    int32_t* tot = off + E + 2;                                    // [E]
+    uint16_t* cbase = reinterpret_cast<uint16_t*>(tot + E);        // [nch][E] assignments of e in earlier chunks
+    uint16_t* esid = cbase + (size_t)nch * E;                      // [total] expert of each assignment
+    uint8_t* ccnt = reinterpret_cast<uint8_t*>(esid + total);      // [nch][E] count of e in the chunk
+    uint8_t* rank = ccnt + (size_t)nch * E;                        // [total] rank inside its chunk
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < nch * E; i += 1024) ccnt[i] = 0;
     __syncthreads();
-    for (int a = tid; a < total; a += 1024) {
-        int e = ids[a];
-        sid[a] = e;
-        atomicAdd(&cnt[e], 1);
+    int nbits = 1;
+    while ((1 << nbits) <= E) ++nbits;  // ids 0..E (E marks an empty lane)
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    for (int c = wave; c < nch; c += 16) {
+        const int a = c * 64 + lane;
+        const int e = a < total ? ids[a] : E;
+        unsigned long long peers = ~0ull;
+        for (int bit = 0; bit < nbits; ++bit) {
+            const unsigned long long m = __ballot((e >> bit) & 1);
+            peers &= ((e >> bit) & 1) ? m : ~m;
+        }
+        if (a < total) {
+            const int r = __popcll(peers & lt);
+            esid[a] = (uint16_t)e;
+            rank[a] = (uint8_t)r;
+            if (r == 0) ccnt[c * E + e] = (uint8_t)__popcll(peers);
+        }
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0, h = 0, mbm = n > 0 ? (n + 63) / 64 : 0;
-        for (int e = 0; e < E; ++e) {
-            off[e] = run;
-            run += cnt[e];
-            if (cnt[e] > 0) {
-                hit[1 + h++] = e;
-                mbm = max(mbm, (cnt[e] + 63) / 64);
-            }
+    // per expert: running count over the chunks
+    for (int e = tid; e < E; e += 1024) {
+        int run = 0;
+        for (int c = 0; c < nch; ++c) {
+            cbase[c * E + e] = (uint16_t)run;
+            run += ccnt[c * E + e];
         }
-        off[E] = run;
-        off[E + 1] = run + n;
-        if (n > 0) hit[1 + h++] = E;   // the shared expert: every token
-        hit[0] = h;
-        *hit_mb = mbm;
+        tot[e] = run;
+    }
+    __syncthreads();
+    // exclusive scan over the experts, the hit list and the largest block
+    // count, by wavefront 0 (each lane takes a run of consecutive experts)
+    if (wave == 0) {
+        const int per = (E + 63) / 64;
+        const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+        int sum = 0, nz = 0, mb = 0;
+        for (int e = e0; e < e1; ++e) {
+            sum += tot[e];
+            nz += tot[e] > 0;
+            mb = max(mb, (tot[e] + 63) / 64);
+        }
+        int isum = sum, inz = nz;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int vs = __shfl_up(isum, o, 64), vz = __shfl_up(inz, o, 64);
+            if (lane >= o) { isum += vs; inz += vz; }
+            mb = max(mb, __shfl_xor(mb, o, 64));
+        }
+        int run = isum - sum, h = inz - nz;
+        for (int e = e0; e < e1; ++e) {
+            off[e] = run;
+            run += tot[e];
+            if (tot[e] > 0) hit[1 + h++] = e;
+        }
+        if (lane == 63) {
+            // inz is now the number of routed experts hit
+            off[E] = isum;
+            off[E + 1] = isum + n;
+            int hh = inz;
+            if (hit_out) *hit_out = hh;  // routed experts only
+            if (n > 0) hit[1 + hh++] = E;  // the shared expert: every token
+            hit[0] = hh;
+            *hit_mb = max(mb, n > 0 ? (n + 63) / 64 : 0);
+        }
     }
     __syncthreads();
     for (int e = tid; e <= E + 1; e += 1024) offsets[e] = off[e];
-    for (int e = wave; e < E; e += 16) {
-        if (cnt[e] == 0) continue;
-        int base = off[e];
-        for (int c = 0; c < total; c += 64) {
-            const int a = c + lane;
-            const bool hit = a < total && sid[a] == e;
-            const unsigned long long m = __ballot(hit);
-            if (hit) {
-                const int rank = __popcll(m & ((1ull << lane) - 1ull));
-                const int slot = base + rank;
-                perm[slot] = a / k;
-                slot_of[a] = slot;
-            }
-            base += __popcll(m);
-        }
+    for (int a = tid; a < total; a += 1024) {
+        const int e = esid[a];
+        const int slot = off[e] + cbase[(a >> 6) * E + e] + rank[a];
+        perm[slot] = a / k;
+        slot_of[a] = slot;
     }
     for (int i = tid; i < n; i += 1024) perm[off[E] + i] = i;
 }
 
 // ---------------------------------------------------------------------------
 // X[i] += Y[shared slot of i] + sum_j gate[i][j] * Y[slot_of[i][j]] (j ascending).
-// One workgroup per token.
+// One workgroup per token (d % 4 == 0, d <= 4096). With nw != NULL the new row
+// is also normalised (the next layer's pre-attention RMSNorm, or the final
+// norm) into A, from the registers that hold it.
 // ---------------------------------------------------------------------------
+template <typename TO>
 __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int d, const float* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gates, int k, int shared_off,
+                                                      const float* __restrict__ nw, float eps, TO* __restrict__ A,
                                                       const int32_t* __restrict__ state) {
     if (state && state[0]) return;
-    const int i = blockIdx.x;
+    const int i = blockIdx.x, nv = d / 4;
     __shared__ int sl[16];
     __shared__ float gt[16];
     if (threadIdx.x < k) {
@@ -247,12 +408,26 @@ __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int
         gt[threadIdx.x] = gates[(int64_t)i * k + threadIdx.x];
     }
     __syncthreads();
-    const float* ysh = Y + (int64_t)(shared_off + i) * d;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        float acc = ysh[c];
-        for (int j = 0; j < k; ++j) acc += gt[j] * Y[(int64_t)sl[j] * d + c];
-        X[(int64_t)i * d + c] += acc;
+    const float4* ysh = reinterpret_cast<const float4*>(Y + (int64_t)(shared_off + i) * d);
+    float4* xr = reinterpret_cast<float4*>(X + (int64_t)i * d);
+    float4 x[NORM_V4];
+#pragma unroll
+    for (int j = 0; j < NORM_V4; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c >= nv) continue;
+        float4 acc = ysh[c];
+        for (int e = 0; e < k; ++e) {
+            const float4 y = reinterpret_cast<const float4*>(Y + (int64_t)sl[e] * d)[c];
+            const float g = gt[e];
+            acc.x += g * y.x; acc.y += g * y.y; acc.z += g * y.z; acc.w += g * y.w;
+        }
+        float4 v = xr[c];
+        v.x += acc.x; v.y += acc.y; v.z += acc.z; v.w += acc.w;
+        xr[c] = v;
+        x[j] = v;
     }
+    if (nw) norm_row_store<TO>(x, nv, nw, eps, d, A + (int64_t)i * d);
 }
 
 // ---------------------------------------------------------------------------
@@ -267,24 +442,43 @@ hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, i
 
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
                           const int32_t* state, hipStream_t st) {
+    if (d % 4 || d > 4 * 256 * NORM_V4) return hipErrorInvalidValue;
     if (act_f32) rmsnorm_kernel<float><<<n, 256, 0, st>>>(X, d, w, eps, (float*)Y, state);
     else rmsnorm_kernel<uint16_t><<<n, 256, 0, st>>>(X, d, w, eps, (uint16_t*)Y, state);
     return hipGetLastError();
 }
 
-hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, int64_t pos0,
-                               double base, void* Q, int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld,
-                               int64_t kv_off, int v_zero_to, const int32_t* state, hipStream_t st) {
+hipError_t launch_rope_table(int n, int hd, int64_t pos0, double base, float* cs, const int32_t* state,
+                             hipStream_t st) {
+    rope_table_kernel<<<n, std::max(64, std::min(256, hd / 2)), 0, st>>>(hd, pos0, base, cs, state);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, const float* cs, void* Q,
+                               int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld, int64_t kv_off,
+                               int v_zero_to, const int32_t* state, hipStream_t st) {
+    if (hd % 16 || hd > 256) return hipErrorInvalidValue;
     const int rows = std::max(n, v_zero_to);
-    const int threads = std::max(64, std::min(256, hd / 2));
+    const dim3 grid((rows + 15) / 16, Hq + 2 * Hkv);
+    const size_t lds = (size_t)64 * (hd + 1) * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rope_scatter_kernel<float>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 257 * 4);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(rope_scatter_kernel<uint16_t>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 257 * 4);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
     if (act_f32)
-        rope_scatter_kernel<float><<<rows, threads, 0, st>>>((const float*)qkv, n, Hq, Hkv, hd, pos0, base, (float*)Q,
-                                                             q_ld, q_off, (float*)K, (float*)V, kv_ld, kv_off,
-                                                             v_zero_to, state);
+        rope_scatter_kernel<float><<<grid, 256, lds, st>>>((const float*)qkv, n, Hq, Hkv, hd, cs, (float*)Q, q_ld,
+                                                           q_off, (float*)K, (float*)V, kv_ld, kv_off, v_zero_to,
+                                                           state);
     else
-        rope_scatter_kernel<uint16_t><<<rows, threads, 0, st>>>((const uint16_t*)qkv, n, Hq, Hkv, hd, pos0, base,
-                                                                (uint16_t*)Q, q_ld, q_off, (uint16_t*)K,
-                                                                (uint16_t*)V, kv_ld, kv_off, v_zero_to, state);
+        rope_scatter_kernel<uint16_t><<<grid, 256, lds, st>>>((const uint16_t*)qkv, n, Hq, Hkv, hd, cs, (uint16_t*)Q,
+                                                              q_ld, q_off, (uint16_t*)K, (uint16_t*)V, kv_ld, kv_off,
+                                                              v_zero_to, state);
     return hipGetLastError();
 }
 
@@ -295,10 +489,12 @@ hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, i
 }
 
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
-                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, const int32_t* state,
-                               hipStream_t st) {
-    size_t lds = (size_t)(2 * E + 3 + n * k) * sizeof(int32_t);
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
+                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hit_out,
+                               const int32_t* state, hipStream_t st) {
+    const size_t total = (size_t)n * k, nch = (total + 63) / 64;
+    // off, tot (int32); cbase (u16 [nch][E]); esid (u16 [total]); ccnt (u8 [nch][E]); rank (u8 [total])
+    const size_t lds = (size_t)(2 * E + 2) * 4 + nch * E * 2 + total * 2 + nch * E + total;
+    if (lds > 160 * 1024 || E > 65535 || total > 65535) return hipErrorInvalidValue;
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(hist_permute_kernel),
@@ -306,13 +502,20 @@ hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t*
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hist_permute_kernel<<<1, 1024, lds, st>>>(ids, n, k, E, offsets, perm, slot_of, hit, hit_mb, state);
+    hist_permute_kernel<<<1, 1024, lds, st>>>(ids, n, k, E, offsets, perm, slot_of, hit, hit_mb, hit_out, state);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
-                          int shared_off, const int32_t* state, hipStream_t st) {
-    combine_kernel<<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, state);
+                          int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
+                          hipStream_t st) {
+    if (d % 4 || d > 4 * 256 * NORM_V4 || k > 16) return hipErrorInvalidValue;
+    if (act_f32)
+        combine_kernel<float><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
+                                                 state);
+    else
+        combine_kernel<uint16_t><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
+                                                    (uint16_t*)A, state);
     return hipGetLastError();
 }
 

@@ -10,16 +10,19 @@ hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, i
                         const int32_t* state, hipStream_t st);
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
                           const int32_t* state, hipStream_t st);
-hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, int64_t pos0,
-                               double base, void* Q, int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld,
-                               int64_t kv_off, int v_zero_to, const int32_t* state, hipStream_t st);
+hipError_t launch_rope_table(int n, int hd, int64_t pos0, double base, float* cs, const int32_t* state,
+                             hipStream_t st);
+hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, const float* cs, void* Q,
+                               int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld, int64_t kv_off,
+                               int v_zero_to, const int32_t* state, hipStream_t st);
 hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, int k, int32_t* ids, float* gates,
                               const int32_t* state, hipStream_t st);
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
-                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, const int32_t* state,
-                               hipStream_t st);
+                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hit_out,
+                               const int32_t* state, hipStream_t st);
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
-                          int shared_off, const int32_t* state, hipStream_t st);
+                          int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
+                          hipStream_t st);
 
 // Attention over up to two key segments per KV head (V stored transposed):
 //   segment 1: K1 [Hkv][ld1][hd], V1^T [Hkv][hd][ld1], rows [s1, e1) (cache),

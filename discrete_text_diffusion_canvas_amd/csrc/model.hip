@@ -46,6 +46,7 @@ struct Work {
     void* Kc;          // [Hkv][T64][hd]
     void* Vc;          // [Hkv][hd][T64] (transposed)
     void* O;           // [T][Hq hd]
+    float* rope_cs;    // [T][hd/2][2] cos, sin of the rows' RoPE angles
     float* part_o;     // attention split partials
     float* part_ml;
     float* rlog;       // [T][E]
@@ -64,6 +65,7 @@ struct Work {
     size_t bytes;
     int rows;
     int rows64;        // T rounded up to a multiple of 64 (canvas K/V row stride)
+    int32_t* experts_hit = nullptr;  // optional [n_layers] routed experts hit per layer (caller's buffer)
 };
 
 Work carve(const dg_model* m, void* base, int T) {
@@ -82,6 +84,7 @@ Work carve(const dg_model* m, void* base, int T) {
     w.Kc = cv.take<char>((size_t)T64 * Hkv * hd * ab);
     w.Vc = cv.take<char>((size_t)T64 * Hkv * hd * ab);
     w.O = cv.take<char>((size_t)T * Hq * hd * ab);
+    w.rope_cs = cv.take<float>((size_t)T * hd);
     w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
     w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
     w.rlog = cv.take<float>((size_t)T * E);
@@ -127,7 +130,8 @@ dg::GemmArgs gargs() {
 // ---------------------------------------------------------------------------
 // The MoE half of a layer on rows X[0..n): X += shared(b) + sum_j g_j expert_j(b)
 // ---------------------------------------------------------------------------
-dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_t* state, hipStream_t st) {
+dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float* next_norm, const int32_t* state,
+                    hipStream_t st) {
     const dg_config& c = m->cfg;
     const dg_layer_weights& L = m->layers[l];
     const int d = c.d_model, E = c.n_experts, k = c.top_k, F = c.ffn_hidden;
@@ -140,7 +144,8 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
     }
     DG_TRY(dg::launch_router_topk(w.rlog, L.router_bias, n, E, k, w.ids, w.gates, state, st), "router topk");
-    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, w.hit, w.hit_mb, state, st),
+    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, w.hit, w.hit_mb,
+                                   w.experts_hit ? w.experts_hit + l : nullptr, state, st),
            "hist permute");
     {   // gate/up with SwiGLU
         dg::GemmArgs g = gargs();
@@ -149,7 +154,9 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         g.w_scale = (const uint16_t*)L.gate_scale; g.w2_scale = (const uint16_t*)L.up_scale; g.scale_group_stride = F;
         g.M = n; g.N = 2 * F; g.K = d; g.group_offsets = w.offsets; g.hit = w.hit; g.hit_mb = w.hit_mb;
         g.C = w.Hbuf; g.ldc = F; g.c_f32 = f32; g.state = state;
+        const int slot = timing_begin(st, DG_TIME_EXPERT_GATE_UP);
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, dg::SHAPE_SMALL_M, st), "expert gate/up");
+        timing_end(slot, st);
     }
     {   // down
         dg::GemmArgs g = gargs();
@@ -158,9 +165,13 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const int32_
         g.w_scale = (const uint16_t*)L.down_scale; g.scale_group_stride = d;
         g.M = n; g.N = d; g.K = F; g.group_offsets = w.offsets; g.hit = w.hit; g.hit_mb = w.hit_mb;
         g.C = w.Y; g.ldc = d; g.c_f32 = 1; g.state = state;
+        const int slot = timing_begin(st, DG_TIME_EXPERT_DOWN);
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_STORE_F32, E + 1, dg::SHAPE_SMALL_M, st), "expert down");
+        timing_end(slot, st);
     }
-    DG_TRY(dg::launch_combine(w.X, n, d, w.Y, w.slot_of, w.gates, k, n * k, state, st), "combine");
+    DG_TRY(dg::launch_combine(w.X, n, d, w.Y, w.slot_of, w.gates, k, n * k, next_norm, c.norm_eps, w.A, f32, state,
+                              st),
+           "combine");
     return DG_OK;
 }
 
@@ -176,23 +187,27 @@ int attn_splits(const dg_config& c, int nq, int64_t keys) {
 // ---------------------------------------------------------------------------
 // Decoder layer over the canvas rows X[0..n) at positions P..P+n-1.
 // ---------------------------------------------------------------------------
+// With normed_in, w.A already holds rmsnorm(X) with this layer's attention
+// norm; next_norm (or NULL) is normalised into w.A by the closing combine.
 dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg_kv* kv, const int32_t* state,
-                        hipStream_t st) {
+                        bool normed_in, const float* next_norm, hipStream_t st) {
     const dg_config& c = m->cfg;
     const dg_layer_weights& L = m->layers[l];
     const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
     const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
     const int64_t P = kv->len;
-    DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
+    if (!normed_in) DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
     {
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N; g.state = state;
+        const int slot = timing_begin(st, DG_TIME_QKV);
         DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
                "qkv gemm");
+        timing_end(slot, st);
     }
-    DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows64,
-                                   0, w.rows64, state, st),
+    DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows64, 0,
+                                   w.rows64, state, st),
            "rope");
     {
         dg::AttnArgs a;
@@ -206,15 +221,19 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
         a.O = w.O; a.part_o = w.part_o; a.part_ml = w.part_ml;
         a.splits = attn_splits(c, n, (a.e1 - a.s1) + n);
         a.state = state;
+        const int slot = timing_begin(st, DG_TIME_ATTENTION);
         DG_TRY(dg::launch_attention(a, f32, st), "attention");
+        timing_end(slot, st);
     }
     {
         dg::GemmArgs g = gargs();
         g.A = w.O; g.lda = Hq * hd; g.W = L.wo; g.ldw = Hq * hd; g.w_scale = (const uint16_t*)L.wo_scale;
         g.M = n; g.N = d; g.K = Hq * hd; g.X = w.X; g.ldx = d; g.state = state;
+        const int slot = timing_begin(st, DG_TIME_O_PROJ);
         DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_RESIDUAL, 0, dg::SHAPE_PROJ, st), "o gemm");
+        timing_end(slot, st);
     }
-    return moe_block(m, l, w, n, state, st);
+    return moe_block(m, l, w, n, next_norm, state, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -225,16 +244,17 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
     const dg_config& c = m->cfg;
     const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
     const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
+    DG_TRY(dg::launch_rope_table(n, hd, P, c.rope_base, w.rope_cs, nullptr, st), "rope table");
     for (int l = 0; l < c.n_layers; ++l) {
         const dg_layer_weights& L = m->layers[l];
-        DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, nullptr, st), "rmsnorm");
+        if (l == 0) DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, nullptr, st), "rmsnorm");
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N;
         DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
                "qkv gemm");
-        DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, P, c.rope_base, w.Q, w.rows, 0, kv->k[l],
-                                       kv->v[l], kv->capacity, P, 0, nullptr, st),
+        DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0, kv->k[l], kv->v[l],
+                                       kv->capacity, P, 0, nullptr, st),
                "rope");
         if (l == c.n_layers - 1) break;  // nothing in the cache depends on the rest
         dg::AttnArgs a;
@@ -251,17 +271,19 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         go.A = w.O; go.lda = Hq * hd; go.W = L.wo; go.ldw = Hq * hd; go.w_scale = (const uint16_t*)L.wo_scale;
         go.M = n; go.N = d; go.K = Hq * hd; go.X = w.X; go.ldx = d;
         DG_TRY(dg::gemm_launch(go, f32, fp8, dg::EPI_RESIDUAL, 0, dg::SHAPE_PROJ, st), "o gemm");
-        if (dg_status s = moe_block(m, l, w, n, nullptr, st)) return s;
+        // the next layer's attention norm rides on this layer's combine
+        if (dg_status s = moe_block(m, l, w, n, m->layers[l + 1].attn_norm, nullptr, st)) return s;
     }
     return DG_OK;
 }
 
 dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerParams& sp, int step_override,
                   const int32_t* state, const int32_t* bias_tok, const float* bias_val, dg_step_stats* stats,
-                  hipStream_t st) {
+                  bool normed_in, hipStream_t st) {
     const dg_config& c = m->cfg;
     const int f32 = c.act_dtype == DG_F32;
-    DG_TRY(dg::launch_rmsnorm(w.X, n, c.d_model, m->final_norm, c.norm_eps, w.A, f32, state, st), "final norm");
+    if (!normed_in)
+        DG_TRY(dg::launch_rmsnorm(w.X, n, c.d_model, m->final_norm, c.norm_eps, w.A, f32, state, st), "final norm");
     dg::GemmArgs g = gargs();
     g.A = w.A; g.lda = c.d_model; g.W = m->embed; g.ldw = c.d_model;
     g.M = n; g.N = c.vocab; g.K = c.d_model;
@@ -269,7 +291,7 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
     g.parts = w.parts; g.nsplit = lm_nsplit(c);
     g.state = state; g.step_override = step_override; g.sp = sp; g.mask_id = c.mask_id;
     g.bias_tok = bias_tok; g.bias_val = bias_val;
-    int slot = timing_begin(st);
+    int slot = timing_begin(st, DG_TIME_LM_HEAD);
     DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
     timing_end(slot, st);
     DG_TRY(dg::launch_merge_rows(w.parts, n, lm_nsplit(c), state, stats->entropy, stats->lse, stats->argmax, st),
@@ -309,7 +331,8 @@ extern "C" {
 dg_status dg_model_create(const dg_config* c, const dg_weights* w, dg_model** out) {
     if (!c || !w || !out) return fail(DG_E_INVALID, "NULL argument");
     *out = nullptr;
-    if (c->n_layers < 1 || c->d_model < 32 || c->d_model % 32) return fail(DG_E_SHAPE, "d_model must be a multiple of 32");
+    if (c->n_layers < 1 || c->d_model < 32 || c->d_model % 32 || c->d_model > 4096)
+        return fail(DG_E_SHAPE, "d_model must be a multiple of 32 in 32..4096");
     if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads)
         return fail(DG_E_SHAPE, "n_q_heads must be a positive multiple of n_kv_heads");
     if (c->act_dtype != DG_F32 && c->act_dtype != DG_BF16) return fail(DG_E_UNSUPPORTED, "act_dtype");
@@ -329,12 +352,17 @@ dg_status dg_model_create(const dg_config* c, const dg_weights* w, dg_model** ou
     if (c->window < 0 || c->global_every < 0) return fail(DG_E_INVALID, "window/global_every must be >= 0");
     if (!(c->rope_base > 1.f) || !(c->norm_eps >= 0.f)) return fail(DG_E_INVALID, "rope_base/norm_eps");
     if (!w->embed || !w->final_norm || !w->layers) return fail(DG_E_INVALID, "weight pointer is NULL");
+    auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+    if (!a16(w->embed) || !a16(w->final_norm)) return fail(DG_E_INVALID, "weights must be 16-byte aligned");
     const bool fp8 = c->weight_dtype == DG_FP8_E4M3;
     for (int l = 0; l < c->n_layers; ++l) {
         const dg_layer_weights& L = w->layers[l];
         if (!L.attn_norm || !L.moe_norm || !L.wqkv || !L.wo || !L.router || !L.router_bias || !L.w_gate ||
             !L.w_up || !L.w_down)
             return fail(DG_E_INVALID, "layer %d: weight pointer is NULL", l);
+        if (!a16(L.attn_norm) || !a16(L.moe_norm) || !a16(L.wqkv) || !a16(L.wo) || !a16(L.router) ||
+            !a16(L.w_gate) || !a16(L.w_up) || !a16(L.w_down))
+            return fail(DG_E_INVALID, "layer %d: weights must be 16-byte aligned", l);
         if (fp8 && (!L.wqkv_scale || !L.wo_scale || !L.gate_scale || !L.up_scale || !L.down_scale))
             return fail(DG_E_INVALID, "layer %d: e4m3 weights need scales", l);
     }
@@ -374,7 +402,8 @@ dg_status dg_decoder_layer(const dg_model* m, int32_t layer, float* X, int32_t n
     hipStream_t st = (hipStream_t)stream;
     const size_t xb = (size_t)n * m->cfg.d_model * sizeof(float);
     DG_TRY(hipMemcpyAsync(w.X, X, xb, hipMemcpyDeviceToDevice, st), "copy X in");
-    if (dg_status s = decoder_layer(m, layer, w, n, kv, nullptr, st)) return s;
+    DG_TRY(dg::launch_rope_table(n, m->cfg.head_dim, kv->len, m->cfg.rope_base, w.rope_cs, nullptr, st), "rope table");
+    if (dg_status s = decoder_layer(m, layer, w, n, kv, nullptr, false, nullptr, st)) return s;
     DG_TRY(hipMemcpyAsync(X, w.X, xb, hipMemcpyDeviceToDevice, st), "copy X out");
     const size_t kb = (size_t)n * m->cfg.top_k;
     if (route_ids) DG_TRY(hipMemcpyAsync(route_ids, w.ids, kb * 4, hipMemcpyDeviceToDevice, st), "copy ids");
@@ -395,7 +424,7 @@ dg_status dg_lm_head(const dg_model* m, const float* X, int32_t n, const dg_samp
     if (dg_status s = ws_for(m, ws, ws_bytes, n, &w)) return s;
     hipStream_t st = (hipStream_t)stream;
     DG_TRY(hipMemcpyAsync(w.X, X, (size_t)n * m->cfg.d_model * 4, hipMemcpyDeviceToDevice, st), "copy X");
-    return lm_head(m, w, n, to_params(scfg), step_idx, nullptr, bias_tok, bias_val, stats, st);
+    return lm_head(m, w, n, to_params(scfg), step_idx, nullptr, bias_tok, bias_val, stats, false, st);
 }
 
 dg_status dg_prefill_append(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t n, void* ws,
@@ -438,14 +467,19 @@ dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, 
     if (step_idx < -1 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
     Work w;
     if (dg_status s = ws_for(m, ws, ws_bytes, n, &w)) return s;
+    w.experts_hit = stats->experts_hit;
     hipStream_t st = (hipStream_t)stream;
     const dg::SamplerParams sp = to_params(scfg);
     const dg_config& c = m->cfg;
     DG_TRY(dg::launch_embed(m->embed, c.act_dtype == DG_F32, c.d_model, canvas->tokens, n, w.X, canvas->state, st),
            "embed");
-    for (int l = 0; l < c.n_layers; ++l)
-        if (dg_status s = decoder_layer(m, l, w, n, kv, canvas->state, st)) return s;
-    if (dg_status s = lm_head(m, w, n, sp, step_idx, canvas->state, canvas->bias_tok, canvas->bias_val, stats, st))
+    DG_TRY(dg::launch_rope_table(n, c.head_dim, kv->len, c.rope_base, w.rope_cs, canvas->state, st), "rope table");
+    for (int l = 0; l < c.n_layers; ++l) {
+        const float* next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
+        if (dg_status s = decoder_layer(m, l, w, n, kv, canvas->state, l > 0, next, st)) return s;
+    }
+    if (dg_status s = lm_head(m, w, n, sp, step_idx, canvas->state, canvas->bias_tok, canvas->bias_val, stats, true,
+                              st))
         return s;
     return hip_check(dg::launch_sampler_tail(stats->logits, c.act_dtype == DG_F32, stats->logits_ld, n, c.vocab,
                                              c.mask_id, canvas->bias_tok, canvas->bias_val, stats->entropy,

@@ -103,6 +103,9 @@ typedef struct dg_step_stats {
     void* logits;          /* dg_canvas_step: [n][logits_ld] logits of record (act dtype), written;
                               dg_sampler_step: unused */
     int64_t logits_ld;
+    int32_t* experts_hit;  /* optional (NULL = not written), dg_canvas_step only: [n_layers] number of
+                              routed experts that received at least one canvas row in each layer
+                              (the shared expert not counted) */
 } dg_step_stats;
 
 /* Library version string. */
@@ -120,15 +123,33 @@ dg_sampler_cfg dg_sampler_default(void);
 dg_status dg_canvas_reset(dg_canvas* canvas, int32_t mask_id, void* stream);
 
 /*
- * Event timing of each step's dominant kernel (measurement support, not part
- * of the method). dg_timing_enable(1) creates the event pool on first use and
- * starts recording a start/stop event pair on the caller's stream around the
- * dominant kernel of every following eager step (the logit-statistics kernel
- * of dg_sampler_step); dg_timing_read synchronises on the recorded events,
- * returns their summed elapsed milliseconds and count, and clears the list.
- * At most 8192 pairs are kept; later launches are not timed. Not thread-safe.
+ * Event timing of one kernel of the step (measurement support, not part of
+ * the method). dg_timing_enable(target) creates the event pool on first use
+ * and starts recording a start/stop event pair on the caller's stream around
+ * every following eager launch of the chosen kernel:
+ *   DG_TIME_LM_HEAD          the LM-head GEMM with its statistics epilogue
+ *                            (dg_canvas_step, dg_lm_head), or the
+ *                            logit-statistics kernel of dg_sampler_step;
+ *   DG_TIME_EXPERT_GATE_UP   the grouped expert gate/up GEMM with SwiGLU;
+ *   DG_TIME_EXPERT_DOWN      the grouped expert down GEMM;
+ *   DG_TIME_QKV              the QKV projection;
+ *   DG_TIME_ATTENTION        the canvas + prefix attention kernel;
+ *   DG_TIME_O_PROJ           the output projection.
+ * DG_TIME_OFF (0) stops recording. dg_timing_read synchronises on the
+ * recorded events, returns their summed elapsed milliseconds and count, and
+ * clears the list. At most 8192 pairs are kept; later launches are not
+ * timed. Not thread-safe.
  */
-dg_status dg_timing_enable(int32_t on);
+enum {
+    DG_TIME_OFF = 0,
+    DG_TIME_LM_HEAD = 1,
+    DG_TIME_EXPERT_GATE_UP = 2,
+    DG_TIME_EXPERT_DOWN = 3,
+    DG_TIME_QKV = 4,
+    DG_TIME_ATTENTION = 5,
+    DG_TIME_O_PROJ = 6
+};
+dg_status dg_timing_enable(int32_t target);
 dg_status dg_timing_read(double* total_ms, int32_t* launches);
 
 /* Workspace bytes dg_sampler_step needs for n rows of `vocab` logits. */
