@@ -52,6 +52,10 @@ hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int g
 hipError_t launch_lmhead_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t stream_gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int max_rows,
                               hipStream_t st);
+// LDS-staged grouped GEMM over the big-group list in g.hit / g.hit_mb
+// (bf16 activations and weights, K % 64 == 0; SwiGLU or f32 store).
+bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi);
+hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // LM-head epilogue: logits of record (accumulator rounded to the storage

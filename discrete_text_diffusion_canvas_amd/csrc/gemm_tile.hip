@@ -1,0 +1,300 @@
+// LDS-staged grouped GEMM for gfx950 (bf16): C[m][n] = sum_k A[m][k] W[n][k]
+// for the expert groups that received many rows.
+//
+// The expert SwiGLU layers of the MoE (DiffusionGemma model card (zh-TW),
+// intro list and spec table: 8 of 128 experts active plus 1 shared expert)
+// read each hit expert's weights once. When a group holds many rows, the
+// register-fragment streaming kernel (gemm_stream.hip) would re-read the
+// weight tile once per 64-row block and load as many activation bytes as
+// weight bytes through the fragment path, whose total throughput is bounded
+// well below HBM bandwidth. Here a workgroup owns up to 256 rows of one group
+// (one m-block) and BN weight rows, so each weight byte is fetched once, and
+// both operands arrive as whole 128-byte row segments:
+//
+//   * stages of 64 k: each lane loads 16-byte pieces of the A rows (gathered
+//     through the permutation) and of the BN weight rows into registers, two
+//     stages ahead, 8 lanes per 128-byte row segment, then writes them into
+//     one of two LDS slots; chunk c of LDS row r is stored at
+//     c ^ ((r >> 1) & 7) so MFMA fragment reads are conflict-free. (Register
+//     loads keep overlapping with the MFMAs; LDS-direct copies measured here
+//     serialise with them.) One barrier per stage;
+//   * 4 waves, wave w owns rows [64w, 64w + 64) x all BN columns (4 x BN/16
+//     MFMA 16x16x32 tiles); a wave whose rows lie past the group's rows skips
+//     its MFMAs (its copies read one valid row);
+//   * the epilogue transposes the tile through LDS and leaves in 16-byte
+//     coalesced stores: SwiGLU (BN/2 gate + BN/2 up columns of the same
+//     hidden units) to bf16, or a plain f32 store.
+//
+// Work items (group from the big-group list, m-block, n-tile) are walked by a
+// persistent grid; the m-blocks of one (group, n-tile) get ids 8 apart so they
+// run on one XCD and the repeated weight reads hit its L2.
+#include "common.hpp"
+#include "gemm.hpp"
+
+// build-time tunables: weight rows per workgroup of the gate/up and down GEMMs
+#ifndef DG_TILE_BN_GU
+#define DG_TILE_BN_GU 64
+#endif
+#ifndef DG_TILE_BN_DN
+#define DG_TILE_BN_DN 64
+#endif
+
+
+namespace dg {
+
+namespace {
+
+constexpr int TBM = 256;                       // rows per m-block
+constexpr int TBK = 64;                        // k per stage
+constexpr int TROWB = TBK * 2;                 // bytes per LDS row
+constexpr int TA_BYTES = TBM * TROWB;          // 32 KB
+constexpr int TA_INSTR = TA_BYTES / 1024 / 4;  // 1 KB copies per wave (its 64 rows)
+
+__device__ __forceinline__ int tswz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// every wave's LDS writes done and visible, without waiting for the global
+// loads in flight (a __syncthreads would also wait for those)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ float tsilu(float x) { return x / (1.f + __expf(-x)); }
+
+// two stage slots, or the epilogue tile if larger
+template <int BN>
+constexpr size_t tile_lds_bytes() {
+    return std::max<size_t>(2 * (size_t)(TA_BYTES + BN * TROWB), (size_t)TBM * (BN + 4) * 4);
+}
+
+}  // namespace
+
+template <int BN, int EPI>
+__global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles) {
+    if (g.state && g.state[0]) return;
+    constexpr int B_BYTES = BN * TROWB;
+    constexpr int STAGE = TA_BYTES + B_BYTES;
+    constexpr int B_INSTR = B_BYTES / 1024 / 4;
+    constexpr int TN = BN / 16;
+    constexpr int TS = BN + 4;  // epilogue tile row stride (floats)
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int pos = lane & 7;
+    const int ngroups = g.hit[0];
+    const int mb_max = *g.hit_mb;
+    const int units = ngroups * n_tiles;
+    const int64_t items = (int64_t)((units + 7) / 8) * 8 * mb_max;
+    const int KT = g.K / TBK;
+    const uint16_t* Ab = reinterpret_cast<const uint16_t*>(g.A);
+
+    for (int64_t id = blockIdx.x; id < items; id += gridDim.x) {
+        const int blk = (int)(id / (8 * mb_max)), rem = (int)(id % (8 * mb_max));
+        const int mb = rem / 8;
+        const int u = blk * 8 + rem % 8;
+        if (u >= units) continue;
+        const int gi = u / n_tiles, tile = u % n_tiles;
+        const int grp = g.hit[1 + gi];
+        const int row0 = g.group_offsets[grp];
+        const int mrows = g.group_offsets[grp + 1] - row0;
+        const int m0 = mb * TBM;
+        if (m0 >= mrows) continue;  // uniform over the workgroup
+        const int mcount = min(TBM, mrows - m0);
+        const bool live = wave * 64 < mcount;
+
+        // load sources: load j of this wave covers LDS rows 64*wave + 8j + lane/8
+        // (A) and 8*(wave*B_INSTR + j) + lane/8 (W), position lane%8, i.e.
+        // logical chunk tswz(row, lane%8)
+        const uint16_t* asrc[TA_INSTR];
+#pragma unroll
+        for (int j = 0; j < TA_INSTR; ++j) {
+            const int r = wave * 64 + 8 * j + (lane >> 3);
+            const int rr = min(r, mcount - 1);  // past the rows: a valid row, never stored
+            const int ar = row0 + m0 + rr;
+            const int src = g.a_rows ? g.a_rows[ar] : ar;
+            asrc[j] = Ab + (int64_t)src * g.lda + 8 * tswz(r, pos);
+        }
+        const uint16_t* bsrc[B_INSTR];
+#pragma unroll
+        for (int j = 0; j < B_INSTR; ++j) {
+            const int r = 8 * (wave * B_INSTR + j) + (lane >> 3);
+            const uint16_t* base;
+            int wr;
+            if constexpr (EPI == EPI_SWIGLU) {
+                // rows [0, BN/2): gate rows; [BN/2, BN): up rows of the same hidden units
+                base = reinterpret_cast<const uint16_t*>(r < BN / 2 ? g.W : g.W2);
+                wr = min(tile * (BN / 2) + (r % (BN / 2)), g.N / 2 - 1);
+            } else {
+                base = reinterpret_cast<const uint16_t*>(g.W);
+                wr = min(tile * BN + r, g.N - 1);
+            }
+            bsrc[j] = base + (int64_t)grp * g.w_group_stride + (int64_t)wr * g.ldw + 8 * tswz(r, pos);
+        }
+        // two register slots of one stage each, loaded two stages ahead; loads
+        // past the last stage re-read it (branch-free, so the waits stay exact)
+        u32x4 ra[2][TA_INSTR], rb[2][B_INSTR];
+        auto load = [&](int d, int kt) {
+            const int k0 = min(kt, KT - 1) * TBK;
+#pragma unroll
+            for (int j = 0; j < TA_INSTR; ++j) ra[d][j] = *reinterpret_cast<const u32x4*>(asrc[j] + k0);
+#pragma unroll
+            for (int j = 0; j < B_INSTR; ++j) rb[d][j] = *reinterpret_cast<const u32x4*>(bsrc[j] + k0);
+        };
+        auto store = [&](int d) {
+            unsigned char* st = smem + d * STAGE;
+#pragma unroll
+            for (int j = 0; j < TA_INSTR; ++j)
+                *reinterpret_cast<u32x4*>(st + (wave * TA_INSTR + j) * 1024 + lane * 16) = ra[d][j];
+#pragma unroll
+            for (int j = 0; j < B_INSTR; ++j)
+                *reinterpret_cast<u32x4*>(st + TA_BYTES + (wave * B_INSTR + j) * 1024 + lane * 16) = rb[d][j];
+        };
+
+        f32x4 acc[4][TN];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](int d) {
+            const unsigned char* as = smem + d * STAGE;
+            const unsigned char* bs = as + TA_BYTES;
+#pragma unroll
+            for (int ks = 0; ks < TBK / 32; ++ks) {
+                const int c = ks * 4 + lg;
+                u16x8 bfr[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int r = j * 16 + lr;
+                    bfr[j] = *reinterpret_cast<const u16x8*>(bs + r * TROWB + tswz(r, c) * 16);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = wave * 64 + i * 16 + lr;
+                    const u16x8 afr = *reinterpret_cast<const u16x8*>(as + r * TROWB + tswz(r, c) * 16);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, afr), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+                }
+            }
+        };
+        // stage kt: its registers go to LDS slot kt % 2, the slot's registers
+        // are refilled with stage kt + 2, one barrier publishes the slot (the
+        // slot written here was last read two stages ago, before the previous
+        // barrier), then the MFMAs read it
+        auto step = [&](int d, int kt) {
+            store(d);
+            load(d, kt + 2);
+            lds_barrier();
+            if (live) compute(d);
+        };
+        load(0, 0);
+        load(1, 1);
+        int kt = 0;
+        for (; kt + 1 < KT; kt += 2) {
+            step(0, kt);
+            step(1, kt + 1);
+        }
+        if (kt < KT) step(0, kt);
+        __syncthreads();  // retire the tail loads; every wave done with the slots
+
+        // ---- epilogue: the tile through LDS, then coalesced row stores ----
+        __syncthreads();
+        float* T = reinterpret_cast<float*>(smem);
+        if (live) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        T[(wave * 64 + i * 16 + lg * 4 + q) * TS + j * 16 + lr] = acc[i][j][q];
+        }
+        __syncthreads();
+        if constexpr (EPI == EPI_SWIGLU) {
+            constexpr int CH = BN / 2 / 8;  // 8-column chunks of hidden units per row
+            uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
+            const int f0 = tile * (BN / 2), F = g.N / 2;
+            for (int e = tid; e < mcount * CH; e += 256) {
+                const int r = e / CH, c0 = (e % CH) * 8;
+                const int f = f0 + c0;
+                if (f >= F) continue;
+                const float* gt = T + r * TS + c0;
+                const float* up = gt + BN / 2;
+                uint16_t h[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) h[q] = f2bf(tsilu(gt[q]) * up[q]);
+                uint16_t* dst = C + (int64_t)(row0 + m0 + r) * g.ldc + f;
+                if (f + 8 <= F) {
+                    uint4 v;
+                    v.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    v.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                    v.z = (uint32_t)h[4] | ((uint32_t)h[5] << 16);
+                    v.w = (uint32_t)h[6] | ((uint32_t)h[7] << 16);
+                    *reinterpret_cast<uint4*>(dst) = v;
+                } else {
+                    for (int q = 0; q < 8 && f + q < F; ++q) dst[q] = h[q];
+                }
+            }
+        } else {
+            constexpr int CH = BN / 4;  // float4 chunks per row
+            float* C = reinterpret_cast<float*>(g.C);
+            const int n0 = tile * BN;
+            for (int e = tid; e < mcount * CH; e += 256) {
+                const int r = e / CH, c0 = (e % CH) * 4;
+                const int n = n0 + c0;
+                if (n >= g.N) continue;
+                const float4 v = *reinterpret_cast<const float4*>(T + r * TS + c0);
+                float* dst = C + (int64_t)(row0 + m0 + r) * g.ldc + n;
+                if (n + 4 <= g.N) {
+                    *reinterpret_cast<float4*>(dst) = v;
+                } else {
+                    const float vv[4] = {v.x, v.y, v.z, v.w};
+                    for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] = vv[q];
+                }
+            }
+        }
+        __syncthreads();  // the LDS is refilled by the next item
+    }
+}
+
+template <int BN, int EPI>
+static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hipStream_t st) {
+    const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
+    const int mb_max = std::max(1, (max_rows + TBM - 1) / TBM);
+    const int64_t items = (int64_t)((groups * n_tiles + 7) / 8) * 8 * mb_max;  // upper bound
+    const size_t lds = tile_lds_bytes<BN>();
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    // persistent grid: as many workgroups as fit on the 256 CUs, a multiple of 8
+    static int per_cu = 0;
+    if (!per_cu) {
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI>), 256, lds);
+        if (e != hipSuccess) return e;
+        per_cu = std::max(per_cu, 1);
+    }
+    int64_t grid = std::min<int64_t>(items, 256 * per_cu);
+    grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
+    tile_gemm_kernel<BN, EPI><<<(unsigned)grid, 256, lds, st>>>(g, n_tiles);
+    return hipGetLastError();
+}
+
+bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
+    if (act_f32 || w_fp8 || g.w_scale) return false;
+    if (epi != EPI_SWIGLU && epi != EPI_STORE_F32) return false;
+    if (g.K % TBK || g.lda % 8 || g.ldw % 8) return false;
+    if (epi == EPI_SWIGLU && (g.c_f32 || g.ldc % 8 || (g.N / 2) % 8)) return false;
+    if (epi == EPI_STORE_F32 && g.ldc % 4) return false;
+    return true;
+}
+
+hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
+    if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU>(g, groups, max_rows, st);
+    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32>(g, groups, max_rows, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dg

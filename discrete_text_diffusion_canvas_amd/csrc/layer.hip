@@ -284,8 +284,11 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
 // order (token-major); then the shared expert's n slots in token order.
 // offsets has E+2 entries (group g = [offsets[g], offsets[g+1]), g = E is the
 // shared expert); perm[slot] = token; slot_of[token*k + j] = slot of its j-th
-// expert; hit = [count, hit groups in increasing id..., E]; hit_mb = the
-// largest number of 64-row blocks of a group.
+// expert. The groups with rows are listed in increasing id (the shared expert
+// last) in two lists: hitB = [count, ids...] for groups of at least big_min
+// rows (none if big_min <= 0) with hitB_mb = their largest number of 256-row
+// blocks, and hit = [count, ids...] for the rest with hit_mb = their largest
+// number of 64-row blocks.
 //
 // A stable counting sort without serial scans: the assignments are cut into
 // chunks of 64 (one wavefront each). Inside a chunk the lanes holding the
@@ -298,6 +301,8 @@ __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __res
                                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                             int32_t* __restrict__ slot_of, int32_t* __restrict__ hit,
                                                             int32_t* __restrict__ hit_mb,
+                                                            int32_t* __restrict__ hitB,
+                                                            int32_t* __restrict__ hitB_mb, int big_min,
                                                             int32_t* __restrict__ hit_out,
                                                             const int32_t* __restrict__ state) {
     if (state && state[0]) return;
@@ -347,33 +352,46 @@ __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __res
     if (wave == 0) {
         const int per = (E + 63) / 64;
         const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
-        int sum = 0, nz = 0, mb = 0;
+        auto is_big = [&](int rows) { return big_min > 0 && rows >= big_min; };
+        int sum = 0, nzs = 0, nzb = 0, mbs = 0, mbb = 0;
         for (int e = e0; e < e1; ++e) {
-            sum += tot[e];
-            nz += tot[e] > 0;
-            mb = max(mb, (tot[e] + 63) / 64);
+            const int t = tot[e];
+            sum += t;
+            if (t > 0) {
+                if (is_big(t)) { ++nzb; mbb = max(mbb, (t + 255) / 256); }
+                else { ++nzs; mbs = max(mbs, (t + 63) / 64); }
+            }
         }
-        int isum = sum, inz = nz;
+        int isum = sum, izs = nzs, izb = nzb;
         for (int o = 1; o < 64; o <<= 1) {
-            const int vs = __shfl_up(isum, o, 64), vz = __shfl_up(inz, o, 64);
-            if (lane >= o) { isum += vs; inz += vz; }
-            mb = max(mb, __shfl_xor(mb, o, 64));
+            const int vs = __shfl_up(isum, o, 64), va = __shfl_up(izs, o, 64), vb = __shfl_up(izb, o, 64);
+            if (lane >= o) { isum += vs; izs += va; izb += vb; }
+            mbs = max(mbs, __shfl_xor(mbs, o, 64));
+            mbb = max(mbb, __shfl_xor(mbb, o, 64));
         }
-        int run = isum - sum, h = inz - nz;
+        int run = isum - sum, hs = izs - nzs, hb = izb - nzb;
         for (int e = e0; e < e1; ++e) {
             off[e] = run;
             run += tot[e];
-            if (tot[e] > 0) hit[1 + h++] = e;
+            if (tot[e] > 0) {
+                if (is_big(tot[e])) hitB[1 + hb++] = e;
+                else hit[1 + hs++] = e;
+            }
         }
         if (lane == 63) {
-            // inz is now the number of routed experts hit
+            // izs / izb are now the numbers of routed groups in each list
             off[E] = isum;
             off[E + 1] = isum + n;
-            int hh = inz;
-            if (hit_out) *hit_out = hh;  // routed experts only
-            if (n > 0) hit[1 + hh++] = E;  // the shared expert: every token
-            hit[0] = hh;
-            *hit_mb = max(mb, n > 0 ? (n + 63) / 64 : 0);
+            if (hit_out) *hit_out = izs + izb;  // routed experts only
+            int cs = izs, cb = izb;
+            if (n > 0) {  // the shared expert: every token
+                if (is_big(n)) { hitB[1 + cb++] = E; mbb = max(mbb, (n + 255) / 256); }
+                else { hit[1 + cs++] = E; mbs = max(mbs, (n + 63) / 64); }
+            }
+            hit[0] = cs;
+            hitB[0] = cb;
+            *hit_mb = max(mbs, 1);
+            *hitB_mb = max(mbb, 1);
         }
     }
     __syncthreads();
@@ -489,8 +507,8 @@ hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, i
 }
 
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
-                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hit_out,
-                               const int32_t* state, hipStream_t st) {
+                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hitB, int32_t* hitB_mb,
+                               int big_min, int32_t* hit_out, const int32_t* state, hipStream_t st) {
     const size_t total = (size_t)n * k, nch = (total + 63) / 64;
     // off, tot (int32); cbase (u16 [nch][E]); esid (u16 [total]); ccnt (u8 [nch][E]); rank (u8 [total])
     const size_t lds = (size_t)(2 * E + 2) * 4 + nch * E * 2 + total * 2 + nch * E + total;
@@ -502,7 +520,8 @@ hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t*
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hist_permute_kernel<<<1, 1024, lds, st>>>(ids, n, k, E, offsets, perm, slot_of, hit, hit_mb, hit_out, state);
+    hist_permute_kernel<<<1, 1024, lds, st>>>(ids, n, k, E, offsets, perm, slot_of, hit, hit_mb, hitB, hitB_mb,
+                                               big_min, hit_out, state);
     return hipGetLastError();
 }
 

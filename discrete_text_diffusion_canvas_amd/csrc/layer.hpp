@@ -18,8 +18,8 @@ hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int 
 hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, int k, int32_t* ids, float* gates,
                               const int32_t* state, hipStream_t st);
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
-                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hit_out,
-                               const int32_t* state, hipStream_t st);
+                               int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hitB, int32_t* hitB_mb,
+                               int big_min, int32_t* hit_out, const int32_t* state, hipStream_t st);
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
                           int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
                           hipStream_t st);

@@ -57,6 +57,8 @@ struct Work {
     int32_t* slot_of;  // [T k]
     int32_t* hit;      // [E+2]: groups with rows ([0] = count)
     int32_t* hit_mb;   // [1]: largest 64-row block count of a group
+    int32_t* hitB;     // [E+2]: groups of many rows, for the LDS-staged GEMM ([0] = count)
+    int32_t* hitB_mb;  // [1]: largest 256-row block count of those
     void* Hbuf;        // [T(k+1)][F]
     float* Y;          // [T(k+1)][d]
     dg::RowPart* parts;  // [min(T, canvas)][nsplit]
@@ -95,6 +97,8 @@ Work carve(const dg_model* m, void* base, int T) {
     w.slot_of = cv.take<int32_t>((size_t)T * k);
     w.hit = cv.take<int32_t>(E + 2);
     w.hit_mb = cv.take<int32_t>(1);
+    w.hitB = cv.take<int32_t>(E + 2);
+    w.hitB_mb = cv.take<int32_t>(1);
     w.Hbuf = cv.take<char>((size_t)T * (k + 1) * F * ab);
     w.Y = cv.take<float>((size_t)T * (k + 1) * d);
     w.parts = cv.take<dg::RowPart>((size_t)Nc * lm_nsplit(c));
@@ -144,29 +148,45 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
     }
     DG_TRY(dg::launch_router_topk(w.rlog, L.router_bias, n, E, k, w.ids, w.gates, state, st), "router topk");
-    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, w.hit, w.hit_mb,
-                                   w.experts_hit ? w.experts_hit + l : nullptr, state, st),
+    // groups of more than 64 rows go to the LDS-staged GEMM (bf16 only)
+    dg::GemmArgs gu = gargs(), dn = gargs();
+    gu.A = w.A; gu.lda = d; gu.a_rows = w.perm;
+    gu.W = L.w_gate; gu.W2 = L.w_up; gu.ldw = d; gu.w_group_stride = (int64_t)F * d;
+    gu.w_scale = (const uint16_t*)L.gate_scale; gu.w2_scale = (const uint16_t*)L.up_scale; gu.scale_group_stride = F;
+    gu.M = n; gu.N = 2 * F; gu.K = d; gu.group_offsets = w.offsets;
+    gu.C = w.Hbuf; gu.ldc = F; gu.c_f32 = f32; gu.state = state;
+    dn.A = w.Hbuf; dn.lda = F;
+    dn.W = L.w_down; dn.ldw = F; dn.w_group_stride = (int64_t)d * F;
+    dn.w_scale = (const uint16_t*)L.down_scale; dn.scale_group_stride = d;
+    dn.M = n; dn.N = d; dn.K = F; dn.group_offsets = w.offsets;
+    dn.C = w.Y; dn.ldc = d; dn.c_f32 = 1; dn.state = state;
+    const bool tiled = dg::tile_gemm_supported(gu, f32, fp8, dg::EPI_SWIGLU) &&
+                       dg::tile_gemm_supported(dn, f32, fp8, dg::EPI_STORE_F32);
+    const int big_min = tiled ? 65 : 0;
+    DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, w.hit, w.hit_mb, w.hitB, w.hitB_mb,
+                                   big_min, w.experts_hit ? w.experts_hit + l : nullptr, state, st),
            "hist permute");
+    const int small_rows = tiled ? 64 : n;  // bound on the rows of a stream-GEMM group
     {   // gate/up with SwiGLU
-        dg::GemmArgs g = gargs();
-        g.A = w.A; g.lda = d; g.a_rows = w.perm;
-        g.W = L.w_gate; g.W2 = L.w_up; g.ldw = d; g.w_group_stride = (int64_t)F * d;
-        g.w_scale = (const uint16_t*)L.gate_scale; g.w2_scale = (const uint16_t*)L.up_scale; g.scale_group_stride = F;
-        g.M = n; g.N = 2 * F; g.K = d; g.group_offsets = w.offsets; g.hit = w.hit; g.hit_mb = w.hit_mb;
-        g.C = w.Hbuf; g.ldc = F; g.c_f32 = f32; g.state = state;
         const int slot = timing_begin(st, DG_TIME_EXPERT_GATE_UP);
-        DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, dg::SHAPE_SMALL_M, st), "expert gate/up");
+        dg::GemmArgs g = gu;
+        g.hit = w.hit; g.hit_mb = w.hit_mb;
+        DG_TRY(dg::stream_gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, small_rows, st), "expert gate/up");
+        if (tiled) {
+            g.hit = w.hitB; g.hit_mb = w.hitB_mb;
+            DG_TRY(dg::tile_gemm_launch(g, dg::EPI_SWIGLU, E + 1, n, st), "expert gate/up (tiled)");
+        }
         timing_end(slot, st);
     }
     {   // down
-        dg::GemmArgs g = gargs();
-        g.A = w.Hbuf; g.lda = F;
-        g.W = L.w_down; g.ldw = F; g.w_group_stride = (int64_t)d * F;
-        g.w_scale = (const uint16_t*)L.down_scale; g.scale_group_stride = d;
-        g.M = n; g.N = d; g.K = F; g.group_offsets = w.offsets; g.hit = w.hit; g.hit_mb = w.hit_mb;
-        g.C = w.Y; g.ldc = d; g.c_f32 = 1; g.state = state;
         const int slot = timing_begin(st, DG_TIME_EXPERT_DOWN);
-        DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_STORE_F32, E + 1, dg::SHAPE_SMALL_M, st), "expert down");
+        dg::GemmArgs g = dn;
+        g.hit = w.hit; g.hit_mb = w.hit_mb;
+        DG_TRY(dg::stream_gemm_launch(g, f32, fp8, dg::EPI_STORE_F32, E + 1, small_rows, st), "expert down");
+        if (tiled) {
+            g.hit = w.hitB; g.hit_mb = w.hitB_mb;
+            DG_TRY(dg::tile_gemm_launch(g, dg::EPI_STORE_F32, E + 1, n, st), "expert down (tiled)");
+        }
         timing_end(slot, st);
     }
     DG_TRY(dg::launch_combine(w.X, n, d, w.Y, w.slot_of, w.gates, k, n * k, next_norm, c.norm_eps, w.A, f32, state,

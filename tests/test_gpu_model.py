@@ -22,9 +22,14 @@ SEED = 0x5EED
 # decode the same codes exactly, so the error budget is the bf16 one
 SMALL_FP8 = SMALL_BF16.replace(name="small_fp8", weight_dtype="fp8")
 CFGS = {"tiny_f32": wl.TINY, "small_bf16": SMALL_BF16, "small_fp8": SMALL_FP8}
+# 320 canvas rows: expert groups of more than 64 rows take the LDS-staged
+# grouped GEMM, the shared expert spans two 256-row blocks (the second with
+# one live wave), and smaller groups stay on the streaming GEMM
+WIDE_BF16 = SMALL_BF16.replace(name="wide_bf16", canvas=320)
+LAYER_CFGS = dict(CFGS, wide_bf16=WIDE_BF16)
 # per-row relative L2 bounds against the float64 oracle: f32 path vs bf16 path
-LAYER_TOL = {"tiny_f32": 1e-4, "small_bf16": 1.5e-2, "small_fp8": 1.5e-2}
-DELTA_TOL = {"tiny_f32": 1e-4, "small_bf16": 3e-2, "small_fp8": 3e-2}
+LAYER_TOL = {"tiny_f32": 1e-4, "small_bf16": 1.5e-2, "small_fp8": 1.5e-2, "wide_bf16": 1.5e-2}
+DELTA_TOL = {"tiny_f32": 1e-4, "small_bf16": 3e-2, "small_fp8": 3e-2, "wide_bf16": 3e-2}
 LOGIT_TOL = {"tiny_f32": 1e-5, "small_bf16": 1e-2, "small_fp8": 1e-2}
 KV_TOL = {"tiny_f32": 1e-4, "small_bf16": 3e-2, "small_fp8": 3e-2}
 
@@ -52,10 +57,10 @@ def test_embed_is_exact_row_copy(B):
     assert torch.equal(X, model.embed[tok.long()].float())
 
 
-@pytest.mark.parametrize("name", list(CFGS))
+@pytest.mark.parametrize("name", list(LAYER_CFGS))
 @pytest.mark.parametrize("layer", [0, 1])
 def test_decoder_layer(B, name, layer):
-    cfg = CFGS[name]
+    cfg = LAYER_CFGS[name]
     model = device_model(B, cfg)
     P = 300 if name != "tiny_f32" else wl.TINY_PREFIX
     n = cfg.canvas
