@@ -35,6 +35,9 @@ struct GemmArgs {
     int c_f32;                      // C element type: 1 f32, 0 bf16 (SwiGLU / LM head)
     float* X;                       // EPI_RESIDUAL: X[row][n] += C
     int64_t ldx;
+    // split-K (LDS-staged dense GEMM): K slices, f32 partials [ksplit][M][N]
+    int ksplit;
+    float* part;
     // control
     const int32_t* state;           // canvas state (done flag, step) or NULL
     // LM head
@@ -52,10 +55,13 @@ hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int g
 hipError_t launch_lmhead_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t stream_gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int max_rows,
                               hipStream_t st);
-// LDS-staged grouped GEMM over the big-group list in g.hit / g.hit_mb
-// (bf16 activations and weights, K % 64 == 0; SwiGLU or f32 store).
+// LDS-staged GEMM (bf16 activations and weights, K % 64 == 0): grouped over
+// the big-group list in g.hit / g.hit_mb (SwiGLU or f32 store), or dense
+// (g.group_offsets NULL) with optional split-K through g.part.
 bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi);
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st);
+// K slices for a dense M x N x K product (1 = no split)
+int tile_dense_ksplit(int M, int N, int K);
 
 // ---------------------------------------------------------------------------
 // LM-head epilogue: logits of record (accumulator rounded to the storage

@@ -38,6 +38,9 @@
 #ifndef DG_TILE_BN_DN
 #define DG_TILE_BN_DN 64
 #endif
+#ifndef DG_TILE_BN_DENSE
+#define DG_TILE_BN_DENSE 64
+#endif
 
 
 namespace dg {
@@ -66,6 +69,54 @@ constexpr size_t tile_lds_bytes() {
 
 }  // namespace
 
+// columns n..n+3 of output row `row` (columns past N are dropped)
+template <int EPI>
+__device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int n, const float4& v) {
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    const bool full = n + 4 <= g.N;
+    if constexpr (EPI == EPI_STORE_F32) {
+        float* dst = reinterpret_cast<float*>(g.C) + row * g.ldc + n;
+        if (full) *reinterpret_cast<float4*>(dst) = v;
+        else for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] = vv[q];
+    } else if constexpr (EPI == EPI_STORE_BF16) {
+        uint16_t* dst = reinterpret_cast<uint16_t*>(g.C) + row * g.ldc + n;
+        if (full) {
+            uint2 o;
+            o.x = (uint32_t)f2bf(vv[0]) | ((uint32_t)f2bf(vv[1]) << 16);
+            o.y = (uint32_t)f2bf(vv[2]) | ((uint32_t)f2bf(vv[3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = o;
+        } else {
+            for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] = f2bf(vv[q]);
+        }
+    } else if constexpr (EPI == EPI_RESIDUAL) {
+        float* dst = g.X + row * g.ldx + n;
+        if (full) {
+            float4 x = *reinterpret_cast<const float4*>(dst);
+            x.x += v.x; x.y += v.y; x.z += v.z; x.w += v.w;
+            *reinterpret_cast<float4*>(dst) = x;
+        } else {
+            for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] += vv[q];
+        }
+    }
+}
+
+// Sum of the K-slice partials part[s][row][n] in slice order, then the
+// epilogue. One thread per 4 columns.
+template <int EPI>
+__global__ void __launch_bounds__(256) tile_reduce_kernel(GemmArgs g) {
+    if (g.state && g.state[0]) return;
+    const int n4 = g.N / 4;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)g.M * n4) return;
+    const int row = (int)(e / n4), n = (int)(e % n4) * 4;
+    float4 acc = *reinterpret_cast<const float4*>(g.part + (int64_t)row * g.N + n);
+    for (int s = 1; s < g.ksplit; ++s) {
+        const float4 p = *reinterpret_cast<const float4*>(g.part + ((int64_t)s * g.M + row) * g.N + n);
+        acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    tile_store4<EPI>(g, row, n, acc);
+}
+
 template <int BN, int EPI>
 __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles) {
     if (g.state && g.state[0]) return;
@@ -78,22 +129,26 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int pos = lane & 7;
-    const int ngroups = g.hit[0];
-    const int mb_max = *g.hit_mb;
+    const bool grouped = g.group_offsets != nullptr;
+    const int ngroups = grouped ? g.hit[0] : 1;
+    const int mb_max = grouped ? *g.hit_mb : (g.M + TBM - 1) / TBM;
+    const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
     const int units = ngroups * n_tiles;
-    const int64_t items = (int64_t)((units + 7) / 8) * 8 * mb_max;
-    const int KT = g.K / TBK;
+    const int64_t items = (int64_t)((units * ksplit + 7) / 8) * 8 * mb_max;
+    const int KT = g.K / TBK / ksplit;  // stages per K slice
     const uint16_t* Ab = reinterpret_cast<const uint16_t*>(g.A);
 
     for (int64_t id = blockIdx.x; id < items; id += gridDim.x) {
         const int blk = (int)(id / (8 * mb_max)), rem = (int)(id % (8 * mb_max));
         const int mb = rem / 8;
-        const int u = blk * 8 + rem % 8;
-        if (u >= units) continue;
+        const int uk = blk * 8 + rem % 8;
+        if (uk >= units * ksplit) continue;
+        const int u = uk % units, ks = uk / units;
         const int gi = u / n_tiles, tile = u % n_tiles;
-        const int grp = g.hit[1 + gi];
-        const int row0 = g.group_offsets[grp];
-        const int mrows = g.group_offsets[grp + 1] - row0;
+        const int grp = grouped ? g.hit[1 + gi] : 0;
+        const int row0 = grouped ? g.group_offsets[grp] : 0;
+        const int mrows = grouped ? g.group_offsets[grp + 1] - row0 : g.M;
+        const int kbase = ks * KT * TBK;  // first k of this slice
         const int m0 = mb * TBM;
         if (m0 >= mrows) continue;  // uniform over the workgroup
         const int mcount = min(TBM, mrows - m0);
@@ -131,7 +186,7 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
         // past the last stage re-read it (branch-free, so the waits stay exact)
         u32x4 ra[2][TA_INSTR], rb[2][B_INSTR];
         auto load = [&](int d, int kt) {
-            const int k0 = min(kt, KT - 1) * TBK;
+            const int k0 = kbase + min(kt, KT - 1) * TBK;
 #pragma unroll
             for (int j = 0; j < TA_INSTR; ++j) ra[d][j] = *reinterpret_cast<const u32x4*>(asrc[j] + k0);
 #pragma unroll
@@ -208,7 +263,19 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
                         T[(wave * 64 + i * 16 + lg * 4 + q) * TS + j * 16 + lr] = acc[i][j][q];
         }
         __syncthreads();
-        if constexpr (EPI == EPI_SWIGLU) {
+        if (ksplit > 1) {
+            // raw f32 partial of this K slice: part[ks][row][n]
+            constexpr int CH = BN / 4;
+            const int n0 = tile * BN;
+            float* P = g.part + (int64_t)ks * g.M * g.N;
+            for (int e = tid; e < mcount * CH; e += 256) {
+                const int r = e / CH, c0 = (e % CH) * 4;
+                const int n = n0 + c0;
+                if (n >= g.N) continue;
+                const float4 v = *reinterpret_cast<const float4*>(T + r * TS + c0);
+                *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 4 == 0
+            }
+        } else if constexpr (EPI == EPI_SWIGLU) {
             constexpr int CH = BN / 2 / 8;  // 8-column chunks of hidden units per row
             uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
             const int f0 = tile * (BN / 2), F = g.N / 2;
@@ -235,20 +302,14 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
             }
         } else {
             constexpr int CH = BN / 4;  // float4 chunks per row
-            float* C = reinterpret_cast<float*>(g.C);
             const int n0 = tile * BN;
             for (int e = tid; e < mcount * CH; e += 256) {
                 const int r = e / CH, c0 = (e % CH) * 4;
                 const int n = n0 + c0;
                 if (n >= g.N) continue;
                 const float4 v = *reinterpret_cast<const float4*>(T + r * TS + c0);
-                float* dst = C + (int64_t)(row0 + m0 + r) * g.ldc + n;
-                if (n + 4 <= g.N) {
-                    *reinterpret_cast<float4*>(dst) = v;
-                } else {
-                    const float vv[4] = {v.x, v.y, v.z, v.w};
-                    for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] = vv[q];
-                }
+                const int64_t row = row0 + m0 + r;
+                tile_store4<EPI>(g, row, n, v);
             }
         }
         __syncthreads();  // the LDS is refilled by the next item
@@ -259,7 +320,8 @@ template <int BN, int EPI>
 static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hipStream_t st) {
     const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     const int mb_max = std::max(1, (max_rows + TBM - 1) / TBM);
-    const int64_t items = (int64_t)((groups * n_tiles + 7) / 8) * 8 * mb_max;  // upper bound
+    const int ks = g.ksplit > 1 ? g.ksplit : 1;
+    const int64_t items = (int64_t)((groups * n_tiles * ks + 7) / 8) * 8 * mb_max;  // upper bound
     const size_t lds = tile_lds_bytes<BN>();
     static bool attr = false;
     if (!attr) {
@@ -279,21 +341,45 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     int64_t grid = std::min<int64_t>(items, 256 * per_cu);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
     tile_gemm_kernel<BN, EPI><<<(unsigned)grid, 256, lds, st>>>(g, n_tiles);
+    if (ks > 1) {
+        const int64_t n = (int64_t)g.M * (g.N / 4);
+        tile_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g);
+    }
     return hipGetLastError();
 }
 
 bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
     if (act_f32 || w_fp8 || g.w_scale) return false;
-    if (epi != EPI_SWIGLU && epi != EPI_STORE_F32) return false;
     if (g.K % TBK || g.lda % 8 || g.ldw % 8) return false;
-    if (epi == EPI_SWIGLU && (g.c_f32 || g.ldc % 8 || (g.N / 2) % 8)) return false;
-    if (epi == EPI_STORE_F32 && g.ldc % 4) return false;
-    return true;
+    switch (epi) {
+        case EPI_SWIGLU: return !g.c_f32 && g.ldc % 8 == 0 && (g.N / 2) % 8 == 0;
+        case EPI_STORE_F32: return g.ldc % 4 == 0 && g.N % 4 == 0;
+        case EPI_STORE_BF16: return g.ldc % 4 == 0 && g.N % 4 == 0;
+        case EPI_RESIDUAL: return g.ldx % 4 == 0 && g.N % 4 == 0;
+        default: return false;
+    }
+}
+
+int tile_dense_ksplit(int M, int N, int K) {
+    // split until there are enough work items for most CUs (each slice keeps
+    // at least 4 stages); every split adds M x N f32 partials to write and read
+    const int items = (N + DG_TILE_BN_DENSE - 1) / DG_TILE_BN_DENSE * ((M + TBM - 1) / TBM);
+    int ks = 1;
+    while (items * ks < 160 && (K / TBK) % (ks * 2) == 0 && K / TBK / (ks * 2) >= 4) ks *= 2;
+    return ks;
 }
 
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
-    if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU>(g, groups, max_rows, st);
-    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32>(g, groups, max_rows, st);
+    if (g.group_offsets) {
+        if (g.ksplit > 1) return hipErrorInvalidValue;
+        if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU>(g, groups, max_rows, st);
+        if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32>(g, groups, max_rows, st);
+        return hipErrorInvalidValue;
+    }
+    if (g.ksplit > 1 && (!g.part || (g.K / TBK) % g.ksplit)) return hipErrorInvalidValue;
+    if (epi == EPI_STORE_BF16) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_BF16>(g, 1, g.M, st);
+    if (epi == EPI_RESIDUAL) return launch_tile_t<DG_TILE_BN_DENSE, EPI_RESIDUAL>(g, 1, g.M, st);
+    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_F32>(g, 1, g.M, st);
     return hipErrorInvalidValue;
 }
 

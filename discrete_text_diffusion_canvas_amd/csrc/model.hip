@@ -47,6 +47,7 @@ struct Work {
     void* Vc;          // [Hkv][hd][T64] (transposed)
     void* O;           // [T][Hq hd]
     float* rope_cs;    // [T][hd/2][2] cos, sin of the rows' RoPE angles
+    float* gemm_part;  // split-K partials of the dense projections
     float* part_o;     // attention split partials
     float* part_ml;
     float* rlog;       // [T][E]
@@ -87,6 +88,12 @@ Work carve(const dg_model* m, void* base, int T) {
     w.Vc = cv.take<char>((size_t)T64 * Hkv * hd * ab);
     w.O = cv.take<char>((size_t)T * Hq * hd * ab);
     w.rope_cs = cv.take<float>((size_t)T * hd);
+    {   // split-K partials of the QKV and output projections (when they split)
+        const int nqkv = (Hq + 2 * Hkv) * hd;
+        const int ka = dg::tile_dense_ksplit(T, nqkv, d), kb = dg::tile_dense_ksplit(T, d, Hq * hd);
+        const size_t parts = std::max(ka > 1 ? (size_t)ka * T * nqkv : 0, kb > 1 ? (size_t)kb * T * d : 0);
+        w.gemm_part = parts ? cv.take<float>(parts) : nullptr;
+    }
     w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
     w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
     w.rlog = cv.take<float>((size_t)T * E);
@@ -130,6 +137,20 @@ dg::GemmArgs gargs() {
     do {                                                          \
         if (dg_status _s = hip_check((expr), what)) return _s;    \
     } while (0)
+
+// A dense projection of n rows: the LDS-staged GEMM (split over K when there
+// are too few column tiles to fill the chip) where it applies, else the
+// weight-streaming GEMM.
+hipError_t dense_gemm(dg::GemmArgs g, const Work& w, int f32, int fp8, int epi, hipStream_t st) {
+    if (dg::tile_gemm_supported(g, f32, fp8, epi)) {
+        g.ksplit = dg::tile_dense_ksplit(g.M, g.N, g.K);
+        g.part = w.gemm_part;
+        if (g.ksplit <= 1 || g.part) return dg::tile_gemm_launch(g, epi, 1, g.M, st);
+        g.ksplit = 0;
+        g.part = nullptr;
+    }
+    return dg::gemm_launch(g, f32, fp8, epi, 0, dg::SHAPE_PROJ, st);
+}
 
 // ---------------------------------------------------------------------------
 // The MoE half of a layer on rows X[0..n): X += shared(b) + sum_j g_j expert_j(b)
@@ -222,8 +243,7 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N; g.state = state;
         const int slot = timing_begin(st, DG_TIME_QKV);
-        DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
-               "qkv gemm");
+        DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st), "qkv gemm");
         timing_end(slot, st);
     }
     DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows64, 0,
@@ -250,7 +270,7 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
         g.A = w.O; g.lda = Hq * hd; g.W = L.wo; g.ldw = Hq * hd; g.w_scale = (const uint16_t*)L.wo_scale;
         g.M = n; g.N = d; g.K = Hq * hd; g.X = w.X; g.ldx = d; g.state = state;
         const int slot = timing_begin(st, DG_TIME_O_PROJ);
-        DG_TRY(dg::gemm_launch(g, f32, fp8, dg::EPI_RESIDUAL, 0, dg::SHAPE_PROJ, st), "o gemm");
+        DG_TRY(dense_gemm(g, w, f32, fp8, dg::EPI_RESIDUAL, st), "o gemm");
         timing_end(slot, st);
     }
     return moe_block(m, l, w, n, next_norm, state, st);
@@ -271,8 +291,7 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N;
-        DG_TRY(dg::gemm_launch(g, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, 0, dg::SHAPE_PROJ, st),
-               "qkv gemm");
+        DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st), "qkv gemm");
         DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0, kv->k[l], kv->v[l],
                                        kv->capacity, P, 0, nullptr, st),
                "rope");
@@ -290,7 +309,7 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         dg::GemmArgs go = gargs();
         go.A = w.O; go.lda = Hq * hd; go.W = L.wo; go.ldw = Hq * hd; go.w_scale = (const uint16_t*)L.wo_scale;
         go.M = n; go.N = d; go.K = Hq * hd; go.X = w.X; go.ldx = d;
-        DG_TRY(dg::gemm_launch(go, f32, fp8, dg::EPI_RESIDUAL, 0, dg::SHAPE_PROJ, st), "o gemm");
+        DG_TRY(dense_gemm(go, w, f32, fp8, dg::EPI_RESIDUAL, st), "o gemm");
         // the next layer's attention norm rides on this layer's combine
         if (dg_status s = moe_block(m, l, w, n, m->layers[l + 1].attn_norm, nullptr, st)) return s;
     }
@@ -400,7 +419,10 @@ void dg_model_destroy(dg_model* m) { delete m; }
 
 size_t dg_workspace_bytes(const dg_model* m, int32_t max_rows) {
     if (!m || max_rows < 1 || max_rows > 4096) return 0;
-    return carve(m, nullptr, max_rows).bytes;
+    // the split-K partials make the need non-monotonic in the row count
+    size_t best = 0;
+    for (int T = 1; T <= max_rows; ++T) best = std::max(best, carve(m, nullptr, T).bytes);
+    return best;
 }
 
 dg_status dg_embed(const dg_model* m, const int32_t* tokens, int32_t n, float* X, void* stream) {
