@@ -60,47 +60,71 @@ __device__ __forceinline__ void from_f(float* p, float v) { *p = v; }
 
 constexpr int KB = 64;  // keys per block
 
+// Max / sum over the 16 lanes of a DPP row (the 16 keys of an S tile column
+// group): swap neighbours, swap pairs, mirror halves of 8, mirror the row.
+// Each step combines two partial results commutatively, so all 16 lanes end
+// with bit-identical totals.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+    return v;
+}
+
 // Online-softmax update of one wave's 16 rows from its S tile (4 n-tiles of
 // 16 keys, already masked and scaled); writes P (storage type) to pw
-// ([16][SP]) and rescales O.
+// ([16][SP]) and rescales O. The reference max m_run of a row moves only when
+// the block's max exceeds it by more than SM_SLACK (then, wave-uniformly,
+// every row takes its exact new max and O, l are rescaled); otherwise the
+// probabilities are exp(s - m_run) <= e^SM_SLACK. The normalisation O / l and
+// the split merge use the same reference, so the result is unchanged up to
+// rounding while most blocks skip the rescale of O.
+constexpr float SM_SLACK = 8.f;
 template <typename TL, int NT_D, int SP>
 __device__ __forceinline__ void softmax_block(f32x4 (&s)[4], float (&m_run)[4], float (&l_run)[4],
                                               f32x4 (&o)[NT_D], TL* pw, int lr, int lg) {
     float pmax[4];
+    bool grow = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        pmax[i] = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
-#pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) pmax[i] = fmaxf(pmax[i], __shfl_xor(pmax[i], o2, 64));
+        pmax[i] = row16_max(fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i])));
+        grow |= pmax[i] > m_run[i] + SM_SLACK;
     }
-    float alpha[4], mnew[4], psum[4];
+    if (__ballot(grow)) {  // wave-uniform
+        float alpha[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        mnew[i] = fmaxf(m_run[i], pmax[i]);
-        alpha[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew[i]);
-        psum[i] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const float mnew = fmaxf(m_run[i], pmax[i]);
+            alpha[i] = (m_run[i] == -INFINITY) ? 0.f : __expf(m_run[i] - mnew);
+            m_run[i] = mnew;
+            l_run[i] *= alpha[i];
+        }
+#pragma unroll
+        for (int j = 0; j < NT_D; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
     }
+    float psum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float p = (mnew[i] == -INFINITY) ? 0.f : __expf(s[nt][i] - mnew[i]);
+            const float p = (m_run[i] == -INFINITY) ? 0.f : __expf(s[nt][i] - m_run[i]);
             TL pl;
             from_f(&pl, p);
             psum[i] += to_f(pl);  // the probabilities the MFMA sees
             pw[(lg * 4 + i) * SP + nt * 16 + lr] = pl;
         }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) psum[i] += __shfl_xor(psum[i], o2, 64);
-        l_run[i] = l_run[i] * alpha[i] + psum[i];
-        m_run[i] = mnew[i];
-    }
-#pragma unroll
-    for (int j = 0; j < NT_D; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
+    for (int i = 0; i < 4; ++i) l_run[i] += row16_sum(psum[i]);
 }
 
 // ===========================================================================
@@ -262,28 +286,35 @@ __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
 
 }  // namespace
 
+// every wave's LDS writes done and visible, without waiting for the global
+// loads in flight (a __syncthreads would also wait for those)
+__device__ __forceinline__ void attn_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int HD>
-__global__ void __launch_bounds__(256) attn_dma_kernel(AttnArgs a, int R) {
+__global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
     if (a.state && a.state[0]) return;
     constexpr int KROWB = HD * 2;                 // bytes per K row
     constexpr int K_BYTES = KB * KROWB;           // K tile
     constexpr int V_BYTES = HD * KB * 2;          // V^T tile (rows of 128 bytes)
     constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int K_INSTR = K_BYTES / 1024 / 4;   // per wave
-    constexpr int V_INSTR = V_BYTES / 1024 / 4;
-    constexpr int LOADS = K_INSTR + V_INSTR;
+    constexpr int K_LD = K_BYTES / 1024 / 4;      // 16-byte loads per lane and block
+    constexpr int V_LD = V_BYTES / 1024 / 4;
+    constexpr int KRPI = 1024 / KROWB;            // K rows per 1 KB piece
+    constexpr int KCPR = KROWB / 16;              // chunks per K row
     constexpr int NT_D = HD / 16;
     constexpr int KS = HD / 32;
     constexpr int SP = KB + 8;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* Ps = reinterpret_cast<uint16_t*>(smem + 2 * STAGE);
+    unsigned char* Qs = smem + STAGE;                                  // [128 rows][HD], swizzled
+    uint16_t* Ps = reinterpret_cast<uint16_t*>(smem + STAGE + 128 * KROWB);  // [4 waves][32 rows][SP]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int g = blockIdx.y;
-    const int QP = 64 / R;                        // positions per workgroup
+    const int QP = 128 / R;                       // positions per workgroup
     const int qx0 = blockIdx.x * QP;
-    // this wave's 16 rows: workgroup rows [16 wave, +16) = (head, position)
+    // workgroup row rho in [0, 128) = (head g*R + rho / QP, position qx0 + rho % QP);
+    // wave w owns rows [32w, 32w + 32) as two 16-row tiles
     auto row_head = [&](int rho) { return g * R + rho / QP; };
     auto row_pos = [&](int rho) { return qx0 + rho % QP; };
 
@@ -310,139 +341,203 @@ __global__ void __launch_bounds__(256) attn_dma_kernel(AttnArgs a, int R) {
     const uint16_t* K2 = a.K2 ? reinterpret_cast<const uint16_t*>(a.K2) + (int64_t)g * a.ld2 * HD : nullptr;
     const uint16_t* V2 = a.V2 ? reinterpret_cast<const uint16_t*>(a.V2) + (int64_t)g * HD * a.ld2 : nullptr;
 
-    // issue the copies of virtual block vb into stage buffer st
-    auto issue = [&](int64_t vb, int stg) {
-        unsigned char* base = smem + stg * STAGE;
+    // register loads of virtual block vb (clamped to this workgroup's last
+    // block, so the loop stays branch-free); the LDS layout written by store()
+    // is K [64 keys][HD] and V^T [HD][64 keys], XOR-swizzled by 16-byte chunk
+    u32x4 kr[K_LD], vr[V_LD];
+    auto load = [&](int64_t vb) {
+        vb = min<int64_t>(vb, bb1 - 1);
         const bool seg1 = vb < nb1;
         const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
         const int64_t rlim = seg1 ? a.e1 : a.n2;   // rows >= rlim: any valid row (masked)
         const uint16_t* Kb = seg1 ? K1 : K2;
         const uint16_t* Vb = seg1 ? V1 : V2;
         const int64_t vld = seg1 ? a.ld1 : a.ld2;
-        constexpr int KRPI = 1024 / KROWB;           // K rows per instruction
-        constexpr int KCPR = KROWB / 16;             // chunks per K row
 #pragma unroll
-        for (int j = 0; j < K_INSTR; ++j) {
-            const int r = (wave * K_INSTR + j) * KRPI + lane / KCPR;
+        for (int j = 0; j < K_LD; ++j) {
+            const int r = (wave * K_LD + j) * KRPI + lane / KCPR;
             const int pos = lane % KCPR;
-            int64_t kr = row0 + r;
-            if (kr >= rlim) kr = rlim - 1;
-            if (kr < 0) kr = 0;
-            const uint16_t* src = Kb + kr * HD + 8 * kswz(r, pos);
-            __builtin_amdgcn_global_load_lds(src, base + (wave * K_INSTR + j) * 1024, 16, 0, 0);
+            int64_t kr_row = row0 + r;
+            if (kr_row >= rlim) kr_row = rlim - 1;
+            if (kr_row < 0) kr_row = 0;
+            kr[j] = *reinterpret_cast<const u32x4*>(Kb + kr_row * HD + 8 * kswz(r, pos));
         }
 #pragma unroll
-        for (int j = 0; j < V_INSTR; ++j) {
-            const int d = (wave * V_INSTR + j) * 8 + lane / 8;
+        for (int j = 0; j < V_LD; ++j) {
+            const int d = (wave * V_LD + j) * 8 + lane / 8;
             const int pos = lane % 8;
-            const uint16_t* src = Vb + (int64_t)d * vld + row0 + 8 * vswz(d, pos);
-            __builtin_amdgcn_global_load_lds(src, base + K_BYTES + (wave * V_INSTR + j) * 1024, 16, 0, 0);
+            vr[j] = *reinterpret_cast<const u32x4*>(Vb + (int64_t)d * vld + row0 + 8 * vswz(d, pos));
         }
     };
+    auto store = [&]() {
+        unsigned char* base = smem;
+#pragma unroll
+        for (int j = 0; j < K_LD; ++j) *reinterpret_cast<u32x4*>(base + (wave * K_LD + j) * 1024 + lane * 16) = kr[j];
+#pragma unroll
+        for (int j = 0; j < V_LD; ++j)
+            *reinterpret_cast<u32x4*>(base + K_BYTES + (wave * V_LD + j) * 1024 + lane * 16) = vr[j];
+    };
 
-    // ---- Q fragments ----
-    const int rho_l = wave * 16 + lr;
-    const int hq_l = row_head(rho_l), qp_l = row_pos(rho_l);
-    const bool qok_l = qp_l < a.nq;
-    const uint16_t* Qh = reinterpret_cast<const uint16_t*>(a.Q) + ((int64_t)hq_l * a.ldq + (qok_l ? qp_l : 0)) * HD;
-    u16x8 qf[KS];
+    // ---- Q rows of the workgroup into LDS (row rho, 16-byte chunk c at kswz):
+    // all loads first (rows past nq read row 0 and are zeroed), then the writes
+    {
+        constexpr int QL = 128 * KCPR / 256;  // 16-byte pieces per thread
+        u16x8 qv[QL];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = qok_l ? *reinterpret_cast<const u16x8*>(Qh + ks * 32 + lg * 8) : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-
-    f32x4 o[NT_D];
-#pragma unroll
-    for (int j = 0; j < NT_D; ++j) o[j] = f32x4{0, 0, 0, 0};
-    float m_run[4], l_run[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { m_run[i] = -INFINITY; l_run[i] = 0.f; }
-    const float scale = 1.f / sqrtf((float)HD);
-    // positions of this lane's 4 output rows
-    int64_t qpos[4];
-    bool qok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rho = wave * 16 + lg * 4 + i;
-        qpos[i] = a.qpos0 + row_pos(rho);
-        qok[i] = row_pos(rho) < a.nq;
-    }
-
-    if (bb0 < bb1) issue(bb0, 0);
-    for (int64_t vb = bb0; vb < bb1; ++vb) {
-        const int stg = (int)((vb - bb0) & 1);
-        if (vb + 1 < bb1) {
-            issue(vb + 1, stg ^ 1);
-            wait_vmcnt_a<LOADS>();
-        } else {
-            wait_vmcnt_a<0>();
+        for (int j = 0; j < QL; ++j) {
+            const int e = tid + 256 * j, rho = e / KCPR, c = e % KCPR;
+            const int qp = row_pos(rho);
+            qv[j] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(a.Q) +
+                                                    ((int64_t)row_head(rho) * a.ldq + (qp < a.nq ? qp : 0)) * HD +
+                                                    c * 8);
         }
-        __builtin_amdgcn_s_barrier();
-        const unsigned char* Kt = smem + stg * STAGE;
+#pragma unroll
+        for (int j = 0; j < QL; ++j) {
+            const int e = tid + 256 * j, rho = e / KCPR, c = e % KCPR;
+            const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            *reinterpret_cast<u16x8*>(Qs + rho * KROWB + kswz(rho, c) * 16) = row_pos(rho) < a.nq ? qv[j] : z;
+        }
+    }
+    f32x4 o[2][NT_D];
+    float m_run[2][4], l_run[2][4];
+    int qpos[2][4];  // absolute positions (< 2^31)
+    bool qok[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int j = 0; j < NT_D; ++j) o[t][j] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            m_run[t][i] = -INFINITY;
+            l_run[t][i] = 0.f;
+            const int rho = wave * 32 + t * 16 + lg * 4 + i;
+            qpos[t][i] = (int)(a.qpos0 + row_pos(rho));
+            qok[t][i] = row_pos(rho) < a.nq;
+        }
+    }
+    const float scale = 1.f / sqrtf((float)HD);
+
+    // pipeline: block vb is computed from the LDS slot while block vb + 1 sits
+    // in registers; after a barrier vb + 1 replaces it and vb + 2 is loaded
+    if (bb0 < bb1) {
+        load(bb0);
+        store();
+        load(bb0 + 1);
+    }
+    attn_lds_barrier();
+    for (int64_t vb = bb0; vb < bb1; ++vb) {
+        const unsigned char* Kt = smem;
         const unsigned char* Vt = Kt + K_BYTES;
         const bool seg1 = vb < nb1;
         const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
-        // ---- S = Q K^T ----
-        f32x4 s[4];
+        // ---- S = Q K^T (each K fragment feeds both row tiles); the fragments
+        // of k-step ks + 1 are read while the MFMAs of ks run ----
+        f32x4 s[2][4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            s[nt] = f32x4{0, 0, 0, 0};
-            const int r = nt * 16 + lr;
+            s[0][nt] = f32x4{0, 0, 0, 0};
+            s[1][nt] = f32x4{0, 0, 0, 0};
+        }
+        const int q0 = wave * 32 + lr, q1 = q0 + 16;
+        u16x8 qa[2], qb[2], kf[2][4];
+        auto ld_s = [&](int bsel, int ks) {
+            const int c = ks * 4 + lg;
+            qa[bsel] = *reinterpret_cast<const u16x8*>(Qs + q0 * KROWB + kswz(q0, c) * 16);
+            qb[bsel] = *reinterpret_cast<const u16x8*>(Qs + q1 * KROWB + kswz(q1, c) * 16);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u16x8 kf = *reinterpret_cast<const u16x8*>(Kt + r * KROWB + kswz(r, ks * 4 + lg) * 16);
-                s[nt] = amfma(qf[ks], kf, s[nt]);
+            for (int nt = 0; nt < 4; ++nt) {
+                const int r = nt * 16 + lr;
+                kf[bsel][nt] = *reinterpret_cast<const u16x8*>(Kt + r * KROWB + kswz(r, c) * 16);
+            }
+        };
+        ld_s(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) ld_s((ks + 1) & 1, ks + 1);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                s[0][nt] = amfma(qa[ks & 1], kf[ks & 1][nt], s[0][nt]);
+                s[1][nt] = amfma(qb[ks & 1], kf[ks & 1][nt], s[1][nt]);
             }
         }
-        // ---- mask ----
+        // ---- mask (branch-free, 32-bit positions), online softmax, P to LDS ----
+        int kp[4];
+        bool kin[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int64_t row = row0 + nt * 16 + lr;
-            bool kin;
-            int64_t kpos;
-            if (seg1) { kin = row >= a.s1 && row < a.e1; kpos = row; }
-            else { kin = row < a.n2; kpos = a.pos2_0 + row; }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bool ok = kin && qok[i];
-                if (a.causal) ok = ok && kpos <= qpos[i] && (a.window <= 0 || qpos[i] - kpos < a.window);
-                s[nt][i] = ok ? s[nt][i] * scale : -INFINITY;
-            }
+            const int row = (int)(row0 + nt * 16 + lr);
+            kin[nt] = seg1 ? (row >= (int)a.s1) & (row < (int)a.e1) : (row < a.n2);
+            kp[nt] = seg1 ? row : (int)a.pos2_0 + row;
         }
-        uint16_t* pw = Ps + wave * 16 * SP;
-        softmax_block<uint16_t, NT_D, SP>(s, m_run, l_run, o, pw, lr, lg);
-        // ---- O += P V (P rows are this wave's; V^T from LDS) ----
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bool ok = kin[nt] & qok[t][i];
+                    if (a.causal) {  // uniform
+                        const int dq = qpos[t][i] - kp[nt];
+                        ok = ok & (dq >= 0) & ((a.window <= 0) | (dq < a.window));
+                    }
+                    s[t][nt][i] = ok ? s[t][nt][i] * scale : -INFINITY;
+                }
+            softmax_block<uint16_t, NT_D, SP>(s[t], m_run[t], l_run[t], o[t], Ps + (wave * 32 + t * 16) * SP, lr, lg);
+        }
+        // ---- O += P V (each V^T fragment feeds both row tiles); V fragments in
+        // groups of 4, the next group read during the current MFMAs ----
+        const uint16_t* pw = Ps + wave * 32 * SP;
 #pragma unroll
         for (int ks2 = 0; ks2 < KB / 32; ++ks2) {
-            const u16x8 pf = *reinterpret_cast<const u16x8*>(pw + lr * SP + ks2 * 32 + lg * 8);
+            const u16x8 pf0 = *reinterpret_cast<const u16x8*>(pw + lr * SP + ks2 * 32 + lg * 8);
+            const u16x8 pf1 = *reinterpret_cast<const u16x8*>(pw + (16 + lr) * SP + ks2 * 32 + lg * 8);
+            u16x8 vf[2][4];
+            auto ld_v = [&](int bsel, int jg) {
 #pragma unroll
-            for (int j = 0; j < NT_D; ++j) {
-                const int d = j * 16 + lr;
-                const u16x8 vf = *reinterpret_cast<const u16x8*>(Vt + d * 128 + vswz(d, ks2 * 4 + lg) * 16);
-                o[j] = amfma(pf, vf, o[j]);
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int d = (jg * 4 + jj) * 16 + lr;
+                    vf[bsel][jj] = *reinterpret_cast<const u16x8*>(Vt + d * 128 + vswz(d, ks2 * 4 + lg) * 16);
+                }
+            };
+            ld_v(0, 0);
+#pragma unroll
+            for (int jg = 0; jg < NT_D / 4; ++jg) {
+                if (jg + 1 < NT_D / 4) ld_v((jg + 1) & 1, jg + 1);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    o[0][jg * 4 + jj] = amfma(pf0, vf[jg & 1][jj], o[0][jg * 4 + jj]);
+                    o[1][jg * 4 + jj] = amfma(pf1, vf[jg & 1][jj], o[1][jg * 4 + jj]);
+                }
             }
         }
-        __builtin_amdgcn_s_barrier();  // the stage is refilled by the next-but-one block
+        __builtin_amdgcn_s_barrier();  // every wave done with the slot
+        store();
+        load(vb + 2);
+        attn_lds_barrier();
     }
-    wait_vmcnt_a<0>();
+    __syncthreads();  // retire the tail loads
     // ---- write out ----
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (!qok[i]) continue;
-        const int rho = wave * 16 + lg * 4 + i;
-        const int hq = row_head(rho), qr = row_pos(rho);
-        if (a.splits == 1) {
-            const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
-            uint16_t* out = reinterpret_cast<uint16_t*>(a.O) + (int64_t)qr * a.Hq * HD + (int64_t)hq * HD;
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[j][i] * inv);
-        } else {
-            float* po = a.part_o + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * HD;
+        for (int i = 0; i < 4; ++i) {
+            if (!qok[t][i]) continue;
+            const int rho = wave * 32 + t * 16 + lg * 4 + i;
+            const int hq = row_head(rho), qr = row_pos(rho);
+            if (a.splits == 1) {
+                const float inv = l_run[t][i] > 0.f ? 1.f / l_run[t][i] : 0.f;
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.O) + (int64_t)qr * a.Hq * HD + (int64_t)hq * HD;
 #pragma unroll
-            for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[j][i];
-            if (lr == 0) {
-                float* pm = a.part_ml + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * 2;
-                pm[0] = m_run[i];
-                pm[1] = l_run[i];
+                for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[t][j][i] * inv);
+            } else {
+                float* po = a.part_o + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * HD;
+#pragma unroll
+                for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[t][j][i];
+                if (lr == 0) {
+                    float* pm = a.part_ml + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * 2;
+                    pm[0] = m_run[t][i];
+                    pm[1] = l_run[t][i];
+                }
             }
         }
     }
@@ -493,33 +588,49 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
 }
 
 template <int HD>
-static hipError_t launch_attn_dma(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
     const int R = a.Hq / a.Hkv;
     constexpr int STAGE = 64 * HD * 2 * 2;
-    const size_t lds = (size_t)2 * STAGE + (size_t)4 * 16 * (KB + 8) * 2;
+    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2 + (size_t)4 * 32 * (KB + 8) * 2;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_dma_kernel<HD>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_reg_kernel<HD>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    dim3 grid((a.nq + 64 / R - 1) / (64 / R), a.Hkv, a.splits);
-    attn_dma_kernel<HD><<<grid, 256, lds, st>>>(a, R);
+    dim3 grid((a.nq + 128 / R - 1) / (128 / R), a.Hkv, a.splits);
+    attn_reg_kernel<HD><<<grid, 256, lds, st>>>(a, R);
     if (a.splits > 1) attn_merge_kernel<uint16_t><<<dim3(a.nq, a.Hq), 256, 0, st>>>(a, HD);
     return hipGetLastError();
 }
 
-bool attention_uses_dma(const AttnArgs& a, int act_f32) {
-    const int R = a.Hq / a.Hkv;
-    return !act_f32 && (a.hd == 128 || a.hd == 256) && R >= 1 && R <= 64 && 64 % R == 0 &&
-           a.ld1 % 64 == 0 && (a.n2 == 0 || a.ld2 % 64 == 0);
+bool attention_uses_grouped(int Hq, int Hkv, int hd, int act_f32) {
+    const int R = Hq / Hkv;
+    return !act_f32 && (hd == 128 || hd == 256) && R >= 1 && R <= 64 && 128 % R == 0;
+}
+
+int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32, int max_splits, int max_rows) {
+    int s;
+    if (attention_uses_grouped(Hq, Hkv, hd, act_f32)) {
+        // about one workgroup per CU, each with at least 3 key blocks
+        const int64_t wgs = (int64_t)((nq + 128 / (Hq / Hkv) - 1) / (128 / (Hq / Hkv))) * Hkv;
+        const int64_t blocks = (keys + KB - 1) / KB + 1;
+        s = (int)std::min<int64_t>((256 + wgs - 1) / wgs, std::max<int64_t>(1, blocks / 3));
+    } else {
+        const int qtiles = (nq + 63) / 64;
+        s = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (keys + 511) / 512));
+        while (s > 1 && qtiles * Hq * (s / 2) >= 512) s /= 2;
+    }
+    s = std::max(1, std::min(s, max_splits));
+    while (s > 1 && (int64_t)s * nq > (int64_t)max_rows) --s;
+    return s;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st) {
-    if (attention_uses_dma(a, act_f32)) {
-        if (a.hd == 256) return launch_attn_dma<256>(a, st);
-        return launch_attn_dma<128>(a, st);
+    if (attention_uses_grouped(a.Hq, a.Hkv, a.hd, act_f32) && a.ld1 % 64 == 0 && (a.n2 == 0 || a.ld2 % 64 == 0)) {
+        if (a.hd == 256) return launch_attn_reg<256>(a, st);
+        return launch_attn_reg<128>(a, st);
     }
     if (act_f32) {
         if (a.hd == 64) return launch_attn_t<float, 64>(a, st);

@@ -59,5 +59,8 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st);
 size_t attention_partial_floats(int splits, int nq, int Hq, int hd);
+// KV splits for nq queries over `keys` keys: enough workgroups for the chip,
+// at most max_splits and max_splits * nq <= max_rows partial rows
+int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32, int max_splits, int max_rows);
 
 }  // namespace dg

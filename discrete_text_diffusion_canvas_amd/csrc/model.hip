@@ -28,6 +28,11 @@ struct dg_model {
     std::vector<dg_layer_weights> layers;
 };
 
+// expert groups with at least this many rows take the LDS-staged GEMM (bf16)
+#ifndef DG_TILE_MIN_ROWS
+#define DG_TILE_MIN_ROWS 65
+#endif
+
 namespace {
 
 constexpr int MAX_SPLITS = 16;
@@ -183,7 +188,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
     dn.C = w.Y; dn.ldc = d; dn.c_f32 = 1; dn.state = state;
     const bool tiled = dg::tile_gemm_supported(gu, f32, fp8, dg::EPI_SWIGLU) &&
                        dg::tile_gemm_supported(dn, f32, fp8, dg::EPI_STORE_F32);
-    const int big_min = tiled ? 65 : 0;
+    const int big_min = tiled ? DG_TILE_MIN_ROWS : 0;
     DG_TRY(dg::launch_hist_permute(w.ids, n, k, E, w.offsets, w.perm, w.slot_of, w.hit, w.hit_mb, w.hitB, w.hitB_mb,
                                    big_min, w.experts_hit ? w.experts_hit + l : nullptr, state, st),
            "hist permute");
@@ -217,12 +222,8 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
 }
 
 int attn_splits(const dg_config& c, int nq, int64_t keys) {
-    const int qtiles = (nq + 63) / 64;
-    int s = (int)std::min<int64_t>(MAX_SPLITS, std::max<int64_t>(1, (keys + 511) / 512));
-    // enough workgroups without splitting long query sets
-    while (s > 1 && qtiles * c.n_q_heads * (s / 2) >= 512) s /= 2;
-    while (s > 1 && (int64_t)s * nq > (int64_t)MAX_SPLITS * SPLIT_ROWS) s /= 2;
-    return s;
+    return dg::attention_splits(nq, keys, c.n_q_heads, c.n_kv_heads, c.head_dim, c.act_dtype == DG_F32, MAX_SPLITS,
+                                MAX_SPLITS * SPLIT_ROWS);
 }
 
 // ---------------------------------------------------------------------------
@@ -342,6 +343,7 @@ dg_status check_kv(const dg_model* m, const dg_kv* kv) {
     if (!kv || !kv->k || !kv->v) return fail(DG_E_INVALID, "kv cache is NULL");
     if (kv->len < 0 || kv->capacity < kv->len) return fail(DG_E_INVALID, "kv len/capacity inconsistent");
     if (kv->capacity % 64) return fail(DG_E_SHAPE, "kv capacity must be a multiple of 64");
+    if (kv->capacity > (int64_t)1 << 30) return fail(DG_E_SHAPE, "kv capacity above 2^30 rows");
     for (int l = 0; l < m->cfg.n_layers; ++l)
         if (!kv->k[l] || !kv->v[l]) return fail(DG_E_INVALID, "kv layer %d pointer is NULL", l);
     return DG_OK;

@@ -247,7 +247,7 @@ typedef struct dg_weights {
  * [n_kv_heads][capacity][head_dim] and V transposed, [n_kv_heads][head_dim]
  * [capacity], in the act dtype; keys after RoPE. Positions [0, len) are
  * filled; dg_prefill_append advances len on the host. capacity must be a
- * multiple of 64 and the cache must hold finite values beyond len (allocate
+ * multiple of 64, at most 2^30 rows (DG_E_SHAPE otherwise), and the cache must hold finite values beyond len (allocate
  * it zero-filled): attention reads whole 64-key blocks and masks the keys
  * outside the visible range. */
 typedef struct dg_kv {
