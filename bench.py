@@ -189,11 +189,14 @@ def _traffic(kernel, kd):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    src = os.path.join(ROOT, kv.get("kernel_source", ""))
-    if not os.path.isfile(src):
+    srcs = [x for x in kv.get("kernel_source", "").split(",") if x]
+    hashes = kv.get("kernel_source_sha256", "").split(",")
+    if not srcs or len(srcs) != len(hashes):
         return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv.get("kernel_source_sha256"):
-        return None
+    for src, h in zip(srcs, hashes):
+        path = os.path.join(ROOT, src)
+        if not os.path.isfile(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != h:
+            return None
     try:
         return round(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
@@ -320,6 +323,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny"])
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="finish with device copies of BYTES bytes (scale for HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the denoising step here is built for a single MI355X "
@@ -354,6 +359,13 @@ def main():
     for k in ("cpu_baseline", "kernels", "extra"):
         if k in res:
             out[k] = res.pop(k)
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["extra"] = dict(out.get("extra", {}), copy_calibration_bytes=args.copy_calibration)
     print(json.dumps(out), flush=True)
 
 

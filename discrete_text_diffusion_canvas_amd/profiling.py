@@ -1,0 +1,162 @@
+"""Summaries of rocprofv3 output for the measurement record (plain text).
+
+    python -m discrete_text_diffusion_canvas_amd.profiling stats DIR --command "..."
+        DIR holds a `rocprofv3 --kernel-trace --stats` run; prints the per-kernel
+        table (calls, average and total duration) of its *_kernel_stats.csv.
+
+    python -m discrete_text_diffusion_canvas_amd.profiling steps DB --command "..."
+        DB is the rocpd database (*_results.db) of a `rocprofv3 --kernel-trace`
+        run of bench.py; prints the kernels of the denoising steps (everything
+        after the first canvas reset) per step: time, calls, average duration,
+        and the attention / GEMM launches split by grid shape.
+
+    python -m discrete_text_diffusion_canvas_amd.profiling traffic \\
+        --fetch F.csv --write W.csv --kernels REGEX --label NAME \\
+        --copy-bytes B --sources a.hip,b.hip --command "..."
+        F/W are `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` counter
+        collections of one run that also made a device copy of B bytes. The
+        counters of the kernels matching REGEX are averaged per dispatch and
+        summed over the kernels (one logical launch may be several dispatches);
+        each counter is scaled by B / (the counter on the copy), which turns the
+        KiB the counters report into bytes the copy is known to move. The
+        output records the SHA-256 of the kernel sources, so a reader can tell
+        whether the kernel changed since.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import re
+import statistics
+import sys
+
+
+def _name(row: dict) -> str:
+    n = row.get("Kernel_Name") or row.get("Kernel-Name") or row.get("Name") or ""
+    return re.sub(r"\(.*", "", n).replace("void ", "").strip()
+
+
+def stats(args) -> None:
+    files = glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        sys.exit(f"no *kernel_stats.csv under {args.dir}")
+    rows = [r for r in csv.DictReader(open(files[0])) if re.search(args.filter, _name(r))]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print(f"# rocprofv3 kernel statistics ({os.path.basename(files[0])})")
+    print(f"# command: {args.command}")
+    if args.filter:
+        print(f"# kernels matching {args.filter!r} only")
+    print(f"# total kernel time {total / 1e6:.2f} ms over {sum(int(r['Calls']) for r in rows)} dispatches")
+    print(f"{'calls':>7} {'avg_us':>10} {'total_ms':>10} {'pct':>6}  kernel")
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    for r in rows[: args.top]:
+        print(f"{int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['TotalDurationNs']) / 1e6:10.3f} "
+              f"{100 * float(r['TotalDurationNs']) / total:6.2f}  {_name(r)[:90]}")
+
+
+def steps(args) -> None:
+    import collections
+    import sqlite3
+    db = sqlite3.connect(args.db)
+    cols = [r[1] for r in db.execute("pragma table_info(kernels)")]
+    gz = "grid_z" if "grid_z" in cols else "grid_x"
+    rows = list(db.execute(f"select name, start, end, duration, grid_x, {gz} from kernels order by start"))
+    i0 = next(i for i, r in enumerate(rows) if "canvas_reset_kernel" in r[0])
+    dec = rows[i0 + 1:]
+    nsteps = max(1, sum(1 for r in dec if "lmhead_kernel" in r[0] or "EPI_LMHEAD" in r[0]))
+    agg = collections.OrderedDict()
+    shp = collections.OrderedDict()
+    for r in dec:
+        n = _name({"Name": r[0]}).replace("dg::", "")
+        a = agg.setdefault(n, [0, 0.0])
+        a[0] += 1
+        a[1] += r[3]
+        if re.search(r"attn|gemm_kernel|lmhead", n):
+            b = shp.setdefault((n, r[4], r[5]), [0, 0.0])
+            b[0] += 1
+            b[1] += r[3]
+    tot = sum(a[1] for a in agg.values())
+    wall = dec[-1][2] - dec[0][1]
+    print("# kernels of the denoising steps (rocprofv3 kernel trace)")
+    print(f"# command: {args.command}")
+    print(f"# steps: {nsteps}; kernel time per step {tot / nsteps / 1e6:.3f} ms; wall per step {wall / nsteps / 1e6:.3f} ms; "
+          f"launches per step {sum(a[0] for a in agg.values()) / nsteps:.0f}")
+    print(f"{'ms/step':>8} {'pct':>6} {'calls/step':>10} {'avg_us':>9}  kernel")
+    for n, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"{t / nsteps / 1e6:8.3f} {100 * t / tot:6.1f} {c / nsteps:10.1f} {t / c / 1e3:9.1f}  {n[:80]}")
+    print("# by grid shape (grid x in threads, z = KV splits for attention)")
+    for (n, gx, gzv), (c, t) in sorted(shp.items(), key=lambda kv: -kv[1][1]):
+        print(f"  {n[:46]:46s} grid=({gx},{gzv}) calls/step={c / nsteps:6.1f} avg={t / c / 1e3:8.1f} us")
+
+
+def _per_dispatch(path: str, counter: str, regex: str) -> dict:
+    vals: dict = {}
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        n = _name(r)
+        if re.search(regex, n):
+            vals.setdefault(n, []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(args) -> None:
+    out = {}
+    for which, path, counter in (("fetch", args.fetch, "FETCH_SIZE"), ("write", args.write, "WRITE_SIZE")):
+        kern = _per_dispatch(path, counter, args.kernels)
+        copy = _per_dispatch(path, counter, args.copy_kernel)
+        if not kern or not copy:
+            sys.exit(f"{which}: no dispatches matched ({args.kernels!r} / {args.copy_kernel!r})")
+        # the copy: its largest dispatch is the calibration copy
+        cal = max(max(v) for v in copy.values())
+        scale = args.copy_bytes / cal
+        # the last dispatches of a run are decode steps (the prompt prefill comes first)
+        per = {n: statistics.median(v[-args.last:]) for n, v in kern.items()}
+        out[which] = (per, cal, scale)
+    print(f"# HBM traffic of one launch of {args.label} (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB per dispatch,")
+    print("# median over the last decode-step dispatches, scaled by a device copy of known size)")
+    print(f"# command: {args.command}")
+    srcs = [s for s in args.sources.split(",") if s]
+    print(f"kernel: {args.label}")
+    print(f"kernel_source: {','.join(srcs)}")
+    print("kernel_source_sha256: " + ",".join(hashlib.sha256(open(s, 'rb').read()).hexdigest() for s in srcs))
+    total = 0.0
+    for which in ("fetch", "write"):
+        per, cal, scale = out[which]
+        print(f"{which}_copy_counter_kib: {cal:.1f}  ({args.copy_bytes} bytes -> scale {scale:.2f} bytes per unit)")
+        for n, v in sorted(per.items()):
+            print(f"{which}_{n}: {v:.1f} units -> {v * scale / 1e6:.2f} MB")
+        total += sum(per.values()) * scale
+    print(f"hbm_bytes_per_launch: {total:.0f}")
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    a.add_argument("--top", type=int, default=30)
+    a.add_argument("--command", default="")
+    a.add_argument("--filter", default="", help="only kernels whose name matches this regex")
+    c = sub.add_parser("steps")
+    c.add_argument("db")
+    c.add_argument("--command", default="")
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--kernels", required=True)
+    b.add_argument("--copy-kernel", default=r"copyBuffer|copy_kernel|CopyKernel|elementwise")
+    b.add_argument("--copy-bytes", type=float, required=True)
+    b.add_argument("--label", required=True)
+    b.add_argument("--sources", default="")
+    b.add_argument("--command", default="")
+    b.add_argument("--last", type=int, default=30, help="dispatches per kernel at the end of the run to use")
+    args = ap.parse_args(argv)
+    {"stats": stats, "steps": steps, "traffic": traffic}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    main()
