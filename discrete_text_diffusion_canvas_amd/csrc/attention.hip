@@ -290,15 +290,17 @@ __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
 // loads in flight (a __syncthreads would also wait for those)
 __device__ __forceinline__ void attn_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int HD>
-__global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
+template <int HD, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
     if (a.state && a.state[0]) return;
     constexpr int KROWB = HD * 2;                 // bytes per K row
     constexpr int K_BYTES = KB * KROWB;           // K tile
     constexpr int V_BYTES = HD * KB * 2;          // V^T tile (rows of 128 bytes)
     constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int K_LD = K_BYTES / 1024 / 4;      // 16-byte loads per lane and block
-    constexpr int V_LD = V_BYTES / 1024 / 4;
+    constexpr int K_LD = K_BYTES / 1024 / NW;     // 16-byte loads per lane and block
+    constexpr int V_LD = V_BYTES / 1024 / NW;
+    constexpr int TPW = 128 / (16 * NW);          // 16-row tiles per wave
+    constexpr int RPW = 16 * TPW;                 // rows per wave
     constexpr int KRPI = 1024 / KROWB;            // K rows per 1 KB piece
     constexpr int KCPR = KROWB / 16;              // chunks per K row
     constexpr int NT_D = HD / 16;
@@ -306,7 +308,7 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
     constexpr int SP = KB + 8;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* Qs = smem + STAGE;                                  // [128 rows][HD], swizzled
-    uint16_t* Ps = reinterpret_cast<uint16_t*>(smem + STAGE + 128 * KROWB);  // [4 waves][32 rows][SP]
+    uint16_t* Ps = reinterpret_cast<uint16_t*>(smem + STAGE + 128 * KROWB);  // [128 rows][SP]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -314,7 +316,7 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
     const int QP = 128 / R;                       // positions per workgroup
     const int qx0 = blockIdx.x * QP;
     // workgroup row rho in [0, 128) = (head g*R + rho / QP, position qx0 + rho % QP);
-    // wave w owns rows [32w, 32w + 32) as two 16-row tiles
+    // wave w owns rows [RPW w, RPW (w + 1)) as TPW 16-row tiles
     auto row_head = [&](int rho) { return g * R + rho / QP; };
     auto row_pos = [&](int rho) { return qx0 + rho % QP; };
 
@@ -381,11 +383,11 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
     // ---- Q rows of the workgroup into LDS (row rho, 16-byte chunk c at kswz):
     // all loads first (rows past nq read row 0 and are zeroed), then the writes
     {
-        constexpr int QL = 128 * KCPR / 256;  // 16-byte pieces per thread
+        constexpr int QL = 128 * KCPR / (NW * 64);  // 16-byte pieces per thread
         u16x8 qv[QL];
 #pragma unroll
         for (int j = 0; j < QL; ++j) {
-            const int e = tid + 256 * j, rho = e / KCPR, c = e % KCPR;
+            const int e = tid + NW * 64 * j, rho = e / KCPR, c = e % KCPR;
             const int qp = row_pos(rho);
             qv[j] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(a.Q) +
                                                     ((int64_t)row_head(rho) * a.ldq + (qp < a.nq ? qp : 0)) * HD +
@@ -393,24 +395,24 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
         }
 #pragma unroll
         for (int j = 0; j < QL; ++j) {
-            const int e = tid + 256 * j, rho = e / KCPR, c = e % KCPR;
+            const int e = tid + NW * 64 * j, rho = e / KCPR, c = e % KCPR;
             const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
             *reinterpret_cast<u16x8*>(Qs + rho * KROWB + kswz(rho, c) * 16) = row_pos(rho) < a.nq ? qv[j] : z;
         }
     }
-    f32x4 o[2][NT_D];
-    float m_run[2][4], l_run[2][4];
-    int qpos[2][4];  // absolute positions (< 2^31)
-    bool qok[2][4];
+    f32x4 o[TPW][NT_D];
+    float m_run[TPW][4], l_run[TPW][4];
+    int qpos[TPW][4];  // absolute positions (< 2^31)
+    bool qok[TPW][4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TPW; ++t) {
 #pragma unroll
         for (int j = 0; j < NT_D; ++j) o[t][j] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             m_run[t][i] = -INFINITY;
             l_run[t][i] = 0.f;
-            const int rho = wave * 32 + t * 16 + lg * 4 + i;
+            const int rho = wave * RPW + t * 16 + lg * 4 + i;
             qpos[t][i] = (int)(a.qpos0 + row_pos(rho));
             qok[t][i] = row_pos(rho) < a.nq;
         }
@@ -432,18 +434,19 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
         const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
         // ---- S = Q K^T (each K fragment feeds both row tiles); the fragments
         // of k-step ks + 1 are read while the MFMAs of ks run ----
-        f32x4 s[2][4];
+        f32x4 s[TPW][4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            s[0][nt] = f32x4{0, 0, 0, 0};
-            s[1][nt] = f32x4{0, 0, 0, 0};
-        }
-        const int q0 = wave * 32 + lr, q1 = q0 + 16;
-        u16x8 qa[2], qb[2], kf[2][4];
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) s[t][nt] = f32x4{0, 0, 0, 0};
+        u16x8 qf[2][TPW], kf[2][4];
         auto ld_s = [&](int bsel, int ks) {
             const int c = ks * 4 + lg;
-            qa[bsel] = *reinterpret_cast<const u16x8*>(Qs + q0 * KROWB + kswz(q0, c) * 16);
-            qb[bsel] = *reinterpret_cast<const u16x8*>(Qs + q1 * KROWB + kswz(q1, c) * 16);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int q = wave * RPW + t * 16 + lr;
+                qf[bsel][t] = *reinterpret_cast<const u16x8*>(Qs + q * KROWB + kswz(q, c) * 16);
+            }
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int r = nt * 16 + lr;
@@ -455,10 +458,9 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS) ld_s((ks + 1) & 1, ks + 1);
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                s[0][nt] = amfma(qa[ks & 1], kf[ks & 1][nt], s[0][nt]);
-                s[1][nt] = amfma(qb[ks & 1], kf[ks & 1][nt], s[1][nt]);
-            }
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) s[t][nt] = amfma(qf[ks & 1][t], kf[ks & 1][nt], s[t][nt]);
         }
         // ---- mask (branch-free, 32-bit positions), online softmax, P to LDS ----
         int kp[4];
@@ -470,7 +472,7 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
             kp[nt] = seg1 ? row : (int)a.pos2_0 + row;
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < TPW; ++t) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
@@ -482,15 +484,17 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
                     }
                     s[t][nt][i] = ok ? s[t][nt][i] * scale : -INFINITY;
                 }
-            softmax_block<uint16_t, NT_D, SP>(s[t], m_run[t], l_run[t], o[t], Ps + (wave * 32 + t * 16) * SP, lr, lg);
+            softmax_block<uint16_t, NT_D, SP>(s[t], m_run[t], l_run[t], o[t], Ps + (wave * RPW + t * 16) * SP, lr, lg);
         }
         // ---- O += P V (each V^T fragment feeds both row tiles); V fragments in
         // groups of 4, the next group read during the current MFMAs ----
-        const uint16_t* pw = Ps + wave * 32 * SP;
+        const uint16_t* pw = Ps + wave * RPW * SP;
 #pragma unroll
         for (int ks2 = 0; ks2 < KB / 32; ++ks2) {
-            const u16x8 pf0 = *reinterpret_cast<const u16x8*>(pw + lr * SP + ks2 * 32 + lg * 8);
-            const u16x8 pf1 = *reinterpret_cast<const u16x8*>(pw + (16 + lr) * SP + ks2 * 32 + lg * 8);
+            u16x8 pf[TPW];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                pf[t] = *reinterpret_cast<const u16x8*>(pw + (t * 16 + lr) * SP + ks2 * 32 + lg * 8);
             u16x8 vf[2][4];
             auto ld_v = [&](int bsel, int jg) {
 #pragma unroll
@@ -504,10 +508,9 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
             for (int jg = 0; jg < NT_D / 4; ++jg) {
                 if (jg + 1 < NT_D / 4) ld_v((jg + 1) & 1, jg + 1);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    o[0][jg * 4 + jj] = amfma(pf0, vf[jg & 1][jj], o[0][jg * 4 + jj]);
-                    o[1][jg * 4 + jj] = amfma(pf1, vf[jg & 1][jj], o[1][jg * 4 + jj]);
-                }
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) o[t][jg * 4 + jj] = amfma(pf[t], vf[jg & 1][jj], o[t][jg * 4 + jj]);
             }
         }
         __builtin_amdgcn_s_barrier();  // every wave done with the slot
@@ -518,11 +521,11 @@ __global__ void __launch_bounds__(256) attn_reg_kernel(AttnArgs a, int R) {
     __syncthreads();  // retire the tail loads
     // ---- write out ----
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TPW; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (!qok[t][i]) continue;
-            const int rho = wave * 32 + t * 16 + lg * 4 + i;
+            const int rho = wave * RPW + t * 16 + lg * 4 + i;
             const int hq = row_head(rho), qr = row_pos(rho);
             if (a.splits == 1) {
                 const float inv = l_run[t][i] > 0.f ? 1.f / l_run[t][i] : 0.f;
@@ -587,20 +590,24 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+#ifndef DG_ATTN_WAVES
+#define DG_ATTN_WAVES 8
+#endif
 template <int HD>
 static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
+    constexpr int NW = DG_ATTN_WAVES;
     const int R = a.Hq / a.Hkv;
     constexpr int STAGE = 64 * HD * 2 * 2;
-    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2 + (size_t)4 * 32 * (KB + 8) * 2;
+    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2 + (size_t)128 * (KB + 8) * 2;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_reg_kernel<HD>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_reg_kernel<HD, NW>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
     }
     dim3 grid((a.nq + 128 / R - 1) / (128 / R), a.Hkv, a.splits);
-    attn_reg_kernel<HD><<<grid, 256, lds, st>>>(a, R);
+    attn_reg_kernel<HD, NW><<<grid, NW * 64, lds, st>>>(a, R);
     if (a.splits > 1) attn_merge_kernel<uint16_t><<<dim3(a.nq, a.Hq), 256, 0, st>>>(a, HD);
     return hipGetLastError();
 }
