@@ -25,6 +25,15 @@
 #include "common.hpp"
 #include "layer.hpp"
 
+// build-time tunables: waves per attention workgroup (8: one 16-row tile each;
+// 4: two tiles each) and the fewest 64-key blocks a KV split should hold
+#ifndef DG_ATTN_WAVES
+#define DG_ATTN_WAVES 8
+#endif
+#ifndef DG_ATTN_MIN_BLOCKS
+#define DG_ATTN_MIN_BLOCKS 3
+#endif
+
 namespace dg {
 
 template <typename TL> struct AFrag;
@@ -590,9 +599,6 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-#ifndef DG_ATTN_WAVES
-#define DG_ATTN_WAVES 8
-#endif
 template <int HD>
 static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
     constexpr int NW = DG_ATTN_WAVES;
@@ -620,10 +626,10 @@ bool attention_uses_grouped(int Hq, int Hkv, int hd, int act_f32) {
 int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32, int max_splits, int max_rows) {
     int s;
     if (attention_uses_grouped(Hq, Hkv, hd, act_f32)) {
-        // about one workgroup per CU, each with at least 3 key blocks
+        // about one workgroup per CU, each with at least DG_ATTN_MIN_BLOCKS key blocks
         const int64_t wgs = (int64_t)((nq + 128 / (Hq / Hkv) - 1) / (128 / (Hq / Hkv))) * Hkv;
         const int64_t blocks = (keys + KB - 1) / KB + 1;
-        s = (int)std::min<int64_t>((256 + wgs - 1) / wgs, std::max<int64_t>(1, blocks / 3));
+        s = (int)std::min<int64_t>((256 + wgs - 1) / wgs, std::max<int64_t>(1, blocks / DG_ATTN_MIN_BLOCKS));
     } else {
         const int qtiles = (nq + 63) / 64;
         s = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (keys + 511) / 512));

@@ -18,9 +18,10 @@
 //     c ^ ((r >> 1) & 7) so MFMA fragment reads are conflict-free. (Register
 //     loads keep overlapping with the MFMAs; LDS-direct copies measured here
 //     serialise with them.) One barrier per stage;
-//   * 4 waves, wave w owns rows [64w, 64w + 64) x all BN columns (4 x BN/16
-//     MFMA 16x16x32 tiles); a wave whose rows lie past the group's rows skips
-//     its MFMAs (its copies read one valid row);
+//   * BN/16 waves: wave w owns rows [64 (w % 4), + 64) x columns
+//     [64 (w / 4), + 64) (4 x 4 MFMA 16x16x32 tiles; with BN = 128 two waves
+//     share a SIMD); a wave whose rows lie past the group's rows skips its
+//     MFMAs (its copies of those rows read one valid row);
 //   * the epilogue transposes the tile through LDS and leaves in 16-byte
 //     coalesced stores: SwiGLU (BN/2 gate + BN/2 up columns of the same
 //     hidden units) to bf16, or a plain f32 store.
@@ -36,10 +37,10 @@
 #define DG_TILE_BN_GU 64
 #endif
 #ifndef DG_TILE_BN_DN
-#define DG_TILE_BN_DN 64
+#define DG_TILE_BN_DN 128
 #endif
 #ifndef DG_TILE_BN_DENSE
-#define DG_TILE_BN_DENSE 64
+#define DG_TILE_BN_DENSE 128
 #endif
 
 
@@ -51,7 +52,6 @@ constexpr int TBM = 256;                       // rows per m-block
 constexpr int TBK = 64;                        // k per stage
 constexpr int TROWB = TBK * 2;                 // bytes per LDS row
 constexpr int TA_BYTES = TBM * TROWB;          // 32 KB
-constexpr int TA_INSTR = TA_BYTES / 1024 / 4;  // 1 KB copies per wave (its 64 rows)
 
 __device__ __forceinline__ int tswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -100,6 +100,81 @@ __device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int 
     }
 }
 
+// LM-head epilogue on the tile T[r][c] (logits of record, bf16-rounded) of
+// vocabulary rows [tile*BN, +BN): (1) the bf16 logits leave in 16-byte
+// coalesced stores; (2) one thread per canvas row walks its BN logits in
+// vocabulary order for the tile's partial statistics: the max and the 2^x
+// partition sum and entropy partial of the tempered logits (log2 units), and
+// the raw argmax (first index among equal values), with the row's bias token
+// added and the mask token excluded. merge_rows combines the partials.
+template <int BN, int NT>
+__device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, const float* T, int mcount, int tile) {
+    constexpr int TS = BN + 4;
+    const int tid = threadIdx.x, N = g.N, n0 = tile * BN;
+    uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
+    for (int e = tid; e < mcount * (BN / 8); e += NT) {
+        const int r = e / (BN / 8), c0 = (e % (BN / 8)) * 8;
+        const int n = n0 + c0;
+        const float* t = T + r * TS + c0;
+        uint16_t* dst = C + (int64_t)r * g.ldc + n;
+        if (n + 8 <= N) {
+            uint4 w;
+            w.x = (uint32_t)f2bf(t[0]) | ((uint32_t)f2bf(t[1]) << 16);
+            w.y = (uint32_t)f2bf(t[2]) | ((uint32_t)f2bf(t[3]) << 16);
+            w.z = (uint32_t)f2bf(t[4]) | ((uint32_t)f2bf(t[5]) << 16);
+            w.w = (uint32_t)f2bf(t[6]) | ((uint32_t)f2bf(t[7]) << 16);
+            *reinterpret_cast<uint4*>(dst) = w;
+        } else {
+            for (int u = 0; u < 8 && n + u < N; ++u) dst[u] = f2bf(t[u]);
+        }
+    }
+    const int r = tid;
+    if (r >= mcount) return;
+    const int step = g.step_override >= 0 ? g.step_override : (g.state ? g.state[1] : 0);
+    const float c2 = (float)(1.4426950408889634 / lm_tau_at(g.sp, step));
+    const int bt = g.bias_tok ? g.bias_tok[r] : -1;
+    const float bv = g.bias_tok ? g.bias_val[r] : 0.f;
+    const float* row = T + r * TS;
+    float vm = -INFINITY, rawm = -INFINITY;
+    int vi = 0x7fffffff;
+#pragma unroll 4
+    for (int c = 0; c < BN; c += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(row + c);
+        const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int n = n0 + c + u;
+            float lb = e4[u] + (n == bt ? bv : 0.f);
+            if (n >= N || n == g.mask_id) lb = -INFINITY;
+            vm = fmaxf(vm, lb * c2);
+            if (lb > rawm) { rawm = lb; vi = n; }
+        }
+    }
+    float sum = 0.f, tt = 0.f;
+    if (vm != -INFINITY) {
+#pragma unroll 4
+        for (int c = 0; c < BN; c += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(row + c);
+            const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int n = n0 + c + u;
+                float lb = e4[u] + (n == bt ? bv : 0.f);
+                if (n >= N || n == g.mask_id) lb = -INFINITY;
+                const float d = lb * c2 - vm;
+                const float w = exp2f(d);
+                sum += w;
+                tt += w > 0.f ? w * d : 0.f;
+            }
+        }
+    }
+    RowPart p;
+    p.m2 = vm; p.s = sum; p.t = tt; p.lmax = rawm;
+    p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
+    p.pad[0] = p.pad[1] = p.pad[2] = 0;
+    g.parts[(int64_t)r * g.nsplit + tile] = p;
+}
+
 // Sum of the K-slice partials part[s][row][n] in slice order, then the
 // epilogue. One thread per 4 columns.
 template <int EPI>
@@ -118,15 +193,19 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmArgs g) {
 }
 
 template <int BN, int EPI>
-__global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles) {
+__global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_tiles) {
     if (g.state && g.state[0]) return;
     constexpr int B_BYTES = BN * TROWB;
     constexpr int STAGE = TA_BYTES + B_BYTES;
-    constexpr int B_INSTR = B_BYTES / 1024 / 4;
-    constexpr int TN = BN / 16;
+    constexpr int NW = BN / 16;                   // waves
+    constexpr int NT = NW * 64;                   // threads
+    constexpr int TA_INSTR = TA_BYTES / 1024 / NW;  // 1 KB row pieces of A per wave and stage
+    constexpr int B_INSTR = B_BYTES / 1024 / NW;
+    constexpr int TN = 4;                         // 16-column tiles per wave
     constexpr int TS = BN + 4;  // epilogue tile row stride (floats)
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 3, wn = wave >> 2;      // row block, column block
     const int lr = lane & 15, lg = lane >> 4;
     const int pos = lane & 7;
     const bool grouped = g.group_offsets != nullptr;
@@ -152,15 +231,15 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
         const int m0 = mb * TBM;
         if (m0 >= mrows) continue;  // uniform over the workgroup
         const int mcount = min(TBM, mrows - m0);
-        const bool live = wave * 64 < mcount;
+        const bool live = wm * 64 < mcount;
 
-        // load sources: load j of this wave covers LDS rows 64*wave + 8j + lane/8
-        // (A) and 8*(wave*B_INSTR + j) + lane/8 (W), position lane%8, i.e.
-        // logical chunk tswz(row, lane%8)
+        // load sources: load j of this wave covers LDS rows
+        // 8*(wave*TA_INSTR + j) + lane/8 (A) and 8*(wave*B_INSTR + j) + lane/8
+        // (W), position lane%8, i.e. logical chunk tswz(row, lane%8)
         const uint16_t* asrc[TA_INSTR];
 #pragma unroll
         for (int j = 0; j < TA_INSTR; ++j) {
-            const int r = wave * 64 + 8 * j + (lane >> 3);
+            const int r = 8 * (wave * TA_INSTR + j) + (lane >> 3);
             const int rr = min(r, mcount - 1);  // past the rows: a valid row, never stored
             const int ar = row0 + m0 + rr;
             const int src = g.a_rows ? g.a_rows[ar] : ar;
@@ -216,12 +295,12 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
                 u16x8 bfr[TN];
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int r = j * 16 + lr;
+                    const int r = wn * 64 + j * 16 + lr;
                     bfr[j] = *reinterpret_cast<const u16x8*>(bs + r * TROWB + tswz(r, c) * 16);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = wave * 64 + i * 16 + lr;
+                    const int r = wm * 64 + i * 16 + lr;
                     const u16x8 afr = *reinterpret_cast<const u16x8*>(as + r * TROWB + tswz(r, c) * 16);
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
@@ -260,7 +339,8 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        T[(wave * 64 + i * 16 + lg * 4 + q) * TS + j * 16 + lr] = acc[i][j][q];
+                        T[(wm * 64 + i * 16 + lg * 4 + q) * TS + wn * 64 + j * 16 + lr] =
+                            EPI == EPI_LMHEAD ? round_bf(acc[i][j][q]) : acc[i][j][q];
         }
         __syncthreads();
         if (ksplit > 1) {
@@ -268,18 +348,20 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
             constexpr int CH = BN / 4;
             const int n0 = tile * BN;
             float* P = g.part + (int64_t)ks * g.M * g.N;
-            for (int e = tid; e < mcount * CH; e += 256) {
+            for (int e = tid; e < mcount * CH; e += NT) {
                 const int r = e / CH, c0 = (e % CH) * 4;
                 const int n = n0 + c0;
                 if (n >= g.N) continue;
                 const float4 v = *reinterpret_cast<const float4*>(T + r * TS + c0);
                 *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 4 == 0
             }
+        } else if constexpr (EPI == EPI_LMHEAD) {
+            tile_lmhead_epilogue<BN, NT>(g, T, mcount, tile);
         } else if constexpr (EPI == EPI_SWIGLU) {
             constexpr int CH = BN / 2 / 8;  // 8-column chunks of hidden units per row
             uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
             const int f0 = tile * (BN / 2), F = g.N / 2;
-            for (int e = tid; e < mcount * CH; e += 256) {
+            for (int e = tid; e < mcount * CH; e += NT) {
                 const int r = e / CH, c0 = (e % CH) * 8;
                 const int f = f0 + c0;
                 if (f >= F) continue;
@@ -303,7 +385,7 @@ __global__ void __launch_bounds__(256) tile_gemm_kernel(GemmArgs g, int n_tiles)
         } else {
             constexpr int CH = BN / 4;  // float4 chunks per row
             const int n0 = tile * BN;
-            for (int e = tid; e < mcount * CH; e += 256) {
+            for (int e = tid; e < mcount * CH; e += NT) {
                 const int r = e / CH, c0 = (e % CH) * 4;
                 const int n = n0 + c0;
                 if (n >= g.N) continue;
@@ -334,13 +416,13 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     static int per_cu = 0;
     if (!per_cu) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI>), 256, lds);
+            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI>), BN * 4, lds);
         if (e != hipSuccess) return e;
         per_cu = std::max(per_cu, 1);
     }
     int64_t grid = std::min<int64_t>(items, 256 * per_cu);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
-    tile_gemm_kernel<BN, EPI><<<(unsigned)grid, 256, lds, st>>>(g, n_tiles);
+    tile_gemm_kernel<BN, EPI><<<(unsigned)grid, BN * 4, lds, st>>>(g, n_tiles);
     if (ks > 1) {
         const int64_t n = (int64_t)g.M * (g.N / 4);
         tile_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g);
@@ -356,6 +438,7 @@ bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
         case EPI_STORE_F32: return g.ldc % 4 == 0 && g.N % 4 == 0;
         case EPI_STORE_BF16: return g.ldc % 4 == 0 && g.N % 4 == 0;
         case EPI_RESIDUAL: return g.ldx % 4 == 0 && g.N % 4 == 0;
+        case EPI_LMHEAD: return !g.c_f32 && g.M <= TBM && g.ldc % 8 == 0;
         default: return false;
     }
 }
@@ -380,6 +463,11 @@ hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows
     if (epi == EPI_STORE_BF16) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_BF16>(g, 1, g.M, st);
     if (epi == EPI_RESIDUAL) return launch_tile_t<DG_TILE_BN_DENSE, EPI_RESIDUAL>(g, 1, g.M, st);
     if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_F32>(g, 1, g.M, st);
+    if (epi == EPI_LMHEAD) {
+        // one 256-row block; statistics partials per 128 vocabulary rows
+        if (g.ksplit > 1 || g.M > TBM || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
+        return launch_tile_t<128, EPI_LMHEAD>(g, 1, g.M, st);
+    }
     return hipErrorInvalidValue;
 }
 

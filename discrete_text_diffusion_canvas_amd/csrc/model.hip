@@ -332,7 +332,10 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
     g.state = state; g.step_override = step_override; g.sp = sp; g.mask_id = c.mask_id;
     g.bias_tok = bias_tok; g.bias_val = bias_val;
     int slot = timing_begin(st, DG_TIME_LM_HEAD);
-    DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
+    if (dg::tile_gemm_supported(g, f32, 0, dg::EPI_LMHEAD))
+        DG_TRY(dg::tile_gemm_launch(g, dg::EPI_LMHEAD, 1, n, st), "lm head");
+    else
+        DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
     timing_end(slot, st);
     DG_TRY(dg::launch_merge_rows(w.parts, n, lm_nsplit(c), state, stats->entropy, stats->lse, stats->argmax, st),
            "merge rows");
