@@ -7,7 +7,10 @@ experts, combine), the tied 262144-way LM head with the fused tempered
 statistics, and the EB sampler (selection, Philox draws, re-mask, stop).
 Canvases run back to back: every canvas starts all-MASK and, once finished,
 is run through the encoder and appended to the KV cache (inside the timed
-region). `value` = timed steps / timed wall time (HIP-synchronised);
+region). Each step is a replay of the step captured as a HIP graph
+(dg_step_graph; captured once per canvas, inside the timed region); the
+per-kernel timing passes run eager steps. `value` = timed steps / timed wall
+time (HIP-synchronised);
 committed tokens/s = canvas tokens finalised in the timed region / its time.
 
 Workloads (synthetic, seeded; random-init weights ~N(0, 0.02)):
@@ -79,26 +82,35 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     scfg = B.sampler_default()
     sched = {"t": 0, "canvas": 0, "committed": 0}
 
-    def run(K, record=None):
+    def run(K, record=None, use_graph=False):
+        # use_graph: each step is a replay of one captured step (HIP graph,
+        # captured once per canvas: the KV length is part of the capture)
         for _ in range(K):
             if sched["t"] == 0:
                 canvas.canvas_idx = sched["canvas"]
                 canvas.reset()
             P = kv.length
-            B.canvas_step(model, canvas, kv, sched["t"], SEED, scfg, stats, ws)
+            if use_graph:
+                if sched.get("graph") is None:
+                    sched["graph"] = B.StepGraph(model, canvas, kv, scfg, SEED, stats, ws)
+                sched["graph"].launch()
+            else:
+                B.canvas_step(model, canvas, kv, sched["t"], SEED, scfg, stats, ws)
             sched["t"] += 1
             done = bool(canvas.state[B.ST_DONE].item())
             if record is not None:
                 record.append((P, stats.experts_hit.cpu().tolist()))
             if done or sched["t"] == scfg.max_steps:
                 B.prefill_append(model, kv, canvas.tokens, ws)
+                sched["graph"] = None
                 sched["committed"] += n
                 sched["canvas"] += 1
                 sched["t"] = 0
 
-    run(args.warmup)
+    run(args.warmup, use_graph=True)
     c0 = sched["committed"]
-    ms = _sync_ms(lambda: run(args.steps), torch)
+    ms = _sync_ms(lambda: run(args.steps, use_graph=True), torch)
+    sched["graph"] = None
     committed = sched["committed"] - c0
     # per-kernel timing: further passes over the same kind of steps with HIP
     # events bracketing every launch of one kernel on the stream it runs on

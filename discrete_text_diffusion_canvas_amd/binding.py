@@ -97,8 +97,14 @@ def _load() -> C.CDLL:
     lib.dg_embed.argtypes = [vp, vp, i32, vp, vp]
     lib.dg_decoder_layer.argtypes = [vp, i32, vp, i32, P(KVStruct), vp, vp, vp, sz, vp]
     lib.dg_lm_head.argtypes = [vp, vp, i32, P(SamplerCfg), i32, vp, vp, P(StepStatsStruct), vp, sz, vp]
+    lib.dg_step_graph_create.argtypes = [vp, P(CanvasStruct), P(KVStruct), P(SamplerCfg), u64, P(StepStatsStruct),
+                                         vp, sz, P(C.c_void_p)]
+    lib.dg_step_graph_launch.argtypes = [vp, vp]
+    lib.dg_step_graph_destroy.argtypes = [vp]
+    lib.dg_step_graph_destroy.restype = None
     for name in ("dg_canvas_reset", "dg_sampler_step", "dg_model_create", "dg_prefill_append",
-                 "dg_canvas_step", "dg_generate_canvas", "dg_embed", "dg_decoder_layer", "dg_lm_head"):
+                 "dg_canvas_step", "dg_generate_canvas", "dg_embed", "dg_decoder_layer", "dg_lm_head",
+                 "dg_step_graph_create", "dg_step_graph_launch"):
         getattr(lib, name).restype = i32
     return lib
 
@@ -253,7 +259,7 @@ class Model:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        if h is not None and h.value and lib is not None:
             lib.dg_model_destroy(h)
             self.handle = None
 
@@ -304,6 +310,31 @@ def canvas_step(model: Model, canvas: Canvas, kv: KVCache, step_idx: int, seed: 
     s = stats.struct()
     check(lib.dg_canvas_step(model.handle, C.byref(c), C.byref(kv.struct_), step_idx, seed, C.byref(scfg),
                              C.byref(s), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class StepGraph:
+    """One dg_canvas_step captured as a HIP graph, the step index read from the
+    canvas state; valid until the next prefill_append on ``kv``. Holds the
+    buffers it was captured with."""
+
+    def __init__(self, model: Model, canvas: Canvas, kv: KVCache, scfg: SamplerCfg, seed: int, stats: StepStats,
+                 ws: torch.Tensor):
+        c = canvas.struct()
+        s = stats.struct()
+        h = C.c_void_p()
+        check(lib.dg_step_graph_create(model.handle, C.byref(c), C.byref(kv.struct_), C.byref(scfg), seed,
+                                       C.byref(s), _ptr(ws), ws.numel(), C.byref(h)))
+        self.handle = h
+        self._keep = (model, canvas, kv, stats, ws)
+
+    def launch(self, stream=None) -> None:
+        check(lib.dg_step_graph_launch(self.handle, _stream(stream)))
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and lib is not None:
+            lib.dg_step_graph_destroy(h)
+            self.handle = None
 
 
 def generate_canvas(model: Model, canvas: Canvas, kv: KVCache, scfg: SamplerCfg, seed: int,

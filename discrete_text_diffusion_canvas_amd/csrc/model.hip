@@ -565,4 +565,56 @@ dg_status dg_generate_canvas(const dg_model* m, dg_canvas* canvas, dg_kv* kv, co
     return DG_OK;
 }
 
+struct dg_step_graph {
+    hipStream_t cap = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+void dg_step_graph_destroy(dg_step_graph* g) {
+    if (!g) return;
+    if (g->exec) (void)hipGraphExecDestroy(g->exec);
+    if (g->graph) (void)hipGraphDestroy(g->graph);
+    if (g->cap) (void)hipStreamDestroy(g->cap);
+    delete g;
+}
+
+dg_status dg_step_graph_create(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, const dg_sampler_cfg* scfg,
+                               uint64_t seed, dg_step_stats* stats, void* ws, size_t ws_bytes, dg_step_graph** out) {
+    if (!out) return fail(DG_E_INVALID, "out is NULL");
+    *out = nullptr;
+    dg_step_graph* g = new (std::nothrow) dg_step_graph;
+    if (!g) return fail(DG_E_INVALID, "out of host memory");
+    // a capture stream of its own (default priority)
+    if (dg_status s = hip_check(hipStreamCreateWithFlags(&g->cap, hipStreamNonBlocking), "capture stream")) {
+        dg_step_graph_destroy(g);
+        return s;
+    }
+    if (dg_status s = hip_check(hipStreamBeginCapture(g->cap, hipStreamCaptureModeRelaxed), "begin capture")) {
+        dg_step_graph_destroy(g);
+        return s;
+    }
+    const dg_status st = dg_canvas_step(m, canvas, kv, -1, seed, scfg, stats, ws, ws_bytes, g->cap);
+    const hipError_t e = hipStreamEndCapture(g->cap, &g->graph);
+    if (st != DG_OK) {
+        dg_step_graph_destroy(g);
+        return st;
+    }
+    if (dg_status s = hip_check(e, "end capture")) {
+        dg_step_graph_destroy(g);
+        return s;
+    }
+    if (dg_status s = hip_check(hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0), "instantiate")) {
+        dg_step_graph_destroy(g);
+        return s;
+    }
+    *out = g;
+    return DG_OK;
+}
+
+dg_status dg_step_graph_launch(dg_step_graph* g, void* stream) {
+    if (!g || !g->exec) return fail(DG_E_INVALID, "graph is NULL");
+    return hip_check(hipGraphLaunch(g->exec, (hipStream_t)stream), "graph launch");
+}
+
 }  // extern "C"

@@ -308,6 +308,25 @@ dg_status dg_generate_canvas(const dg_model* m, dg_canvas* canvas, dg_kv* kv, co
                              int32_t* steps_taken, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * A denoising step captured as a HIP graph (the model card's step, zh-TW best
+ * practice 1, replayed without host launches). dg_step_graph_create records
+ * one dg_canvas_step with the step index read from canvas->state (step_idx
+ * -1) on a stream of its own and instantiates it; every pointer (model,
+ * canvas, kv arrays, stats, workspace) and the KV length kv->len at creation
+ * are baked in, so the graph is valid until the next dg_prefill_append on
+ * that cache (then destroy it and create another). dg_step_graph_launch
+ * enqueues one step on `stream`; after the canvas is finished a launch is a
+ * no-op on the device. Validation errors are those of dg_canvas_step
+ * (nothing is recorded then); HIP errors map to DG_E_HIP. The object is a
+ * host allocation owned by the caller until dg_step_graph_destroy.
+ */
+typedef struct dg_step_graph dg_step_graph;
+dg_status dg_step_graph_create(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, const dg_sampler_cfg* scfg,
+                               uint64_t seed, dg_step_stats* stats, void* ws, size_t ws_bytes, dg_step_graph** out);
+dg_status dg_step_graph_launch(dg_step_graph* graph, void* stream);
+void dg_step_graph_destroy(dg_step_graph* graph);
+
+/*
  * Component entry points (the stages of dg_canvas_step, exposed so each can
  * be checked on its own; same validation and ownership rules):
  *   dg_embed:          X[i][:] = embed[tokens[i]][:]                 (X f32 [n][d])

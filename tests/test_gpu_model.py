@@ -256,3 +256,37 @@ def test_experts_hit_counts_the_routed_experts(B, name):
         want.append(int(torch.unique(ids).numel()))
     torch.cuda.synchronize()
     assert stats.experts_hit.cpu().tolist() == want
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16"])
+def test_step_graph_replays_match_eager_steps(B, name):
+    """A captured step replayed with eager work and synchronisation between the
+    replays gives, at every step, bit-for-bit the eager step's canvas, state,
+    statistics and logits."""
+    cfg = CFGS[name]
+    model = device_model(B, cfg)
+    P = 300 if name != "tiny_f32" else wl.TINY_PREFIX
+    n = cfg.canvas
+    kv = B.KVCache(model, P + n)
+    fill_synthetic_kv(kv, cfg, P)
+    bt, bv = wl.canvas_boost(cfg, 0)
+    bt, bv = bt.cuda(), bv.cuda()
+    dt = model.act_dtype
+    ca, cb = B.Canvas(n, cfg.mask_id, 0, "cuda", bt, bv), B.Canvas(n, cfg.mask_id, 0, "cuda", bt, bv)
+    sa = B.StepStats(n, vocab=cfg.vocab, logits_dtype=dt)
+    sb = B.StepStats(n, vocab=cfg.vocab, logits_dtype=dt)
+    ws_a, ws_b = model.workspace(n), model.workspace(n)
+    scfg = B.sampler_default()
+    graph = B.StepGraph(model, cb, kv, scfg, SEED, sb, ws_b)
+    for t in range(6):
+        B.canvas_step(model, ca, kv, t, SEED, scfg, sa, ws_a)
+        graph.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(ca.tokens, cb.tokens), t
+        assert torch.equal(ca.committed, cb.committed), t
+        assert torch.equal(ca.state, cb.state), t
+        assert torch.equal(sa.entropy, sb.entropy), t
+        assert torch.equal(sa.argmax, sb.argmax), t
+        assert torch.equal(sa.logits, sb.logits), t
+        # eager work of the program between replays
+        _ = (sb.entropy * 2).sum().item()
