@@ -38,6 +38,7 @@ struct GemmArgs {
     // split-K (LDS-staged dense GEMM): K slices, f32 partials [ksplit][M][N]
     int ksplit;
     float* part;
+    int ksplit_min_rows;            // grouped split-K: groups of fewer rows are not tiled
     // control
     const int32_t* state;           // canvas state (done flag, step) or NULL
     // LM head
@@ -62,6 +63,8 @@ bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi);
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st);
 // K slices for a dense M x N x K product (1 = no split)
 int tile_dense_ksplit(int M, int N, int K);
+// K slices of the grouped gate/up GEMM for a batch of `rows` tokens
+int tile_grouped_ksplit(int rows);
 
 // ---------------------------------------------------------------------------
 // LM-head epilogue: logits of record (accumulator rounded to the storage

@@ -91,14 +91,15 @@ __device__ __forceinline__ float ssilu(float x) { return x / (1.f + __expf(-x));
 // past this wave's range contributes zero through a select on the W frags).
 template <int TMV, typename TL, int WK>
 __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[STM][STN], const TL* const (&arow)[STM],
-                                             const unsigned char* const (&wrow)[STN], int wave, int lg, int KS) {
+                                             const unsigned char* const (&wrow)[STN], int wave, int lg, int KS,
+                                             int kbase) {
     constexpr int WES = (WK == WK_FP8) ? 1 : (int)sizeof(TL);
     SFrag<TL, WK_SAME> fa[2][TMV];
     SFrag<TL, WK> fb[2][STN];
     const int nmax = (KS + 3) / 4;
     auto load = [&](int d, int s) {
         const int ks = min(wave + 4 * s, KS - 1);
-        const int k = ks * 32 + lg * 8;
+        const int k = kbase + ks * 32 + lg * 8;
 #pragma unroll
         for (int i = 0; i < TMV; ++i) fa[d][i].load(arow[i] + k);
 #pragma unroll
@@ -128,7 +129,10 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[STM][STN], const TL* c
 // ids place the m-blocks of one unit 8 apart, so with a persistent grid (a
 // multiple of 8) they run on one XCD. Grouped mode reads the hit groups from
 // g.hit ([0] = count, then group ids) and the largest m-block count from
-// g.hit_mb; non-grouped mode has one group of g.M rows.
+// g.hit_mb; non-grouped mode has one group of g.M rows. With g.ksplit > 1
+// (non-grouped, plain f32 store) the K range is cut into g.ksplit slices, one
+// more item dimension, and slice s leaves its raw sums in
+// g.part[s][row][n]; the consumer adds the slices in order.
 template <typename TL, int WK, int EPI>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_STREAM_WAVES)))
 stream_gemm_kernel(GemmArgs g, int n_tiles) {
@@ -140,14 +144,17 @@ stream_gemm_kernel(GemmArgs g, int n_tiles) {
     const int ngroups = g.group_offsets ? g.hit[0] : 1;
     const int mb_max = g.group_offsets ? *g.hit_mb : (g.M + SBM - 1) / SBM;
     const int units = ngroups * n_tiles;
-    const int64_t items = (int64_t)((units + 7) / 8) * 8 * mb_max;
+    const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
+    const int64_t items = (int64_t)((units * ksplit + 7) / 8) * 8 * mb_max;
+    const int KS = g.K / 32 / ksplit;  // k-steps per slice
     __shared__ float tile_s[SBM][SBN + 1];
 
     for (int64_t id = blockIdx.x; id < items; id += gridDim.x) {
         const int blk = (int)(id / (8 * mb_max)), rem = (int)(id % (8 * mb_max));
         const int mb = rem / 8;
-        const int u = blk * 8 + rem % 8;
-        if (u >= units) continue;
+        const int uk = blk * 8 + rem % 8;
+        if (uk >= units * ksplit) continue;
+        const int u = uk % units, kslice = uk / units;
         const int gi = u / n_tiles, tile = u % n_tiles;
         const int grp = g.group_offsets ? g.hit[1 + gi] : 0;
         int row0, mrows;
@@ -200,10 +207,10 @@ stream_gemm_kernel(GemmArgs g, int n_tiles) {
         for (int i = 0; i < STM; ++i)
 #pragma unroll
             for (int j = 0; j < STN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int KS = g.K / 32;
-        if (tm_live == 1) stream_kloop<1, TL, WK>(acc, arow, wrow, wave, lg, KS);
-        else if (tm_live == 2) stream_kloop<2, TL, WK>(acc, arow, wrow, wave, lg, KS);
-        else stream_kloop<4, TL, WK>(acc, arow, wrow, wave, lg, KS);
+        const int kbase = kslice * KS * 32;
+        if (tm_live == 1) stream_kloop<1, TL, WK>(acc, arow, wrow, wave, lg, KS, kbase);
+        else if (tm_live == 2) stream_kloop<2, TL, WK>(acc, arow, wrow, wave, lg, KS, kbase);
+        else stream_kloop<4, TL, WK>(acc, arow, wrow, wave, lg, KS, kbase);
 
         // ---- sum the 4 waves' partial tiles in LDS, in wave order ----
         for (int w = 0; w < 4; ++w) {
@@ -248,7 +255,8 @@ stream_gemm_kernel(GemmArgs g, int n_tiles) {
                 float v = tile_s[r][c];
                 if (g.w_scale) v *= bf2f(g.w_scale[(int64_t)grp * g.scale_group_stride + n]);
                 const int64_t orow = row0 + m0 + r;
-                if constexpr (EPI == EPI_STORE_F32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = v;
+                if (ksplit > 1) g.part[((int64_t)kslice * g.M + orow) * g.N + n] = v;
+                else if constexpr (EPI == EPI_STORE_F32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = v;
                 else if constexpr (EPI == EPI_STORE_BF16) reinterpret_cast<uint16_t*>(g.C)[orow * g.ldc + n] = f2bf(v);
                 else if constexpr (EPI == EPI_RESIDUAL) g.X[orow * g.ldx + n] += v;
             }
@@ -263,7 +271,9 @@ static hipError_t launch_stream_t(const GemmArgs& g, int groups, int max_rows, h
     const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + SBN / 2 - 1) / (SBN / 2) : (g.N + SBN - 1) / SBN;
     const int units = G * n_tiles;
     const int mb_max = std::max(1, (max_rows + SBM - 1) / SBM);
-    const int64_t items = (int64_t)((units + 7) / 8) * 8 * mb_max;  // upper bound
+    const int ks = g.ksplit > 1 ? g.ksplit : 1;
+    if (ks > 1 && (EPI != EPI_STORE_F32 || g.group_offsets || !g.part || (g.K / 32) % ks)) return hipErrorInvalidValue;
+    const int64_t items = (int64_t)((units * ks + 7) / 8) * 8 * mb_max;  // upper bound
     // persistent grid: a multiple of 8 (one slot per XCD), at most 4 per CU
     int64_t grid = std::min<int64_t>(items, 256 * 4);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);

@@ -42,6 +42,24 @@
 #ifndef DG_TILE_BN_DENSE
 #define DG_TILE_BN_DENSE 128
 #endif
+// gate/up split over K (decode-sized batches): tile width and slices
+#ifndef DG_TILE_BN_GU_SPLIT
+#define DG_TILE_BN_GU_SPLIT 128
+#endif
+#ifndef DG_GU_KSPLIT
+#define DG_GU_KSPLIT 2
+#endif
+// LM head tile width (128 or 256; statistics partials stay per 128 rows)
+#ifndef DG_TILE_BN_LM
+#define DG_TILE_BN_LM 128
+#endif
+// stages the operand registers are loaded ahead (dense/grouped; LM head)
+#ifndef DG_TILE_DEPTH
+#define DG_TILE_DEPTH 2
+#endif
+#ifndef DG_TILE_DEPTH_LM
+#define DG_TILE_DEPTH_LM DG_TILE_DEPTH
+#endif
 
 
 namespace dg {
@@ -61,10 +79,16 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ float tsilu(float x) { return x / (1.f + __expf(-x)); }
 
+// waves of a BN-wide workgroup: 4 row blocks x (BN / 64, at most 2) column blocks
+template <int BN>
+constexpr int tile_waves() { return BN >= 128 ? 8 : BN / 16; }
+// columns of one epilogue pass through LDS
+template <int BN>
+constexpr int tile_epi_cols() { return BN < 128 ? BN : 128; }
 // two stage slots, or the epilogue tile if larger
 template <int BN>
 constexpr size_t tile_lds_bytes() {
-    return std::max<size_t>(2 * (size_t)(TA_BYTES + BN * TROWB), (size_t)TBM * (BN + 4) * 4);
+    return std::max<size_t>(2 * (size_t)(TA_BYTES + BN * TROWB), (size_t)TBM * (tile_epi_cols<BN>() + 4) * 4);
 }
 
 }  // namespace
@@ -192,17 +216,52 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmArgs g) {
     tile_store4<EPI>(g, row, n, acc);
 }
 
-template <int BN, int EPI>
-__global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_tiles) {
+// Grouped split-K SwiGLU: for the slots of groups in the tiled list (g.hit),
+// gate and up summed over the K slices in slice order, then
+// h = silu(gate) * up to bf16. Slots of other groups are left alone. The
+// group of a slot is found by bisection of g.group_offsets.
+__global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int groups, int big_min) {
+    if (g.state && g.state[0]) return;
+    const int F = g.N / 2, f4 = F / 4;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int total = g.group_offsets[groups];
+    if (e >= (int64_t)total * f4) return;
+    const int slot = (int)(e / f4), f = (int)(e % f4) * 4;
+    int lo = 0, hi = groups;  // group gr with off[gr] <= slot < off[gr + 1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (g.group_offsets[mid] <= slot) lo = mid; else hi = mid;
+    }
+    if (g.group_offsets[lo + 1] - g.group_offsets[lo] < big_min) return;
+    float4 ga = *reinterpret_cast<const float4*>(g.part + (int64_t)slot * g.N + f);
+    float4 ua = *reinterpret_cast<const float4*>(g.part + (int64_t)slot * g.N + F + f);
+    for (int s = 1; s < g.ksplit; ++s) {
+        const float* P = g.part + ((int64_t)s * g.M + slot) * g.N;
+        const float4 gp = *reinterpret_cast<const float4*>(P + f);
+        const float4 up = *reinterpret_cast<const float4*>(P + F + f);
+        ga.x += gp.x; ga.y += gp.y; ga.z += gp.z; ga.w += gp.w;
+        ua.x += up.x; ua.y += up.y; ua.z += up.z; ua.w += up.w;
+    }
+    uint2 o;
+    o.x = (uint32_t)f2bf(tsilu(ga.x) * ua.x) | ((uint32_t)f2bf(tsilu(ga.y) * ua.y) << 16);
+    o.y = (uint32_t)f2bf(tsilu(ga.z) * ua.z) | ((uint32_t)f2bf(tsilu(ga.w) * ua.w) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.C) + (int64_t)slot * g.ldc + f) = o;
+}
+
+template <int BN, int EPI, int DEPTH>
+__global__ void __launch_bounds__(tile_waves<BN>() * 64) tile_gemm_kernel(GemmArgs g, int n_tiles) {
     if (g.state && g.state[0]) return;
     constexpr int B_BYTES = BN * TROWB;
     constexpr int STAGE = TA_BYTES + B_BYTES;
-    constexpr int NW = BN / 16;                   // waves
+    constexpr int NW = tile_waves<BN>();          // waves
     constexpr int NT = NW * 64;                   // threads
     constexpr int TA_INSTR = TA_BYTES / 1024 / NW;  // 1 KB row pieces of A per wave and stage
     constexpr int B_INSTR = B_BYTES / 1024 / NW;
-    constexpr int TN = 4;                         // 16-column tiles per wave
-    constexpr int TS = BN + 4;  // epilogue tile row stride (floats)
+    constexpr int WC = BN / (NW / 4);             // columns per wave
+    constexpr int TN = WC / 16;                   // 16-column tiles per wave
+    constexpr int EP = tile_epi_cols<BN>();       // columns per epilogue pass
+    constexpr int NPASS = BN / EP;
+    constexpr int TS = EP + 4;  // epilogue tile row stride (floats)
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave & 3, wn = wave >> 2;      // row block, column block
@@ -252,18 +311,21 @@ __global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_til
             const uint16_t* base;
             int wr;
             if constexpr (EPI == EPI_SWIGLU) {
-                // rows [0, BN/2): gate rows; [BN/2, BN): up rows of the same hidden units
-                base = reinterpret_cast<const uint16_t*>(r < BN / 2 ? g.W : g.W2);
-                wr = min(tile * (BN / 2) + (r % (BN / 2)), g.N / 2 - 1);
+                // per EP rows (one epilogue pass): EP/2 gate rows, then the up
+                // rows of the same hidden units
+                const int pp = r / EP, rr = r % EP;
+                base = reinterpret_cast<const uint16_t*>(rr < EP / 2 ? g.W : g.W2);
+                wr = min(tile * (BN / 2) + pp * (EP / 2) + (rr % (EP / 2)), g.N / 2 - 1);
             } else {
                 base = reinterpret_cast<const uint16_t*>(g.W);
                 wr = min(tile * BN + r, g.N - 1);
             }
             bsrc[j] = base + (int64_t)grp * g.w_group_stride + (int64_t)wr * g.ldw + 8 * tswz(r, pos);
         }
-        // two register slots of one stage each, loaded two stages ahead; loads
-        // past the last stage re-read it (branch-free, so the waits stay exact)
-        u32x4 ra[2][TA_INSTR], rb[2][B_INSTR];
+        // DEPTH register slots of one stage each, loaded DEPTH stages ahead;
+        // loads past the last stage re-read it (branch-free, so the waits stay
+        // exact)
+        u32x4 ra[DEPTH][TA_INSTR], rb[DEPTH][B_INSTR];
         auto load = [&](int d, int kt) {
             const int k0 = kbase + min(kt, KT - 1) * TBK;
 #pragma unroll
@@ -271,8 +333,8 @@ __global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_til
 #pragma unroll
             for (int j = 0; j < B_INSTR; ++j) rb[d][j] = *reinterpret_cast<const u32x4*>(bsrc[j] + k0);
         };
-        auto store = [&](int d) {
-            unsigned char* st = smem + d * STAGE;
+        auto store = [&](int d, int slot) {
+            unsigned char* st = smem + slot * STAGE;
 #pragma unroll
             for (int j = 0; j < TA_INSTR; ++j)
                 *reinterpret_cast<u32x4*>(st + (wave * TA_INSTR + j) * 1024 + lane * 16) = ra[d][j];
@@ -295,7 +357,7 @@ __global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_til
                 u16x8 bfr[TN];
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const int r = wn * 64 + j * 16 + lr;
+                    const int r = wn * WC + j * 16 + lr;
                     bfr[j] = *reinterpret_cast<const u16x8*>(bs + r * TROWB + tswz(r, c) * 16);
                 }
 #pragma unroll
@@ -309,64 +371,81 @@ __global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_til
                 }
             }
         };
-        // stage kt: its registers go to LDS slot kt % 2, the slot's registers
-        // are refilled with stage kt + 2, one barrier publishes the slot (the
-        // slot written here was last read two stages ago, before the previous
-        // barrier), then the MFMAs read it
-        auto step = [&](int d, int kt) {
-            store(d);
-            load(d, kt + 2);
+        // stage kt: its registers (slot kt % DEPTH) go to LDS slot kt % 2, the
+        // register slot is refilled with stage kt + DEPTH, one barrier
+        // publishes the LDS slot (written here, it was last read two stages
+        // ago, before the previous barrier), then the MFMAs read it
+        auto step = [&](int d, int slot, int kt) {
+            store(d, slot);
+            load(d, kt + DEPTH);
             lds_barrier();
-            if (live) compute(d);
+            if (live) compute(slot);
         };
-        load(0, 0);
-        load(1, 1);
+        constexpr int UNROLL = DEPTH % 2 ? 2 * DEPTH : DEPTH;
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) load(d, d);
         int kt = 0;
-        for (; kt + 1 < KT; kt += 2) {
-            step(0, kt);
-            step(1, kt + 1);
+        for (; kt + UNROLL <= KT; kt += UNROLL) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) step(u % DEPTH, u % 2, kt + u);
         }
-        if (kt < KT) step(0, kt);
+#pragma unroll
+        for (int u = 0; u + 1 < UNROLL; ++u)
+            if (kt + u < KT) step(u % DEPTH, u % 2, kt + u);
         __syncthreads();  // retire the tail loads; every wave done with the slots
 
-        // ---- epilogue: the tile through LDS, then coalesced row stores ----
-        __syncthreads();
+        // ---- epilogue: per pass of EP columns, the tile through LDS, then
+        // coalesced row stores; ptile numbers EP-column tiles ----
         float* T = reinterpret_cast<float*>(smem);
+#pragma unroll 1
+        for (int p = 0; p < NPASS; ++p) {
+        const int ptile = tile * NPASS + p;
+        __syncthreads();
         if (live) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < TN; ++j) {
+                const int c = wn * WC + j * 16 - p * EP;  // a whole 16-column tile is in the pass or not
+                if (c < 0 || c >= EP) continue;
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        T[(wm * 64 + i * 16 + lg * 4 + q) * TS + wn * 64 + j * 16 + lr] =
+                        T[(wm * 64 + i * 16 + lg * 4 + q) * TS + c + lr] =
                             EPI == EPI_LMHEAD ? round_bf(acc[i][j][q]) : acc[i][j][q];
+            }
         }
         __syncthreads();
         if (ksplit > 1) {
-            // raw f32 partial of this K slice: part[ks][row][n]
-            constexpr int CH = BN / 4;
-            const int n0 = tile * BN;
+            // raw f32 partial of this K slice: part[ks][row][n] (SwiGLU: gate
+            // columns f at n = f, up columns at n = N/2 + f)
+            constexpr int CH = EP / 4;
             float* P = g.part + (int64_t)ks * g.M * g.N;
             for (int e = tid; e < mcount * CH; e += NT) {
                 const int r = e / CH, c0 = (e % CH) * 4;
-                const int n = n0 + c0;
-                if (n >= g.N) continue;
+                int n;
+                if constexpr (EPI == EPI_SWIGLU) {
+                    const int f = ptile * (EP / 2) + (c0 % (EP / 2));
+                    if (f >= g.N / 2) continue;
+                    n = (c0 < EP / 2 ? 0 : g.N / 2) + f;
+                } else {
+                    n = ptile * EP + c0;
+                    if (n >= g.N) continue;
+                }
                 const float4 v = *reinterpret_cast<const float4*>(T + r * TS + c0);
-                *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 4 == 0
+                *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 8 == 0
             }
         } else if constexpr (EPI == EPI_LMHEAD) {
-            tile_lmhead_epilogue<BN, NT>(g, T, mcount, tile);
+            if (ptile < g.nsplit) tile_lmhead_epilogue<EP, NT>(g, T, mcount, ptile);  // past N: no columns
         } else if constexpr (EPI == EPI_SWIGLU) {
-            constexpr int CH = BN / 2 / 8;  // 8-column chunks of hidden units per row
+            constexpr int CH = EP / 2 / 8;  // 8-column chunks of hidden units per row
             uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
-            const int f0 = tile * (BN / 2), F = g.N / 2;
+            const int f0 = ptile * (EP / 2), F = g.N / 2;
             for (int e = tid; e < mcount * CH; e += NT) {
                 const int r = e / CH, c0 = (e % CH) * 8;
                 const int f = f0 + c0;
                 if (f >= F) continue;
                 const float* gt = T + r * TS + c0;
-                const float* up = gt + BN / 2;
+                const float* up = gt + EP / 2;
                 uint16_t h[8];
 #pragma unroll
                 for (int q = 0; q < 8; ++q) h[q] = f2bf(tsilu(gt[q]) * up[q]);
@@ -383,8 +462,8 @@ __global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_til
                 }
             }
         } else {
-            constexpr int CH = BN / 4;  // float4 chunks per row
-            const int n0 = tile * BN;
+            constexpr int CH = EP / 4;  // float4 chunks per row
+            const int n0 = ptile * EP;
             for (int e = tid; e < mcount * CH; e += NT) {
                 const int r = e / CH, c0 = (e % CH) * 4;
                 const int n = n0 + c0;
@@ -394,11 +473,12 @@ __global__ void __launch_bounds__(BN * 4) tile_gemm_kernel(GemmArgs g, int n_til
                 tile_store4<EPI>(g, row, n, v);
             }
         }
+        }  // passes
         __syncthreads();  // the LDS is refilled by the next item
     }
 }
 
-template <int BN, int EPI>
+template <int BN, int EPI, int DEPTH = DG_TILE_DEPTH>
 static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hipStream_t st) {
     const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     const int mb_max = std::max(1, (max_rows + TBM - 1) / TBM);
@@ -407,7 +487,7 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     const size_t lds = tile_lds_bytes<BN>();
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
@@ -416,14 +496,14 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     static int per_cu = 0;
     if (!per_cu) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI>), BN * 4, lds);
+            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH>), tile_waves<BN>() * 64, lds);
         if (e != hipSuccess) return e;
         per_cu = std::max(per_cu, 1);
     }
     int64_t grid = std::min<int64_t>(items, 256 * per_cu);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
-    tile_gemm_kernel<BN, EPI><<<(unsigned)grid, BN * 4, lds, st>>>(g, n_tiles);
-    if (ks > 1) {
+    tile_gemm_kernel<BN, EPI, DEPTH><<<(unsigned)grid, tile_waves<BN>() * 64, lds, st>>>(g, n_tiles);
+    if (ks > 1 && !g.group_offsets) {  // grouped split-K: the caller's reduce
         const int64_t n = (int64_t)g.M * (g.N / 4);
         tile_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g);
     }
@@ -452,9 +532,19 @@ int tile_dense_ksplit(int M, int N, int K) {
     return ks;
 }
 
+int tile_grouped_ksplit(int rows) { return rows <= TBM ? DG_GU_KSPLIT : 1; }
+
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
     if (g.group_offsets) {
-        if (g.ksplit > 1) return hipErrorInvalidValue;
+        if (g.ksplit > 1) {
+            // SwiGLU over K slices: partials [ksplit][M slots][2F], M = all slots
+            if (epi != EPI_SWIGLU || !g.part || (g.K / TBK) % g.ksplit || (g.N / 2) % 4) return hipErrorInvalidValue;
+            hipError_t e = launch_tile_t<DG_TILE_BN_GU_SPLIT, EPI_SWIGLU>(g, groups, max_rows, st);
+            if (e != hipSuccess) return e;
+            const int64_t n = (int64_t)g.M * (g.N / 8);
+            tile_swiglu_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, groups, g.ksplit_min_rows);
+            return hipGetLastError();
+        }
         if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU>(g, groups, max_rows, st);
         if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32>(g, groups, max_rows, st);
         return hipErrorInvalidValue;
@@ -466,7 +556,7 @@ hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows
     if (epi == EPI_LMHEAD) {
         // one 256-row block; statistics partials per 128 vocabulary rows
         if (g.ksplit > 1 || g.M > TBM || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
-        return launch_tile_t<128, EPI_LMHEAD>(g, 1, g.M, st);
+        return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM>(g, 1, g.M, st);
     }
     return hipErrorInvalidValue;
 }

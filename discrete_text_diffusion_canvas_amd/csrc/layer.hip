@@ -237,9 +237,10 @@ __global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__
 // k rounds of a wavefront argmax (value desc, expert id asc); gates are the
 // softmax over the k selected logits (f32).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) router_topk_kernel(const float* __restrict__ r, const float* __restrict__ bias,
-                                                          int n, int E, int k, int32_t* __restrict__ ids,
-                                                          float* __restrict__ gates, const int32_t* __restrict__ state) {
+__global__ void __launch_bounds__(256) router_topk_kernel(const float* __restrict__ r, int nparts, int64_t pstride,
+                                                          const float* __restrict__ bias, int n, int E, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                          const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     const int tokn = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -249,7 +250,14 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         int e = lane + 64 * j;
-        v[j] = e < E ? r[(int64_t)tokn * E + e] + bias[e] : -INFINITY;
+        if (e < E) {
+            // the logit: its K-slice partial sums added in slice order
+            float x = r[(int64_t)tokn * E + e];
+            for (int p = 1; p < nparts; ++p) x += r[p * pstride + (int64_t)tokn * E + e];
+            v[j] = x + bias[e];
+        } else {
+            v[j] = -INFINITY;
+        }
     }
     float sel[16];
     int sid[16];
@@ -500,9 +508,10 @@ hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int 
     return hipGetLastError();
 }
 
-hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, int k, int32_t* ids, float* gates,
-                              const int32_t* state, hipStream_t st) {
-    router_topk_kernel<<<(n + 3) / 4, 256, 0, st>>>(r, bias, n, E, k, ids, gates, state);
+hipError_t launch_router_topk(const float* r, int nparts, const float* bias, int n, int E, int k, int32_t* ids,
+                              float* gates, const int32_t* state, hipStream_t st) {
+    router_topk_kernel<<<(n + 3) / 4, 256, 0, st>>>(r, std::max(nparts, 1), (int64_t)n * E, bias, n, E, k, ids, gates,
+                                                    state);
     return hipGetLastError();
 }
 

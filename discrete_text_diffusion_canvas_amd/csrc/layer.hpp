@@ -15,8 +15,8 @@ hipError_t launch_rope_table(int n, int hd, int64_t pos0, double base, float* cs
 hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, const float* cs, void* Q,
                                int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld, int64_t kv_off,
                                int v_zero_to, const int32_t* state, hipStream_t st);
-hipError_t launch_router_topk(const float* r, const float* bias, int n, int E, int k, int32_t* ids, float* gates,
-                              const int32_t* state, hipStream_t st);
+hipError_t launch_router_topk(const float* r, int nparts, const float* bias, int n, int E, int k, int32_t* ids,
+                              float* gates, const int32_t* state, hipStream_t st);
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
                                int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hitB, int32_t* hitB_mb,
                                int big_min, int32_t* hit_out, const int32_t* state, hipStream_t st);

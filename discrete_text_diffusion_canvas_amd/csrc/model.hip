@@ -53,9 +53,10 @@ struct Work {
     void* O;           // [T][Hq hd]
     float* rope_cs;    // [T][hd/2][2] cos, sin of the rows' RoPE angles
     float* gemm_part;  // split-K partials of the dense projections
+    float* gu_part;    // split-K partials of the tiled expert gate/up GEMM
     float* part_o;     // attention split partials
     float* part_ml;
-    float* rlog;       // [T][E]
+    float* rlog;       // router logits: [K slices][n][E] partial sums
     int32_t* ids;      // [T][k]
     float* gates;      // [T][k]
     int32_t* offsets;  // [E+2]
@@ -75,6 +76,17 @@ struct Work {
     int rows64;        // T rounded up to a multiple of 64 (canvas K/V row stride)
     int32_t* experts_hit = nullptr;  // optional [n_layers] routed experts hit per layer (caller's buffer)
 };
+
+// K slices of the router GEMM: the most (up to 16) that divide its 32-wide
+// k-steps and leave each slice at least 8 (two per wave), so the few output
+// tiles still spread over many workgroups
+int router_ksplit(const dg_config& c) {
+    const int ks_total = c.d_model / 32;
+    int best = 1;
+    for (int s = 2; s <= 16; ++s)
+        if (ks_total % s == 0 && ks_total / s >= 8) best = s;
+    return best;
+}
 
 Work carve(const dg_model* m, void* base, int T) {
     const dg_config& c = m->cfg;
@@ -99,9 +111,13 @@ Work carve(const dg_model* m, void* base, int T) {
         const size_t parts = std::max(ka > 1 ? (size_t)ka * T * nqkv : 0, kb > 1 ? (size_t)kb * T * d : 0);
         w.gemm_part = parts ? cv.take<float>(parts) : nullptr;
     }
+    {   // split-K partials of the tiled gate/up GEMM: [slices][T (k + 1) slots][2F]
+        const int gks = ab == 2 ? dg::tile_grouped_ksplit(T) : 1;
+        w.gu_part = gks > 1 ? cv.take<float>((size_t)gks * T * (k + 1) * 2 * F) : nullptr;
+    }
     w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
     w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
-    w.rlog = cv.take<float>((size_t)T * E);
+    w.rlog = cv.take<float>((size_t)router_ksplit(c) * T * E);
     w.ids = cv.take<int32_t>((size_t)T * k);
     w.gates = cv.take<float>((size_t)T * k);
     w.offsets = cv.take<int32_t>(E + 2);
@@ -171,9 +187,11 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.router; g.ldw = d; g.M = n; g.N = E; g.K = d;
         g.C = w.rlog; g.ldc = E; g.state = state;
+        g.ksplit = router_ksplit(c); g.part = w.rlog;
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
     }
-    DG_TRY(dg::launch_router_topk(w.rlog, L.router_bias, n, E, k, w.ids, w.gates, state, st), "router topk");
+    DG_TRY(dg::launch_router_topk(w.rlog, router_ksplit(c), L.router_bias, n, E, k, w.ids, w.gates, state, st),
+           "router topk");
     // groups of more than 64 rows go to the LDS-staged GEMM (bf16 only)
     dg::GemmArgs gu = gargs(), dn = gargs();
     gu.A = w.A; gu.lda = d; gu.a_rows = w.perm;
@@ -200,6 +218,10 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
         DG_TRY(dg::stream_gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, small_rows, st), "expert gate/up");
         if (tiled) {
             g.hit = w.hitB; g.hit_mb = w.hitB_mb;
+            const int gks = dg::tile_grouped_ksplit(n);
+            if (gks > 1 && w.gu_part) {
+                g.ksplit = gks; g.part = w.gu_part; g.M = n * (k + 1); g.ksplit_min_rows = big_min;
+            }
             DG_TRY(dg::tile_gemm_launch(g, dg::EPI_SWIGLU, E + 1, n, st), "expert gate/up (tiled)");
         }
         timing_end(slot, st);

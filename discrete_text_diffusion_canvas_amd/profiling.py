@@ -66,7 +66,7 @@ def steps(args) -> None:
     rows = list(db.execute(f"select name, start, end, duration, grid_x, {gz} from kernels order by start"))
     i0 = next(i for i, r in enumerate(rows) if "canvas_reset_kernel" in r[0])
     dec = rows[i0 + 1:]
-    nsteps = max(1, sum(1 for r in dec if "lmhead_kernel" in r[0] or "EPI_LMHEAD" in r[0]))
+    nsteps = max(1, sum(1 for r in dec if "eb_select_kernel" in r[0]))  # one sampler selection per step
     agg = collections.OrderedDict()
     shp = collections.OrderedDict()
     for r in dec:
@@ -74,7 +74,7 @@ def steps(args) -> None:
         a = agg.setdefault(n, [0, 0.0])
         a[0] += 1
         a[1] += r[3]
-        if re.search(r"attn|gemm_kernel|lmhead", n):
+        if re.search(r"attn|gemm_kernel|lmhead|reduce", n):
             b = shp.setdefault((n, r[4], r[5]), [0, 0.0])
             b[0] += 1
             b[1] += r[3]
