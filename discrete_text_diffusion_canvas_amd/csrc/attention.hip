@@ -556,29 +556,64 @@ __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
 }
 
 // Merge split-KV partials: O = sum_s O_s e^(m_s - M) / sum_s l_s e^(m_s - M).
+// One wave per (query row, head); a lane owns 4 consecutive dims. Every
+// split's (m, l) and partial loads are issued before the sums, which run in
+// split order.
+constexpr int MERGE_MAX_SPLITS = 16;
 template <typename TL>
-__global__ void attn_merge_kernel(AttnArgs a, int hd) {
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int hd) {
     if (a.state && a.state[0]) return;
-    const int qr = blockIdx.x, h = blockIdx.y;
+    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (pair >= a.nq * a.Hq) return;
+    const int qr = pair / a.Hq, h = pair % a.Hq;
+    const int64_t rs = (int64_t)a.nq * a.Hq;  // (row, head) pairs per split
+    constexpr int MS = MERGE_MAX_SPLITS;
+    float2 ml[MS];
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+        if (s < a.splits) ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * rs + pair) * 2);
     float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s)
-        M = fmaxf(M, a.part_ml[(((int64_t)s * a.nq + qr) * a.Hq + h) * 2]);
-    float L = 0.f;
-    for (int s = 0; s < a.splits; ++s) {
-        const float* pm = a.part_ml + (((int64_t)s * a.nq + qr) * a.Hq + h) * 2;
-        if (pm[0] != -INFINITY) L += pm[1] * __expf(pm[0] - M);
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+        if (s < a.splits) M = fmaxf(M, ml[s].x);
+    float L = 0.f, wgt[MS];
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+        wgt[s] = 0.f;
+        if (s < a.splits && ml[s].x != -INFINITY) {
+            wgt[s] = __expf(ml[s].x - M);
+            L += ml[s].y * wgt[s];
+        }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     TL* out = reinterpret_cast<TL*>(a.O) + (int64_t)qr * a.Hq * hd + (int64_t)h * hd;
-    for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-        float acc = 0.f;
-        for (int s = 0; s < a.splits; ++s) {
-            const float* pm = a.part_ml + (((int64_t)s * a.nq + qr) * a.Hq + h) * 2;
-            if (pm[0] == -INFINITY) continue;
-            acc += a.part_o[(((int64_t)s * a.nq + qr) * a.Hq + h) * hd + d] * __expf(pm[0] - M);
+    for (int c = lane * 4; c < hd; c += 256) {
+        float4 po[MS];
+#pragma unroll
+        for (int s = 0; s < MS; ++s)
+            if (s < a.splits && ml[s].x != -INFINITY)
+                po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * rs + pair) * hd + c);
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int s = 0; s < MS; ++s) {
+            if (s < a.splits && ml[s].x != -INFINITY) {
+                acc.x += po[s].x * wgt[s];
+                acc.y += po[s].y * wgt[s];
+                acc.z += po[s].z * wgt[s];
+                acc.w += po[s].w * wgt[s];
+            }
         }
-        from_f(out + d, acc * inv);
+        from_f(out + c, acc.x * inv);
+        from_f(out + c + 1, acc.y * inv);
+        from_f(out + c + 2, acc.z * inv);
+        from_f(out + c + 3, acc.w * inv);
     }
+}
+
+static void launch_merge_any(const AttnArgs& a, bool bf16, hipStream_t st) {
+    const unsigned grid = (unsigned)(((int64_t)a.nq * a.Hq + 3) / 4);
+    if (bf16) attn_merge_kernel<uint16_t><<<grid, 256, 0, st>>>(a, a.hd);
+    else attn_merge_kernel<float><<<grid, 256, 0, st>>>(a, a.hd);
 }
 
 template <typename TL, int HD>
@@ -595,7 +630,7 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
     }
     dim3 grid((a.nq + 63) / 64, a.Hq, a.splits);
     kern<<<grid, 256, lds, st>>>(a);
-    if (a.splits > 1) attn_merge_kernel<TL><<<dim3(a.nq, a.Hq), 256, 0, st>>>(a, HD);
+    if (a.splits > 1) launch_merge_any(a, sizeof(TL) == 2, st);
     return hipGetLastError();
 }
 
@@ -614,7 +649,7 @@ static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
     }
     dim3 grid((a.nq + 128 / R - 1) / (128 / R), a.Hkv, a.splits);
     attn_reg_kernel<HD, NW><<<grid, NW * 64, lds, st>>>(a, R);
-    if (a.splits > 1) attn_merge_kernel<uint16_t><<<dim3(a.nq, a.Hq), 256, 0, st>>>(a, HD);
+    if (a.splits > 1) launch_merge_any(a, true, st);
     return hipGetLastError();
 }
 
@@ -641,6 +676,7 @@ int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32,
 }
 
 hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st) {
+    if (a.splits > MERGE_MAX_SPLITS || a.hd % 4) return hipErrorInvalidValue;
     if (attention_uses_grouped(a.Hq, a.Hkv, a.hd, act_f32) && a.ld1 % 64 == 0 && (a.n2 == 0 || a.ld2 % 64 == 0)) {
         if (a.hd == 256) return launch_attn_reg<256>(a, st);
         return launch_attn_reg<128>(a, st);

@@ -38,7 +38,7 @@ struct GemmArgs {
     // split-K (LDS-staged dense GEMM): K slices, f32 partials [ksplit][M][N]
     int ksplit;
     float* part;
-    int ksplit_min_rows;            // grouped split-K: groups of fewer rows are not tiled
+    int defer_reduce;               // dense split-K: leave the partials to the consumer
     // control
     const int32_t* state;           // canvas state (done flag, step) or NULL
     // LM head
@@ -65,6 +65,10 @@ hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows
 int tile_dense_ksplit(int M, int N, int K);
 // K slices of the grouped gate/up GEMM for a batch of `rows` tokens
 int tile_grouped_ksplit(int rows);
+// Grouped SwiGLU split over K: slot rows of groups of >= big_min rows hold
+// ks_big partial slices in g.part, the others ks_small (1: already stored);
+// adds them in slice order and stores silu(gate) * up to g.C (bf16)
+hipError_t swiglu_reduce_launch(const GemmArgs& g, int groups, int big_min, int ks_big, int ks_small, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // LM-head epilogue: logits of record (accumulator rounded to the storage

@@ -130,9 +130,11 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[STM][STN], const TL* c
 // multiple of 8) they run on one XCD. Grouped mode reads the hit groups from
 // g.hit ([0] = count, then group ids) and the largest m-block count from
 // g.hit_mb; non-grouped mode has one group of g.M rows. With g.ksplit > 1
-// (non-grouped, plain f32 store) the K range is cut into g.ksplit slices, one
-// more item dimension, and slice s leaves its raw sums in
-// g.part[s][row][n]; the consumer adds the slices in order.
+// (non-grouped plain f32 store, or grouped SwiGLU without weight scales) the
+// K range is cut into g.ksplit slices, one more item dimension, and slice s
+// leaves its raw sums in g.part[s][row][n] (SwiGLU: gate of hidden unit f at
+// n = f, up at n = N/2 + f; rows are slots, g.M of them); the consumer adds
+// the slices in order.
 template <typename TL, int WK, int EPI>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_STREAM_WAVES)))
 stream_gemm_kernel(GemmArgs g, int n_tiles) {
@@ -242,8 +244,14 @@ stream_gemm_kernel(GemmArgs g, int n_tiles) {
                     gv *= bf2f(g.w_scale[(int64_t)grp * g.scale_group_stride + n]);
                     uv *= bf2f(g.w2_scale[(int64_t)grp * g.scale_group_stride + n]);
                 }
-                const float h = ssilu(gv) * uv;
                 const int64_t orow = row0 + m0 + r;
+                if (ksplit > 1) {
+                    float* P = g.part + ((int64_t)kslice * g.M + orow) * g.N;
+                    P[n] = gv;
+                    P[g.N / 2 + n] = uv;
+                    continue;
+                }
+                const float h = ssilu(gv) * uv;
                 if (g.c_f32) reinterpret_cast<float*>(g.C)[orow * g.ldc + n] = h;
                 else reinterpret_cast<uint16_t*>(g.C)[orow * g.ldc + n] = f2bf(h);
             }
@@ -272,7 +280,8 @@ static hipError_t launch_stream_t(const GemmArgs& g, int groups, int max_rows, h
     const int units = G * n_tiles;
     const int mb_max = std::max(1, (max_rows + SBM - 1) / SBM);
     const int ks = g.ksplit > 1 ? g.ksplit : 1;
-    if (ks > 1 && (EPI != EPI_STORE_F32 || g.group_offsets || !g.part || (g.K / 32) % ks)) return hipErrorInvalidValue;
+    const bool split_ok = EPI == EPI_STORE_F32 ? !g.group_offsets : EPI == EPI_SWIGLU && g.group_offsets && !g.w_scale;
+    if (ks > 1 && (!split_ok || !g.part || (g.K / 32) % ks)) return hipErrorInvalidValue;
     const int64_t items = (int64_t)((units * ks + 7) / 8) * 8 * mb_max;  // upper bound
     // persistent grid: a multiple of 8 (one slot per XCD), at most 4 per CU
     int64_t grid = std::min<int64_t>(items, 256 * 4);

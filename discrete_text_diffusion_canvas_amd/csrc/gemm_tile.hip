@@ -216,11 +216,13 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmArgs g) {
     tile_store4<EPI>(g, row, n, acc);
 }
 
-// Grouped split-K SwiGLU: for the slots of groups in the tiled list (g.hit),
-// gate and up summed over the K slices in slice order, then
-// h = silu(gate) * up to bf16. Slots of other groups are left alone. The
+// Grouped split-K SwiGLU: for every slot whose group's GEMM was split, gate
+// and up summed over the K slices in slice order, then h = silu(gate) * up to
+// bf16. Groups of at least big_min rows were cut into ks_big slices, the
+// others into ks_small; a count of 1 means that GEMM stored h itself. The
 // group of a slot is found by bisection of g.group_offsets.
-__global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int groups, int big_min) {
+__global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int groups, int big_min, int ks_big,
+                                                                 int ks_small) {
     if (g.state && g.state[0]) return;
     const int F = g.N / 2, f4 = F / 4;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -232,10 +234,11 @@ __global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int
         const int mid = (lo + hi) / 2;
         if (g.group_offsets[mid] <= slot) lo = mid; else hi = mid;
     }
-    if (g.group_offsets[lo + 1] - g.group_offsets[lo] < big_min) return;
+    const int ks = g.group_offsets[lo + 1] - g.group_offsets[lo] >= big_min ? ks_big : ks_small;
+    if (ks <= 1) return;
     float4 ga = *reinterpret_cast<const float4*>(g.part + (int64_t)slot * g.N + f);
     float4 ua = *reinterpret_cast<const float4*>(g.part + (int64_t)slot * g.N + F + f);
-    for (int s = 1; s < g.ksplit; ++s) {
+    for (int s = 1; s < ks; ++s) {
         const float* P = g.part + ((int64_t)s * g.M + slot) * g.N;
         const float4 gp = *reinterpret_cast<const float4*>(P + f);
         const float4 up = *reinterpret_cast<const float4*>(P + F + f);
@@ -503,7 +506,7 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     int64_t grid = std::min<int64_t>(items, 256 * per_cu);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
     tile_gemm_kernel<BN, EPI, DEPTH><<<(unsigned)grid, tile_waves<BN>() * 64, lds, st>>>(g, n_tiles);
-    if (ks > 1 && !g.group_offsets) {  // grouped split-K: the caller's reduce
+    if (ks > 1 && !g.group_offsets && !g.defer_reduce) {  // grouped or deferred: the caller's reduce
         const int64_t n = (int64_t)g.M * (g.N / 4);
         tile_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g);
     }
@@ -534,16 +537,20 @@ int tile_dense_ksplit(int M, int N, int K) {
 
 int tile_grouped_ksplit(int rows) { return rows <= TBM ? DG_GU_KSPLIT : 1; }
 
+hipError_t swiglu_reduce_launch(const GemmArgs& g, int groups, int big_min, int ks_big, int ks_small, hipStream_t st) {
+    if (!g.part || (g.N / 2) % 4 || g.c_f32) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)g.M * (g.N / 8);
+    tile_swiglu_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, groups, big_min, ks_big, ks_small);
+    return hipGetLastError();
+}
+
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
     if (g.group_offsets) {
         if (g.ksplit > 1) {
-            // SwiGLU over K slices: partials [ksplit][M slots][2F], M = all slots
+            // SwiGLU over K slices: partials [ksplit][M slots][2F], M = all
+            // slots; swiglu_reduce_launch finishes them
             if (epi != EPI_SWIGLU || !g.part || (g.K / TBK) % g.ksplit || (g.N / 2) % 4) return hipErrorInvalidValue;
-            hipError_t e = launch_tile_t<DG_TILE_BN_GU_SPLIT, EPI_SWIGLU>(g, groups, max_rows, st);
-            if (e != hipSuccess) return e;
-            const int64_t n = (int64_t)g.M * (g.N / 8);
-            tile_swiglu_reduce_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g, groups, g.ksplit_min_rows);
-            return hipGetLastError();
+            return launch_tile_t<DG_TILE_BN_GU_SPLIT, EPI_SWIGLU>(g, groups, max_rows, st);
         }
         if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU>(g, groups, max_rows, st);
         if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32>(g, groups, max_rows, st);

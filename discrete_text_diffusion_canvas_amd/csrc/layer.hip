@@ -69,17 +69,47 @@ __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int n
     }
 }
 
+// With nparts > 0 the row first takes a residual update: X += the sum, in
+// slice order, of the K-slice partials part[s][i][.] of the product that
+// produces it; the updated row is stored back to X and normalised.
 template <typename TO>
-__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ X, int d, const float* __restrict__ w,
-                                                      float eps, TO* __restrict__ Y, const int32_t* __restrict__ state) {
+__global__ void __launch_bounds__(256) rmsnorm_kernel(float* __restrict__ X, const float* __restrict__ part, int nparts,
+                                                      int n, int d, const float* __restrict__ w, float eps,
+                                                      TO* __restrict__ Y, const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     const int i = blockIdx.x, nv = d / 4;
-    const float4* x4 = reinterpret_cast<const float4*>(X + (int64_t)i * d);
+    float4* x4 = reinterpret_cast<float4*>(X + (int64_t)i * d);
     float4 x[NORM_V4];
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
         const int c = threadIdx.x + 256 * j;
         x[j] = c < nv ? x4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (nparts > 0) {
+        const float4* p4 = reinterpret_cast<const float4*>(part + (int64_t)i * d);
+        const int64_t ps = (int64_t)n * nv;  // float4 per slice
+#pragma unroll
+        for (int j = 0; j < NORM_V4; ++j) {
+            const int c = threadIdx.x + 256 * j;
+            if (c >= nv) continue;
+            float4 pv[8];  // the loads of up to 8 slices go out before the adds
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s < nparts) pv[s] = p4[s * ps + c];
+            float4 acc = pv[0];
+#pragma unroll
+            for (int s = 1; s < 8; ++s) {
+                if (s < nparts) {
+                    acc.x += pv[s].x; acc.y += pv[s].y; acc.z += pv[s].z; acc.w += pv[s].w;
+                }
+            }
+            for (int s = 8; s < nparts; ++s) {
+                const float4 v = p4[s * ps + c];
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+            }
+            x[j].x += acc.x; x[j].y += acc.y; x[j].z += acc.z; x[j].w += acc.w;
+            x4[c] = x[j];
+        }
     }
     norm_row_store<TO>(x, nv, w, eps, d, Y + (int64_t)i * d);
 }
@@ -139,22 +169,67 @@ template <> struct Vec8<uint16_t> {
     }
 };
 
+// 8 consecutive projection outputs at element offset `off` of qkv, or, when
+// the projection was split over K (nparts > 1), the sum of its f32 partials
+// part[p][.] in slice order rounded to the activation type, exactly what the
+// split GEMM's own reduce would have stored in qkv
+template <typename T>
+__device__ __forceinline__ void qkv_load8(const T* qkv, const float* part, int nparts, int64_t pstride, int64_t off,
+                                          float (&v)[8]) {
+    if (nparts <= 1) {
+        Vec8<T>::load(qkv + off, v);
+        return;
+    }
+    // the loads of up to 8 slices are all issued before the adds
+    constexpr int MAXP = 8;
+    float4 a[MAXP], b[MAXP];
+#pragma unroll
+    for (int p = 0; p < MAXP; ++p) {
+        if (p < nparts) {
+            const float4* src = reinterpret_cast<const float4*>(part + p * pstride + off);
+            a[p] = src[0];
+            b[p] = src[1];
+        }
+    }
+    v[0] = a[0].x; v[1] = a[0].y; v[2] = a[0].z; v[3] = a[0].w;
+    v[4] = b[0].x; v[5] = b[0].y; v[6] = b[0].z; v[7] = b[0].w;
+#pragma unroll
+    for (int p = 1; p < MAXP; ++p) {
+        if (p < nparts) {
+            v[0] += a[p].x; v[1] += a[p].y; v[2] += a[p].z; v[3] += a[p].w;
+            v[4] += b[p].x; v[5] += b[p].y; v[6] += b[p].z; v[7] += b[p].w;
+        }
+    }
+    for (int p = MAXP; p < nparts; ++p) {
+        float t[8];
+        Vec8<float>::load(part + p * pstride + off, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] += t[e];
+    }
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf2f(f2bf(v[e]));
+    }
+}
+
 // ---------------------------------------------------------------------------
-// RoPE + scatter. qkv [n][(Hq+2Hkv)*hd] (row i at position pos0+i) ->
+// RoPE + scatter. qkv [n][(Hq+2Hkv)*hd] (row i at position pos0+i; or its
+// K-slice partials, see qkv_load8) ->
 //   Q  [Hq][q_ld][hd]        rows q_off + i   (rotated)
 //   K  [Hkv][kv_ld][hd]      rows kv_off + i  (rotated)
 //   V^T [Hkv][hd][kv_ld]     columns kv_off + i (V stored transposed)
 // Columns i in [n, v_zero_to) of V^T are set to 0 (the canvas V^T is read in
 // whole 64-key blocks). Rotate-half with the angles of rope_table_kernel:
 //   out[d] = x[d] cos a - x[d+hd/2] sin a;  out[d+hd/2] = x[d+hd/2] cos a + x[d] sin a.
-// Grid: (16-row tiles, heads), 256 threads. A Q/K workgroup rotates its 16
-// rows in 8-element chunks (one chunk pair per thread for hd = 256). A V
-// workgroup (x < 64-row tile count) transposes a 64 x hd tile through LDS:
-// all of its loads are issued before the first LDS write, and each V^T row
-// segment leaves as 16-byte stores of 8 consecutive columns.
+// Grid: (tiles, heads), 256 threads. A Q/K workgroup rotates 16 rows in
+// 8-element chunks (one chunk pair per thread for hd = 256). A V workgroup
+// transposes a 64-row x 64-dim tile through LDS: its loads are issued before
+// the first LDS write, and each V^T row segment leaves as 16-byte stores of 8
+// consecutive columns.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__ qkv, int n, int Hq, int Hkv, int hd,
+__global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__ qkv, const float* __restrict__ part,
+                                                           int nparts, int n, int Hq, int Hkv, int hd,
                                                            const float* __restrict__ cs, T* __restrict__ Q,
                                                            int64_t q_ld, int64_t q_off, T* __restrict__ K,
                                                            T* __restrict__ V, int64_t kv_ld, int64_t kv_off,
@@ -162,16 +237,17 @@ __global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__
     if (state && state[0]) return;
     const int h = blockIdx.y;
     const int half = hd / 2, width = (Hq + 2 * Hkv) * hd;
+    const int64_t pstride = (int64_t)n * width;
     if (h < Hq + Hkv) {
         const int r0 = blockIdx.x * 16;
         const int cpr = half / 8;  // 8-element chunks per half row
         const int rows = min(16, n - r0);
         for (int u = threadIdx.x; u < rows * cpr; u += 256) {
             const int i = r0 + u / cpr, d0 = (u % cpr) * 8;
-            const T* src = qkv + (int64_t)i * width + h * hd;
+            const int64_t src = (int64_t)i * width + h * hd;
             float x1[8], x2[8], y1[8], y2[8];
-            Vec8<T>::load(src + d0, x1);
-            Vec8<T>::load(src + half + d0, x2);
+            qkv_load8<T>(qkv, part, nparts, pstride, src + d0, x1);
+            qkv_load8<T>(qkv, part, nparts, pstride, src + half + d0, x2);
             const float4* c4 = reinterpret_cast<const float4*>(cs + ((int64_t)i * half + d0) * 2);
             const float4 c[4] = {c4[0], c4[1], c4[2], c4[3]};
 #pragma unroll
@@ -187,40 +263,42 @@ __global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__
             Vec8<T>::store(dst + half + d0, y2);
         }
     } else {
-        extern __shared__ float vt[];  // [64][hd + 1]
-        const int r0 = blockIdx.x * 64;
+        // V: a 64-row x 64-dim tile per workgroup (x = row tile * hd/64 + dim
+        // tile), transposed through LDS
+        __shared__ float vt[64 * 65];
+        const int dq = hd / 64;
+        const int r0 = (blockIdx.x / dq) * 64, d0 = (blockIdx.x % dq) * 64;
         const int rows = min(64, max(n, v_zero_to) - r0);
         if (rows <= 0) return;
         const int hv = h - Hq - Hkv;
-        const int cpr = hd / 8;      // 8-element chunks per row
-        constexpr int MAXU = 8;      // 64 rows x 32 chunks (hd 256) / 256 threads
-        float v[MAXU][8];
+        float v[2][8];
 #pragma unroll
-        for (int j = 0; j < MAXU; ++j) {
+        for (int j = 0; j < 2; ++j) {  // 64 rows x 8 chunks of 8 dims: two per thread
             const int u = threadIdx.x + 256 * j;
-            const int r = u / cpr, i = r0 + r;
+            const int r = u / 8, i = r0 + r;
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
-            if (r < rows && i < n) Vec8<T>::load(qkv + (int64_t)i * width + h * hd + (u % cpr) * 8, v[j]);
+            if (r < rows && i < n)
+                qkv_load8<T>(qkv, part, nparts, pstride, (int64_t)i * width + h * hd + d0 + (u % 8) * 8, v[j]);
         }
 #pragma unroll
-        for (int j = 0; j < MAXU; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const int u = threadIdx.x + 256 * j;
-            const int r = u / cpr, c = (u % cpr) * 8;
+            const int r = u / 8, c = (u % 8) * 8;
             if (r < rows)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vt[r * (hd + 1) + c + e] = v[j][e];
+                for (int e = 0; e < 8; ++e) vt[r * 65 + c + e] = v[j][e];
         }
         __syncthreads();
         // output unit: (dim d, 8 consecutive columns)
         const int cgs = (rows + 7) / 8;
         const bool vec = ((kv_off + r0) % 8) == 0 && rows % 8 == 0;
-        for (int u = threadIdx.x; u < hd * cgs; u += 256) {
+        for (int u = threadIdx.x; u < 64 * cgs; u += 256) {
             const int d = u / cgs, c0 = (u % cgs) * 8;
             float o[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = c0 + e < rows ? vt[(c0 + e) * (hd + 1) + d] : 0.f;
-            T* dst = V + ((int64_t)hv * hd + d) * kv_ld + kv_off + r0 + c0;
+            for (int e = 0; e < 8; ++e) o[e] = c0 + e < rows ? vt[(c0 + e) * 65 + d] : 0.f;
+            T* dst = V + ((int64_t)hv * hd + d0 + d) * kv_ld + kv_off + r0 + c0;
             if (vec) {
                 Vec8<T>::store(dst, o);
             } else {
@@ -250,13 +328,20 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         int e = lane + 64 * j;
+        v[j] = -INFINITY;
         if (e < E) {
-            // the logit: its K-slice partial sums added in slice order
-            float x = r[(int64_t)tokn * E + e];
-            for (int p = 1; p < nparts; ++p) x += r[p * pstride + (int64_t)tokn * E + e];
+            // the logit: its K-slice partial sums added in slice order (the
+            // loads of up to 16 slices are all issued before the adds)
+            const float* src = r + (int64_t)tokn * E + e;
+            float xs[16];
+#pragma unroll
+            for (int p = 0; p < 16; ++p) xs[p] = p < nparts ? src[p * pstride] : 0.f;
+            float x = xs[0];
+#pragma unroll
+            for (int p = 1; p < 16; ++p)
+                if (p < nparts) x += xs[p];
+            for (int p = 16; p < nparts; ++p) x += src[p * pstride];
             v[j] = x + bias[e];
-        } else {
-            v[j] = -INFINITY;
         }
     }
     float sel[16];
@@ -468,9 +553,14 @@ hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, i
 
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
                           const int32_t* state, hipStream_t st) {
-    if (d % 4 || d > 4 * 256 * NORM_V4) return hipErrorInvalidValue;
-    if (act_f32) rmsnorm_kernel<float><<<n, 256, 0, st>>>(X, d, w, eps, (float*)Y, state);
-    else rmsnorm_kernel<uint16_t><<<n, 256, 0, st>>>(X, d, w, eps, (uint16_t*)Y, state);
+    return launch_residual_rmsnorm(const_cast<float*>(X), nullptr, 0, n, d, w, eps, Y, act_f32, state, st);
+}
+
+hipError_t launch_residual_rmsnorm(float* X, const float* part, int nparts, int n, int d, const float* w, float eps,
+                                   void* Y, int act_f32, const int32_t* state, hipStream_t st) {
+    if (d % 4 || d > 4 * 256 * NORM_V4 || (nparts > 0 && !part)) return hipErrorInvalidValue;
+    if (act_f32) rmsnorm_kernel<float><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (float*)Y, state);
+    else rmsnorm_kernel<uint16_t><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (uint16_t*)Y, state);
     return hipGetLastError();
 }
 
@@ -480,29 +570,21 @@ hipError_t launch_rope_table(int n, int hd, int64_t pos0, double base, float* cs
     return hipGetLastError();
 }
 
-hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, const float* cs, void* Q,
+hipError_t launch_rope_scatter(const void* qkv, const float* part, int nparts, int act_f32, int n, int Hq, int Hkv,
+                               int hd, const float* cs, void* Q,
                                int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld, int64_t kv_off,
                                int v_zero_to, const int32_t* state, hipStream_t st) {
-    if (hd % 16 || hd > 256) return hipErrorInvalidValue;
+    if (hd % 64 || hd > 256) return hipErrorInvalidValue;
     const int rows = std::max(n, v_zero_to);
-    const dim3 grid((rows + 15) / 16, Hq + 2 * Hkv);
-    const size_t lds = (size_t)64 * (hd + 1) * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(rope_scatter_kernel<float>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 257 * 4);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(rope_scatter_kernel<uint16_t>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 257 * 4);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    // x: 16-row tiles (Q/K) or 64-row x 64-dim tiles (V), whichever are more
+    const dim3 grid(std::max((rows + 15) / 16, (rows + 63) / 64 * (hd / 64)), Hq + 2 * Hkv);
+    const size_t lds = 0;
     if (act_f32)
-        rope_scatter_kernel<float><<<grid, 256, lds, st>>>((const float*)qkv, n, Hq, Hkv, hd, cs, (float*)Q, q_ld,
+        rope_scatter_kernel<float><<<grid, 256, lds, st>>>((const float*)qkv, part, nparts, n, Hq, Hkv, hd, cs, (float*)Q, q_ld,
                                                            q_off, (float*)K, (float*)V, kv_ld, kv_off, v_zero_to,
                                                            state);
     else
-        rope_scatter_kernel<uint16_t><<<grid, 256, lds, st>>>((const uint16_t*)qkv, n, Hq, Hkv, hd, cs, (uint16_t*)Q,
+        rope_scatter_kernel<uint16_t><<<grid, 256, lds, st>>>((const uint16_t*)qkv, part, nparts, n, Hq, Hkv, hd, cs, (uint16_t*)Q,
                                                               q_ld, q_off, (uint16_t*)K, (uint16_t*)V, kv_ld, kv_off,
                                                               v_zero_to, state);
     return hipGetLastError();

@@ -10,9 +10,15 @@ hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, i
                         const int32_t* state, hipStream_t st);
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
                           const int32_t* state, hipStream_t st);
+// X += sum over the nparts K-slice partials part[s][n][d] (slice order), then
+// Y = rmsnorm(X); nparts = 0: the plain norm
+hipError_t launch_residual_rmsnorm(float* X, const float* part, int nparts, int n, int d, const float* w, float eps,
+                                   void* Y, int act_f32, const int32_t* state, hipStream_t st);
 hipError_t launch_rope_table(int n, int hd, int64_t pos0, double base, float* cs, const int32_t* state,
                              hipStream_t st);
-hipError_t launch_rope_scatter(const void* qkv, int act_f32, int n, int Hq, int Hkv, int hd, const float* cs, void* Q,
+// qkv, or (nparts > 1) its K-slice f32 partials part[nparts][n][width]
+hipError_t launch_rope_scatter(const void* qkv, const float* part, int nparts, int act_f32, int n, int Hq, int Hkv,
+                               int hd, const float* cs, void* Q,
                                int64_t q_ld, int64_t q_off, void* K, void* V, int64_t kv_ld, int64_t kv_off,
                                int v_zero_to, const int32_t* state, hipStream_t st);
 hipError_t launch_router_topk(const float* r, int nparts, const float* bias, int n, int E, int k, int32_t* ids,

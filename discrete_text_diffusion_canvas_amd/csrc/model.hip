@@ -77,10 +77,11 @@ struct Work {
     int32_t* experts_hit = nullptr;  // optional [n_layers] routed experts hit per layer (caller's buffer)
 };
 
-// K slices of the router GEMM: the most (up to 16) that divide its 32-wide
-// k-steps and leave each slice at least 8 (two per wave), so the few output
-// tiles still spread over many workgroups
-int router_ksplit(const dg_config& c) {
+// K slices of a weight-streaming GEMM over d_model inputs (the router, the
+// gate/up products of the small expert groups): the most (up to 16) that
+// divide its 32-wide k-steps and leave each slice at least 8 (two per wave),
+// so few output tiles still spread over many workgroups
+int stream_ksplit(const dg_config& c) {
     const int ks_total = c.d_model / 32;
     int best = 1;
     for (int s = 2; s <= 16; ++s)
@@ -112,12 +113,12 @@ Work carve(const dg_model* m, void* base, int T) {
         w.gemm_part = parts ? cv.take<float>(parts) : nullptr;
     }
     {   // split-K partials of the tiled gate/up GEMM: [slices][T (k + 1) slots][2F]
-        const int gks = ab == 2 ? dg::tile_grouped_ksplit(T) : 1;
+        const int gks = ab == 2 ? std::max(dg::tile_grouped_ksplit(T), stream_ksplit(c)) : 1;
         w.gu_part = gks > 1 ? cv.take<float>((size_t)gks * T * (k + 1) * 2 * F) : nullptr;
     }
     w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
     w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
-    w.rlog = cv.take<float>((size_t)router_ksplit(c) * T * E);
+    w.rlog = cv.take<float>((size_t)stream_ksplit(c) * T * E);
     w.ids = cv.take<int32_t>((size_t)T * k);
     w.gates = cv.take<float>((size_t)T * k);
     w.offsets = cv.take<int32_t>(E + 2);
@@ -161,11 +162,19 @@ dg::GemmArgs gargs() {
 
 // A dense projection of n rows: the LDS-staged GEMM (split over K when there
 // are too few column tiles to fill the chip) where it applies, else the
-// weight-streaming GEMM.
-hipError_t dense_gemm(dg::GemmArgs g, const Work& w, int f32, int fp8, int epi, hipStream_t st) {
+// weight-streaming GEMM. With parts != NULL a split product leaves its K-slice
+// partials in w.gemm_part for the consumer to add (*parts = their count;
+// 1 = the result is in g.C).
+hipError_t dense_gemm(dg::GemmArgs g, const Work& w, int f32, int fp8, int epi, hipStream_t st,
+                      int* parts = nullptr) {
+    if (parts) *parts = 1;
     if (dg::tile_gemm_supported(g, f32, fp8, epi)) {
         g.ksplit = dg::tile_dense_ksplit(g.M, g.N, g.K);
         g.part = w.gemm_part;
+        if (g.ksplit > 1 && g.part && parts) {
+            g.defer_reduce = 1;
+            *parts = g.ksplit;
+        }
         if (g.ksplit <= 1 || g.part) return dg::tile_gemm_launch(g, epi, 1, g.M, st);
         g.ksplit = 0;
         g.part = nullptr;
@@ -176,21 +185,25 @@ hipError_t dense_gemm(dg::GemmArgs g, const Work& w, int f32, int fp8, int epi, 
 // ---------------------------------------------------------------------------
 // The MoE half of a layer on rows X[0..n): X += shared(b) + sum_j g_j expert_j(b)
 // ---------------------------------------------------------------------------
+// resid_parts > 1: the output projection left that many K-slice partials in
+// w.gemm_part, added to X here before the norm.
 dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float* next_norm, const int32_t* state,
-                    hipStream_t st) {
+                    hipStream_t st, int resid_parts = 1) {
     const dg_config& c = m->cfg;
     const dg_layer_weights& L = m->layers[l];
     const int d = c.d_model, E = c.n_experts, k = c.top_k, F = c.ffn_hidden;
     const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
-    DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.moe_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
+    DG_TRY(dg::launch_residual_rmsnorm(w.X, w.gemm_part, resid_parts > 1 ? resid_parts : 0, n, d, L.moe_norm,
+                                       c.norm_eps, w.A, f32, state, st),
+           "rmsnorm");
     {   // router logits (router weights are never e4m3)
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.router; g.ldw = d; g.M = n; g.N = E; g.K = d;
         g.C = w.rlog; g.ldc = E; g.state = state;
-        g.ksplit = router_ksplit(c); g.part = w.rlog;
+        g.ksplit = stream_ksplit(c); g.part = w.rlog;
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
     }
-    DG_TRY(dg::launch_router_topk(w.rlog, router_ksplit(c), L.router_bias, n, E, k, w.ids, w.gates, state, st),
+    DG_TRY(dg::launch_router_topk(w.rlog, stream_ksplit(c), L.router_bias, n, E, k, w.ids, w.gates, state, st),
            "router topk");
     // groups of more than 64 rows go to the LDS-staged GEMM (bf16 only)
     dg::GemmArgs gu = gargs(), dn = gargs();
@@ -211,19 +224,21 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
                                    big_min, w.experts_hit ? w.experts_hit + l : nullptr, state, st),
            "hist permute");
     const int small_rows = tiled ? 64 : n;  // bound on the rows of a stream-GEMM group
-    {   // gate/up with SwiGLU
+    {   // gate/up with SwiGLU; products split over K leave partials for one reduce
         const int slot = timing_begin(st, DG_TIME_EXPERT_GATE_UP);
+        const int ks_small = tiled && w.gu_part ? stream_ksplit(c) : 1;
+        const int ks_big = tiled && w.gu_part ? dg::tile_grouped_ksplit(n) : 1;
         dg::GemmArgs g = gu;
-        g.hit = w.hit; g.hit_mb = w.hit_mb;
+        g.M = n * (k + 1);  // slots: the rows of the partials
+        g.part = w.gu_part;
+        g.hit = w.hit; g.hit_mb = w.hit_mb; g.ksplit = ks_small;
         DG_TRY(dg::stream_gemm_launch(g, f32, fp8, dg::EPI_SWIGLU, E + 1, small_rows, st), "expert gate/up");
         if (tiled) {
-            g.hit = w.hitB; g.hit_mb = w.hitB_mb;
-            const int gks = dg::tile_grouped_ksplit(n);
-            if (gks > 1 && w.gu_part) {
-                g.ksplit = gks; g.part = w.gu_part; g.M = n * (k + 1); g.ksplit_min_rows = big_min;
-            }
+            g.hit = w.hitB; g.hit_mb = w.hitB_mb; g.ksplit = ks_big;
             DG_TRY(dg::tile_gemm_launch(g, dg::EPI_SWIGLU, E + 1, n, st), "expert gate/up (tiled)");
         }
+        if (ks_small > 1 || ks_big > 1)
+            DG_TRY(dg::swiglu_reduce_launch(g, E + 1, big_min, ks_big, ks_small, st), "swiglu reduce");
         timing_end(slot, st);
     }
     {   // down
@@ -261,16 +276,17 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
     const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
     const int64_t P = kv->len;
     if (!normed_in) DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
+    int qkv_parts = 1, o_parts = 1;
     {
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N; g.state = state;
         const int slot = timing_begin(st, DG_TIME_QKV);
-        DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st), "qkv gemm");
+        DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st, &qkv_parts), "qkv gemm");
         timing_end(slot, st);
     }
-    DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0, w.Kc, w.Vc, w.rows64, 0,
-                                   w.rows64, state, st),
+    DG_TRY(dg::launch_rope_scatter(w.QKV, w.gemm_part, qkv_parts, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0,
+                                   w.Kc, w.Vc, w.rows64, 0, w.rows64, state, st),
            "rope");
     {
         dg::AttnArgs a;
@@ -293,10 +309,10 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
         g.A = w.O; g.lda = Hq * hd; g.W = L.wo; g.ldw = Hq * hd; g.w_scale = (const uint16_t*)L.wo_scale;
         g.M = n; g.N = d; g.K = Hq * hd; g.X = w.X; g.ldx = d; g.state = state;
         const int slot = timing_begin(st, DG_TIME_O_PROJ);
-        DG_TRY(dense_gemm(g, w, f32, fp8, dg::EPI_RESIDUAL, st), "o gemm");
+        DG_TRY(dense_gemm(g, w, f32, fp8, dg::EPI_RESIDUAL, st, &o_parts), "o gemm");
         timing_end(slot, st);
     }
-    return moe_block(m, l, w, n, next_norm, state, st);
+    return moe_block(m, l, w, n, next_norm, state, st, o_parts);
 }
 
 // ---------------------------------------------------------------------------
@@ -314,9 +330,10 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N;
-        DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st), "qkv gemm");
-        DG_TRY(dg::launch_rope_scatter(w.QKV, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0, kv->k[l], kv->v[l],
-                                       kv->capacity, P, 0, nullptr, st),
+        int qkv_parts = 1;
+        DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st, &qkv_parts), "qkv gemm");
+        DG_TRY(dg::launch_rope_scatter(w.QKV, w.gemm_part, qkv_parts, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0,
+                                       kv->k[l], kv->v[l], kv->capacity, P, 0, nullptr, st),
                "rope");
         if (l == c.n_layers - 1) break;  // nothing in the cache depends on the rest
         dg::AttnArgs a;
