@@ -23,6 +23,9 @@
 #ifndef DG_STREAM_WAVES
 #define DG_STREAM_WAVES 2
 #endif
+#ifndef DG_STREAM_W_NT
+#define DG_STREAM_W_NT 1
+#endif
 
 namespace dg {
 
@@ -37,11 +40,17 @@ template <typename TL, int WK> struct SFrag;
 template <> struct SFrag<uint16_t, WK_SAME> {
     u16x8 v;
     __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u16x8*>(p); }
+    __device__ __forceinline__ void load_nt(const void* p) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
+    }
     __device__ __forceinline__ void zero() { v = u16x8{0, 0, 0, 0, 0, 0, 0, 0}; }
 };
 template <> struct SFrag<uint16_t, WK_FP8> {
     u32x2 v;
     __device__ __forceinline__ void load(const void* p) { v = *reinterpret_cast<const u32x2*>(p); }
+    __device__ __forceinline__ void load_nt(const void* p) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    }
     __device__ __forceinline__ void zero() { v = u32x2{0u, 0u}; }
 };
 template <> struct SFrag<float, WK_SAME> {
@@ -51,6 +60,7 @@ template <> struct SFrag<float, WK_SAME> {
         b = reinterpret_cast<const f32x4*>(p)[1];
     }
     __device__ __forceinline__ void zero() { a = f32x4{0, 0, 0, 0}; b = a; }
+    __device__ __forceinline__ void load_nt(const void* p) { load(p); }
 };
 
 __device__ __forceinline__ u16x8 widen_e4m3(const u32x2& v) {
@@ -103,7 +113,10 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[STM][STN], const TL* c
 #pragma unroll
         for (int i = 0; i < TMV; ++i) fa[d][i].load(arow[i] + k);
 #pragma unroll
-        for (int j = 0; j < STN; ++j) fb[d][j].load(wrow[j] + (int64_t)k * WES);
+        for (int j = 0; j < STN; ++j) {  // weights are read once: non-temporal
+            if (DG_STREAM_W_NT) fb[d][j].load_nt(wrow[j] + (int64_t)k * WES);
+            else fb[d][j].load(wrow[j] + (int64_t)k * WES);
+        }
     };
     auto consume = [&](int d, int s) {
         const bool ok = wave + 4 * s < KS;

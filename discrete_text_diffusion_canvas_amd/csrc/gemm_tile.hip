@@ -42,6 +42,16 @@
 #ifndef DG_TILE_BN_DENSE
 #define DG_TILE_BN_DENSE 128
 #endif
+// rows per m-block of the dense products (256: one block for a 256-token
+// canvas; 64: four blocks sharing each weight tile through L2, measured
+// slower on the 256 x 8192 x 2816 projection)
+#ifndef DG_TILE_BM_DENSE
+#define DG_TILE_BM_DENSE 256
+#endif
+// weight loads as non-temporal (streamed once; measured faster HBM streaming)
+#ifndef DG_TILE_W_NT
+#define DG_TILE_W_NT 1
+#endif
 // gate/up split over K (decode-sized batches): tile width and slices
 #ifndef DG_TILE_BN_GU_SPLIT
 #define DG_TILE_BN_GU_SPLIT 128
@@ -66,10 +76,9 @@ namespace dg {
 
 namespace {
 
-constexpr int TBM = 256;                       // rows per m-block
+constexpr int TBM = 256;                       // rows per m-block (largest)
 constexpr int TBK = 64;                        // k per stage
 constexpr int TROWB = TBK * 2;                 // bytes per LDS row
-constexpr int TA_BYTES = TBM * TROWB;          // 32 KB
 
 __device__ __forceinline__ int tswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
@@ -79,16 +88,17 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 __device__ __forceinline__ float tsilu(float x) { return x / (1.f + __expf(-x)); }
 
-// waves of a BN-wide workgroup: 4 row blocks x (BN / 64, at most 2) column blocks
-template <int BN>
-constexpr int tile_waves() { return BN >= 128 ? 8 : BN / 16; }
+// waves of a BM x BN workgroup: BM/64 row blocks; 256 rows: BN/64 (at most
+// 2) column blocks; 64 rows: 4 column blocks
+template <int BN, int BM>
+constexpr int tile_waves() { return BM == 64 ? 4 : BN >= 128 ? 8 : BN / 16; }
 // columns of one epilogue pass through LDS
 template <int BN>
 constexpr int tile_epi_cols() { return BN < 128 ? BN : 128; }
 // two stage slots, or the epilogue tile if larger
-template <int BN>
+template <int BN, int BM>
 constexpr size_t tile_lds_bytes() {
-    return std::max<size_t>(2 * (size_t)(TA_BYTES + BN * TROWB), (size_t)TBM * (tile_epi_cols<BN>() + 4) * 4);
+    return std::max<size_t>(2 * (size_t)(BM + BN) * TROWB, (size_t)BM * (tile_epi_cols<BN>() + 4) * 4);
 }
 
 }  // namespace
@@ -251,28 +261,33 @@ __global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.C) + (int64_t)slot * g.ldc + f) = o;
 }
 
-template <int BN, int EPI, int DEPTH>
-__global__ void __launch_bounds__(tile_waves<BN>() * 64) tile_gemm_kernel(GemmArgs g, int n_tiles) {
+template <int BN, int EPI, int DEPTH, int BM>
+__global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(GemmArgs g, int n_tiles) {
     if (g.state && g.state[0]) return;
+    static_assert(BM == 64 || BM == 256, "m-blocks of 64 or 256 rows");
+    constexpr int TA_BYTES = BM * TROWB;
     constexpr int B_BYTES = BN * TROWB;
     constexpr int STAGE = TA_BYTES + B_BYTES;
-    constexpr int NW = tile_waves<BN>();          // waves
+    constexpr int NW = tile_waves<BN, BM>();      // waves
     constexpr int NT = NW * 64;                   // threads
     constexpr int TA_INSTR = TA_BYTES / 1024 / NW;  // 1 KB row pieces of A per wave and stage
     constexpr int B_INSTR = B_BYTES / 1024 / NW;
-    constexpr int WC = BN / (NW / 4);             // columns per wave
+    constexpr int RB = BM / 64, CB = NW / RB;     // row blocks, column blocks
+    constexpr int WC = BN / CB;                   // columns per wave
     constexpr int TN = WC / 16;                   // 16-column tiles per wave
+    static_assert(TA_INSTR >= 1 && B_INSTR >= 1 && TN >= 1, "tile shape");
     constexpr int EP = tile_epi_cols<BN>();       // columns per epilogue pass
     constexpr int NPASS = BN / EP;
     constexpr int TS = EP + 4;  // epilogue tile row stride (floats)
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;      // row block, column block
+    const int wm = wave % RB, wn = wave / RB;     // row block, column block
     const int lr = lane & 15, lg = lane >> 4;
     const int pos = lane & 7;
     const bool grouped = g.group_offsets != nullptr;
     const int ngroups = grouped ? g.hit[0] : 1;
-    const int mb_max = grouped ? *g.hit_mb : (g.M + TBM - 1) / TBM;
+    // grouped: hit_mb counts 256-row blocks (an upper bound for 64-row ones)
+    const int mb_max = grouped ? *g.hit_mb * (TBM / BM) : (g.M + BM - 1) / BM;
     const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
     const int units = ngroups * n_tiles;
     const int64_t items = (int64_t)((units * ksplit + 7) / 8) * 8 * mb_max;
@@ -290,9 +305,9 @@ __global__ void __launch_bounds__(tile_waves<BN>() * 64) tile_gemm_kernel(GemmAr
         const int row0 = grouped ? g.group_offsets[grp] : 0;
         const int mrows = grouped ? g.group_offsets[grp + 1] - row0 : g.M;
         const int kbase = ks * KT * TBK;  // first k of this slice
-        const int m0 = mb * TBM;
+        const int m0 = mb * BM;
         if (m0 >= mrows) continue;  // uniform over the workgroup
-        const int mcount = min(TBM, mrows - m0);
+        const int mcount = min(BM, mrows - m0);
         const bool live = wm * 64 < mcount;
 
         // load sources: load j of this wave covers LDS rows
@@ -334,7 +349,10 @@ __global__ void __launch_bounds__(tile_waves<BN>() * 64) tile_gemm_kernel(GemmAr
 #pragma unroll
             for (int j = 0; j < TA_INSTR; ++j) ra[d][j] = *reinterpret_cast<const u32x4*>(asrc[j] + k0);
 #pragma unroll
-            for (int j = 0; j < B_INSTR; ++j) rb[d][j] = *reinterpret_cast<const u32x4*>(bsrc[j] + k0);
+            for (int j = 0; j < B_INSTR; ++j) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(bsrc[j] + k0);
+                rb[d][j] = DG_TILE_W_NT ? __builtin_nontemporal_load(src) : *src;
+            }
         };
         auto store = [&](int d, int slot) {
             unsigned char* st = smem + slot * STAGE;
@@ -481,16 +499,16 @@ __global__ void __launch_bounds__(tile_waves<BN>() * 64) tile_gemm_kernel(GemmAr
     }
 }
 
-template <int BN, int EPI, int DEPTH = DG_TILE_DEPTH>
+template <int BN, int EPI, int DEPTH = DG_TILE_DEPTH, int BM = TBM>
 static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hipStream_t st) {
     const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
-    const int mb_max = std::max(1, (max_rows + TBM - 1) / TBM);
+    const int mb_max = std::max(1, (max_rows + BM - 1) / BM);
     const int ks = g.ksplit > 1 ? g.ksplit : 1;
     const int64_t items = (int64_t)((groups * n_tiles * ks + 7) / 8) * 8 * mb_max;  // upper bound
-    const size_t lds = tile_lds_bytes<BN>();
+    const size_t lds = tile_lds_bytes<BN, BM>();
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH, BM>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
@@ -499,13 +517,13 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     static int per_cu = 0;
     if (!per_cu) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH>), tile_waves<BN>() * 64, lds);
+            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH, BM>), tile_waves<BN, BM>() * 64, lds);
         if (e != hipSuccess) return e;
         per_cu = std::max(per_cu, 1);
     }
     int64_t grid = std::min<int64_t>(items, 256 * per_cu);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
-    tile_gemm_kernel<BN, EPI, DEPTH><<<(unsigned)grid, tile_waves<BN>() * 64, lds, st>>>(g, n_tiles);
+    tile_gemm_kernel<BN, EPI, DEPTH, BM><<<(unsigned)grid, tile_waves<BN, BM>() * 64, lds, st>>>(g, n_tiles);
     if (ks > 1 && !g.group_offsets && !g.defer_reduce) {  // grouped or deferred: the caller's reduce
         const int64_t n = (int64_t)g.M * (g.N / 4);
         tile_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g);
@@ -529,7 +547,7 @@ bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
 int tile_dense_ksplit(int M, int N, int K) {
     // split until there are enough work items for most CUs (each slice keeps
     // at least 4 stages); every split adds M x N f32 partials to write and read
-    const int items = (N + DG_TILE_BN_DENSE - 1) / DG_TILE_BN_DENSE * ((M + TBM - 1) / TBM);
+    const int items = (N + DG_TILE_BN_DENSE - 1) / DG_TILE_BN_DENSE * ((M + DG_TILE_BM_DENSE - 1) / DG_TILE_BM_DENSE);
     int ks = 1;
     while (items * ks < 160 && (K / TBK) % (ks * 2) == 0 && K / TBK / (ks * 2) >= 4) ks *= 2;
     return ks;
@@ -557,9 +575,10 @@ hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows
         return hipErrorInvalidValue;
     }
     if (g.ksplit > 1 && (!g.part || (g.K / TBK) % g.ksplit)) return hipErrorInvalidValue;
-    if (epi == EPI_STORE_BF16) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_BF16>(g, 1, g.M, st);
-    if (epi == EPI_RESIDUAL) return launch_tile_t<DG_TILE_BN_DENSE, EPI_RESIDUAL>(g, 1, g.M, st);
-    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_F32>(g, 1, g.M, st);
+    constexpr int D = DG_TILE_DEPTH, BMD = DG_TILE_BM_DENSE;
+    if (epi == EPI_STORE_BF16) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_BF16, D, BMD>(g, 1, g.M, st);
+    if (epi == EPI_RESIDUAL) return launch_tile_t<DG_TILE_BN_DENSE, EPI_RESIDUAL, D, BMD>(g, 1, g.M, st);
+    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_F32, D, BMD>(g, 1, g.M, st);
     if (epi == EPI_LMHEAD) {
         // one 256-row block; statistics partials per 128 vocabulary rows
         if (g.ksplit > 1 || g.M > TBM || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
