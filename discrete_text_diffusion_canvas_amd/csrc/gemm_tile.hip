@@ -136,14 +136,25 @@ __device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int 
 
 // LM-head epilogue on the tile T[r][c] (logits of record, bf16-rounded) of
 // vocabulary rows [tile*BN, +BN): (1) the bf16 logits leave in 16-byte
-// coalesced stores; (2) one thread per canvas row walks its BN logits in
-// vocabulary order for the tile's partial statistics: the max and the 2^x
-// partition sum and entropy partial of the tempered logits (log2 units), and
-// the raw argmax (first index among equal values), with the row's bias token
-// added and the mask token excluded. merge_rows combines the partials.
-template <int BN, int NT>
-__device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, const float* T, int mcount, int tile) {
+// coalesced stores; (2) per canvas row, the tile's partial statistics: the
+// max and the 2^x partition sum and entropy partial of the tempered logits
+// (log2 units), and the raw argmax (first index among equal values), with
+// the row's bias token added and the mask token excluded. merge_rows
+// combines the partials.
+//
+// The statistics use TPR = NT / BM threads per row (1 or 2), each over a
+// contiguous 1/TPR of the columns, in two passes: the raw max and its index,
+// exchanged between the row's threads through the 4 padding floats of its T
+// row; then the sums against the merged max (tempering by 1/tau > 0 keeps the
+// order, so the tempered max is the raw max times the factor), added across
+// the row's threads. A thread whose columns hold no bias or mask token and
+// no column past N runs a loop free of per-column tests.
+template <int BN, int NT, int BM>
+__device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T, int mcount, int tile) {
     constexpr int TS = BN + 4;
+    constexpr int TPR = NT / BM;
+    static_assert(TPR == 1 || TPR == 2, "one or two threads per row");
+    constexpr int CW = BN / TPR;  // columns per thread
     const int tid = threadIdx.x, N = g.N, n0 = tile * BN;
     uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
     for (int e = tid; e < mcount * (BN / 8); e += NT) {
@@ -162,38 +173,66 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, const fl
             for (int u = 0; u < 8 && n + u < N; ++u) dst[u] = f2bf(t[u]);
         }
     }
-    const int r = tid;
-    if (r >= mcount) return;
+    const int r = tid % BM, part = tid / BM;
+    const bool act = r < mcount;
+    const int c0 = part * CW, cn0 = n0 + c0;  // this thread's first column / vocabulary row
+    float* row = T + r * TS;
     const int step = g.step_override >= 0 ? g.step_override : (g.state ? g.state[1] : 0);
     const float c2 = (float)(1.4426950408889634 / lm_tau_at(g.sp, step));
-    const int bt = g.bias_tok ? g.bias_tok[r] : -1;
-    const float bv = g.bias_tok ? g.bias_val[r] : 0.f;
-    const float* row = T + r * TS;
-    float vm = -INFINITY, rawm = -INFINITY;
+    const int bt = act && g.bias_tok ? g.bias_tok[r] : -1;
+    const float bv = act && g.bias_tok ? g.bias_val[r] : 0.f;
+    const bool special = (bt >= cn0 && bt < cn0 + CW) || (g.mask_id >= cn0 && g.mask_id < cn0 + CW) || cn0 + CW > N;
+    // pass 1: raw max and its first index
+    float rawm = -INFINITY;
     int vi = 0x7fffffff;
+    if (act && !special) {
 #pragma unroll 4
-    for (int c = 0; c < BN; c += 4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(row + c);
-        const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int n = n0 + c + u;
-            float lb = e4[u] + (n == bt ? bv : 0.f);
-            if (n >= N || n == g.mask_id) lb = -INFINITY;
-            vm = fmaxf(vm, lb * c2);
-            if (lb > rawm) { rawm = lb; vi = n; }
-        }
-    }
-    float sum = 0.f, tt = 0.f;
-    if (vm != -INFINITY) {
-#pragma unroll 4
-        for (int c = 0; c < BN; c += 4) {
+        for (int c = c0; c < c0 + CW; c += 4) {
             const float4 v4 = *reinterpret_cast<const float4*>(row + c);
             const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int n = n0 + c + u;
-                float lb = e4[u] + (n == bt ? bv : 0.f);
+            for (int u = 0; u < 4; ++u)
+                if (e4[u] > rawm) { rawm = e4[u]; vi = n0 + c + u; }
+        }
+    } else if (act) {
+        for (int c = c0; c < c0 + CW; ++c) {
+            const int n = n0 + c;
+            float lb = row[c] + (n == bt ? bv : 0.f);
+            if (n >= N || n == g.mask_id) lb = -INFINITY;
+            if (lb > rawm) { rawm = lb; vi = n; }
+        }
+    }
+    if constexpr (TPR == 2) {
+        __syncthreads();  // every thread done reading T's values
+        if (act) { row[BN + 2 * part] = rawm; row[BN + 2 * part + 1] = __int_as_float(vi); }
+        __syncthreads();
+        if (act) {
+            const float om = row[BN + 2 * (1 - part)];
+            const int oi = __float_as_int(row[BN + 2 * (1 - part) + 1]);
+            if (om > rawm || (om == rawm && oi < vi)) { rawm = om; vi = oi; }
+        }
+    }
+    // pass 2: partition sum and entropy partial against the merged max
+    const float vm = rawm * c2;
+    float sum = 0.f, tt = 0.f;
+    if (act && rawm != -INFINITY) {
+        if (!special) {
+#pragma unroll 4
+            for (int c = c0; c < c0 + CW; c += 4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(row + c);
+                const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float d = e4[u] * c2 - vm;
+                    const float w = exp2f(d);
+                    sum += w;
+                    tt += w * d;
+                }
+            }
+        } else {
+            for (int c = c0; c < c0 + CW; ++c) {
+                const int n = n0 + c;
+                float lb = row[c] + (n == bt ? bv : 0.f);
                 if (n >= N || n == g.mask_id) lb = -INFINITY;
                 const float d = lb * c2 - vm;
                 const float w = exp2f(d);
@@ -202,11 +241,19 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, const fl
             }
         }
     }
-    RowPart p;
-    p.m2 = vm; p.s = sum; p.t = tt; p.lmax = rawm;
-    p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
-    p.pad[0] = p.pad[1] = p.pad[2] = 0;
-    g.parts[(int64_t)r * g.nsplit + tile] = p;
+    if constexpr (TPR == 2) {
+        __syncthreads();  // both halves' maxima read
+        if (act && part == 1) { row[BN] = sum; row[BN + 1] = tt; }
+        __syncthreads();
+        if (act && part == 0) { sum += row[BN]; tt += row[BN + 1]; }
+    }
+    if (act && part == 0) {
+        RowPart p;
+        p.m2 = rawm == -INFINITY ? -INFINITY : vm; p.s = sum; p.t = tt; p.lmax = rawm;
+        p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
+        p.pad[0] = p.pad[1] = p.pad[2] = 0;
+        g.parts[(int64_t)r * g.nsplit + tile] = p;
+    }
 }
 
 // Sum of the K-slice partials part[s][row][n] in slice order, then the
@@ -456,7 +503,7 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
                 *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 8 == 0
             }
         } else if constexpr (EPI == EPI_LMHEAD) {
-            if (ptile < g.nsplit) tile_lmhead_epilogue<EP, NT>(g, T, mcount, ptile);  // past N: no columns
+            if (ptile < g.nsplit) tile_lmhead_epilogue<EP, NT, BM>(g, T, mcount, ptile);  // past N: no columns
         } else if constexpr (EPI == EPI_SWIGLU) {
             constexpr int CH = EP / 2 / 8;  // 8-column chunks of hidden units per row
             uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
