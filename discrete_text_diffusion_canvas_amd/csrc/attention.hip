@@ -9,19 +9,20 @@
 // [prefix rows in the window || canvas rows] is the reading taken for how the
 // two attentions combine.
 //
-// Flash-style, split-KV: a workgroup owns 64 query rows and a slice of the
-// 64-key blocks; each wave owns 16 query rows, S = Q K^T and O += P V run on
-// MFMA, the softmax is online in f32, P goes through LDS to become an A
+// Flash-style, split-KV: a workgroup owns a set of query rows and a slice of
+// the 64-key blocks; each wave owns 16 query rows, S = Q K^T and O += P V run
+// on MFMA, the softmax is online in f32, P goes through LDS to become an A
 // operand, and split slices write unnormalised partials (O, max, sum) that a
 // merge kernel combines. V is stored transposed ([d][key]) so that the B
 // operand of P V reads contiguous keys.
 //
-// bf16 (attn_dma_kernel): the 64 query rows are the 64/R positions of all R
-// query heads of one KV group, so K/V tiles are shared by the whole group;
-// the K tile [64 keys][hd] and V^T tile [hd][64 keys] of the next block are
-// copied into XOR-swizzled LDS by global_load_lds while the current block is
-// computed. Key blocks are aligned to multiples of 64 in each segment and
-// masked outside the visible range.
+// bf16 (attn_reg_kernel): a workgroup's 128 query rows are the 128/R
+// positions of all R query heads of one KV group, so every K/V tile is shared
+// by the whole group; Q sits in LDS; the K tile [64 keys][hd] and V^T tile
+// [hd][64 keys] of the next block are loaded into registers while the current
+// block is computed and written into the XOR-swizzled LDS slot after it. Key
+// blocks are aligned to multiples of 64 in each segment and masked outside
+// the visible range.
 #include "common.hpp"
 #include "layer.hpp"
 
@@ -278,15 +279,10 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
 }
 
 // ===========================================================================
-// bf16 kernel with LDS-DMA double buffering and GQA-shared K/V tiles.
+// bf16 kernel: register-staged K/V blocks shared by the query heads of a KV
+// group.
 // ===========================================================================
 namespace {
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_a() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
 
 // K tile rows are HD*2 bytes (>= 256): chunk c of key row r sits at c ^ (r & 15).
 __device__ __forceinline__ int kswz(int r, int c) { return c ^ (r & 15); }

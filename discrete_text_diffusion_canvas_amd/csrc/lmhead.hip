@@ -7,6 +7,9 @@
 // computed from the logits of record in the epilogue, so probabilities are
 // never written to memory.
 //
+// bf16 models run the LM head on the tiled GEMM (gemm_tile.hip, its LM-head
+// epilogue); this kernel serves f32 models.
+//
 // Shape: all canvas rows (<= 256) x 128 vocabulary rows per workgroup, 4 waves
 // as 2 x 2 (each 128 x 64, 8 x 4 MFMA tiles of 16x16x32 bf16). K advances in
 // stages of 64; each stage of A (256 x 64) and E (128 x 64) is copied from

@@ -18,7 +18,9 @@
         counters of the kernels matching REGEX are averaged per dispatch and
         summed over the kernels (one logical launch may be several dispatches);
         each counter is scaled by B / (the counter on the copy), which turns the
-        KiB the counters report into bytes the copy is known to move. The
+        KiB the counters report into bytes the copy is known to move. With
+        --after REGEX, dispatches before the first one of a kernel matching
+        REGEX are left out (the prompt prefill runs other shapes). The
         output records the SHA-256 of the kernel sources, so a reader can tell
         whether the kernel changed since.
 """
@@ -92,13 +94,16 @@ def steps(args) -> None:
         print(f"  {n[:46]:46s} grid=({gx},{gzv}) calls/step={c / nsteps:6.1f} avg={t / c / 1e3:8.1f} us")
 
 
-def _per_dispatch(path: str, counter: str, regex: str) -> dict:
+def _per_dispatch(path: str, counter: str, regex: str, after: str = "") -> dict:
+    rows = [r for r in csv.DictReader(open(path)) if r.get("Counter_Name") == counter]
+    first = 0
+    if after:  # only dispatches from the first one of a kernel matching `after` on
+        ids = [int(r["Dispatch_Id"]) for r in rows if re.search(after, _name(r))]
+        first = min(ids) if ids else 0
     vals: dict = {}
-    for r in csv.DictReader(open(path)):
-        if r.get("Counter_Name") != counter:
-            continue
+    for r in rows:
         n = _name(r)
-        if re.search(regex, n):
+        if re.search(regex, n) and int(r.get("Dispatch_Id", 0)) >= first:
             vals.setdefault(n, []).append(float(r["Counter_Value"]))
     return vals
 
@@ -106,7 +111,7 @@ def _per_dispatch(path: str, counter: str, regex: str) -> dict:
 def traffic(args) -> None:
     out = {}
     for which, path, counter in (("fetch", args.fetch, "FETCH_SIZE"), ("write", args.write, "WRITE_SIZE")):
-        kern = _per_dispatch(path, counter, args.kernels)
+        kern = _per_dispatch(path, counter, args.kernels, args.after)
         copy = _per_dispatch(path, counter, args.copy_kernel)
         if not kern or not copy:
             sys.exit(f"{which}: no dispatches matched ({args.kernels!r} / {args.copy_kernel!r})")
@@ -154,6 +159,8 @@ def main(argv=None) -> None:
     b.add_argument("--sources", default="")
     b.add_argument("--command", default="")
     b.add_argument("--last", type=int, default=30, help="dispatches per kernel at the end of the run to use")
+    b.add_argument("--after", default="", help="ignore dispatches before the first of a kernel matching this regex "
+                   "(e.g. one that only the decode steps launch, to leave out the prompt prefill)")
     args = ap.parse_args(argv)
     {"stats": stats, "steps": steps, "traffic": traffic}[args.cmd](args)
 
