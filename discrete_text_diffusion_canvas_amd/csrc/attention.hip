@@ -295,9 +295,26 @@ __device__ __forceinline__ int vswz(int d, int c) { return c ^ ((d >> 1) & 7); }
 // loads in flight (a __syncthreads would also wait for those)
 __device__ __forceinline__ void attn_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Workgroup id -> (query tile qt, KV group g, split sp). The query tiles of
+// one (group, split) read the same K/V blocks, so they get ids 8 apart: with
+// workgroups dealt to the 8 XCDs in id order they share one XCD's L2 instead
+// of fetching the blocks once per XCD.
+__device__ __forceinline__ void attn_ids(int nqt, int& qt, int& gs) {
+    const int id = blockIdx.x;
+    const int lane8 = id % 8, rest = id / 8;      // rest = (gs / 8) * nqt + qt
+    qt = rest % nqt;
+    gs = (rest / nqt) * 8 + lane8;                // (group, split) pair; past the last: no work
+}
+
 template <int HD, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
     if (a.state && a.state[0]) return;
+    const int QP = 128 / R;                       // positions per workgroup
+    const int nqt = (a.nq + QP - 1) / QP;
+    int qt, gs;
+    attn_ids(nqt, qt, gs);
+    if (gs >= a.Hkv * a.splits) return;
+    const int g = gs % a.Hkv, sp = gs / a.Hkv;
     constexpr int KROWB = HD * 2;                 // bytes per K row
     constexpr int K_BYTES = KB * KROWB;           // K tile
     constexpr int V_BYTES = HD * KB * 2;          // V^T tile (rows of 128 bytes)
@@ -317,9 +334,7 @@ __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int g = blockIdx.y;
-    const int QP = 128 / R;                       // positions per workgroup
-    const int qx0 = blockIdx.x * QP;
+    const int qx0 = qt * QP;
     // workgroup row rho in [0, 128) = (head g*R + rho / QP, position qx0 + rho % QP);
     // wave w owns rows [RPW w, RPW (w + 1)) as TPW 16-row tiles
     auto row_head = [&](int rho) { return g * R + rho / QP; };
@@ -341,7 +356,7 @@ __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
     const int64_t nb2 = a.n2 > 0 ? (a.n2 + KB - 1) / KB : 0;
     const int64_t nb = nb1 + nb2;
     const int64_t per = (nb + a.splits - 1) / a.splits;
-    const int64_t bb0 = per * blockIdx.z, bb1 = min<int64_t>(nb, bb0 + per);
+    const int64_t bb0 = per * sp, bb1 = min<int64_t>(nb, bb0 + per);
 
     const uint16_t* K1 = reinterpret_cast<const uint16_t*>(a.K1) + (int64_t)g * a.ld1 * HD;
     const uint16_t* V1 = reinterpret_cast<const uint16_t*>(a.V1) + (int64_t)g * HD * a.ld1;
@@ -538,11 +553,11 @@ __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
 #pragma unroll
                 for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[t][j][i] * inv);
             } else {
-                float* po = a.part_o + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * HD;
+                float* po = a.part_o + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
 #pragma unroll
                 for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[t][j][i];
                 if (lr == 0) {
-                    float* pm = a.part_ml + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + hq) * 2;
+                    float* pm = a.part_ml + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * 2;
                     pm[0] = m_run[t][i];
                     pm[1] = l_run[t][i];
                 }
@@ -643,7 +658,8 @@ static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
         if (e != hipSuccess) return e;
         attr = true;
     }
-    dim3 grid((a.nq + 128 / R - 1) / (128 / R), a.Hkv, a.splits);
+    const int nqt = (a.nq + 128 / R - 1) / (128 / R), ngs = a.Hkv * a.splits;
+    const unsigned grid = (unsigned)(((ngs + 7) / 8) * nqt * 8);  // see attn_ids
     attn_reg_kernel<HD, NW><<<grid, NW * 64, lds, st>>>(a, R);
     if (a.splits > 1) launch_merge_any(a, true, st);
     return hipGetLastError();

@@ -16,16 +16,18 @@ namespace dg {
 // X[i][:] = E[tok[i]][:] as f32. One workgroup per row.
 // ---------------------------------------------------------------------------
 template <typename TE>
-__global__ void __launch_bounds__(256) embed_kernel(const TE* __restrict__ E, int d, const int32_t* __restrict__ tok,
-                                                    float* __restrict__ X, const int32_t* __restrict__ state) {
+__global__ void __launch_bounds__(256) embed_kernel(const TE* __restrict__ E, int d, int V,
+                                                    const int32_t* __restrict__ tok, float* __restrict__ X,
+                                                    const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     const int i = blockIdx.x;
     const int64_t t = tok[i];
-    const TE* src = E + t * d;
+    const bool ok = t >= 0 && t < V;  // an id outside the vocabulary embeds as a zero row
+    const TE* src = E + (ok ? t : 0) * d;
     for (int k = threadIdx.x; k < d; k += 256) {
         float v;
         if constexpr (sizeof(TE) == 2) v = bf2f(src[k]); else v = src[k];
-        X[(int64_t)i * d + k] = v;
+        X[(int64_t)i * d + k] = ok ? v : 0.f;
     }
 }
 
@@ -341,9 +343,15 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
             for (int p = 1; p < 16; ++p)
                 if (p < nparts) x += xs[p];
             for (int p = 16; p < nparts; ++p) x += src[p * pstride];
-            v[j] = x + bias[e];
+            x += bias[e];
+            v[j] = x == x ? x : -INFINITY;  // a NaN logit ranks last
         }
     }
+    // every round picks an expert not taken yet (ties and -inf go to the lowest
+    // id), so the k ids are always distinct and valid
+    bool taken[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) taken[j] = false;
     float sel[16];
     int sid[16];
     for (int s = 0; s < k; ++s) {
@@ -351,14 +359,14 @@ __global__ void __launch_bounds__(256) router_topk_kernel(const float* __restric
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             int e = lane + 64 * j;
-            if (e < E) best = argmax_merge(best, ArgMax{v[j], e});
+            if (e < E && !taken[j]) best = argmax_merge(best, ArgMax{v[j], e});
         }
         best = wave_argmax(best);
         sel[s] = best.v;
         sid[s] = best.i;
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            if (lane + 64 * j == best.i) v[j] = -INFINITY;
+            if (lane + 64 * j == best.i) taken[j] = true;
     }
     if (lane == 0) {
         float m = sel[0];
@@ -544,10 +552,10 @@ __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int
 // ---------------------------------------------------------------------------
 // Host launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, int n, float* X,
+hipError_t launch_embed(const void* E, int act_f32, int d, int V, const int32_t* tok, int n, float* X,
                         const int32_t* state, hipStream_t st) {
-    if (act_f32) embed_kernel<float><<<n, 256, 0, st>>>((const float*)E, d, tok, X, state);
-    else embed_kernel<uint16_t><<<n, 256, 0, st>>>((const uint16_t*)E, d, tok, X, state);
+    if (act_f32) embed_kernel<float><<<n, 256, 0, st>>>((const float*)E, d, V, tok, X, state);
+    else embed_kernel<uint16_t><<<n, 256, 0, st>>>((const uint16_t*)E, d, V, tok, X, state);
     return hipGetLastError();
 }
 

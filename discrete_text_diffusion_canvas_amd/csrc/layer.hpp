@@ -6,7 +6,7 @@
 
 namespace dg {
 
-hipError_t launch_embed(const void* E, int act_f32, int d, const int32_t* tok, int n, float* X,
+hipError_t launch_embed(const void* E, int act_f32, int d, int V, const int32_t* tok, int n, float* X,
                         const int32_t* state, hipStream_t st);
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
                           const int32_t* state, hipStream_t st);

@@ -472,8 +472,8 @@ size_t dg_workspace_bytes(const dg_model* m, int32_t max_rows) {
 dg_status dg_embed(const dg_model* m, const int32_t* tokens, int32_t n, float* X, void* stream) {
     if (!m || !tokens || !X) return fail(DG_E_INVALID, "NULL argument");
     if (n < 1) return fail(DG_E_SHAPE, "n must be >= 1");
-    return hip_check(dg::launch_embed(m->embed, m->cfg.act_dtype == DG_F32, m->cfg.d_model, tokens, n, X, nullptr,
-                                      (hipStream_t)stream),
+    return hip_check(dg::launch_embed(m->embed, m->cfg.act_dtype == DG_F32, m->cfg.d_model, m->cfg.vocab, tokens, n, X,
+                                      nullptr, (hipStream_t)stream),
                      "embed");
 }
 
@@ -529,8 +529,8 @@ dg_status dg_prefill_append(const dg_model* m, dg_kv* kv, const int32_t* tokens,
     int64_t P = kv->len;
     for (int off = 0; off < n; off += T) {
         const int cn = std::min(T, n - off);
-        DG_TRY(dg::launch_embed(m->embed, m->cfg.act_dtype == DG_F32, m->cfg.d_model, tokens + off, cn, w.X, nullptr,
-                                st),
+        DG_TRY(dg::launch_embed(m->embed, m->cfg.act_dtype == DG_F32, m->cfg.d_model, m->cfg.vocab, tokens + off, cn,
+                                w.X, nullptr, st),
                "embed");
         if (dg_status s = encoder_chunk(m, w, cn, kv, P, st)) return s;
         P += cn;
@@ -557,7 +557,7 @@ dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, 
     hipStream_t st = (hipStream_t)stream;
     const dg::SamplerParams sp = to_params(scfg);
     const dg_config& c = m->cfg;
-    DG_TRY(dg::launch_embed(m->embed, c.act_dtype == DG_F32, c.d_model, canvas->tokens, n, w.X, canvas->state, st),
+    DG_TRY(dg::launch_embed(m->embed, c.act_dtype == DG_F32, c.d_model, c.vocab, canvas->tokens, n, w.X, canvas->state, st),
            "embed");
     DG_TRY(dg::launch_rope_table(n, c.head_dim, kv->len, c.rope_base, w.rope_cs, canvas->state, st), "rope table");
     for (int l = 0; l < c.n_layers; ++l) {

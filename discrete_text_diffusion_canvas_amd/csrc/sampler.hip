@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(256) merge_rows_kernel(
         float h = LN2 * (l2s - e.t / e.s);
         H[row] = fmaxf(h, 0.f);
         lse[row] = LN2 * (e.m + l2s);
-        amax[row] = am.i;
+        amax[row] = am.i == 0x7fffffff ? 0 : am.i;  // no finite logit (NaN input): id 0
     }
 }
 
@@ -434,7 +434,7 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
             run += wv;
             if (run > target) { pick = v; break; }
         }
-        if (pick < 0) pick = last;
+        if (pick < 0) pick = last >= 0 ? last : amax[row];  // no mass (NaN input): the argmax
         tokens[row] = pick;
         committed[row] = 1;
     }

@@ -278,6 +278,8 @@ size_t dg_workspace_bytes(const dg_model* m, int32_t max_rows);
  * at rows kv->len ..; the last layer's attention output and MoE are skipped.
  * Tokens are processed in chunks of the workspace's max_rows. Updates
  * kv->len on the host when enqueued. DG_E_CAPACITY if len + n > capacity.
+ * Token ids outside [0, vocab) are not checked on the host (they are device
+ * data); the embedding reads them as zero rows.
  */
 dg_status dg_prefill_append(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t n, void* ws,
                             size_t ws_bytes, void* stream);
@@ -329,7 +331,8 @@ void dg_step_graph_destroy(dg_step_graph* graph);
 /*
  * Component entry points (the stages of dg_canvas_step, exposed so each can
  * be checked on its own; same validation and ownership rules):
- *   dg_embed:          X[i][:] = embed[tokens[i]][:]                 (X f32 [n][d])
+ *   dg_embed:          X[i][:] = embed[tokens[i]][:]                 (X f32 [n][d];
+ *                      ids outside [0, vocab) give zero rows)
  *   dg_decoder_layer:  X <- decoder layer `layer` over n canvas rows at
  *                      positions kv->len .. (X f32 [n][d], in place); if
  *                      route_ids/route_gates are not NULL the router's top-k

@@ -57,6 +57,41 @@ def test_embed_is_exact_row_copy(B):
     assert torch.equal(X, model.embed[tok.long()].float())
 
 
+def test_embed_ids_outside_the_vocabulary_give_zero_rows(B):
+    cfg = SMALL_BF16
+    model = device_model(B, cfg)
+    tok = _canvas_tokens(cfg, 20)
+    bad = torch.tensor([-1, cfg.vocab, 2**31 - 1, -(2**31)], dtype=torch.int32, device="cuda")
+    tok[5:9] = bad
+    X = torch.full((cfg.canvas, cfg.d_model), 7.0, dtype=torch.float32, device="cuda")
+    B.embed(model, tok, X)
+    torch.cuda.synchronize()
+    good = torch.ones(cfg.canvas, dtype=torch.bool, device="cuda")
+    good[5:9] = False
+    assert torch.equal(X[good], model.embed[tok[good].long()].float())
+    assert torch.count_nonzero(X[~good]) == 0
+
+
+def test_router_ids_stay_valid_and_distinct_on_nan_activations(B):
+    # a NaN activation must not turn into an expert id outside [0, E) (the
+    # permutation and the expert GEMMs index with them)
+    cfg = SMALL_BF16
+    model = device_model(B, cfg)
+    n = cfg.canvas
+    kv = B.KVCache(model, 300 + n)
+    fill_synthetic_kv(kv, cfg, 300)
+    X = torch.randn(n, cfg.d_model, dtype=torch.float32, device="cuda")
+    X[3] = float("nan")
+    X[17, :5] = float("nan")
+    ids = torch.zeros(n, cfg.top_k, dtype=torch.int32, device="cuda")
+    gates = torch.zeros(n, cfg.top_k, dtype=torch.float32, device="cuda")
+    B.decoder_layer(model, 0, X, kv, model.workspace(n), ids, gates)
+    torch.cuda.synchronize()
+    g = ids.cpu().numpy()
+    assert g.min() >= 0 and g.max() < cfg.n_experts
+    assert all(len(set(r.tolist())) == cfg.top_k for r in g)
+
+
 @pytest.mark.parametrize("name", list(LAYER_CFGS))
 @pytest.mark.parametrize("layer", [0, 1])
 def test_decoder_layer(B, name, layer):

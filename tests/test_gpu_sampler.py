@@ -184,3 +184,25 @@ def test_deterministic_and_done_is_sticky(B):
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1])
     assert torch.equal(outs[0][2], outs[1][2])
+
+
+def test_nan_logits_still_give_tokens_inside_the_vocabulary(B):
+    # rows whose logits are NaN (all or some) have no meaningful distribution;
+    # whatever is committed must still be a valid id, since the next step
+    # embeds it
+    n, V = 64, 4096
+    dev = torch.device("cuda")
+    canvas = B.Canvas(n, V - 1, 0, dev)
+    stats = B.StepStats(n, dev)
+    ws = torch.empty(B.sampler_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
+    for t in range(48):
+        L = wl.sampler_logits(t, shape=(n, V), device="cuda")
+        L[3] = float("nan")
+        L[10, 100:200] = float("nan")
+        B.sampler_step(B.sampler_default(), L, V - 1, canvas, t, SEED, stats, ws)
+        torch.cuda.synchronize()
+        tok = canvas.tokens
+        assert int(tok.min()) >= 0 and int(tok.max()) < V
+        if canvas.state[0].item():
+            break
+    assert bool(canvas.committed.all())
