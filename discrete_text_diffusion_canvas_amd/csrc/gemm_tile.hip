@@ -116,8 +116,8 @@ __device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int 
         uint16_t* dst = reinterpret_cast<uint16_t*>(g.C) + row * g.ldc + n;
         if (full) {
             uint2 o;
-            o.x = (uint32_t)f2bf(vv[0]) | ((uint32_t)f2bf(vv[1]) << 16);
-            o.y = (uint32_t)f2bf(vv[2]) | ((uint32_t)f2bf(vv[3]) << 16);
+            o.x = f2bf2(vv[0], vv[1]);
+            o.y = f2bf2(vv[2], vv[3]);
             *reinterpret_cast<uint2*>(dst) = o;
         } else {
             for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] = f2bf(vv[q]);
@@ -164,10 +164,10 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T
         uint16_t* dst = C + (int64_t)r * g.ldc + n;
         if (n + 8 <= N) {
             uint4 w;
-            w.x = (uint32_t)f2bf(t[0]) | ((uint32_t)f2bf(t[1]) << 16);
-            w.y = (uint32_t)f2bf(t[2]) | ((uint32_t)f2bf(t[3]) << 16);
-            w.z = (uint32_t)f2bf(t[4]) | ((uint32_t)f2bf(t[5]) << 16);
-            w.w = (uint32_t)f2bf(t[6]) | ((uint32_t)f2bf(t[7]) << 16);
+            w.x = f2bf2(t[0], t[1]);
+            w.y = f2bf2(t[2], t[3]);
+            w.z = f2bf2(t[4], t[5]);
+            w.w = f2bf2(t[6], t[7]);
             *reinterpret_cast<uint4*>(dst) = w;
         } else {
             for (int u = 0; u < 8 && n + u < N; ++u) dst[u] = f2bf(t[u]);
@@ -303,8 +303,8 @@ __global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int
         ua.x += up.x; ua.y += up.y; ua.z += up.z; ua.w += up.w;
     }
     uint2 o;
-    o.x = (uint32_t)f2bf(tsilu(ga.x) * ua.x) | ((uint32_t)f2bf(tsilu(ga.y) * ua.y) << 16);
-    o.y = (uint32_t)f2bf(tsilu(ga.z) * ua.z) | ((uint32_t)f2bf(tsilu(ga.w) * ua.w) << 16);
+    o.x = f2bf2(tsilu(ga.x) * ua.x, tsilu(ga.y) * ua.y);
+    o.y = f2bf2(tsilu(ga.z) * ua.z, tsilu(ga.w) * ua.w);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.C) + (int64_t)slot * g.ldc + f) = o;
 }
 

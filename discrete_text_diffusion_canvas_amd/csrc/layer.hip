@@ -62,8 +62,8 @@ __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int n
         const float v[4] = {x[j].x * rs * g.x, x[j].y * rs * g.y, x[j].z * rs * g.z, x[j].w * rs * g.w};
         if constexpr (sizeof(TO) == 2) {
             uint2 o;
-            o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-            o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            o.x = f2bf2(v[0], v[1]);
+            o.y = f2bf2(v[2], v[3]);
             reinterpret_cast<uint2*>(y)[c] = o;
         } else {
             reinterpret_cast<float4*>(y)[c] = make_float4(v[0], v[1], v[2], v[3]);
@@ -163,10 +163,10 @@ template <> struct Vec8<uint16_t> {
     }
     static __device__ __forceinline__ void store(uint16_t* p, const float (&v)[8]) {
         uint4 x;
-        x.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-        x.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-        x.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-        x.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+        x.x = f2bf2(v[0], v[1]);
+        x.y = f2bf2(v[2], v[3]);
+        x.z = f2bf2(v[4], v[5]);
+        x.w = f2bf2(v[6], v[7]);
         *reinterpret_cast<uint4*>(p) = x;
     }
 };

@@ -120,10 +120,10 @@ __device__ __forceinline__ void lmhead_tile_epilogue(const GemmArgs& g, const f3
             uint16_t* dst = C + (int64_t)r * g.ldc + n;
             if (vec && n + 7 < N) {
                 uint4 w;
-                w.x = (uint32_t)f2bf(e[0]) | ((uint32_t)f2bf(e[1]) << 16);
-                w.y = (uint32_t)f2bf(e[2]) | ((uint32_t)f2bf(e[3]) << 16);
-                w.z = (uint32_t)f2bf(e[4]) | ((uint32_t)f2bf(e[5]) << 16);
-                w.w = (uint32_t)f2bf(e[6]) | ((uint32_t)f2bf(e[7]) << 16);
+                w.x = f2bf2(e[0], e[1]);
+                w.y = f2bf2(e[2], e[3]);
+                w.z = f2bf2(e[4], e[5]);
+                w.w = f2bf2(e[6], e[7]);
                 *reinterpret_cast<uint4*>(dst) = w;
             } else {
                 for (int u = 0; u < 8; ++u)
