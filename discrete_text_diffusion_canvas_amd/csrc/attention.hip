@@ -34,6 +34,11 @@
 #ifndef DG_ATTN_MIN_BLOCKS
 #define DG_ATTN_MIN_BLOCKS 3
 #endif
+// 1: scores formed transposed, P kept in registers (attn_t_kernel);
+// 0: scores as Q K^T, P through LDS (attn_reg_kernel)
+#ifndef DG_ATTN_TRANSPOSED
+#define DG_ATTN_TRANSPOSED 1
+#endif
 
 namespace dg {
 
@@ -566,6 +571,321 @@ __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
     }
 }
 
+// bf16 kernel with transposed scores. The same work as attn_reg_kernel, but S
+// is formed as K Q^T: a lane then holds, for query row lr of its wave's tile,
+// 16 scores of keys nt*16 + 4*lg + q (nt, q < 4). That layout is already the
+// A operand of the P V product if the keys of each 32-key k-step are taken in
+// the order (first run: 32*ks2 + 4*lg + q, second: 32*ks2 + 16 + 4*lg + q),
+// so P stays in registers; the V^T tile is stored into LDS in that key order
+// (two 8-byte halves per 16-byte chunk). Row max and sum are 16 in-lane
+// values plus two cross-lane steps. Scores are kept unscaled; the softmax
+// runs in base 2 with the 1/sqrt(hd) scale folded into the exponent, and the
+// partial maxima leave in natural-log units for the merge.
+template <int HD, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
+    if (a.state && a.state[0]) return;
+    const int QP = 128 / R;                       // positions per workgroup
+    const int nqt = (a.nq + QP - 1) / QP;
+    int qt, gs;
+    attn_ids(nqt, qt, gs);
+    if (gs >= a.Hkv * a.splits) return;
+    const int g = gs % a.Hkv, sp = gs / a.Hkv;
+    constexpr int KROWB = HD * 2;                 // bytes per K row
+    constexpr int K_BYTES = KB * KROWB;           // K tile
+    constexpr int V_BYTES = HD * KB * 2;          // V^T tile (rows of 128 bytes)
+    constexpr int STAGE = K_BYTES + V_BYTES;
+    constexpr int K_LD = K_BYTES / 1024 / NW;     // 16-byte loads per lane and block
+    constexpr int V_LD = V_BYTES / 1024 / NW;
+    constexpr int TPW = 128 / (16 * NW);          // 16-row tiles per wave
+    constexpr int RPW = 16 * TPW;                 // rows per wave
+    constexpr int KRPI = 1024 / KROWB;            // K rows per 1 KB piece
+    constexpr int KCPR = KROWB / 16;              // chunks per K row
+    constexpr int NT_D = HD / 16;
+    constexpr int KS = HD / 32;
+    extern __shared__ __align__(16) unsigned char smem[];
+    unsigned char* Qs = smem + STAGE;             // [128 rows][HD], swizzled
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int qx0 = qt * QP;
+    auto row_head = [&](int rho) { return g * R + rho / QP; };
+    auto row_pos = [&](int rho) { return qx0 + rho % QP; };
+
+    // ---- the key blocks of this workgroup ----
+    const int64_t qlo = a.qpos0 + qx0, qhi = a.qpos0 + min(qx0 + QP, a.nq) - 1;
+    int64_t b1lo, b1hi;                           // segment-1 blocks [b1lo, b1hi)
+    if (a.causal) {
+        int64_t kmin = a.s1, kmax = min<int64_t>(a.e1 - 1, qhi);
+        if (a.window > 0) kmin = max<int64_t>(kmin, qlo - a.window + 1);
+        b1lo = kmin / KB;
+        b1hi = kmax >= kmin ? kmax / KB + 1 : b1lo;
+    } else {
+        b1lo = a.s1 / KB;
+        b1hi = a.e1 > a.s1 ? (a.e1 - 1) / KB + 1 : b1lo;
+    }
+    const int64_t nb1 = b1hi - b1lo;
+    const int64_t nb2 = a.n2 > 0 ? (a.n2 + KB - 1) / KB : 0;
+    const int64_t nb = nb1 + nb2;
+    const int64_t per = (nb + a.splits - 1) / a.splits;
+    const int64_t bb0 = per * sp, bb1 = min<int64_t>(nb, bb0 + per);
+
+    const uint16_t* K1 = reinterpret_cast<const uint16_t*>(a.K1) + (int64_t)g * a.ld1 * HD;
+    const uint16_t* V1 = reinterpret_cast<const uint16_t*>(a.V1) + (int64_t)g * HD * a.ld1;
+    const uint16_t* K2 = a.K2 ? reinterpret_cast<const uint16_t*>(a.K2) + (int64_t)g * a.ld2 * HD : nullptr;
+    const uint16_t* V2 = a.V2 ? reinterpret_cast<const uint16_t*>(a.V2) + (int64_t)g * HD * a.ld2 : nullptr;
+
+    // register loads of virtual block vb (clamped to this workgroup's last
+    // block, so the loop stays branch-free): K rows with the LDS swizzle
+    // applied on the read side; V^T rows as plain 16-byte chunks of 8 keys
+    u32x4 kr[K_LD], vr[V_LD];
+    auto load = [&](int64_t vb) {
+        vb = min<int64_t>(vb, bb1 - 1);
+        const bool seg1 = vb < nb1;
+        const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
+        const int64_t rlim = seg1 ? a.e1 : a.n2;   // rows >= rlim: any valid row (masked)
+        const uint16_t* Kb = seg1 ? K1 : K2;
+        const uint16_t* Vb = seg1 ? V1 : V2;
+        const int64_t vld = seg1 ? a.ld1 : a.ld2;
+#pragma unroll
+        for (int j = 0; j < K_LD; ++j) {
+            const int r = (wave * K_LD + j) * KRPI + lane / KCPR;
+            const int pos = lane % KCPR;
+            int64_t kr_row = row0 + r;
+            if (kr_row >= rlim) kr_row = rlim - 1;
+            if (kr_row < 0) kr_row = 0;
+            kr[j] = *reinterpret_cast<const u32x4*>(Kb + kr_row * HD + 8 * kswz(r, pos));
+        }
+#pragma unroll
+        for (int j = 0; j < V_LD; ++j) {
+            const int d = (wave * V_LD + j) * 8 + lane / 8;
+            vr[j] = *reinterpret_cast<const u32x4*>(Vb + (int64_t)d * vld + row0 + 8 * (lane % 8));
+        }
+    };
+    // V^T row d: 16-byte slot L = 4*ks2 + l4 holds keys 32*ks2 + 4*l4 + (0..3)
+    // then 32*ks2 + 16 + 4*l4 + (0..3), at position vswz(d, L). Chunk c = 4*ks2
+    // + m of 8 keys gives its half h to slot 4*ks2 + 2*(m % 2) + h, byte
+    // offset 8*(m / 2).
+    auto store = [&]() {
+        unsigned char* base = smem;
+#pragma unroll
+        for (int j = 0; j < K_LD; ++j) *reinterpret_cast<u32x4*>(base + (wave * K_LD + j) * 1024 + lane * 16) = kr[j];
+#pragma unroll
+        for (int j = 0; j < V_LD; ++j) {
+            const int d = (wave * V_LD + j) * 8 + lane / 8;
+            const int c = lane % 8, ks2 = c / 4, m = c % 4;
+            unsigned char* row = base + K_BYTES + d * 128 + 8 * (m / 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int L = 4 * ks2 + 2 * (m % 2) + h;
+                *reinterpret_cast<u32x2*>(row + vswz(d, L) * 16) = u32x2{vr[j][2 * h], vr[j][2 * h + 1]};
+            }
+        }
+    };
+
+    // ---- Q rows of the workgroup into LDS (row rho, 16-byte chunk c at kswz):
+    // all loads first (rows past nq read row 0 and are zeroed), then the writes
+    {
+        constexpr int QL = 128 * KCPR / (NW * 64);  // 16-byte pieces per thread
+        u16x8 qv[QL];
+#pragma unroll
+        for (int j = 0; j < QL; ++j) {
+            const int e = tid + NW * 64 * j, rho = e / KCPR, c = e % KCPR;
+            const int qp = row_pos(rho);
+            qv[j] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(a.Q) +
+                                                    ((int64_t)row_head(rho) * a.ldq + (qp < a.nq ? qp : 0)) * HD +
+                                                    c * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < QL; ++j) {
+            const int e = tid + NW * 64 * j, rho = e / KCPR, c = e % KCPR;
+            const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            *reinterpret_cast<u16x8*>(Qs + rho * KROWB + kswz(rho, c) * 16) = row_pos(rho) < a.nq ? qv[j] : z;
+        }
+    }
+    f32x4 o[TPW][NT_D];
+    float m_run[TPW], l_run[TPW];  // row lr of tile t, base-2 units (scaled)
+    int qpos[TPW];                 // absolute position of row lr (< 2^31)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+        for (int j = 0; j < NT_D; ++j) o[t][j] = f32x4{0, 0, 0, 0};
+        m_run[t] = -INFINITY;
+        l_run[t] = 0.f;
+        qpos[t] = (int)(a.qpos0 + row_pos(wave * RPW + t * 16 + lr));
+    }
+    const float c2 = 1.4426950408889634f / sqrtf((float)HD);  // log2(e) / sqrt(hd)
+    constexpr float SLACK2 = SM_SLACK * 1.4426950408889634f;
+
+    if (bb0 < bb1) {
+        load(bb0);
+        store();
+        load(bb0 + 1);
+    }
+    attn_lds_barrier();
+    for (int64_t vb = bb0; vb < bb1; ++vb) {
+        const unsigned char* Kt = smem;
+        const unsigned char* Vt = Kt + K_BYTES;
+        const bool seg1 = vb < nb1;
+        const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
+        // ---- S^T = K Q^T; the fragments of k-step ks + 1 are read while the
+        // MFMAs of ks run ----
+        f32x4 s[TPW][4];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) s[t][nt] = f32x4{0, 0, 0, 0};
+        u16x8 qf[2][TPW], kf[2][4];
+        auto ld_s = [&](int bsel, int ks) {
+            const int c = ks * 4 + lg;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int q = wave * RPW + t * 16 + lr;
+                qf[bsel][t] = *reinterpret_cast<const u16x8*>(Qs + q * KROWB + kswz(q, c) * 16);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const int r = nt * 16 + lr;
+                kf[bsel][nt] = *reinterpret_cast<const u16x8*>(Kt + r * KROWB + kswz(r, c) * 16);
+            }
+        };
+        ld_s(0, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) ld_s((ks + 1) & 1, ks + 1);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) s[t][nt] = amfma(kf[ks & 1][nt], qf[ks & 1][t], s[t][nt]);
+        }
+        // ---- mask: only blocks that reach past the visible keys, or causal ----
+        const bool full = !a.causal && (seg1 ? (row0 >= a.s1) & (row0 + KB <= a.e1) : (row0 + KB <= a.n2));
+        if (!full) {  // uniform
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int key = (int)(row0 + nt * 16 + 4 * lg + q);
+                    const bool kin = seg1 ? (key >= (int)a.s1) & (key < (int)a.e1) : (key < a.n2);
+                    const int kp = seg1 ? key : (int)a.pos2_0 + key;
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        bool ok = kin;
+                        if (a.causal) {
+                            const int dq = qpos[t] - kp;
+                            ok = ok & (dq >= 0) & ((a.window <= 0) | (dq < a.window));
+                        }
+                        if (!ok) s[t][nt][q] = -INFINITY;
+                    }
+                }
+        }
+        // ---- online softmax (base 2), P into registers as the A operand ----
+        u16x8 pf[TPW][2];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            float mx = fmaxf(fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3])),
+                             fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
+            mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[t][2][0], s[t][2][1]), fmaxf(s[t][2][2], s[t][2][3])),
+                                 fmaxf(fmaxf(s[t][3][0], s[t][3][1]), fmaxf(s[t][3][2], s[t][3][3]))));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+            const float pm = mx * c2;  // the row's block max, base-2 units
+            if (__ballot(pm > m_run[t] + SLACK2)) {  // wave-uniform
+                const float mnew = fmaxf(m_run[t], pm);
+                const float alpha = m_run[t] == -INFINITY ? 0.f : exp2f(m_run[t] - mnew);
+                m_run[t] = mnew;
+                l_run[t] *= alpha;
+                // O rows 4*lg + i: their factors sit in lanes 4*lg + i
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * lg + i, WAVE);
+#pragma unroll
+                    for (int j = 0; j < NT_D; ++j) o[t][j][i] *= ai;
+                }
+            }
+            const float mr = m_run[t];
+            const bool live = mr != -INFINITY;
+            float psum = 0.f;
+#pragma unroll
+            for (int ks2 = 0; ks2 < 2; ++ks2) {
+                u32x4 w;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {  // first / second run of 4 keys: n-tile 2*ks2 + hh
+                    const f32x4 sv = s[t][2 * ks2 + hh];
+                    float pv[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) pv[q] = live ? exp2f(fmaf(sv[q], c2, -mr)) : 0.f;
+                    const uint32_t w0 = f2bf2(pv[0], pv[1]), w1 = f2bf2(pv[2], pv[3]);
+                    w[2 * hh] = w0;
+                    w[2 * hh + 1] = w1;
+                    // the probabilities the MFMA sees
+                    psum += (__uint_as_float(w0 << 16) + __uint_as_float(w0 & 0xffff0000u)) +
+                            (__uint_as_float(w1 << 16) + __uint_as_float(w1 & 0xffff0000u));
+                }
+                pf[t][ks2] = __builtin_bit_cast(u16x8, w);
+            }
+            psum += __shfl_xor(psum, 16, WAVE);
+            psum += __shfl_xor(psum, 32, WAVE);
+            l_run[t] += psum;
+        }
+        // ---- O += P V: V^T fragments in groups of 4, the next group read
+        // during the current MFMAs ----
+#pragma unroll
+        for (int ks2 = 0; ks2 < KB / 32; ++ks2) {
+            u16x8 vf[2][4];
+            auto ld_v = [&](int bsel, int jg) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int d = (jg * 4 + jj) * 16 + lr;
+                    vf[bsel][jj] = *reinterpret_cast<const u16x8*>(Vt + d * 128 + vswz(d, ks2 * 4 + lg) * 16);
+                }
+            };
+            ld_v(0, 0);
+#pragma unroll
+            for (int jg = 0; jg < NT_D / 4; ++jg) {
+                if (jg + 1 < NT_D / 4) ld_v((jg + 1) & 1, jg + 1);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t)
+                        o[t][jg * 4 + jj] = amfma(pf[t][ks2], vf[jg & 1][jj], o[t][jg * 4 + jj]);
+            }
+        }
+        __builtin_amdgcn_s_barrier();  // every wave done with the slot
+        store();
+        load(vb + 2);
+        attn_lds_barrier();
+    }
+    __syncthreads();  // retire the tail loads
+    // ---- write out: O row 4*lg + i takes its (m, l) from lane 4*lg + i ----
+    constexpr float LN2 = 0.6931471805599453f;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float li = __shfl(l_run[t], 4 * lg + i, WAVE);
+            const float mi = __shfl(m_run[t], 4 * lg + i, WAVE);
+            const int rho = wave * RPW + t * 16 + lg * 4 + i;
+            if (row_pos(rho) >= a.nq) continue;
+            const int hq = row_head(rho), qr = row_pos(rho);
+            if (a.splits == 1) {
+                const float inv = li > 0.f ? 1.f / li : 0.f;
+                uint16_t* out = reinterpret_cast<uint16_t*>(a.O) + (int64_t)qr * a.Hq * HD + (int64_t)hq * HD;
+#pragma unroll
+                for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[t][j][i] * inv);
+            } else {
+                float* po = a.part_o + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
+#pragma unroll
+                for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[t][j][i];
+                if (lr == 0) {
+                    float* pm = a.part_ml + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * 2;
+                    pm[0] = mi * LN2;  // natural-log units, as the merge expects
+                    pm[1] = li;
+                }
+            }
+        }
+    }
+}
+
 // Merge split-KV partials: O = sum_s O_s e^(m_s - M) / sum_s l_s e^(m_s - M).
 // One wave per (query row, head); a lane owns 4 consecutive dims. Every
 // split's (m, l) and partial loads are issued before the sums, which run in
@@ -650,17 +970,18 @@ static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
     constexpr int NW = DG_ATTN_WAVES;
     const int R = a.Hq / a.Hkv;
     constexpr int STAGE = 64 * HD * 2 * 2;
-    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2 + (size_t)128 * (KB + 8) * 2;
+    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2 + (DG_ATTN_TRANSPOSED ? 0 : (size_t)128 * (KB + 8) * 2);
+    auto kern = DG_ATTN_TRANSPOSED ? attn_t_kernel<HD, NW> : attn_reg_kernel<HD, NW>;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_reg_kernel<HD, NW>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
     }
     const int nqt = (a.nq + 128 / R - 1) / (128 / R), ngs = a.Hkv * a.splits;
     const unsigned grid = (unsigned)(((ngs + 7) / 8) * nqt * 8);  // see attn_ids
-    attn_reg_kernel<HD, NW><<<grid, NW * 64, lds, st>>>(a, R);
+    kern<<<grid, NW * 64, lds, st>>>(a, R);
     if (a.splits > 1) launch_merge_any(a, true, st);
     return hipGetLastError();
 }
