@@ -78,14 +78,24 @@ __device__ __forceinline__ ArgMax argmax_merge(ArgMax a, ArgMax b) {
     if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
     return a;
 }
+// The merge is commutative and associative, so any pairing tree leaves the
+// same result in every lane. Inside each row of 16 lanes the pairs come from
+// DPP moves (swap neighbours, swap pairs, mirror halves of 8, mirror the
+// row); the two cross-row steps are lane shuffles.
+#define DG_ARGMAX_DPP_STEP(a, ctrl)                                                                       \
+    a = argmax_merge(a, ArgMax{__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                    \
+                                   0, __builtin_bit_cast(int, a.v), ctrl, 0xF, 0xF, false)),             \
+                               __builtin_amdgcn_update_dpp(0, a.i, ctrl, 0xF, 0xF, false)})
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        ArgMax b{__shfl_xor(a.v, o, WAVE), __shfl_xor(a.i, o, WAVE)};
-        a = argmax_merge(a, b);
-    }
+    DG_ARGMAX_DPP_STEP(a, 0xB1);
+    DG_ARGMAX_DPP_STEP(a, 0x4E);
+    DG_ARGMAX_DPP_STEP(a, 0x141);
+    DG_ARGMAX_DPP_STEP(a, 0x140);
+    a = argmax_merge(a, ArgMax{__shfl_xor(a.v, 16, WAVE), __shfl_xor(a.i, 16, WAVE)});
+    a = argmax_merge(a, ArgMax{__shfl_xor(a.v, 32, WAVE), __shfl_xor(a.i, 32, WAVE)});
     return a;
 }
+#undef DG_ARGMAX_DPP_STEP
 
 // Base-2 entropy partials of a set of tempered logits z2 = z * log2(e):
 // m = max z2, s = sum 2^(z2-m), t = sum 2^(z2-m) (z2-m).

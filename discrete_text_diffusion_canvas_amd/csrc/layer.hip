@@ -313,17 +313,17 @@ __global__ void __launch_bounds__(256) rope_scatter_kernel(const T* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Router top-k. logits r [n][E] f32 (+ bias [E]); one wavefront per token.
+// Router top-k. logits r [n][E] f32 (+ bias [E]); one wavefront (workgroup) per token.
 // k rounds of a wavefront argmax (value desc, expert id asc); gates are the
 // softmax over the k selected logits (f32).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) router_topk_kernel(const float* __restrict__ r, int nparts, int64_t pstride,
-                                                          const float* __restrict__ bias, int n, int E, int k,
-                                                          int32_t* __restrict__ ids, float* __restrict__ gates,
-                                                          const int32_t* __restrict__ state) {
+__global__ void __launch_bounds__(64) router_topk_kernel(const float* __restrict__ r, int nparts, int64_t pstride,
+                                                         const float* __restrict__ bias, int n, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                         const int32_t* __restrict__ state) {
     if (state && state[0]) return;
-    const int tokn = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int tokn = blockIdx.x;
+    const int lane = threadIdx.x;
     if (tokn >= n) return;
     constexpr int PER = 8;  // up to 512 experts
     float v[PER];
@@ -600,8 +600,7 @@ hipError_t launch_rope_scatter(const void* qkv, const float* part, int nparts, i
 
 hipError_t launch_router_topk(const float* r, int nparts, const float* bias, int n, int E, int k, int32_t* ids,
                               float* gates, const int32_t* state, hipStream_t st) {
-    router_topk_kernel<<<(n + 3) / 4, 256, 0, st>>>(r, std::max(nparts, 1), (int64_t)n * E, bias, n, E, k, ids, gates,
-                                                    state);
+    router_topk_kernel<<<n, 64, 0, st>>>(r, std::max(nparts, 1), (int64_t)n * E, bias, n, E, k, ids, gates, state);
     return hipGetLastError();
 }
 
