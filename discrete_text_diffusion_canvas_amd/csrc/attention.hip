@@ -786,8 +786,7 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
                              fmaxf(fmaxf(s[t][1][0], s[t][1][1]), fmaxf(s[t][1][2], s[t][1][3])));
             mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[t][2][0], s[t][2][1]), fmaxf(s[t][2][2], s[t][2][3])),
                                  fmaxf(fmaxf(s[t][3][0], s[t][3][1]), fmaxf(s[t][3][2], s[t][3][3]))));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, WAVE));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+            mx = xor32_max(xor16_max(mx));
             const float pm = mx * c2;  // the row's block max, base-2 units
             if (__ballot(pm > m_run[t] + SLACK2)) {  // wave-uniform
                 const float mnew = fmaxf(m_run[t], pm);
@@ -823,8 +822,7 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
                 }
                 pf[t][ks2] = __builtin_bit_cast(u16x8, w);
             }
-            psum += __shfl_xor(psum, 16, WAVE);
-            psum += __shfl_xor(psum, 32, WAVE);
+            psum = xor32_sum(xor16_sum(psum));
             l_run[t] += psum;
         }
         // ---- O += P V: V^T fragments in groups of 4, the next group read

@@ -69,6 +69,28 @@ __device__ __forceinline__ int wave_min_i(int v) {
     return v;
 }
 
+// Combine a value with the one in lane l ^ 16 (or l ^ 32) through gfx950's
+// v_permlane16_swap / v_permlane32_swap with both operands the same register:
+// each lane gets the pair {its value, the partner's} (checked on the device),
+// so a commutative op leaves both lanes with the same bits. VALU only, no
+// LDS round trip.
+__device__ __forceinline__ float xor16_max(float v) {
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // (value, index) argmax with lowest index on equal values
 struct ArgMax {
     float v;
@@ -81,7 +103,7 @@ __device__ __forceinline__ ArgMax argmax_merge(ArgMax a, ArgMax b) {
 // The merge is commutative and associative, so any pairing tree leaves the
 // same result in every lane. Inside each row of 16 lanes the pairs come from
 // DPP moves (swap neighbours, swap pairs, mirror halves of 8, mirror the
-// row); the two cross-row steps are lane shuffles.
+// row); the two cross-row steps are permlane swaps.
 #define DG_ARGMAX_DPP_STEP(a, ctrl)                                                                       \
     a = argmax_merge(a, ArgMax{__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                    \
                                    0, __builtin_bit_cast(int, a.v), ctrl, 0xF, 0xF, false)),             \
@@ -91,8 +113,16 @@ __device__ __forceinline__ ArgMax wave_argmax(ArgMax a) {
     DG_ARGMAX_DPP_STEP(a, 0x4E);
     DG_ARGMAX_DPP_STEP(a, 0x141);
     DG_ARGMAX_DPP_STEP(a, 0x140);
-    a = argmax_merge(a, ArgMax{__shfl_xor(a.v, 16, WAVE), __shfl_xor(a.i, 16, WAVE)});
-    a = argmax_merge(a, ArgMax{__shfl_xor(a.v, 32, WAVE), __shfl_xor(a.i, 32, WAVE)});
+    {   // cross-row steps: the swaps move v and i with the same lane pattern
+        const auto v = __builtin_amdgcn_permlane16_swap(__float_as_uint(a.v), __float_as_uint(a.v), false, false);
+        const auto i = __builtin_amdgcn_permlane16_swap((unsigned)a.i, (unsigned)a.i, false, false);
+        a = argmax_merge(ArgMax{__uint_as_float(v[0]), (int)i[0]}, ArgMax{__uint_as_float(v[1]), (int)i[1]});
+    }
+    {
+        const auto v = __builtin_amdgcn_permlane32_swap(__float_as_uint(a.v), __float_as_uint(a.v), false, false);
+        const auto i = __builtin_amdgcn_permlane32_swap((unsigned)a.i, (unsigned)a.i, false, false);
+        a = argmax_merge(ArgMax{__uint_as_float(v[0]), (int)i[0]}, ArgMax{__uint_as_float(v[1]), (int)i[1]});
+    }
     return a;
 }
 #undef DG_ARGMAX_DPP_STEP
