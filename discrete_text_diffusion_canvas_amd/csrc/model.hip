@@ -77,17 +77,26 @@ struct Work {
     int32_t* experts_hit = nullptr;  // optional [n_layers] routed experts hit per layer (caller's buffer)
 };
 
-// K slices of a weight-streaming GEMM over d_model inputs (the router, the
-// gate/up products of the small expert groups): the most (up to 16) that
-// divide its 32-wide k-steps and leave each slice at least 8 (two per wave),
-// so few output tiles still spread over many workgroups
-int stream_ksplit(const dg_config& c) {
+// K slices of a weight-streaming GEMM over d_model inputs: the most (up to
+// 16) that divide its 32-wide k-steps and leave each slice at least
+// min_steps, so few output tiles still spread over many workgroups. Measured
+// best: 8 steps (two per wave) for the router, 16 for the gate/up products of
+// the small expert groups.
+#ifndef DG_ROUTER_SLICE_STEPS
+#define DG_ROUTER_SLICE_STEPS 8
+#endif
+#ifndef DG_SMALL_SLICE_STEPS
+#define DG_SMALL_SLICE_STEPS 16
+#endif
+int stream_ksplit(const dg_config& c, int min_steps) {
     const int ks_total = c.d_model / 32;
     int best = 1;
     for (int s = 2; s <= 16; ++s)
-        if (ks_total % s == 0 && ks_total / s >= 8) best = s;
+        if (ks_total % s == 0 && ks_total / s >= min_steps) best = s;
     return best;
 }
+int router_ksplit(const dg_config& c) { return stream_ksplit(c, DG_ROUTER_SLICE_STEPS); }
+int small_ksplit(const dg_config& c) { return stream_ksplit(c, DG_SMALL_SLICE_STEPS); }
 
 Work carve(const dg_model* m, void* base, int T) {
     const dg_config& c = m->cfg;
@@ -113,12 +122,12 @@ Work carve(const dg_model* m, void* base, int T) {
         w.gemm_part = parts ? cv.take<float>(parts) : nullptr;
     }
     {   // split-K partials of the tiled gate/up GEMM: [slices][T (k + 1) slots][2F]
-        const int gks = ab == 2 ? std::max(dg::tile_grouped_ksplit(T), stream_ksplit(c)) : 1;
+        const int gks = ab == 2 ? std::max(dg::tile_grouped_ksplit(T), small_ksplit(c)) : 1;
         w.gu_part = gks > 1 ? cv.take<float>((size_t)gks * T * (k + 1) * 2 * F) : nullptr;
     }
     w.part_o = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * hd);
     w.part_ml = cv.take<float>((size_t)MAX_SPLITS * SPLIT_ROWS * Hq * 2);
-    w.rlog = cv.take<float>((size_t)stream_ksplit(c) * T * E);
+    w.rlog = cv.take<float>((size_t)router_ksplit(c) * T * E);
     w.ids = cv.take<int32_t>((size_t)T * k);
     w.gates = cv.take<float>((size_t)T * k);
     w.offsets = cv.take<int32_t>(E + 2);
@@ -200,10 +209,10 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
         dg::GemmArgs g = gargs();
         g.A = w.A; g.lda = d; g.W = L.router; g.ldw = d; g.M = n; g.N = E; g.K = d;
         g.C = w.rlog; g.ldc = E; g.state = state;
-        g.ksplit = stream_ksplit(c); g.part = w.rlog;
+        g.ksplit = router_ksplit(c); g.part = w.rlog;
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_STORE_F32, 0, dg::SHAPE_PROJ, st), "router gemm");
     }
-    DG_TRY(dg::launch_router_topk(w.rlog, stream_ksplit(c), L.router_bias, n, E, k, w.ids, w.gates, state, st),
+    DG_TRY(dg::launch_router_topk(w.rlog, router_ksplit(c), L.router_bias, n, E, k, w.ids, w.gates, state, st),
            "router topk");
     // groups of more than 64 rows go to the LDS-staged GEMM (bf16 only)
     dg::GemmArgs gu = gargs(), dn = gargs();
@@ -226,7 +235,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
     const int small_rows = tiled ? 64 : n;  // bound on the rows of a stream-GEMM group
     {   // gate/up with SwiGLU; products split over K leave partials for one reduce
         const int slot = timing_begin(st, DG_TIME_EXPERT_GATE_UP);
-        const int ks_small = tiled && w.gu_part ? stream_ksplit(c) : 1;
+        const int ks_small = tiled && w.gu_part ? small_ksplit(c) : 1;
         const int ks_big = tiled && w.gu_part ? dg::tile_grouped_ksplit(n) : 1;
         dg::GemmArgs g = gu;
         g.M = n * (k + 1);  // slots: the rows of the partials
