@@ -39,6 +39,10 @@
 #ifndef DG_ATTN_TRANSPOSED
 #define DG_ATTN_TRANSPOSED 1
 #endif
+// 1: the transposed kernel keeps each wave's Q fragments in registers
+#ifndef DG_ATTN_QREG
+#define DG_ATTN_QREG 1
+#endif
 
 namespace dg {
 
@@ -722,6 +726,17 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
         load(bb0 + 1);
     }
     attn_lds_barrier();
+#if DG_ATTN_QREG
+    // the wave's Q fragments for every k-step, read from LDS once
+    u16x8 qreg[KS][TPW];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int q = wave * RPW + t * 16 + lr;
+            qreg[ks][t] = *reinterpret_cast<const u16x8*>(Qs + q * KROWB + kswz(q, ks * 4 + lg) * 16);
+        }
+#endif
     for (int64_t vb = bb0; vb < bb1; ++vb) {
         const unsigned char* Kt = smem;
         const unsigned char* Vt = Kt + K_BYTES;
@@ -737,11 +752,13 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
         u16x8 qf[2][TPW], kf[2][4];
         auto ld_s = [&](int bsel, int ks) {
             const int c = ks * 4 + lg;
+#if !DG_ATTN_QREG
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 const int q = wave * RPW + t * 16 + lr;
                 qf[bsel][t] = *reinterpret_cast<const u16x8*>(Qs + q * KROWB + kswz(q, c) * 16);
             }
+#endif
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int r = nt * 16 + lr;
@@ -755,7 +772,13 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) s[t][nt] = amfma(kf[ks & 1][nt], qf[ks & 1][t], s[t][nt]);
+                for (int t = 0; t < TPW; ++t) {
+#if DG_ATTN_QREG
+                    s[t][nt] = amfma(kf[ks & 1][nt], qreg[ks][t], s[t][nt]);
+#else
+                    s[t][nt] = amfma(kf[ks & 1][nt], qf[ks & 1][t], s[t][nt]);
+#endif
+                }
         }
         // ---- mask: only blocks that reach past the visible keys, or causal ----
         const bool full = !a.causal && (seg1 ? (row0 >= a.s1) & (row0 + KB <= a.e1) : (row0 + KB <= a.n2));
