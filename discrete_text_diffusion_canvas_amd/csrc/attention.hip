@@ -920,10 +920,19 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int hd) {
     const int qr = pair / a.Hq, h = pair % a.Hq;
     const int64_t rs = (int64_t)a.nq * a.Hq;  // (row, head) pairs per split
     constexpr int MS = MERGE_MAX_SPLITS;
+    const int c = lane * 4;                   // hd <= 256: one 4-dim chunk per lane
+    const bool has = c < hd;
+    // all loads first: every split's (m, l) and partial chunk (a split with no
+    // keys left zeros there; it gets weight 0 and is skipped in the sum)
     float2 ml[MS];
+    float4 po[MS];
 #pragma unroll
-    for (int s = 0; s < MS; ++s)
-        if (s < a.splits) ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * rs + pair) * 2);
+    for (int s = 0; s < MS; ++s) {
+        if (s < a.splits) {
+            ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * rs + pair) * 2);
+            if (has) po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * rs + pair) * hd + c);
+        }
+    }
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < MS; ++s)
@@ -937,29 +946,23 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int hd) {
             L += ml[s].y * wgt[s];
         }
     }
+    if (!has) return;
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    TL* out = reinterpret_cast<TL*>(a.O) + (int64_t)qr * a.Hq * hd + (int64_t)h * hd;
-    for (int c = lane * 4; c < hd; c += 256) {
-        float4 po[MS];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int s = 0; s < MS; ++s)
-            if (s < a.splits && ml[s].x != -INFINITY)
-                po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * rs + pair) * hd + c);
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-        for (int s = 0; s < MS; ++s) {
-            if (s < a.splits && ml[s].x != -INFINITY) {
-                acc.x += po[s].x * wgt[s];
-                acc.y += po[s].y * wgt[s];
-                acc.z += po[s].z * wgt[s];
-                acc.w += po[s].w * wgt[s];
-            }
+    for (int s = 0; s < MS; ++s) {
+        if (s < a.splits && ml[s].x != -INFINITY) {
+            acc.x += po[s].x * wgt[s];
+            acc.y += po[s].y * wgt[s];
+            acc.z += po[s].z * wgt[s];
+            acc.w += po[s].w * wgt[s];
         }
-        from_f(out + c, acc.x * inv);
-        from_f(out + c + 1, acc.y * inv);
-        from_f(out + c + 2, acc.z * inv);
-        from_f(out + c + 3, acc.w * inv);
     }
+    TL* out = reinterpret_cast<TL*>(a.O) + (int64_t)qr * a.Hq * hd + (int64_t)h * hd;
+    from_f(out + c, acc.x * inv);
+    from_f(out + c + 1, acc.y * inv);
+    from_f(out + c + 2, acc.z * inv);
+    from_f(out + c + 3, acc.w * inv);
 }
 
 static void launch_merge_any(const AttnArgs& a, bool bf16, hipStream_t st) {
@@ -1030,7 +1033,7 @@ int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32,
 }
 
 hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st) {
-    if (a.splits > MERGE_MAX_SPLITS || a.hd % 4) return hipErrorInvalidValue;
+    if (a.splits > MERGE_MAX_SPLITS || a.hd % 4 || a.hd > 256) return hipErrorInvalidValue;
     if (attention_uses_grouped(a.Hq, a.Hkv, a.hd, act_f32) && a.ld1 % 64 == 0 && (a.n2 == 0 || a.ld2 % 64 == 0)) {
         if (a.hd == 256) return launch_attn_reg<256>(a, st);
         return launch_attn_reg<128>(a, st);
