@@ -59,16 +59,18 @@
 #ifndef DG_GU_KSPLIT
 #define DG_GU_KSPLIT 2
 #endif
-// LM head tile width (128 or 256; statistics partials stay per 128 rows)
+// LM head tile width (128 or 256; statistics partials stay per 128 rows).
+// 256 halves the activation bytes per weight byte; its registers allow only
+// one stage loaded ahead (measured 421 vs 455 us on 256 x 262144 x 2816)
 #ifndef DG_TILE_BN_LM
-#define DG_TILE_BN_LM 128
+#define DG_TILE_BN_LM 256
 #endif
 // stages the operand registers are loaded ahead (dense/grouped; LM head)
 #ifndef DG_TILE_DEPTH
 #define DG_TILE_DEPTH 2
 #endif
 #ifndef DG_TILE_DEPTH_LM
-#define DG_TILE_DEPTH_LM DG_TILE_DEPTH
+#define DG_TILE_DEPTH_LM (DG_TILE_BN_LM > 128 ? 1 : DG_TILE_DEPTH)
 #endif
 
 
@@ -422,20 +424,39 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
 #pragma unroll
             for (int ks = 0; ks < TBK / 32; ++ks) {
                 const int c = ks * 4 + lg;
-                u16x8 bfr[TN];
+                if constexpr (TN <= 4) {
+                    u16x8 bfr[TN];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int r = wn * WC + j * 16 + lr;
-                    bfr[j] = *reinterpret_cast<const u16x8*>(bs + r * TROWB + tswz(r, c) * 16);
-                }
+                    for (int j = 0; j < TN; ++j) {
+                        const int r = wn * WC + j * 16 + lr;
+                        bfr[j] = *reinterpret_cast<const u16x8*>(bs + r * TROWB + tswz(r, c) * 16);
+                    }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = wm * 64 + i * 16 + lr;
-                    const u16x8 afr = *reinterpret_cast<const u16x8*>(as + r * TROWB + tswz(r, c) * 16);
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = wm * 64 + i * 16 + lr;
+                        const u16x8 afr = *reinterpret_cast<const u16x8*>(as + r * TROWB + tswz(r, c) * 16);
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, afr), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+                        for (int j = 0; j < TN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, afr), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j], 0, 0, 0);
+                    }
+                } else {
+                    // wide wave tiles: the 4 A fragments stay, one B fragment at a time
+                    u16x8 afr[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = wm * 64 + i * 16 + lr;
+                        afr[i] = *reinterpret_cast<const u16x8*>(as + r * TROWB + tswz(r, c) * 16);
+                    }
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int r = wn * WC + j * 16 + lr;
+                        const u16x8 bfr = *reinterpret_cast<const u16x8*>(bs + r * TROWB + tswz(r, c) * 16);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, afr[i]), __builtin_bit_cast(bf16x8, bfr), acc[i][j], 0, 0, 0);
+                    }
                 }
             }
         };
