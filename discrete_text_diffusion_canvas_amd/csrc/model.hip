@@ -88,10 +88,13 @@ struct Work {
 #ifndef DG_SMALL_SLICE_STEPS
 #define DG_SMALL_SLICE_STEPS 16
 #endif
+#ifndef DG_STREAM_MAX_SLICES
+#define DG_STREAM_MAX_SLICES 16
+#endif
 int stream_ksplit(const dg_config& c, int min_steps) {
     const int ks_total = c.d_model / 32;
     int best = 1;
-    for (int s = 2; s <= 16; ++s)
+    for (int s = 2; s <= DG_STREAM_MAX_SLICES; ++s)
         if (ks_total % s == 0 && ks_total / s >= min_steps) best = s;
     return best;
 }
