@@ -21,6 +21,8 @@ Each function cites the passage of the pages it follows. Sources:
   "알아두면 좋은 것" (good to know) and "기술적 특징" (technical features).
 * [GATE] gate.com news post, section on how the model generates without a
   sequential order.
+* [BLOG] charlie27.com digest, section on DiffusionGemma (its remark that
+  outputs are corrected over the iterations).
 
 Where the pages are silent the plainest reading is taken; every such reading
 is listed in the design notes of the repository.

@@ -14,7 +14,11 @@ numbers.
 Readings taken where the pages are silent:
 * bound: the sum of the selected positions' entropies (nats) is <= bound;
   at least one position is selected while candidates remain;
-* candidates are the uncommitted positions; commits are final;
+* candidates are the uncommitted positions; commits are final (commit mode
+  "keep"). [BLOG]'s self-correction remark is read as commit mode
+  "reselect_all": every position is a candidate at every step, a selected
+  position takes a fresh draw, and every unselected position (committed
+  before or not) is re-masked and loses its commit;
 * entropy, argmax and draws use the tempered distribution softmax(L / tau_t)
   with the MASK id excluded;
 * tau_t = tau0 + (tau1 - tau0) * t / (max_steps - 1), indexed by step;
@@ -50,6 +54,7 @@ class SamplerConfig:
     stop_entropy: float = 0.005
     stable_steps: int = 2
     bound_mode: str = "sum"           # "sum" | "sum_minus_max"
+    commit_mode: str = "keep"         # "keep" | "reselect_all"
     mask_id: int = -1                 # excluded vocabulary id (-1: none)
 
 
@@ -261,8 +266,13 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
     H32 = H.astype(np.float32) if H32_override is None else np.asarray(H32_override, np.float32)
     if argmax_override is not None:
         a = np.asarray(argmax_override, dtype=np.int64)
-    cand = ~state.committed
-    sel = eb_select(H32, state.committed, cfg.bound, cfg.bound_mode)
+    if cfg.commit_mode == "keep":
+        cand = ~state.committed
+    elif cfg.commit_mode == "reselect_all":
+        cand = np.ones_like(state.committed)
+    else:
+        raise ValueError("unknown commit mode")
+    sel = eb_select(H32, ~cand, cfg.bound, cfg.bound_mode)
     drawn = {}
     for i in np.nonzero(sel)[0]:
         u = draw_uniform(seed, int(i), t, state.canvas_idx)
@@ -270,8 +280,10 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
         state.tokens[i] = tok
         state.committed[i] = True
         drawn[int(i)] = tok
-    # full re-noise of the unselected candidates ([MC-zh] BP1)
+    # full re-noise of the unselected candidates ([MC-zh] BP1); under
+    # "reselect_all" this also takes back earlier commits left unselected
     state.tokens[cand & ~sel] = cfg.mask_id
+    state.committed[cand & ~sel] = False
     mH = mean_entropy(H32)
     same = bool(np.array_equal(a, state.prev_argmax))
     state.stable = state.stable + 1 if (t > 0 and same) else 1

@@ -380,3 +380,120 @@ def test_committed_tokens_never_change():
         if st.done:
             break
     assert st.done and st.committed.all()
+
+
+# ---------------------------------------------------- reselect-all commits ---
+
+def _one_hot_or_flat(n, V, confident):
+    """Rows that are one-hot (entropy 0) where ``confident``, flat otherwise
+    (entropy log(V - 1), far above the bound), MASK = V - 1 excluded."""
+    L = np.zeros((n, V))
+    for i in np.nonzero(confident)[0]:
+        L[i, :] = -1e30
+        L[i, i % (V - 1)] = 0.0
+    return L
+
+
+@pytest.mark.parametrize("mode", ["sum", "sum_minus_max"])
+def test_reselect_all_step_equals_brute_force_over_every_position(mode):
+    """Under reselect_all the selected set is the brute-force optimum over all
+    positions, whatever was committed before; after the step the committed
+    set is exactly the selected set, selected rows hold this step's draw and
+    all other rows hold MASK."""
+    rng = np.random.default_rng(21)
+    V, mask, seed = 7, 6, 4242
+    checked = 0
+    for trial in range(300):
+        n = int(rng.integers(1, 10))
+        cfg = S.SamplerConfig(mask_id=mask, bound_mode=mode, commit_mode="reselect_all")
+        H = rng.exponential(float(rng.choice([0.01, 0.03, 0.1])), size=n).astype(np.float32)
+        order = sorted(range(n), key=lambda i: (H[i], i))
+        if any(abs(s - 0.1) < 1e-6 for s in np.cumsum([float(H[i]) for i in order])):
+            continue
+        st = S.CanvasState.fresh(n, mask)
+        st.committed[:] = rng.random(n) < 0.5
+        st.tokens[st.committed] = rng.integers(0, mask, size=int(st.committed.sum()))
+        L = rng.normal(size=(n, V)) * 3.0
+        t = int(rng.integers(0, 47))
+        rec = S.sampler_step(st, L, t, cfg, seed, H32_override=H)
+        want = _brute_force(H, np.zeros(n, bool), 0.1, mode)
+        assert set(np.nonzero(rec.selected)[0].tolist()) == want
+        tau = S.temperature(t, cfg)
+        for i in range(n):
+            if rec.selected[i]:
+                u = S.draw_uniform(seed, i, t, 0)
+                assert st.tokens[i] == S.draw_token(L[i], tau, mask, u)
+            elif not rec.finished:
+                assert st.tokens[i] == mask
+        if not rec.finished:
+            assert np.array_equal(st.committed, rec.selected)
+        checked += 1
+    assert checked > 250
+
+
+def test_reselect_all_takes_back_a_commit_that_keep_retains():
+    n, V = 8, 12
+    first = np.zeros(n, bool)
+    first[0] = True
+    second = np.zeros(n, bool)
+    second[5] = True
+    runs = {}
+    for mode in ("keep", "reselect_all"):
+        cfg = S.SamplerConfig(mask_id=V - 1, commit_mode=mode)
+        st = S.CanvasState.fresh(n, V - 1)
+        r0 = S.sampler_step(st, _one_hot_or_flat(n, V, first), 0, cfg, 9)
+        assert np.array_equal(r0.selected, first) and st.tokens[0] == 0
+        r1 = S.sampler_step(st, _one_hot_or_flat(n, V, second), 1, cfg, 9)
+        assert np.array_equal(r1.selected, second) and st.tokens[5] == 5
+        runs[mode] = st
+    assert runs["keep"].committed[0] and runs["keep"].tokens[0] == 0
+    assert not runs["reselect_all"].committed[0] and runs["reselect_all"].tokens[0] == V - 1
+    assert runs["reselect_all"].committed.sum() == 1
+
+
+def test_reselect_all_can_select_a_committed_position_again():
+    """A committed row that stays confident is selected again and redrawn
+    (one-hot rows redraw the same token); a committed row that is not yet
+    confident competes with the rest on entropy."""
+    n, V = 6, 10
+    cfg = S.SamplerConfig(mask_id=V - 1, commit_mode="reselect_all")
+    st = S.CanvasState.fresh(n, V - 1)
+    conf = np.array([1, 0, 0, 0, 0, 0], bool)
+    S.sampler_step(st, _one_hot_or_flat(n, V, conf), 0, cfg, 3)
+    conf2 = np.array([1, 0, 1, 0, 0, 0], bool)
+    rec = S.sampler_step(st, _one_hot_or_flat(n, V, conf2), 1, cfg, 3)
+    assert np.array_equal(rec.selected, conf2)
+    assert st.tokens[0] == 0 and st.tokens[2] == 2
+    assert np.array_equal(st.committed, conf2)
+
+
+def test_reselect_all_finishes_only_when_one_step_selects_everything():
+    n, V = 16, 9
+    cfg = S.SamplerConfig(mask_id=V - 1, commit_mode="reselect_all")
+    st = S.CanvasState.fresh(n, V - 1)
+    half = np.arange(n) < n // 2
+    for t in range(3):       # the same half is confident: never all selected
+        rec = S.sampler_step(st, _one_hot_or_flat(n, V, half), t, cfg, 1)
+        assert not rec.finished and st.committed.sum() == n // 2
+    rec = S.sampler_step(st, _one_hot_or_flat(n, V, np.ones(n, bool)), 3, cfg, 1)
+    assert rec.finished and not rec.stop and st.committed.all()
+    assert np.array_equal(st.tokens, np.arange(n) % (V - 1))
+
+
+def test_first_step_is_the_same_in_both_commit_modes():
+    rng = np.random.default_rng(5)
+    n, V = 40, 64
+    L = rng.normal(size=(n, V)) * rng.uniform(1, 40, size=(n, 1))
+    out = []
+    for mode in ("keep", "reselect_all"):
+        st = S.CanvasState.fresh(n, V - 1)
+        rec = S.sampler_step(st, L, 0, S.SamplerConfig(mask_id=V - 1, commit_mode=mode), 8)
+        out.append((rec.selected.copy(), st.tokens.copy(), st.committed.copy()))
+    for a, b in zip(out[0], out[1]):
+        assert np.array_equal(a, b)
+
+
+def test_unknown_commit_mode_is_rejected():
+    with pytest.raises(ValueError):
+        S.sampler_step(S.CanvasState.fresh(4, 3), np.zeros((4, 4)), 0,
+                       S.SamplerConfig(mask_id=3, commit_mode="nope"), 1)
