@@ -38,6 +38,8 @@ dg_status check_sampler_cfg(const dg_sampler_cfg* s) {
     if (s->stable_steps < 1) return fail(DG_E_INVALID, "stable_steps must be >= 1");
     if (s->bound_mode != DG_BOUND_SUM && s->bound_mode != DG_BOUND_SUM_MINUS_MAX)
         return fail(DG_E_INVALID, "unknown bound_mode");
+    if (s->commit_mode != DG_COMMIT_KEEP && s->commit_mode != DG_COMMIT_RESELECT_ALL)
+        return fail(DG_E_INVALID, "unknown commit_mode");
     return DG_OK;
 }
 
@@ -50,6 +52,7 @@ dg::SamplerParams to_params(const dg_sampler_cfg* s) {
     p.stop_entropy = s->stop_entropy;
     p.stable_steps = s->stable_steps;
     p.bound_mode = s->bound_mode;
+    p.commit_mode = s->commit_mode;
     return p;
 }
 
@@ -133,6 +136,7 @@ dg_sampler_cfg dg_sampler_default(void) {
     c.stop_entropy = 0.005f;
     c.stable_steps = 2;
     c.bound_mode = DG_BOUND_SUM;
+    c.commit_mode = DG_COMMIT_KEEP;
     return c;
 }
 

@@ -16,7 +16,8 @@ struct SamplerParams {
     float bound;
     float stop_entropy;
     int stable_steps;
-    int bound_mode;  // 0: sum <= bound; 1: sum minus the largest <= bound
+    int bound_mode;   // 0: sum <= bound; 1: sum minus the largest <= bound
+    int commit_mode;  // 0: commits are final; 1: every position re-selected each step
 };
 
 // ---- sampler.hip ----

@@ -8,6 +8,11 @@
 // the canvas-mean entropy is below 0.005 and the most probable tokens are
 // unchanged over two consecutive steps.
 //
+// Candidates are the uncommitted positions (commits final) or, in the
+// reselect-all commit mode that reads the charlie27.com digest's remark on
+// self-correction, every position; then an unselected position returns to
+// MASK whether or not it was committed before.
+//
 // Kernels (one denoising step, in launch order):
 //   logit_stats   per (row, vocab split): base-2 entropy partials, raw argmax
 //   merge_rows    per row: entropy (nats), log-sum-exp, argmax
@@ -199,7 +204,8 @@ __global__ void __launch_bounds__(256) merge_rows_kernel(
 // ---------------------------------------------------------------------------
 // EB selection in one workgroup of 1024 threads (n <= 1024). Keys are
 // (entropy bits, position) as 64-bit integers: entropies are >= 0, so their
-// IEEE bit patterns order like the values. Non-candidates sort last. Writes
+// IEEE bit patterns order like the values. Non-candidates (committed rows,
+// unless every row is re-selected) sort last. Writes
 // the selection mask, the selected positions in sorted order (sel_list) and
 // their count (state word 4).
 // ---------------------------------------------------------------------------
@@ -216,7 +222,7 @@ __global__ void __launch_bounds__(1024) eb_select_kernel(
     while (npow < n) npow <<= 1;
     for (int i = tid; i < npow; i += 1024) {
         unsigned long long k = ~0ull;
-        if (i < n && !committed[i])
+        if (i < n && (sp.commit_mode != 0 || !committed[i]))
             k = ((unsigned long long)__float_as_uint(H[i]) << 32) | (unsigned)i;
         key[i] = k;
     }
@@ -449,7 +455,7 @@ __global__ void __launch_bounds__(1024) finalize_kernel(
     const float* __restrict__ H, const int32_t* __restrict__ amax, int n, int mask_id,
     int32_t* __restrict__ state, int step_override, SamplerParams sp,
     int32_t* __restrict__ tokens, uint8_t* __restrict__ committed, int32_t* __restrict__ prev_amax,
-    double* __restrict__ mean_out) {
+    const uint8_t* __restrict__ selected, double* __restrict__ mean_out) {
     if (state && state[0]) return;
     const int tid = threadIdx.x;
     const int t = step_override >= 0 ? step_override : state[1];
@@ -458,9 +464,12 @@ __global__ void __launch_bounds__(1024) finalize_kernel(
     if (tid == 0) { diff = 0; ncom = 0; }
     __syncthreads();
     int d = 0, c = 0;
+    // Committed after this step's draws: under reselect-all only the rows
+    // selected this step; otherwise every row committed so far.
+    const bool reselect = sp.commit_mode != 0;
     for (int i = tid; i < n; i += 1024) {
         d += amax[i] != prev_amax[i];
-        c += committed[i] != 0;
+        c += (reselect ? selected[i] : committed[i]) != 0;
         hs[i] = H[i];
     }
     if (d) atomicAdd(&diff, d);
@@ -478,9 +487,9 @@ __global__ void __launch_bounds__(1024) finalize_kernel(
     const bool stop = stable >= sp.stable_steps && mH < (double)sp.stop_entropy;
     const bool finished = stop || t == sp.max_steps - 1 || ncom == n;
     for (int i = tid; i < n; i += 1024) {
-        if (!committed[i]) {
+        if (!(reselect ? selected[i] : committed[i])) {
             tokens[i] = finished ? amax[i] : mask_id;
-            if (finished) committed[i] = 1;
+            committed[i] = finished ? 1 : 0;
         }
         prev_amax[i] = amax[i];
     }
@@ -557,7 +566,7 @@ hipError_t launch_sampler_tail(const void* logits, int dtype_f32, int64_t ld, in
                                                       canvas_idx, chunk_sum, tokens, committed);
     }
     finalize_kernel<<<1, 1024, 0, st>>>(H, amax, n, mask_id, state, step_override, sp, tokens, committed,
-                                        prev_amax, mean_out);
+                                        prev_amax, selected, mean_out);
     return hipGetLastError();
 }
 

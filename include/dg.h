@@ -55,6 +55,16 @@ typedef int32_t dg_status;
 #define DG_BOUND_SUM 0          /* sum of selected entropies <= bound */
 #define DG_BOUND_SUM_MINUS_MAX 1 /* sum minus the largest selected entropy <= bound */
 
+/* Commit modes. KEEP: candidates are the uncommitted positions and a commit is
+ * final (the model cards' sampling settings, best practice 1: unselected
+ * tokens are re-noised). RESELECT_ALL: the charlie27.com digest's section on
+ * DiffusionGemma says outputs are corrected over the iterations; read as
+ * every position being a candidate at every step, a selected position taking
+ * a fresh draw, and every unselected position, committed before or not,
+ * returning to mask_id with its commit cleared. */
+#define DG_COMMIT_KEEP 0
+#define DG_COMMIT_RESELECT_ALL 1
+
 /* Canvas state words (int32 device array of DG_STATE_WORDS). */
 #define DG_STATE_WORDS 8
 #define DG_ST_DONE 0        /* 1 once the canvas is finished */
@@ -67,7 +77,7 @@ typedef int32_t dg_status;
 
 /* Sampler settings. dg_sampler_default() returns the model card's values
  * (best practice 1): 48 steps, 0.8 -> 0.4, bound 0.1, stop entropy 0.005,
- * 2 stable steps, DG_BOUND_SUM. */
+ * 2 stable steps, DG_BOUND_SUM, DG_COMMIT_KEEP. */
 typedef struct dg_sampler_cfg {
     int32_t max_steps;
     float temp_start;
@@ -76,10 +86,12 @@ typedef struct dg_sampler_cfg {
     float stop_entropy;   /* nats, strict "<" */
     int32_t stable_steps; /* argmax vector unchanged over this many consecutive steps */
     int32_t bound_mode;   /* DG_BOUND_SUM or DG_BOUND_SUM_MINUS_MAX */
+    int32_t commit_mode;  /* DG_COMMIT_KEEP or DG_COMMIT_RESELECT_ALL */
 } dg_sampler_cfg;
 
 /* One canvas. All pointers are device memory of n elements (state: 8).
- * Commits are final: an uncommitted position always holds mask_id.
+ * An uncommitted position always holds mask_id between steps; under
+ * DG_COMMIT_KEEP a commit is final.
  * bias_tok/bias_val (optional, both NULL or both set) add bias_val[i] to the
  * logit of token bias_tok[i] in row i before the temperature. */
 typedef struct dg_canvas {
@@ -98,7 +110,8 @@ typedef struct dg_step_stats {
     float* entropy;        /* nats, of softmax((L + bias) / tau_t), MASK excluded */
     float* lse;            /* log-sum-exp of (L + bias) / tau_t */
     int32_t* argmax;       /* lowest id on ties, MASK excluded */
-    uint8_t* selected;     /* 1 where the EB selection committed this step */
+    uint8_t* selected;     /* 1 where the EB selection committed (or, under
+                              DG_COMMIT_RESELECT_ALL, re-committed) this step */
     double* mean_entropy;  /* [1] canvas-mean entropy used by the stop test */
     void* logits;          /* dg_canvas_step: [n][logits_ld] logits of record (act dtype), written;
                               dg_sampler_step: unused */

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_defaults_are_the_model_cards_values(lib):
     from discrete_text_diffusion_canvas_amd import binding as B
     c = B.sampler_default()
-    assert (c.max_steps, c.stable_steps, c.bound_mode) == (48, 2, 0)
+    assert (c.max_steps, c.stable_steps, c.bound_mode, c.commit_mode) == (48, 2, 0, 0)
     assert abs(c.temp_start - 0.8) < 1e-7 and abs(c.temp_end - 0.4) < 1e-7
     assert abs(c.bound - 0.1) < 1e-8 and abs(c.stop_entropy - 0.005) < 1e-9
 
@@ -77,5 +77,9 @@ def test_sampler_step_validates_before_launch(lib):
     bad.bound_mode = 9
     assert call(cfg=bad) == -1
     assert b"bound_mode" in L.dg_last_error()
+    bad = B.sampler_default()
+    bad.commit_mode = 2
+    assert call(cfg=bad) == -1
+    assert b"commit_mode" in L.dg_last_error()
     half = B.CanvasStruct(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 16, 0)
     assert call(canvas=half) == -1

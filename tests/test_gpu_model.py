@@ -206,16 +206,19 @@ def _tiny_setup(B):
     return cfg, model, kv, ws, W, okv
 
 
-def test_tiny_canvas_steps_decomposed(B):
+@pytest.mark.parametrize("commit_mode", [0, 1])
+def test_tiny_canvas_steps_decomposed(B, commit_mode):
     """Every step of a tiny f32 canvas: logits against the oracle's decoder on
-    the same input state, then the sampler's decisions on the same logits."""
+    the same input state, then the sampler's decisions on the same logits
+    (commits final, or every position re-selected at every step)."""
     cfg, model, kv, ws, W, okv = _tiny_setup(B)
     n = cfg.canvas
     bt, bv = wl.canvas_boost(cfg, 0)
     canvas = B.Canvas(n, cfg.mask_id, 0, "cuda", bt.cuda(), bv.cuda())
     stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=torch.float32)
     scfg = B.sampler_default()
-    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    scfg.commit_mode = commit_mode
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id, commit_mode=["keep", "reselect_all"][commit_mode])
     st = S.CanvasState.fresh(n, cfg.mask_id, 0)
     for t in range(48):
         before = canvas.tokens.cpu().numpy()

@@ -33,7 +33,7 @@ def _biased(L, bias):
 
 
 def run_and_compare(B, logits_fn, n, V, steps, bias=None, seed=SEED, canvas_idx=0,
-                    bound_mode=0, step_ids=None):
+                    bound_mode=0, step_ids=None, commit_mode=0):
     """Run the GPU sampler step by step and check every step against the oracle.
 
     Returns (gpu tokens, number of steps run, list of per-step records)."""
@@ -48,7 +48,9 @@ def run_and_compare(B, logits_fn, n, V, steps, bias=None, seed=SEED, canvas_idx=
     ws = torch.empty(B.sampler_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
     cfg = B.sampler_default()
     cfg.bound_mode = bound_mode
-    ocfg = S.SamplerConfig(mask_id=mask, bound_mode=["sum", "sum_minus_max"][bound_mode])
+    cfg.commit_mode = commit_mode
+    ocfg = S.SamplerConfig(mask_id=mask, bound_mode=["sum", "sum_minus_max"][bound_mode],
+                           commit_mode=["keep", "reselect_all"][commit_mode])
     st = S.CanvasState.fresh(n, mask, canvas_idx)
     recs = []
     ids = step_ids if step_ids is not None else range(steps)
@@ -120,6 +122,28 @@ def test_sum_minus_max_mode(B):
     n, V = 48, 1024
     run_and_compare(B, lambda t: wl.sampler_logits(t + 7, shape=(n, V), max_peak=30.0, device="cuda"),
                     n, V, 48, bound_mode=1)
+
+
+@pytest.mark.parametrize("bound_mode", [0, 1])
+def test_reselect_all_commit_mode(B, bound_mode):
+    n, V = 48, 1024
+    toks, steps, recs = run_and_compare(
+        B, lambda t: wl.sampler_logits(t + 7, shape=(n, V), max_peak=30.0, device="cuda"),
+        n, V, 48, bound_mode=bound_mode, commit_mode=B.DG_COMMIT_RESELECT_ALL)
+    # earlier commits were taken back on the device, not just never made
+    taken_back = sum(int((recs[k].selected & ~recs[k + 1].selected).sum())
+                     for k in range(len(recs) - 2))
+    assert taken_back > 0
+    assert not np.any(toks == V - 1)
+
+
+def test_reselect_all_on_the_full_vocabulary(B):
+    n, V = wl.SAMPLER_ONLY_SHAPE
+    buf = torch.empty((n, V), dtype=torch.bfloat16, device="cuda")
+
+    def logits(t):
+        return wl.sampler_logits(t, device="cuda", out=buf)
+    run_and_compare(B, logits, n, V, 4, commit_mode=B.DG_COMMIT_RESELECT_ALL)
 
 
 def test_full_vocab_256_rows_selected_steps(B):
