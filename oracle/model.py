@@ -319,3 +319,88 @@ def encoder_append(W: Weights, kv: KVCache, tokens, keep_layers=True) -> None:
         X = X + y
         if not keep_layers:
             W.release(l)
+
+
+def _visible_rows(out: np.ndarray, n: int, layer: int, cfg) -> np.ndarray:
+    """Mask over rows 0..n-1 of the keys that queries ``out`` see on ``layer``
+    of the causal encoder: every q <= r on a global layer, r - q < window on
+    a local one."""
+    mask = np.zeros(n, dtype=bool)
+    if out.size == 0:
+        return mask
+    if is_global_layer(layer, cfg.global_every):
+        mask[: int(out.max()) + 1] = True
+        return mask
+    edge = np.zeros(n + 1, dtype=np.int64)
+    np.add.at(edge, np.maximum(out - cfg.window + 1, 0), 1)
+    np.add.at(edge, out + 1, -1)
+    return np.cumsum(edge[:n]) > 0
+
+
+def encoder_kv_rows(W: Weights, tokens, rows, n_layers: int | None = None, block: int = 256,
+                    trace: dict | None = None):
+    """Keys and values that ``encoder_append`` of all of ``tokens`` into an
+    empty cache writes at cache rows ``rows``, for layers 0 .. n_layers-1,
+    computed over only the rows they depend on ([MC-zh] overview: the
+    encoder's cache of the prompt; causal, windowed on local layers).
+
+    Row r's input to layer l+1 is its input to layer l plus layer l's
+    attention output and MoE at r; the attention at r reads layer l's keys
+    and values at the rows r sees, which depend on those rows' inputs to
+    layer l. Going from the top layer down gives the rows whose input each
+    layer needs; going back up computes them with encoder_append's steps.
+    Queries are taken in blocks of ``block`` rows; each query still sees
+    exactly its own visible keys. Returns (K, V), lists over layers of
+    [Hkv][len(rows)][hd] for the sorted distinct rows. ``trace`` (optional)
+    receives "router": per layer below the last, the router logits at the
+    sorted rows.
+    """
+    cfg = W.cfg
+    L = cfg.n_layers if n_layers is None else n_layers
+    tokens = np.asarray(tokens, dtype=np.int64)
+    n = tokens.shape[0]
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    if rows.size == 0 or rows[0] < 0 or rows[-1] >= n:
+        raise ValueError("rows must be non-empty and inside the token range")
+    need = [None] * L
+    need[L - 1] = rows
+    for l in range(L - 2, -1, -1):
+        mask = _visible_rows(need[l + 1], n, l, cfg)
+        mask[need[l + 1]] = True
+        mask[rows] = True
+        need[l] = np.nonzero(mask)[0]
+    Hq, hd = cfg.n_q_heads, cfg.head_dim
+    cur = need[0]
+    X = W.E[tokens[cur]].copy()
+    K_out, V_out, routers = [], [], []
+    for l in range(L):
+        Wl = W.layer(l)
+        a = rmsnorm(X, Wl["attn_norm"], cfg.norm_eps)
+        q, k, v = qkv(a, Wl, cfg, cur)
+        at = np.searchsorted(cur, rows)
+        K_out.append(k[at].transpose(1, 0, 2).copy())
+        V_out.append(v[at].transpose(1, 0, 2).copy())
+        if l == L - 1:
+            break
+        nxt = need[l + 1]
+        qi = np.searchsorted(cur, nxt)
+        local = not is_global_layer(l, cfg.global_every)
+        o = np.empty((nxt.size, Hq, hd))
+        for b0 in range(0, nxt.size, block):
+            r = nxt[b0: b0 + block]
+            lo = int(r.min()) - cfg.window + 1 if local else 0
+            kidx = np.nonzero((cur >= lo) & (cur <= int(r.max())))[0]
+            kp = cur[kidx]
+            vis = kp[None, :] <= r[:, None]
+            if local:
+                vis &= (r[:, None] - kp[None, :]) < cfg.window
+            o[b0: b0 + block] = attend(q[qi[b0: b0 + block]], k[kidx], v[kidx], vis)
+        Xn = X[qi] + o.reshape(nxt.size, -1) @ Wl["wo"].T
+        b = rmsnorm(Xn, Wl["moe_norm"], cfg.norm_eps)
+        y, _, _, rl = moe(b, Wl, cfg.top_k)
+        routers.append(rl[np.searchsorted(nxt, rows)])
+        X = Xn + y
+        cur = nxt
+    if trace is not None:
+        trace["router"] = routers
+    return K_out, V_out

@@ -230,6 +230,40 @@ def test_encoder_is_causal_and_windowed():
     assert not np.allclose(kv1.K[1][:, 13], kv2.K[1][:, 13])         # 13 - 8 < 6
 
 
+@pytest.mark.parametrize("global_every,n_layers", [(0, 3), (2, 4), (3, 4), (1, 2)])
+def test_encoder_rows_equal_the_full_prefill(global_every, n_layers):
+    """K/V at chosen rows from the dependency-restricted encoder equal the
+    full causal prefill's cache at those rows, on every layer: local and
+    global layers, rows at the start, inside, across window edges and last."""
+    cfg = SMALL.replace(n_layers=n_layers, global_every=global_every, window=5)
+    W = _tiny_model(cfg)
+    n = 61
+    toks = wl.prefix_tokens(cfg, n).numpy()
+    kv = M.KVCache.empty(cfg)
+    M.encoder_append(W, kv, toks)
+    rng = np.random.default_rng(global_every * 10 + n_layers)
+    for rows in ([0], [n - 1], [4, 5, 6], sorted(rng.choice(n, 7, replace=False).tolist()),
+                 list(range(n))):
+        tr = {}
+        K, V = M.encoder_kv_rows(W, toks, rows, block=8, trace=tr)
+        assert len(K) == n_layers and len(tr["router"]) == n_layers - 1
+        for l in range(n_layers):
+            assert K[l].shape == (cfg.n_kv_heads, len(rows), cfg.head_dim)
+            assert np.allclose(K[l], kv.K[l][:, rows], rtol=0, atol=1e-12), (rows, l)
+            assert np.allclose(V[l], kv.V[l][:, rows], rtol=0, atol=1e-12), (rows, l)
+    # a prefix of the layers gives the same values for those layers
+    K2, _ = M.encoder_kv_rows(W, toks, [30, 60], n_layers=2)
+    assert np.allclose(K2[1], kv.K[1][:, [30, 60]], rtol=0, atol=1e-12)
+
+
+def test_encoder_rows_reject_rows_outside_the_tokens():
+    W = _tiny_model(SMALL)
+    toks = wl.prefix_tokens(SMALL, 10).numpy()
+    for rows in ([], [10], [-1]):
+        with pytest.raises(ValueError):
+            M.encoder_kv_rows(W, toks, rows)
+
+
 def test_decoder_is_bidirectional_and_local_window_hides_old_prefix():
     cfg = SMALL.replace(global_every=0)
     W = _tiny_model(cfg)
