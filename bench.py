@@ -21,6 +21,10 @@ Workloads (synthetic, seeded; random-init weights ~N(0, 0.02)):
   one_layer the same widths with 1 layer, 4096-token prompt
   sampler   EB sampler only on bf16 logits [256][262144]
   tiny      2 layers, d=256, fp32, vocab 4096, canvas 32, 128-token prompt
+  prefill   encoder prefill of a 131072-token prompt (--prefill-tokens) into
+            an empty cache through the 30-layer stack with e4m3 expert and
+            attention weights (the long-context geometry); a step is one
+            whole prefill, value = prompt tokens/s
 """
 from __future__ import annotations
 
@@ -262,6 +266,139 @@ def cpu_model_step(cfg, handles, torch, B, plen):
 
 
 # --------------------------------------------------------------------------
+# long-prompt encoder prefill
+# --------------------------------------------------------------------------
+
+PREFILL_CHUNK = 4096
+
+
+def _prefill_algorithmic(cfg, n, name):
+    """Algorithmic flops and HBM bytes of all launches of kernel ``name`` in
+    one causal prefill of n tokens in PREFILL_CHUNK-row chunks. Attention
+    counts only the keys each query sees (p + 1 on a global layer, at most the
+    window on a local one); the last layer computes only its projections."""
+    d, F, k = cfg.d_model, cfg.ffn_hidden, cfg.top_k
+    Hq, Hkv, hd, L = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_layers
+    wb = 1 if cfg.weight_dtype == "fp8" else 2
+    ab = 2
+    n_glob = sum(1 for l in range(L - 1) if cfg.global_every > 0 and l % cfg.global_every == cfg.global_every - 1)
+    n_loc = L - 1 - n_glob
+    fl = nb = 0.0
+    for P in range(0, n, PREFILL_CHUNK):
+        cn = min(PREFILL_CHUNK, n - P)
+        if name == "qkv_proj":
+            fl += L * 2.0 * cn * (Hq + 2 * Hkv) * hd * d
+            nb += L * ((Hq + 2 * Hkv) * hd * d * wb + cn * d * ab + cn * (Hq + 2 * Hkv) * hd * ab)
+        elif name == "attention":
+            keys_glob = (P + 1 + P + cn) * cn / 2.0                     # sum of p + 1 over the chunk
+            w = cfg.window
+            keys_loc = sum(min(p + 1, w) for p in range(P, P + cn))
+            fl += 4.0 * Hq * hd * (n_glob * keys_glob + n_loc * keys_loc)
+            span_loc = P + cn - max(0, P - w + 1)                      # keys a local chunk reads
+            nb += (n_glob * (P + cn) + n_loc * span_loc) * Hkv * hd * 2 * ab + (L - 1) * 2 * cn * Hq * hd * ab
+        elif name == "o_proj":
+            fl += (L - 1) * 2.0 * cn * d * Hq * hd
+            nb += (L - 1) * (d * Hq * hd * wb + cn * Hq * hd * ab + 2 * cn * d * 4)
+        elif name == "expert_gate_up":
+            fl += (L - 1) * 2.0 * cn * (k + 1) * 2 * F * d
+            nb += (L - 1) * ((cfg.n_experts + 1) * 2 * F * d * wb + cn * d * ab + cn * (k + 1) * F * ab)
+        elif name == "expert_down":
+            fl += (L - 1) * 2.0 * cn * (k + 1) * F * d
+            nb += (L - 1) * ((cfg.n_experts + 1) * d * F * wb + cn * (k + 1) * F * ab + cn * (k + 1) * d * 4)
+    return nb, fl
+
+
+def bench_prefill(args, torch, B):
+    from synth import workloads as wl
+    cfg = wl.STACK30_FP8
+    n = args.prefill_tokens
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    embed = wl.embedding(cfg, device=dev)
+    fnorm = wl.final_norm(cfg, device=dev)
+    layers = [wl.layer_weights(cfg, l, device=dev) for l in range(cfg.n_layers)]
+    model = B.Model(cfg, embed, fnorm, layers)
+    torch.cuda.synchronize()
+    t_weights = time.perf_counter() - t0
+    kv = B.KVCache(model, n)
+    ws = model.workspace(PREFILL_CHUNK)
+    toks = wl.prefix_tokens(cfg, n).to(dev)
+
+    def run(K):
+        for _ in range(K):
+            kv.length = 0
+            B.prefill_append(model, kv, toks, ws)
+            print(f"# prefill of {n} tokens enqueued", file=sys.stderr, flush=True)
+
+    run(args.warmup)
+    ms = _sync_ms(lambda: run(args.steps), torch)
+    kernels = {}
+    for name, target in (("attention", B.TIME_ATTENTION), ("expert_gate_up", B.TIME_EXPERT_GATE_UP),
+                         ("expert_down", B.TIME_EXPERT_DOWN), ("qkv_proj", B.TIME_QKV),
+                         ("o_proj", B.TIME_O_PROJ)):
+        B.timing_enable(target)
+        run(1)
+        torch.cuda.synchronize()
+        tot_ms, launches = B.timing_read()
+        B.timing_enable(B.TIME_OFF)
+        nbytes, flops = _prefill_algorithmic(cfg, n, name)
+        kernels[name] = {"launches": launches, "ms_per_prefill": round(tot_ms, 2),
+                         "us_per_launch": round(tot_ms / max(launches, 1) * 1e3, 2),
+                         "achieved_tflops": round(flops / (tot_ms * 1e-3) / 1e12, 1),
+                         "achieved_gbs": round(nbytes / (tot_ms * 1e-3) / 1e9, 1),
+                         "flops_per_prefill": flops}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_prefill"])
+    kd = kernels[dom]
+    res = {
+        "ms_per_step": ms / args.steps,
+        "committed_tokens": 0,
+        "tokens_per_step": n,
+        "roofline": {"bound": "mfma", "achieved": kd["achieved_tflops"], "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": dom, "us_per_launch": kd["us_per_launch"],
+                     "algorithmic_flops_per_launch": round(kd["flops_per_prefill"] / max(kd["launches"], 1))},
+        "kernels": {k: {kk: vv for kk, vv in v.items() if kk != "flops_per_prefill"} for k, v in kernels.items()},
+        "extra": {"weights_setup_s": round(t_weights, 1), "kv_len_end": kv.length, "chunk_rows": PREFILL_CHUNK},
+        "config": {"workload": f"{cfg.name}_prefill{n}", "layers": cfg.n_layers, "d_model": cfg.d_model,
+                   "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
+                   "experts": f"{cfg.n_experts} top-{cfg.top_k} + 1 shared, F={cfg.ffn_hidden}",
+                   "weights": "e4m3 experts and projections, bf16 scales; MFMA in bf16",
+                   "window": cfg.window, "global_every": cfg.global_every, "prompt": n, "batch": 1},
+        "dtype": "bf16",
+        "metric": "encoder prefill tokens/s, long prompt, batch 1; % MFMA peak",
+        "unit": "prefill tokens/s",
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_prefill(cfg, model, n)
+    return res
+
+
+def cpu_prefill(cfg, model, n):
+    """The oracle's causal encoder on a 1024-token prompt: layer 0 (local)
+    complete and layer 1's projections, float64 numpy, scaled to the stack's
+    layers. It leaves out the long-context attention of the global layers,
+    which would only lower the oracle's rate."""
+    from oracle import model as M
+    from synth import workloads as wl
+    cfg2 = cfg.replace(n_layers=2)
+    W = M.Weights(cfg2, model.embed.cpu(), model.final_norm.cpu(),
+                  lambda l: {k: v.cpu() for k, v in model.layers[l].items()})
+    W.layer(0)
+    W.layer(1)
+    m = 1024
+    toks = wl.prefix_tokens(cfg, m).numpy()
+    kv = M.KVCache.empty(cfg2)
+    t0 = time.perf_counter()
+    M.encoder_append(W, kv, toks)
+    t = time.perf_counter() - t0
+    per_token_s = t / m * (cfg.n_layers - 1)
+    return {"value": round(1.0 / per_token_s, 3), "unit": "prefill tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": (f"encoder over {m} tokens: layer 0 complete plus layer 1 projections ({t:.2f} s), "
+                       f"float64 numpy, scaled by {cfg.n_layers - 1} layers; global-layer long-context "
+                       f"attention not included")}
+
+
+# --------------------------------------------------------------------------
 # sampler-only workload
 # --------------------------------------------------------------------------
 
@@ -331,13 +468,18 @@ def bench_sampler(args, torch, B):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=96)
-    ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny"])
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 96; prefill: 2)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 4; prefill: 1)")
+    ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny", "prefill"])
+    ap.add_argument("--prefill-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="finish with device copies of BYTES bytes (scale for HBM traffic counters)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 2 if args.workload == "prefill" else 96
+    if args.warmup is None:
+        args.warmup = 1 if args.workload == "prefill" else 4
     if args.gpus != 1:
         print("bench.py measures one GPU: the denoising step here is built for a single MI355X "
               "and has no multi-GPU path", file=sys.stderr)
@@ -346,20 +488,22 @@ def main():
     from discrete_text_diffusion_canvas_amd import binding as B
     if args.workload == "sampler":
         res = bench_sampler(args, torch, B)
+    elif args.workload == "prefill":
+        res = bench_prefill(args, torch, B)
     else:
         res = bench_stack(args, torch, B, args.workload)
     ms = res.pop("ms_per_step")
     committed = res.pop("committed_tokens")
     total_s = ms * args.steps / 1e3
+    per_step = res.pop("tokens_per_step", 1)
     out = {
-        "metric": METRIC,
-        "value": round(1e3 / ms, 3),
-        "unit": "denoise steps/s",
+        "metric": res.pop("metric", METRIC),
+        "value": round(per_step * 1e3 / ms, 3),
+        "unit": res.pop("unit", "denoise steps/s"),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
-        "committed_tokens_per_s": round(committed / total_s, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -368,6 +512,9 @@ def main():
         "config": res.pop("config"),
         "roofline": res.pop("roofline"),
     }
+    if args.workload != "prefill":
+        out = dict(list(out.items())[:7] + [("committed_tokens_per_s", round(committed / total_s, 2))]
+                   + list(out.items())[7:])
     for k in ("cpu_baseline", "kernels", "extra"):
         if k in res:
             out[k] = res.pop(k)

@@ -604,12 +604,24 @@ hipError_t launch_router_topk(const float* r, int nparts, const float* bias, int
     return hipGetLastError();
 }
 
+static size_t hist_permute_lds(int n, int k, int E) {
+    const size_t total = (size_t)n * k, nch = (total + 63) / 64;
+    // off, tot (int32); cbase (u16 [nch][E]); esid (u16 [total]); ccnt (u8 [nch][E]); rank (u8 [total])
+    return (size_t)(2 * E + 2) * 4 + nch * E * 2 + total * 2 + nch * E + total;
+}
+
+int hist_permute_max_rows(int k, int E) {
+    if (k < 1 || E < 1 || E > 65535) return 0;
+    int best = 0;
+    for (int n = 1; (size_t)n * k <= 65535 && hist_permute_lds(n, k, E) <= 160 * 1024; ++n) best = n;
+    return best;
+}
+
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
                                int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hitB, int32_t* hitB_mb,
                                int big_min, int32_t* hit_out, const int32_t* state, hipStream_t st) {
-    const size_t total = (size_t)n * k, nch = (total + 63) / 64;
-    // off, tot (int32); cbase (u16 [nch][E]); esid (u16 [total]); ccnt (u8 [nch][E]); rank (u8 [total])
-    const size_t lds = (size_t)(2 * E + 2) * 4 + nch * E * 2 + total * 2 + nch * E + total;
+    const size_t total = (size_t)n * k;
+    const size_t lds = hist_permute_lds(n, k, E);
     if (lds > 160 * 1024 || E > 65535 || total > 65535) return hipErrorInvalidValue;
     static bool attr = false;
     if (!attr) {

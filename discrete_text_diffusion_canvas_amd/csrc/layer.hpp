@@ -23,6 +23,9 @@ hipError_t launch_rope_scatter(const void* qkv, const float* part, int nparts, i
                                int v_zero_to, const int32_t* state, hipStream_t st);
 hipError_t launch_router_topk(const float* r, int nparts, const float* bias, int n, int E, int k, int32_t* ids,
                               float* gates, const int32_t* state, hipStream_t st);
+// Largest row count n for which launch_hist_permute can permute n x k
+// (row, slot) pairs over E experts (its one-workgroup LDS bound).
+int hist_permute_max_rows(int k, int E);
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
                                int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hitB, int32_t* hitB_mb,
                                int big_min, int32_t* hit_out, const int32_t* state, hipStream_t st);

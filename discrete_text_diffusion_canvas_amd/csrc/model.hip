@@ -217,7 +217,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
     }
     DG_TRY(dg::launch_router_topk(w.rlog, router_ksplit(c), L.router_bias, n, E, k, w.ids, w.gates, state, st),
            "router topk");
-    // groups of more than 64 rows go to the LDS-staged GEMM (bf16 only)
+    // groups of more than 64 rows go to the LDS-staged GEMM (bf16 activations)
     dg::GemmArgs gu = gargs(), dn = gargs();
     gu.A = w.A; gu.lda = d; gu.a_rows = w.perm;
     gu.W = L.w_gate; gu.W2 = L.w_up; gu.ldw = d; gu.w_group_stride = (int64_t)F * d;
@@ -343,7 +343,9 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         g.A = w.A; g.lda = d; g.W = L.wqkv; g.ldw = d; g.w_scale = (const uint16_t*)L.wqkv_scale;
         g.M = n; g.N = (Hq + 2 * Hkv) * hd; g.K = d; g.C = w.QKV; g.ldc = g.N;
         int qkv_parts = 1;
+        int slot = timing_begin(st, DG_TIME_QKV);
         DG_TRY(dense_gemm(g, w, f32, fp8, f32 ? dg::EPI_STORE_F32 : dg::EPI_STORE_BF16, st, &qkv_parts), "qkv gemm");
+        timing_end(slot, st);
         DG_TRY(dg::launch_rope_scatter(w.QKV, w.gemm_part, qkv_parts, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0,
                                        kv->k[l], kv->v[l], kv->capacity, P, 0, nullptr, st),
                "rope");
@@ -357,11 +359,15 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
         a.O = w.O; a.part_o = w.part_o; a.part_ml = w.part_ml;
         int64_t span = a.window > 0 ? std::min<int64_t>(P + n, (int64_t)a.window + 64) : P + n;
         a.splits = attn_splits(c, n, span);
+        slot = timing_begin(st, DG_TIME_ATTENTION);
         DG_TRY(dg::launch_attention(a, f32, st), "attention");
+        timing_end(slot, st);
         dg::GemmArgs go = gargs();
         go.A = w.O; go.lda = Hq * hd; go.W = L.wo; go.ldw = Hq * hd; go.w_scale = (const uint16_t*)L.wo_scale;
         go.M = n; go.N = d; go.K = Hq * hd; go.X = w.X; go.ldx = d;
+        slot = timing_begin(st, DG_TIME_O_PROJ);
         DG_TRY(dense_gemm(go, w, f32, fp8, dg::EPI_RESIDUAL, st), "o gemm");
+        timing_end(slot, st);
         // the next layer's attention norm rides on this layer's combine
         if (dg_status s = moe_block(m, l, w, n, m->layers[l + 1].attn_norm, nullptr, st)) return s;
     }
@@ -444,6 +450,8 @@ dg_status dg_model_create(const dg_config* c, const dg_weights* w, dg_model** ou
     if (c->vocab < 8 || c->vocab % 8) return fail(DG_E_SHAPE, "vocab must be a multiple of 8");
     if (c->mask_id < 0 || c->mask_id >= c->vocab) return fail(DG_E_INVALID, "mask_id outside the vocabulary");
     if (c->max_canvas < 1 || c->max_canvas > 1024) return fail(DG_E_SHAPE, "max_canvas outside 1..1024");
+    if (dg::hist_permute_max_rows(c->top_k, c->n_experts) < c->max_canvas)
+        return fail(DG_E_UNSUPPORTED, "max_canvas x top_k routed rows exceed the expert permutation's capacity");
     if (c->window < 0 || c->global_every < 0) return fail(DG_E_INVALID, "window/global_every must be >= 0");
     if (!(c->rope_base > 1.f) || !(c->norm_eps >= 0.f)) return fail(DG_E_INVALID, "rope_base/norm_eps");
     if (!w->embed || !w->final_norm || !w->layers) return fail(DG_E_INVALID, "weight pointer is NULL");
@@ -534,7 +542,11 @@ dg_status dg_prefill_append(const dg_model* m, dg_kv* kv, const int32_t* tokens,
                                                 (long long)(kv->len + n));
     if (n == 0) return DG_OK;
     if (!ws) return fail(DG_E_INVALID, "workspace is NULL");
-    const int T = rows_fitting(m, ws_bytes, std::min(n, 4096));
+    // chunk rows: what the workspace holds, at most 4096 and at most what the
+    // expert permutation takes in one pass (a multiple of 256 when larger)
+    int cap = std::min(dg::hist_permute_max_rows(m->cfg.top_k, m->cfg.n_experts), 4096);
+    if (cap >= 256) cap -= cap % 256;
+    const int T = rows_fitting(m, ws_bytes, std::min(n, cap));
     if (T < 1) return fail(DG_E_CAPACITY, "workspace too small for one row");
     Work w = carve(m, ws, T);
     hipStream_t st = (hipStream_t)stream;

@@ -146,8 +146,10 @@ dg_status dg_canvas_reset(dg_canvas* canvas, int32_t mask_id, void* stream);
  *   DG_TIME_EXPERT_GATE_UP   the grouped expert gate/up GEMM with SwiGLU;
  *   DG_TIME_EXPERT_DOWN      the grouped expert down GEMM;
  *   DG_TIME_QKV              the QKV projection;
- *   DG_TIME_ATTENTION        the canvas + prefix attention kernel;
+ *   DG_TIME_ATTENTION        the attention kernel (canvas + prefix in the
+ *                            decoder, causal in dg_prefill_append);
  *   DG_TIME_O_PROJ           the output projection.
+ * The expert and projection targets cover the decoder and the encoder.
  * DG_TIME_OFF (0) stops recording. dg_timing_read synchronises on the
  * recorded events, returns their summed elapsed milliseconds and count, and
  * clears the list. At most 8192 pairs are kept; later launches are not
@@ -214,7 +216,8 @@ typedef struct dg_config {
     int32_t ffn_hidden;   /* SwiGLU hidden width of every expert */
     int32_t vocab;
     int32_t mask_id;      /* placeholder token; excluded from the output distribution */
-    int32_t max_canvas;   /* largest canvas (<= 1024) */
+    int32_t max_canvas;   /* largest canvas (<= 1024; max_canvas x top_k routed rows must fit the
+                             expert permutation, else DG_E_UNSUPPORTED) */
     int32_t window;
     int32_t global_every;
     int32_t weight_dtype; /* DG_F32, DG_BF16 or DG_FP8_E4M3: projection and expert matrices */
@@ -289,7 +292,9 @@ size_t dg_workspace_bytes(const dg_model* m, int32_t max_rows);
  * kv->len + n - 1) through the layers with causal attention (a per-query
  * sliding window on local layers) and appends every layer's rotated K and V
  * at rows kv->len ..; the last layer's attention output and MoE are skipped.
- * Tokens are processed in chunks of the workspace's max_rows. Updates
+ * Tokens are processed in chunks of the workspace's max_rows, at most 4096
+ * and at most the rows whose top_k routed slots the expert permutation holds
+ * in one workgroup (2048 for 128 experts, top-8). Updates
  * kv->len on the host when enqueued. DG_E_CAPACITY if len + n > capacity.
  * Token ids outside [0, vocab) are not checked on the host (they are device
  * data); the embedding reads them as zero rows.

@@ -83,3 +83,31 @@ def test_sampler_step_validates_before_launch(lib):
     assert b"commit_mode" in L.dg_last_error()
     half = B.CanvasStruct(0x1000, 0x1000, 0x1000, 0x1000, 0x1000, None, 16, 0)
     assert call(canvas=half) == -1
+
+
+def test_model_create_rejects_routing_beyond_the_permutation(lib):
+    """128 experts top-8 fit a 1024-row canvas; 512 experts top-16 do not
+    (the one-workgroup expert permutation's LDS bound). Validation runs on
+    the host before any weight is read, so aligned placeholder pointers do."""
+    from discrete_text_diffusion_canvas_amd import binding as B
+    L = B.lib
+    fake = 0x1000
+    layer = B.LayerStruct(*([fake] * 9 + [None] * 5))
+    arr = (B.LayerStruct * 1)(layer)
+    w = B.WeightsStruct(fake, fake, arr)
+
+    def create(E, k, canvas):
+        cs = B.ConfigStruct(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=E,
+                            top_k=k, ffn_hidden=64, vocab=4096, mask_id=4095, max_canvas=canvas, window=128,
+                            global_every=0, weight_dtype=B.DG_BF16, act_dtype=B.DG_BF16, rope_base=1e4,
+                            norm_eps=1e-6)
+        h = C.c_void_p()
+        code = L.dg_model_create(C.byref(cs), C.byref(w), C.byref(h))
+        if code == 0:
+            L.dg_model_destroy(h)
+        return code
+
+    assert create(128, 8, 1024) == 0
+    assert create(512, 16, 1024) == -5
+    assert b"permutation" in L.dg_last_error()
+    assert create(512, 16, 64) == 0
