@@ -143,9 +143,9 @@ __device__ __forceinline__ void stream_kloop(f32x4 (&acc)[STM][STN], const TL* c
 // multiple of 8) they run on one XCD. Grouped mode reads the hit groups from
 // g.hit ([0] = count, then group ids) and the largest m-block count from
 // g.hit_mb; non-grouped mode has one group of g.M rows. With g.ksplit > 1
-// (non-grouped plain f32 store, or grouped SwiGLU without weight scales) the
-// K range is cut into g.ksplit slices, one more item dimension, and slice s
-// leaves its raw sums in g.part[s][row][n] (SwiGLU: gate of hidden unit f at
+// (non-grouped plain f32 store, or grouped SwiGLU) the K range is cut into
+// g.ksplit slices, one more item dimension, and slice s leaves its sums
+// (times the e4m3 row scales, if any) in g.part[s][row][n] (SwiGLU: gate of hidden unit f at
 // n = f, up at n = N/2 + f; rows are slots, g.M of them); the consumer adds
 // the slices in order.
 template <typename TL, int WK, int EPI>
@@ -293,7 +293,7 @@ static hipError_t launch_stream_t(const GemmArgs& g, int groups, int max_rows, h
     const int units = G * n_tiles;
     const int mb_max = std::max(1, (max_rows + SBM - 1) / SBM);
     const int ks = g.ksplit > 1 ? g.ksplit : 1;
-    const bool split_ok = EPI == EPI_STORE_F32 ? !g.group_offsets : EPI == EPI_SWIGLU && g.group_offsets && !g.w_scale;
+    const bool split_ok = EPI == EPI_STORE_F32 ? !g.group_offsets : EPI == EPI_SWIGLU && g.group_offsets;
     if (ks > 1 && (!split_ok || !g.part || (g.K / 32) % ks)) return hipErrorInvalidValue;
     const int64_t items = (int64_t)((units * ks + 7) / 8) * 8 * mb_max;  // upper bound
     // persistent grid: a multiple of 8 (one slot per XCD), at most 4 per CU

@@ -26,11 +26,19 @@
 //     coalesced stores: SwiGLU (BN/2 gate + BN/2 up columns of the same
 //     hidden units) to bf16, or a plain f32 store.
 //
+// e4m3 weights (WF8): a lane loads 8 bytes (8 weights) per 16-byte LDS piece
+// and widens them to bf16 before the LDS store (every e4m3 value is exact in
+// bf16), so the MFMAs and the LDS layout are those of the bf16 path; the
+// per-output-row scale multiplies the f32 accumulators after the K loop,
+// before any epilogue or partial store.
+//
 // Work items (group from the big-group list, m-block, n-tile) are walked by a
 // persistent grid; the m-blocks of one (group, n-tile) get ids 8 apart so they
 // run on one XCD and the repeated weight reads hit its L2.
 #include "common.hpp"
 #include "gemm.hpp"
+
+#include <type_traits>
 
 // build-time tunables: weight rows per workgroup of the gate/up and down GEMMs
 #ifndef DG_TILE_BN_GU
@@ -72,6 +80,11 @@
 #ifndef DG_TILE_DEPTH_LM
 #define DG_TILE_DEPTH_LM (DG_TILE_BN_LM > 128 ? 1 : DG_TILE_DEPTH)
 #endif
+// e4m3 -> bf16 widening of the weight tiles: 1 = the gfx950 scaled pack
+// conversion at scale 1, 0 = bit manipulation
+#ifndef DG_TILE_F8_HWCVT
+#define DG_TILE_F8_HWCVT 1
+#endif
 
 
 namespace dg {
@@ -89,6 +102,25 @@ __device__ __forceinline__ int tswz(int r, int c) { return c ^ ((r >> 1) & 7); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float tsilu(float x) { return x / (1.f + __expf(-x)); }
+
+// 8 e4m3 codes (byte j of the pair = weight j) -> 8 bf16, exact
+__device__ __forceinline__ u32x4 widen8_e4m3(u32x2 v) {
+    u32x4 o;
+#if DG_TILE_F8_HWCVT
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        o[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, false));
+        o[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, true));
+    }
+#else
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t a = (v[j >> 1] >> (16 * (j & 1))) & 0xffu, b = (v[j >> 1] >> (16 * (j & 1) + 8)) & 0xffu;
+        o[j] = (__float_as_uint(e4m3_to_f32(a)) >> 16) | (__float_as_uint(e4m3_to_f32(b)) & 0xffff0000u);
+    }
+#endif
+    return o;
+}
 
 // waves of a BM x BN workgroup: BM/64 row blocks; 256 rows: BN/64 (at most
 // 2) column blocks; 64 rows: 4 column blocks
@@ -310,7 +342,7 @@ __global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(g.C) + (int64_t)slot * g.ldc + f) = o;
 }
 
-template <int BN, int EPI, int DEPTH, int BM>
+template <int BN, int EPI, int DEPTH, int BM, bool WF8>
 __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(GemmArgs g, int n_tiles) {
     if (g.state && g.state[0]) return;
     static_assert(BM == 64 || BM == 256, "m-blocks of 64 or 256 rows");
@@ -371,35 +403,42 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
             const int src = g.a_rows ? g.a_rows[ar] : ar;
             asrc[j] = Ab + (int64_t)src * g.lda + 8 * tswz(r, pos);
         }
-        const uint16_t* bsrc[B_INSTR];
-#pragma unroll
-        for (int j = 0; j < B_INSTR; ++j) {
-            const int r = 8 * (wave * B_INSTR + j) + (lane >> 3);
-            const uint16_t* base;
-            int wr;
+        // weight row of tile-local column r (the B row r of the LDS tile)
+        auto w_row = [&](int r, bool& second) {
             if constexpr (EPI == EPI_SWIGLU) {
                 // per EP rows (one epilogue pass): EP/2 gate rows, then the up
                 // rows of the same hidden units
                 const int pp = r / EP, rr = r % EP;
-                base = reinterpret_cast<const uint16_t*>(rr < EP / 2 ? g.W : g.W2);
-                wr = min(tile * (BN / 2) + pp * (EP / 2) + (rr % (EP / 2)), g.N / 2 - 1);
+                second = rr >= EP / 2;
+                return min(tile * (BN / 2) + pp * (EP / 2) + (rr % (EP / 2)), g.N / 2 - 1);
             } else {
-                base = reinterpret_cast<const uint16_t*>(g.W);
-                wr = min(tile * BN + r, g.N - 1);
+                second = false;
+                return min(tile * BN + r, g.N - 1);
             }
+        };
+        using WT = std::conditional_t<WF8, uint8_t, uint16_t>;  // one weight
+        using WR = std::conditional_t<WF8, u32x2, u32x4>;       // a lane's 8 weights
+        const WT* bsrc[B_INSTR];
+#pragma unroll
+        for (int j = 0; j < B_INSTR; ++j) {
+            const int r = 8 * (wave * B_INSTR + j) + (lane >> 3);
+            bool second;
+            const int wr = w_row(r, second);
+            const WT* base = reinterpret_cast<const WT*>(second ? g.W2 : g.W);
             bsrc[j] = base + (int64_t)grp * g.w_group_stride + (int64_t)wr * g.ldw + 8 * tswz(r, pos);
         }
         // DEPTH register slots of one stage each, loaded DEPTH stages ahead;
         // loads past the last stage re-read it (branch-free, so the waits stay
         // exact)
-        u32x4 ra[DEPTH][TA_INSTR], rb[DEPTH][B_INSTR];
+        u32x4 ra[DEPTH][TA_INSTR];
+        WR rb[DEPTH][B_INSTR];
         auto load = [&](int d, int kt) {
             const int k0 = kbase + min(kt, KT - 1) * TBK;
 #pragma unroll
             for (int j = 0; j < TA_INSTR; ++j) ra[d][j] = *reinterpret_cast<const u32x4*>(asrc[j] + k0);
 #pragma unroll
             for (int j = 0; j < B_INSTR; ++j) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(bsrc[j] + k0);
+                const WR* src = reinterpret_cast<const WR*>(bsrc[j] + k0);
                 rb[d][j] = DG_TILE_W_NT ? __builtin_nontemporal_load(src) : *src;
             }
         };
@@ -409,8 +448,12 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
             for (int j = 0; j < TA_INSTR; ++j)
                 *reinterpret_cast<u32x4*>(st + (wave * TA_INSTR + j) * 1024 + lane * 16) = ra[d][j];
 #pragma unroll
-            for (int j = 0; j < B_INSTR; ++j)
-                *reinterpret_cast<u32x4*>(st + TA_BYTES + (wave * B_INSTR + j) * 1024 + lane * 16) = rb[d][j];
+            for (int j = 0; j < B_INSTR; ++j) {
+                u32x4 v;
+                if constexpr (WF8) v = widen8_e4m3(rb[d][j]);
+                else v = rb[d][j];
+                *reinterpret_cast<u32x4*>(st + TA_BYTES + (wave * B_INSTR + j) * 1024 + lane * 16) = v;
+            }
         };
 
         f32x4 acc[4][TN];
@@ -482,6 +525,20 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
         for (int u = 0; u + 1 < UNROLL; ++u)
             if (kt + u < KT) step(u % DEPTH, u % 2, kt + u);
         __syncthreads();  // retire the tail loads; every wave done with the slots
+        if constexpr (WF8) {
+            // per-output-row scales: column wn*WC + j*16 + lr of the tile
+            if (live) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    bool second;
+                    const int wr = w_row(wn * WC + j * 16 + lr, second);
+                    const uint16_t* sc = second ? g.w2_scale : g.w_scale;
+                    const float s = __uint_as_float((uint32_t)sc[(int64_t)grp * g.scale_group_stride + wr] << 16);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i][j] *= s;
+                }
+            }
+        }
 
         // ---- epilogue: per pass of EP columns, the tile through LDS, then
         // coalesced row stores; ptile numbers EP-column tiles ----
@@ -567,7 +624,7 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
     }
 }
 
-template <int BN, int EPI, int DEPTH = DG_TILE_DEPTH, int BM = TBM>
+template <int BN, int EPI, int DEPTH = DG_TILE_DEPTH, int BM = TBM, bool WF8 = false>
 static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hipStream_t st) {
     const int n_tiles = EPI == EPI_SWIGLU ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     const int mb_max = std::max(1, (max_rows + BM - 1) / BM);
@@ -576,7 +633,7 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     const size_t lds = tile_lds_bytes<BN, BM>();
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH, BM>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH, BM, WF8>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr = true;
@@ -585,13 +642,13 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
     static int per_cu = 0;
     if (!per_cu) {
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH, BM>), tile_waves<BN, BM>() * 64, lds);
+            &per_cu, reinterpret_cast<const void*>(tile_gemm_kernel<BN, EPI, DEPTH, BM, WF8>), tile_waves<BN, BM>() * 64, lds);
         if (e != hipSuccess) return e;
         per_cu = std::max(per_cu, 1);
     }
     int64_t grid = std::min<int64_t>(items, 256 * per_cu);
     grid = std::max<int64_t>(8, (grid + 7) / 8 * 8);
-    tile_gemm_kernel<BN, EPI, DEPTH, BM><<<(unsigned)grid, tile_waves<BN, BM>() * 64, lds, st>>>(g, n_tiles);
+    tile_gemm_kernel<BN, EPI, DEPTH, BM, WF8><<<(unsigned)grid, tile_waves<BN, BM>() * 64, lds, st>>>(g, n_tiles);
     if (ks > 1 && !g.group_offsets && !g.defer_reduce) {  // grouped or deferred: the caller's reduce
         const int64_t n = (int64_t)g.M * (g.N / 4);
         tile_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, st>>>(g);
@@ -600,7 +657,8 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
 }
 
 bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
-    if (act_f32 || w_fp8 || g.w_scale) return false;
+    if (act_f32 || (w_fp8 != 0) != (g.w_scale != nullptr)) return false;
+    if (w_fp8 && (epi == EPI_LMHEAD || (epi == EPI_SWIGLU && !g.w2_scale))) return false;
     if (g.K % TBK || g.lda % 8 || g.ldw % 8) return false;
     switch (epi) {
         case EPI_SWIGLU: return !g.c_f32 && g.ldc % 8 == 0 && (g.N / 2) % 8 == 0;
@@ -630,29 +688,38 @@ hipError_t swiglu_reduce_launch(const GemmArgs& g, int groups, int big_min, int 
     return hipGetLastError();
 }
 
-hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
+template <bool WF8>
+static hipError_t tile_gemm_launch_w(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
+    constexpr int D = DG_TILE_DEPTH;
     if (g.group_offsets) {
         if (g.ksplit > 1) {
             // SwiGLU over K slices: partials [ksplit][M slots][2F], M = all
             // slots; swiglu_reduce_launch finishes them
             if (epi != EPI_SWIGLU || !g.part || (g.K / TBK) % g.ksplit || (g.N / 2) % 4) return hipErrorInvalidValue;
-            return launch_tile_t<DG_TILE_BN_GU_SPLIT, EPI_SWIGLU>(g, groups, max_rows, st);
+            return launch_tile_t<DG_TILE_BN_GU_SPLIT, EPI_SWIGLU, D, TBM, WF8>(g, groups, max_rows, st);
         }
-        if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU>(g, groups, max_rows, st);
-        if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32>(g, groups, max_rows, st);
+        if (epi == EPI_SWIGLU) return launch_tile_t<DG_TILE_BN_GU, EPI_SWIGLU, D, TBM, WF8>(g, groups, max_rows, st);
+        if (epi == EPI_STORE_F32)
+            return launch_tile_t<DG_TILE_BN_DN, EPI_STORE_F32, D, TBM, WF8>(g, groups, max_rows, st);
         return hipErrorInvalidValue;
     }
     if (g.ksplit > 1 && (!g.part || (g.K / TBK) % g.ksplit)) return hipErrorInvalidValue;
-    constexpr int D = DG_TILE_DEPTH, BMD = DG_TILE_BM_DENSE;
-    if (epi == EPI_STORE_BF16) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_BF16, D, BMD>(g, 1, g.M, st);
-    if (epi == EPI_RESIDUAL) return launch_tile_t<DG_TILE_BN_DENSE, EPI_RESIDUAL, D, BMD>(g, 1, g.M, st);
-    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_F32, D, BMD>(g, 1, g.M, st);
-    if (epi == EPI_LMHEAD) {
-        // one 256-row block; statistics partials per 128 vocabulary rows
-        if (g.ksplit > 1 || g.M > TBM || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
-        return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM>(g, 1, g.M, st);
-    }
+    constexpr int BMD = DG_TILE_BM_DENSE;
+    if (epi == EPI_STORE_BF16) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_BF16, D, BMD, WF8>(g, 1, g.M, st);
+    if (epi == EPI_RESIDUAL) return launch_tile_t<DG_TILE_BN_DENSE, EPI_RESIDUAL, D, BMD, WF8>(g, 1, g.M, st);
+    if (epi == EPI_STORE_F32) return launch_tile_t<DG_TILE_BN_DENSE, EPI_STORE_F32, D, BMD, WF8>(g, 1, g.M, st);
     return hipErrorInvalidValue;
+}
+
+hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
+    if (g.w_scale) {
+        if (epi == EPI_LMHEAD || (epi == EPI_SWIGLU && !g.w2_scale)) return hipErrorInvalidValue;
+        return tile_gemm_launch_w<true>(g, epi, groups, max_rows, st);
+    }
+    if (epi != EPI_LMHEAD) return tile_gemm_launch_w<false>(g, epi, groups, max_rows, st);
+    // one 256-row block; statistics partials per 128 vocabulary rows
+    if (g.ksplit > 1 || g.M > TBM || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
+    return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM>(g, 1, g.M, st);
 }
 
 }  // namespace dg
