@@ -19,6 +19,9 @@ Workloads (synthetic, seeded; random-init weights ~N(0, 0.02)):
             25 local (window 1024) + 5 global layers, 8192-token prompt
             prefilled by the encoder, 4 canvases of 256 (default)
   one_layer the same widths with 1 layer, 4096-token prompt
+  longctx   the 30-layer stack with e4m3 expert and attention weights, a
+            131072-token prompt prefilled by the encoder (untimed), then
+            canvases as in stack30
   sampler   EB sampler only on bf16 logits [256][262144]
   tiny      2 layers, d=256, fp32, vocab 4096, canvas 32, 128-token prompt
   prefill   encoder prefill of a 131072-token prompt (--prefill-tokens) into
@@ -78,7 +81,7 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     steps_per_canvas = 48
     n_canv = -(-(args.warmup + args.steps) // steps_per_canvas) + 1
     kv = B.KVCache(model, prompt_len + n * n_canv)
-    ws = model.workspace(1024)
+    ws = model.workspace(4096 if prompt_len > 8192 else 1024)
     prompt = wl.prefix_tokens(cfg, prompt_len).to(dev)
     ms_prefill = _sync_ms(lambda: B.prefill_append(model, kv, prompt, ws), torch)
     canvas = B.Canvas(n, cfg.mask_id, 0, dev)
@@ -221,14 +224,14 @@ def _traffic(kernel, kd):
 
 def bench_stack(args, torch, B, which):
     from synth import workloads as wl
-    cfg = {"stack30": wl.STACK30, "one_layer": wl.FULL_LAYER, "tiny": wl.TINY}[which]
-    plen = {"stack30": 8192, "one_layer": 4096, "tiny": wl.TINY_PREFIX}[which]
+    cfg = {"stack30": wl.STACK30, "one_layer": wl.FULL_LAYER, "tiny": wl.TINY, "longctx": wl.STACK30_FP8}[which]
+    plen = {"stack30": 8192, "one_layer": 4096, "tiny": wl.TINY_PREFIX, "longctx": 131072}[which]
     res, handles = _model_workload(args, torch, B, cfg, plen, 8)
     res["config"] = {"workload": f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}", "layers": cfg.n_layers,
                      "d_model": cfg.d_model, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                      "experts": f"{cfg.n_experts} top-{cfg.top_k} + 1 shared, F={cfg.ffn_hidden}",
                      "vocab": cfg.vocab, "canvas": cfg.canvas, "batch": 1, "window": cfg.window,
-                     "global_every": cfg.global_every, "prompt": plen}
+                     "global_every": cfg.global_every, "prompt": plen, "weights": cfg.weight_dtype}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_model_step(cfg, handles, torch, B, plen)
     return res
@@ -470,7 +473,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 96; prefill: 2)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 4; prefill: 1)")
-    ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny", "prefill"])
+    ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny", "prefill",
+                                                                 "longctx"])
     ap.add_argument("--prefill-tokens", type=int, default=131072)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",

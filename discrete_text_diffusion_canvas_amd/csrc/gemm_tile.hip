@@ -85,6 +85,10 @@
 #ifndef DG_TILE_F8_HWCVT
 #define DG_TILE_F8_HWCVT 1
 #endif
+// e4m3 weights on this kernel at all (0: they stay on the streaming kernel)
+#ifndef DG_TILE_FP8
+#define DG_TILE_FP8 1
+#endif
 
 
 namespace dg {
@@ -657,7 +661,7 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
 }
 
 bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
-    if (act_f32 || (w_fp8 != 0) != (g.w_scale != nullptr)) return false;
+    if (act_f32 || (w_fp8 != 0) != (g.w_scale != nullptr) || (w_fp8 && !DG_TILE_FP8)) return false;
     if (w_fp8 && (epi == EPI_LMHEAD || (epi == EPI_SWIGLU && !g.w2_scale))) return false;
     if (g.K % TBK || g.lda % 8 || g.ldw % 8) return false;
     switch (epi) {
