@@ -63,7 +63,21 @@ template <> struct SFrag<float, WK_SAME> {
     __device__ __forceinline__ void load_nt(const void* p) { load(p); }
 };
 
+// 8 e4m3 codes -> 8 bf16 (exact): the gfx950 scaled pack conversion at
+// scale 1, or bit manipulation
+#ifndef DG_STREAM_F8_HWCVT
+#define DG_STREAM_F8_HWCVT 1
+#endif
 __device__ __forceinline__ u16x8 widen_e4m3(const u32x2& v) {
+#if DG_STREAM_F8_HWCVT
+    u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        o[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, false));
+        o[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[h], 1.0f, true));
+    }
+    return __builtin_bit_cast(u16x8, o);
+#else
     u16x8 o;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -71,6 +85,7 @@ __device__ __forceinline__ u16x8 widen_e4m3(const u32x2& v) {
         o[j] = (uint16_t)(__float_as_uint(e4m3_to_f32(b)) >> 16);
     }
     return o;
+#endif
 }
 
 __device__ __forceinline__ f32x4 smfma(const SFrag<uint16_t, WK_SAME>& a, const SFrag<uint16_t, WK_SAME>& b,
