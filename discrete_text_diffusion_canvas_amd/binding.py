@@ -95,6 +95,10 @@ def _load() -> C.CDLL:
                                    P(StepStatsStruct), vp, sz, vp]
     lib.dg_generate_canvas.argtypes = [vp, P(CanvasStruct), P(KVStruct), P(SamplerCfg), u64, i32, i32,
                                        P(StepStatsStruct), P(C.c_int32), vp, sz, vp]
+    lib.dg_canvas_step_batch.argtypes = [vp, P(CanvasStruct), P(KVStruct), i32, i32, u64, P(SamplerCfg),
+                                         P(StepStatsStruct), vp, sz, vp]
+    lib.dg_generate_batch.argtypes = [vp, P(CanvasStruct), P(KVStruct), i32, P(SamplerCfg), u64, i32, i32,
+                                      P(StepStatsStruct), P(C.c_int32), vp, sz, vp]
     lib.dg_embed.argtypes = [vp, vp, i32, vp, vp]
     lib.dg_decoder_layer.argtypes = [vp, i32, vp, i32, P(KVStruct), vp, vp, vp, sz, vp]
     lib.dg_lm_head.argtypes = [vp, vp, i32, P(SamplerCfg), i32, vp, vp, P(StepStatsStruct), vp, sz, vp]
@@ -104,7 +108,8 @@ def _load() -> C.CDLL:
     lib.dg_step_graph_destroy.argtypes = [vp]
     lib.dg_step_graph_destroy.restype = None
     for name in ("dg_canvas_reset", "dg_sampler_step", "dg_model_create", "dg_prefill_append",
-                 "dg_canvas_step", "dg_generate_canvas", "dg_embed", "dg_decoder_layer", "dg_lm_head",
+                 "dg_canvas_step", "dg_generate_canvas", "dg_canvas_step_batch", "dg_generate_batch",
+                 "dg_embed", "dg_decoder_layer", "dg_lm_head",
                  "dg_step_graph_create", "dg_step_graph_launch"):
         getattr(lib, name).restype = i32
     return lib
@@ -170,12 +175,13 @@ class StepStats:
     ``experts_hit`` ([n_layers] int32, routed experts hit per layer) only when
     ``n_layers`` is given."""
 
-    def __init__(self, n: int, device="cuda", vocab: int = 0, logits_dtype=torch.bfloat16, n_layers: int = 0):
+    def __init__(self, n: int, device="cuda", vocab: int = 0, logits_dtype=torch.bfloat16, n_layers: int = 0,
+                 n_canvases: int = 1):
         self.entropy = torch.zeros(n, dtype=torch.float32, device=device)
         self.lse = torch.zeros(n, dtype=torch.float32, device=device)
         self.argmax = torch.zeros(n, dtype=torch.int32, device=device)
         self.selected = torch.zeros(n, dtype=torch.uint8, device=device)
-        self.mean_entropy = torch.zeros(1, dtype=torch.float64, device=device)
+        self.mean_entropy = torch.zeros(n_canvases, dtype=torch.float64, device=device)
         self.logits = torch.empty((n, vocab), dtype=logits_dtype, device=device) if vocab else None
         self.experts_hit = torch.zeros(n_layers, dtype=torch.int32, device=device) if n_layers else None
 
@@ -236,14 +242,14 @@ class Model:
     ``layers`` a list of dicts of device tensors (names as in dg_layer_weights).
     """
 
-    def __init__(self, cfg, embed, final_norm, layers):
+    def __init__(self, cfg, embed, final_norm, layers, max_canvas: int | None = None):
         self.cfg = cfg
         self.embed, self.final_norm, self.layers = embed, final_norm, layers
         self._cs = ConfigStruct(
             n_layers=cfg.n_layers, d_model=cfg.d_model, n_q_heads=cfg.n_q_heads,
             n_kv_heads=cfg.n_kv_heads, head_dim=cfg.head_dim, n_experts=cfg.n_experts,
             top_k=cfg.top_k, ffn_hidden=cfg.ffn_hidden, vocab=cfg.vocab, mask_id=cfg.mask_id,
-            max_canvas=cfg.canvas, window=cfg.window, global_every=cfg.global_every,
+            max_canvas=max_canvas or cfg.canvas, window=cfg.window, global_every=cfg.global_every,
             weight_dtype=_DT[cfg.weight_dtype], act_dtype=_DT[cfg.act_dtype],
             rope_base=cfg.rope_base, norm_eps=cfg.norm_eps)
         arr = (LayerStruct * cfg.n_layers)()
@@ -311,6 +317,39 @@ def canvas_step(model: Model, canvas: Canvas, kv: KVCache, step_idx: int, seed: 
     s = stats.struct()
     check(lib.dg_canvas_step(model.handle, C.byref(c), C.byref(kv.struct_), step_idx, seed, C.byref(scfg),
                              C.byref(s), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def _batch_structs(canvases, kvs):
+    cs = (CanvasStruct * len(canvases))(*[c.struct() for c in canvases])
+    ks = (KVStruct * len(kvs))(*[k.struct_ for k in kvs])
+    return cs, ks
+
+
+def canvas_step_batch(model: Model, canvases, kvs, step_idx: int, seed: int, scfg: SamplerCfg,
+                      stats: StepStats, ws: torch.Tensor, stream=None) -> None:
+    """One lockstep step of several canvases, each on its own cache; ``stats``
+    covers all their rows in order (mean_entropy one entry per canvas)."""
+    if len(canvases) != len(kvs):
+        raise ValueError("one KV cache per canvas")
+    cs, ks = _batch_structs(canvases, kvs)
+    s = stats.struct()
+    check(lib.dg_canvas_step_batch(model.handle, cs, ks, len(canvases), step_idx, seed, C.byref(scfg),
+                                   C.byref(s), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def generate_batch(model: Model, canvases, kvs, scfg: SamplerCfg, seed: int, append_after: bool,
+                   stats: StepStats, ws: torch.Tensor, poll_every: int = 4, stream=None) -> list:
+    if len(canvases) != len(kvs):
+        raise ValueError("one KV cache per canvas")
+    cs, ks = _batch_structs(canvases, kvs)
+    s = stats.struct()
+    steps = (C.c_int32 * len(canvases))()
+    check(lib.dg_generate_batch(model.handle, cs, ks, len(canvases), C.byref(scfg), seed,
+                                int(bool(append_after)), poll_every, C.byref(s), steps, _ptr(ws), ws.numel(),
+                                _stream(stream)))
+    for kv, k in zip(kvs, ks):      # the appended lengths
+        kv.struct_.len = k.len
+    return list(steps)
 
 
 class StepGraph:

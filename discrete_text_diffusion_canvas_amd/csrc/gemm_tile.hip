@@ -188,7 +188,7 @@ __device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int 
 // the row's threads. A thread whose columns hold no bias or mask token and
 // no column past N runs a loop free of per-column tests.
 template <int BN, int NT, int BM>
-__device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T, int mcount, int tile) {
+__device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T, int mcount, int tile, int rbase) {
     constexpr int TS = BN + 4;
     constexpr int TPR = NT / BM;
     static_assert(TPR == 1 || TPR == 2, "one or two threads per row");
@@ -199,7 +199,7 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T
         const int r = e / (BN / 8), c0 = (e % (BN / 8)) * 8;
         const int n = n0 + c0;
         const float* t = T + r * TS + c0;
-        uint16_t* dst = C + (int64_t)r * g.ldc + n;
+        uint16_t* dst = C + (int64_t)(rbase + r) * g.ldc + n;
         if (n + 8 <= N) {
             uint4 w;
             w.x = f2bf2(t[0], t[1]);
@@ -217,8 +217,8 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T
     float* row = T + r * TS;
     const int step = g.step_override >= 0 ? g.step_override : (g.state ? g.state[1] : 0);
     const float c2 = (float)(1.4426950408889634 / lm_tau_at(g.sp, step));
-    const int bt = act && g.bias_tok ? g.bias_tok[r] : -1;
-    const float bv = act && g.bias_tok ? g.bias_val[r] : 0.f;
+    const int bt = act && g.bias_tok ? g.bias_tok[rbase + r] : -1;
+    const float bv = act && g.bias_tok ? g.bias_val[rbase + r] : 0.f;
     const bool special = (bt >= cn0 && bt < cn0 + CW) || (g.mask_id >= cn0 && g.mask_id < cn0 + CW) || cn0 + CW > N;
     // pass 1: raw max and its first index
     float rawm = -INFINITY;
@@ -290,7 +290,7 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T
         p.m2 = rawm == -INFINITY ? -INFINITY : vm; p.s = sum; p.t = tt; p.lmax = rawm;
         p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
         p.pad[0] = p.pad[1] = p.pad[2] = 0;
-        g.parts[(int64_t)r * g.nsplit + tile] = p;
+        g.parts[(int64_t)(rbase + r) * g.nsplit + tile] = p;
     }
 }
 
@@ -585,7 +585,7 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
                 *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 8 == 0
             }
         } else if constexpr (EPI == EPI_LMHEAD) {
-            if (ptile < g.nsplit) tile_lmhead_epilogue<EP, NT, BM>(g, T, mcount, ptile);  // past N: no columns
+            if (ptile < g.nsplit) tile_lmhead_epilogue<EP, NT, BM>(g, T, mcount, ptile, m0);  // past N: no columns
         } else if constexpr (EPI == EPI_SWIGLU) {
             constexpr int CH = EP / 2 / 8;  // 8-column chunks of hidden units per row
             uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
@@ -669,7 +669,7 @@ bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
         case EPI_STORE_F32: return g.ldc % 4 == 0 && g.N % 4 == 0;
         case EPI_STORE_BF16: return g.ldc % 4 == 0 && g.N % 4 == 0;
         case EPI_RESIDUAL: return g.ldx % 4 == 0 && g.N % 4 == 0;
-        case EPI_LMHEAD: return !g.c_f32 && g.M <= TBM && g.ldc % 8 == 0;
+        case EPI_LMHEAD: return !g.c_f32 && g.ldc % 8 == 0;
         default: return false;
     }
 }
@@ -721,8 +721,10 @@ hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows
         return tile_gemm_launch_w<true>(g, epi, groups, max_rows, st);
     }
     if (epi != EPI_LMHEAD) return tile_gemm_launch_w<false>(g, epi, groups, max_rows, st);
-    // one 256-row block; statistics partials per 128 vocabulary rows
-    if (g.ksplit > 1 || g.M > TBM || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
+    // 256-row blocks (the blocks of one vocabulary tile run on one XCD, so
+    // the tile's weight rows come from its L2 after the first); statistics
+    // partials per 128 vocabulary rows
+    if (g.ksplit > 1 || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
     return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM>(g, 1, g.M, st);
 }
 

@@ -71,6 +71,8 @@ struct Work {
     dg::RowPart* parts;  // [min(T, canvas)][nsplit]
     int32_t* sel_list;
     double* chunk_sum;
+    int32_t* bias_tok;  // [T]: a batch's per-row bias tokens (-1: none)
+    float* bias_val;    // [T]
     size_t bytes;
     int rows;
     int rows64;        // T rounded up to a multiple of 64 (canvas K/V row stride)
@@ -145,6 +147,8 @@ Work carve(const dg_model* m, void* base, int T) {
     w.parts = cv.take<dg::RowPart>((size_t)Nc * lm_nsplit(c));
     w.sel_list = cv.take<int32_t>(Nc);
     w.chunk_sum = cv.take<double>((size_t)Nc * dg::draw_nchunk(c.vocab));
+    w.bias_tok = cv.take<int32_t>(T);
+    w.bias_val = cv.take<float>(T);
     w.bytes = cv.off;
     w.rows = T;
     w.rows64 = T64;
@@ -280,13 +284,20 @@ int attn_splits(const dg_config& c, int nq, int64_t keys) {
 // ---------------------------------------------------------------------------
 // With normed_in, w.A already holds rmsnorm(X) with this layer's attention
 // norm; next_norm (or NULL) is normalised into w.A by the closing combine.
-dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg_kv* kv, const int32_t* state,
-                        bool normed_in, const float* next_norm, hipStream_t st) {
+// One canvas of a step: rows [row0, row0 + n) of the work buffers (row0 a
+// multiple of 64 when there are several), attending its own cache.
+struct Seg {
+    int row0, n;
+    const dg_kv* kv;
+};
+
+dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const Seg* segs, int nseg,
+                        const int32_t* state, bool normed_in, const float* next_norm, hipStream_t st) {
     const dg_config& c = m->cfg;
     const dg_layer_weights& L = m->layers[l];
     const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
     const int f32 = c.act_dtype == DG_F32, fp8 = c.weight_dtype == DG_FP8_E4M3;
-    const int64_t P = kv->len;
+    const size_t ab = act_bytes(c);
     if (!normed_in) DG_TRY(dg::launch_rmsnorm(w.X, n, d, L.attn_norm, c.norm_eps, w.A, f32, state, st), "rmsnorm");
     int qkv_parts = 1, o_parts = 1;
     {
@@ -300,17 +311,21 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const dg
     DG_TRY(dg::launch_rope_scatter(w.QKV, w.gemm_part, qkv_parts, f32, n, Hq, Hkv, hd, w.rope_cs, w.Q, w.rows, 0,
                                    w.Kc, w.Vc, w.rows64, 0, w.rows64, state, st),
            "rope");
-    {
+    for (int s = 0; s < nseg; ++s) {
+        // canvas s: its query rows and canvas K/V rows, its cache
+        const Seg& sg = segs[s];
+        const int64_t P = sg.kv->len;
         dg::AttnArgs a;
         memset(&a, 0, sizeof a);
-        a.Q = w.Q; a.ldq = w.rows; a.nq = n; a.qpos0 = P;
-        a.K1 = kv->k[l]; a.V1 = kv->v[l]; a.ld1 = kv->capacity;
+        a.Q = (char*)w.Q + (size_t)sg.row0 * hd * ab; a.ldq = w.rows; a.nq = sg.n; a.qpos0 = P;
+        a.K1 = sg.kv->k[l]; a.V1 = sg.kv->v[l]; a.ld1 = sg.kv->capacity;
         a.s1 = is_global(c, l) ? 0 : std::max<int64_t>(0, P - c.window);
         a.e1 = P;
-        a.K2 = w.Kc; a.V2 = w.Vc; a.ld2 = w.rows64; a.n2 = n; a.pos2_0 = P;
+        a.K2 = (char*)w.Kc + (size_t)sg.row0 * hd * ab; a.V2 = (char*)w.Vc + (size_t)sg.row0 * ab;
+        a.ld2 = w.rows64; a.n2 = sg.n; a.pos2_0 = P;
         a.Hq = Hq; a.Hkv = Hkv; a.hd = hd; a.causal = 0; a.window = 0;
-        a.O = w.O; a.part_o = w.part_o; a.part_ml = w.part_ml;
-        a.splits = attn_splits(c, n, (a.e1 - a.s1) + n);
+        a.O = (char*)w.O + (size_t)sg.row0 * Hq * hd * ab; a.part_o = w.part_o; a.part_ml = w.part_ml;
+        a.splits = attn_splits(c, sg.n, (a.e1 - a.s1) + sg.n);
         a.state = state;
         const int slot = timing_begin(st, DG_TIME_ATTENTION);
         DG_TRY(dg::launch_attention(a, f32, st), "attention");
@@ -417,6 +432,15 @@ dg_status check_logits(const dg_model* m, const dg_step_stats* s, int n) {
     return DG_OK;
 }
 
+// rows [0, n): no bias token
+__global__ void no_bias_kernel(int32_t* tok, float* val, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        tok[i] = -1;
+        val[i] = 0.f;
+    }
+}
+
 dg_status ws_for(const dg_model* m, void* ws, size_t ws_bytes, int rows, Work* out) {
     if (!ws) return fail(DG_E_INVALID, "workspace is NULL");
     Work w = carve(m, ws, rows);
@@ -509,7 +533,8 @@ dg_status dg_decoder_layer(const dg_model* m, int32_t layer, float* X, int32_t n
     const size_t xb = (size_t)n * m->cfg.d_model * sizeof(float);
     DG_TRY(hipMemcpyAsync(w.X, X, xb, hipMemcpyDeviceToDevice, st), "copy X in");
     DG_TRY(dg::launch_rope_table(n, m->cfg.head_dim, kv->len, m->cfg.rope_base, w.rope_cs, nullptr, st), "rope table");
-    if (dg_status s = decoder_layer(m, layer, w, n, kv, nullptr, false, nullptr, st)) return s;
+    const Seg seg{0, n, kv};
+    if (dg_status s = decoder_layer(m, layer, w, n, &seg, 1, nullptr, false, nullptr, st)) return s;
     DG_TRY(hipMemcpyAsync(X, w.X, xb, hipMemcpyDeviceToDevice, st), "copy X out");
     const size_t kb = (size_t)n * m->cfg.top_k;
     if (route_ids) DG_TRY(hipMemcpyAsync(route_ids, w.ids, kb * 4, hipMemcpyDeviceToDevice, st), "copy ids");
@@ -586,7 +611,8 @@ dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, 
     DG_TRY(dg::launch_rope_table(n, c.head_dim, kv->len, c.rope_base, w.rope_cs, canvas->state, st), "rope table");
     for (int l = 0; l < c.n_layers; ++l) {
         const float* next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        if (dg_status s = decoder_layer(m, l, w, n, kv, canvas->state, l > 0, next, st)) return s;
+        const Seg seg{0, n, kv};
+        if (dg_status s = decoder_layer(m, l, w, n, &seg, 1, canvas->state, l > 0, next, st)) return s;
     }
     if (dg_status s = lm_head(m, w, n, sp, step_idx, canvas->state, canvas->bias_tok, canvas->bias_val, stats, true,
                               st))
@@ -625,6 +651,124 @@ dg_status dg_generate_canvas(const dg_model* m, dg_canvas* canvas, dg_kv* kv, co
     if (append_after) {
         if (dg_status s = dg_prefill_append(m, kv, canvas->tokens, canvas->n, ws, ws_bytes, stream)) return s;
     }
+    return DG_OK;
+}
+
+dg_status dg_canvas_step_batch(const dg_model* m, dg_canvas* canvases, const dg_kv* kvs, int32_t nb, int32_t step_idx,
+                               uint64_t seed, const dg_sampler_cfg* scfg, dg_step_stats* stats, void* ws,
+                               size_t ws_bytes, void* stream) {
+    if (!m || !canvases || !kvs) return fail(DG_E_INVALID, "NULL argument");
+    if (nb < 1 || nb > 64) return fail(DG_E_SHAPE, "batch of %d canvases outside 1..64", nb);
+    if (dg_status s = check_sampler_cfg(scfg)) return s;
+    if (step_idx < 0 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
+    const dg_config& c = m->cfg;
+    Seg segs[64];
+    int rows = 0;
+    bool any_bias = false;
+    for (int b = 0; b < nb; ++b) {
+        const int n = canvases[b].n;
+        if (n < 1) return fail(DG_E_SHAPE, "canvas %d: n must be >= 1", b);
+        if (nb > 1 && n % 64) return fail(DG_E_SHAPE, "canvas %d: n=%d is not a multiple of 64", b, n);
+        if (dg_status s = check_canvas(&canvases[b], n)) return s;
+        if (dg_status s = check_kv(m, &kvs[b])) return s;
+        segs[b] = Seg{rows, n, &kvs[b]};
+        rows += n;
+        any_bias |= canvases[b].bias_tok != nullptr;
+    }
+    if (rows > c.max_canvas) return fail(DG_E_SHAPE, "%d batch rows exceed max_canvas %d", rows, c.max_canvas);
+    if (dg_status s = check_logits(m, stats, rows)) return s;
+    if (!stats->mean_entropy) return fail(DG_E_INVALID, "stats->mean_entropy is NULL");
+    Work w;
+    if (dg_status s = ws_for(m, ws, ws_bytes, rows, &w)) return s;
+    w.experts_hit = stats->experts_hit;
+    hipStream_t st = (hipStream_t)stream;
+    const dg::SamplerParams sp = to_params(scfg);
+    const int f32 = c.act_dtype == DG_F32;
+    for (int b = 0; b < nb; ++b) {
+        const Seg& sg = segs[b];
+        DG_TRY(dg::launch_embed(m->embed, f32, c.d_model, c.vocab, canvases[b].tokens, sg.n,
+                                w.X + (size_t)sg.row0 * c.d_model, nullptr, st),
+               "embed");
+        DG_TRY(dg::launch_rope_table(sg.n, c.head_dim, sg.kv->len, c.rope_base, w.rope_cs + (size_t)sg.row0 * c.head_dim,
+                                     nullptr, st),
+               "rope table");
+    }
+    if (any_bias) {
+        no_bias_kernel<<<(rows + 255) / 256, 256, 0, st>>>(w.bias_tok, w.bias_val, rows);
+        DG_TRY(hipGetLastError(), "bias fill");
+        for (int b = 0; b < nb; ++b) {
+            if (!canvases[b].bias_tok) continue;
+            const Seg& sg = segs[b];
+            DG_TRY(hipMemcpyAsync(w.bias_tok + sg.row0, canvases[b].bias_tok, (size_t)sg.n * 4,
+                                  hipMemcpyDeviceToDevice, st),
+                   "bias tokens");
+            DG_TRY(hipMemcpyAsync(w.bias_val + sg.row0, canvases[b].bias_val, (size_t)sg.n * 4,
+                                  hipMemcpyDeviceToDevice, st),
+                   "bias values");
+        }
+    }
+    for (int l = 0; l < c.n_layers; ++l) {
+        const float* next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
+        if (dg_status s = decoder_layer(m, l, w, rows, segs, nb, nullptr, l > 0, next, st)) return s;
+    }
+    if (dg_status s = lm_head(m, w, rows, sp, step_idx, nullptr, any_bias ? w.bias_tok : nullptr,
+                              any_bias ? w.bias_val : nullptr, stats, true, st))
+        return s;
+    const size_t lb = (size_t)stats->logits_ld * act_bytes(c);
+    for (int b = 0; b < nb; ++b) {
+        const Seg& sg = segs[b];
+        dg_canvas& cv = canvases[b];
+        DG_TRY(dg::launch_sampler_tail((const char*)stats->logits + sg.row0 * lb, f32, stats->logits_ld, sg.n, c.vocab,
+                                       c.mask_id, cv.bias_tok, cv.bias_val, stats->entropy + sg.row0,
+                                       stats->argmax + sg.row0, cv.state, step_idx, sp, seed, cv.canvas_idx,
+                                       cv.tokens, cv.committed, cv.prev_argmax, stats->selected + sg.row0,
+                                       w.sel_list, w.chunk_sum, stats->mean_entropy + b, st),
+               "sampler tail");
+    }
+    return DG_OK;
+}
+
+dg_status dg_generate_batch(const dg_model* m, dg_canvas* canvases, dg_kv* kvs, int32_t nb, const dg_sampler_cfg* scfg,
+                            uint64_t seed, int32_t append_after, int32_t poll_every, dg_step_stats* stats,
+                            int32_t* steps_taken, void* ws, size_t ws_bytes, void* stream) {
+    if (!m || !canvases || !kvs || !steps_taken) return fail(DG_E_INVALID, "NULL argument");
+    if (nb < 1 || nb > 64) return fail(DG_E_SHAPE, "batch of %d canvases outside 1..64", nb);
+    if (dg_status s = check_sampler_cfg(scfg)) return s;
+    if (poll_every < 1) return fail(DG_E_INVALID, "poll_every must be >= 1");
+    for (int b = 0; b < nb; ++b) {
+        if (dg_status s = check_canvas(&canvases[b], canvases[b].n)) return s;
+        if (dg_status s = check_kv(m, &kvs[b])) return s;
+        if (append_after && kvs[b].len + canvases[b].n > kvs[b].capacity)
+            return fail(DG_E_CAPACITY, "canvas %d: kv cache full", b);
+    }
+    hipStream_t st = (hipStream_t)stream;
+    for (int b = 0; b < nb; ++b)
+        if (dg_status s = dg_canvas_reset(&canvases[b], m->cfg.mask_id, stream)) return s;
+    std::vector<int32_t> hstate((size_t)nb * DG_STATE_WORDS);
+    for (int t = 0; t < scfg->max_steps; ++t) {
+        if (dg_status s = dg_canvas_step_batch(m, canvases, kvs, nb, t, seed, scfg, stats, ws, ws_bytes, stream))
+            return s;
+        if ((t + 1) % poll_every == 0 || t + 1 == scfg->max_steps) {
+            for (int b = 0; b < nb; ++b)
+                DG_TRY(hipMemcpyAsync(&hstate[(size_t)b * DG_STATE_WORDS], canvases[b].state,
+                                      DG_STATE_WORDS * sizeof(int32_t), hipMemcpyDeviceToHost, st),
+                       "read state");
+            DG_TRY(hipStreamSynchronize(st), "sync");
+            bool all = true;
+            for (int b = 0; b < nb; ++b) all &= hstate[(size_t)b * DG_STATE_WORDS + DG_ST_DONE] != 0;
+            if (all) break;
+        }
+    }
+    for (int b = 0; b < nb; ++b)
+        DG_TRY(hipMemcpyAsync(&hstate[(size_t)b * DG_STATE_WORDS], canvases[b].state, DG_STATE_WORDS * sizeof(int32_t),
+                              hipMemcpyDeviceToHost, st),
+               "read state");
+    DG_TRY(hipStreamSynchronize(st), "sync");
+    for (int b = 0; b < nb; ++b) steps_taken[b] = hstate[(size_t)b * DG_STATE_WORDS + DG_ST_STEP];
+    if (append_after)
+        for (int b = 0; b < nb; ++b)
+            if (dg_status s = dg_prefill_append(m, &kvs[b], canvases[b].tokens, canvases[b].n, ws, ws_bytes, stream))
+                return s;
     return DG_OK;
 }
 

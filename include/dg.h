@@ -328,6 +328,42 @@ dg_status dg_generate_canvas(const dg_model* m, dg_canvas* canvas, dg_kv* kv, co
                              int32_t* steps_taken, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dg_canvas_step_batch - one denoising step of nb canvases of several users
+ * at once (model card zh-TW, capabilities: low-batch serving), each with its
+ * own KV cache: canvases[b] attends kvs[b] (rows [0, kvs[b].len), canvas
+ * positions kvs[b].len ..) and only its own rows; the projections, router,
+ * expert GEMMs and LM head run once over all canvas rows, so each weight
+ * byte is read once per step for the whole batch. Every canvas then takes
+ * the sampler step of dg_sampler_step on its rows with its own state, bias
+ * and canvas_idx.
+ *   canvases, kvs: arrays of nb (1..64) structs; sum of canvases[b].n <=
+ *     max_canvas; with nb > 1 every n is a multiple of 64.
+ *   step_idx: the step index of every canvas (0 <= step_idx < max_steps;
+ *     the batch moves in lockstep). A finished canvas's rows are still
+ *     computed, but its sampler step changes nothing.
+ *   stats: one set for the batch; canvas b owns rows [r_b, r_b + n_b) of
+ *     entropy, lse, argmax, selected and logits (r_b = sum of the earlier
+ *     n), and mean_entropy[b] (nb entries). experts_hit counts over all rows.
+ *   ws: dg_workspace_bytes(m, sum of n) bytes at least.
+ * Errors as dg_canvas_step; DG_E_SHAPE for the batch limits above.
+ */
+dg_status dg_canvas_step_batch(const dg_model* m, dg_canvas* canvases, const dg_kv* kvs, int32_t nb, int32_t step_idx,
+                               uint64_t seed, const dg_sampler_cfg* scfg, dg_step_stats* stats, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * dg_generate_batch - denoise nb canvases to completion together: reset them
+ * all, run dg_canvas_step_batch for t = 0, 1, ... until every canvas is
+ * finished (polling the device every poll_every steps) or max_steps, then,
+ * if append_after != 0, append each canvas to its own cache with
+ * dg_prefill_append. steps_taken[b] (host, nb entries) receives the steps
+ * canvas b took before it finished.
+ */
+dg_status dg_generate_batch(const dg_model* m, dg_canvas* canvases, dg_kv* kvs, int32_t nb, const dg_sampler_cfg* scfg,
+                            uint64_t seed, int32_t append_after, int32_t poll_every, dg_step_stats* stats,
+                            int32_t* steps_taken, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * A denoising step captured as a HIP graph (the model card's step, zh-TW best
  * practice 1, replayed without host launches). dg_step_graph_create records
  * one dg_canvas_step with the step index read from canvas->state (step_idx

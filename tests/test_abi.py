@@ -111,3 +111,37 @@ def test_model_create_rejects_routing_beyond_the_permutation(lib):
     assert create(512, 16, 1024) == -5
     assert b"permutation" in L.dg_last_error()
     assert create(512, 16, 64) == 0
+
+
+def test_batch_step_validates_before_launch(lib):
+    """Batch limits are checked on the host before any device work:
+    placeholder pointers are never dereferenced."""
+    from discrete_text_diffusion_canvas_amd import binding as B
+    L = B.lib
+    fake = 0x1000
+    layer = B.LayerStruct(*([fake] * 9 + [None] * 5))
+    arr = (B.LayerStruct * 1)(layer)
+    w = B.WeightsStruct(fake, fake, arr)
+    cs = B.ConfigStruct(n_layers=1, d_model=256, n_q_heads=4, n_kv_heads=2, head_dim=64, n_experts=8,
+                        top_k=2, ffn_hidden=64, vocab=4096, mask_id=4095, max_canvas=256, window=128,
+                        global_every=0, weight_dtype=B.DG_BF16, act_dtype=B.DG_BF16, rope_base=1e4, norm_eps=1e-6)
+    h = C.c_void_p()
+    assert L.dg_model_create(C.byref(cs), C.byref(w), C.byref(h)) == 0
+    kp = (C.c_void_p * 1)(fake)
+    kvs = (B.KVStruct * 3)(*[B.KVStruct(kp, kp, 1024, 0) for _ in range(3)])
+    stats = B.StepStatsStruct(fake, fake, fake, fake, fake, fake, 4096, None)
+    cfg = B.sampler_default()
+
+    def call(ns, nb=None, step=0):
+        cv = (B.CanvasStruct * len(ns))(*[B.CanvasStruct(fake, fake, fake, fake, None, None, n, 0) for n in ns])
+        return L.dg_canvas_step_batch(h, cv, kvs, len(ns) if nb is None else nb, step, 1, C.byref(cfg),
+                                      C.byref(stats), C.c_void_p(fake), 1 << 40, None)
+    try:
+        assert call([64, 64], nb=0) == -2
+        assert call([64, 96]) == -2                     # not a multiple of 64
+        assert b"multiple of 64" in L.dg_last_error()
+        assert call([128, 128, 64]) == -2               # 320 rows > max_canvas 256
+        assert b"max_canvas" in L.dg_last_error()
+        assert call([64, 64], step=48) == -1
+    finally:
+        L.dg_model_destroy(h)
