@@ -70,47 +70,60 @@ def _sync_ms(fn, torch):
 def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     from synth import workloads as wl
     dev = torch.device("cuda:0")
+    nb = args.batch
     t0 = time.perf_counter()
     embed = wl.embedding(cfg, device=dev)
     fnorm = wl.final_norm(cfg, device=dev)
     layers = [wl.layer_weights(cfg, l, device=dev) for l in range(cfg.n_layers)]
-    model = B.Model(cfg, embed, fnorm, layers)
+    model = B.Model(cfg, embed, fnorm, layers, max_canvas=cfg.canvas * nb)
     torch.cuda.synchronize()
     t_weights = time.perf_counter() - t0
     n = cfg.canvas
     steps_per_canvas = 48
     n_canv = -(-(args.warmup + args.steps) // steps_per_canvas) + 1
-    kv = B.KVCache(model, prompt_len + n * n_canv)
-    ws = model.workspace(4096 if prompt_len > 8192 else 1024)
-    prompt = wl.prefix_tokens(cfg, prompt_len).to(dev)
-    ms_prefill = _sync_ms(lambda: B.prefill_append(model, kv, prompt, ws), torch)
-    canvas = B.Canvas(n, cfg.mask_id, 0, dev)
-    stats = B.StepStats(n, device=dev, vocab=cfg.vocab, logits_dtype=model.act_dtype, n_layers=cfg.n_layers)
+    kvs = [B.KVCache(model, prompt_len + n * n_canv) for _ in range(nb)]
+    kv = kvs[0]
+    ws = model.workspace(max(4096 if prompt_len > 8192 else 1024, n * nb))
+    prompts = [wl.prefix_tokens(cfg, prompt_len, stream=b).to(dev) for b in range(nb)]
+    ms_prefill = _sync_ms(lambda: [B.prefill_append(model, k, p, ws) for k, p in zip(kvs, prompts)], torch)
+    canvases = [B.Canvas(n, cfg.mask_id, b, dev) for b in range(nb)]
+    canvas = canvases[0]
+    stats = B.StepStats(n * nb, device=dev, vocab=cfg.vocab, logits_dtype=model.act_dtype, n_layers=cfg.n_layers,
+                        n_canvases=nb)
     scfg = B.sampler_default()
     sched = {"t": 0, "canvas": 0, "committed": 0}
 
     def run(K, record=None, use_graph=False):
-        # use_graph: each step is a replay of one captured step (HIP graph,
-        # captured once per canvas: the KV length is part of the capture)
+        # use_graph (one canvas): each step is a replay of one captured step
+        # (HIP graph, captured once per canvas: the KV length is part of the
+        # capture). Several canvases step in lockstep, eagerly, until all
+        # are finished.
         for _ in range(K):
             if sched["t"] == 0:
-                canvas.canvas_idx = sched["canvas"]
-                canvas.reset()
+                for b, c in enumerate(canvases):
+                    c.canvas_idx = sched["canvas"] * nb + b
+                    c.reset()
             P = kv.length
-            if use_graph:
+            if nb > 1:
+                B.canvas_step_batch(model, canvases, kvs, sched["t"], SEED, scfg, stats, ws)
+            elif use_graph:
                 if sched.get("graph") is None:
                     sched["graph"] = B.StepGraph(model, canvas, kv, scfg, SEED, stats, ws)
                 sched["graph"].launch()
             else:
                 B.canvas_step(model, canvas, kv, sched["t"], SEED, scfg, stats, ws)
             sched["t"] += 1
-            done = bool(canvas.state[B.ST_DONE].item())
+            if nb > 1:
+                done = bool(torch.stack([c.state[B.ST_DONE] for c in canvases]).all().item())
+            else:
+                done = bool(canvas.state[B.ST_DONE].item())
             if record is not None:
                 record.append((P, stats.experts_hit.cpu().tolist()))
             if done or sched["t"] == scfg.max_steps:
-                B.prefill_append(model, kv, canvas.tokens, ws)
+                for c, k in zip(canvases, kvs):
+                    B.prefill_append(model, k, c.tokens, ws)
                 sched["graph"] = None
-                sched["committed"] += n
+                sched["committed"] += n * nb
                 sched["canvas"] += 1
                 sched["t"] = 0
 
@@ -131,7 +144,7 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
         torch.cuda.synchronize()
         tot_ms, launches = B.timing_read()
         B.timing_enable(B.TIME_OFF)
-        nbytes, flops = _algorithmic(cfg, name, rec)
+        nbytes, flops = _algorithmic(cfg, name, rec, nb)
         kernels[name] = {"launches": launches, "ms_total": tot_ms, "bytes": nbytes, "flops": flops,
                          "us_per_launch": round(tot_ms / max(launches, 1) * 1e3, 2),
                          "ms_per_step": round(tot_ms / max(len(rec), 1), 4),
@@ -160,11 +173,12 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     return res, (model, kv, ws, canvas, stats)
 
 
-def _algorithmic(cfg, name, rec):
+def _algorithmic(cfg, name, rec, nbat=1):
     """Algorithmic HBM bytes and flops of every launch of kernel ``name`` over
-    the recorded steps [(prefix length P, experts hit per layer)]: each weight
-    byte of the experts actually hit once, activations in and out once."""
-    n, d, F, k = cfg.canvas, cfg.d_model, cfg.ffn_hidden, cfg.top_k
+    the recorded steps [(prefix length P, experts hit per layer)] of nbat
+    canvases in lockstep (each with a cache of P rows): each weight byte of
+    the experts actually hit once per step, activations in and out once."""
+    n, d, F, k = cfg.canvas * nbat, cfg.d_model, cfg.ffn_hidden, cfg.top_k
     Hq, Hkv, hd, V, L = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.vocab, cfg.n_layers
     wb = 1 if cfg.weight_dtype == "fp8" else (4 if cfg.weight_dtype == "f32" else 2)
     ab = 4 if cfg.act_dtype == "f32" else 2
@@ -186,8 +200,8 @@ def _algorithmic(cfg, name, rec):
                 fl += 2.0 * n * d * Hq * hd
             elif name == "attention":
                 glob = cfg.global_every > 0 and l % cfg.global_every == cfg.global_every - 1
-                keys = (P if glob else min(P, cfg.window)) + n
-                nb += keys * Hkv * hd * 2 * ab + 2 * n * Hq * hd * ab
+                keys = (P if glob else min(P, cfg.window)) + cfg.canvas      # per canvas
+                nb += nbat * keys * Hkv * hd * 2 * ab + 2 * n * Hq * hd * ab
                 fl += 4.0 * n * Hq * keys * hd
         if name == "lm_head":
             nb += V * d * ab + n * d * ab + n * V * ab
@@ -227,19 +241,21 @@ def bench_stack(args, torch, B, which):
     cfg = {"stack30": wl.STACK30, "one_layer": wl.FULL_LAYER, "tiny": wl.TINY, "longctx": wl.STACK30_FP8}[which]
     plen = {"stack30": 8192, "one_layer": 4096, "tiny": wl.TINY_PREFIX, "longctx": 131072}[which]
     res, handles = _model_workload(args, torch, B, cfg, plen, 8)
-    res["config"] = {"workload": f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}", "layers": cfg.n_layers,
+    wname = f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}" + (f"_batch{args.batch}" if args.batch > 1 else "")
+    res["config"] = {"workload": wname, "layers": cfg.n_layers,
                      "d_model": cfg.d_model, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                      "experts": f"{cfg.n_experts} top-{cfg.top_k} + 1 shared, F={cfg.ffn_hidden}",
-                     "vocab": cfg.vocab, "canvas": cfg.canvas, "batch": 1, "window": cfg.window,
+                     "vocab": cfg.vocab, "canvas": cfg.canvas, "batch": args.batch, "window": cfg.window,
                      "global_every": cfg.global_every, "prompt": plen, "weights": cfg.weight_dtype}
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_model_step(cfg, handles, torch, B, plen)
+        res["cpu_baseline"] = cpu_model_step(cfg, handles, torch, B, plen, args.batch)
     return res
 
 
-def cpu_model_step(cfg, handles, torch, B, plen):
+def cpu_model_step(cfg, handles, torch, B, plen, nb=1):
     """The oracle on one decoder layer plus the LM head (float64 numpy), on the
-    canvas state and KV the GPU run left, extrapolated to all layers."""
+    canvas state and KV the GPU run left, extrapolated to all layers (and to
+    nb canvases: a batched step is nb canvas steps for the oracle)."""
     import numpy as np
     from oracle import model as M
     from oracle import sampler as S
@@ -262,10 +278,11 @@ def cpu_model_step(cfg, handles, torch, B, plen):
     st = S.CanvasState.fresh(n, cfg.mask_id)
     S.sampler_step(st, L, 0, ocfg, SEED)
     t_head = time.perf_counter() - t0
-    step_s = t_layer * cfg.n_layers + t_head
+    step_s = (t_layer * cfg.n_layers + t_head) * nb
     return {"value": round(1.0 / step_s, 5), "unit": "denoise steps/s", "cores": _cores(), "kind": "oracle",
             "sample": (f"1 decoder layer ({t_layer:.2f} s) + LM head and sampler ({t_head:.2f} s), float64 numpy, "
-                       f"extrapolated to {cfg.n_layers} layers; canvas {n}, KV {P} rows")}
+                       f"extrapolated to {cfg.n_layers} layers" + (f" and {nb} canvases" if nb > 1 else "")
+                       + f"; canvas {n}, KV {P} rows")}
 
 
 # --------------------------------------------------------------------------
@@ -476,6 +493,8 @@ def main():
     ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny", "prefill",
                                                                  "longctx"])
     ap.add_argument("--prefill-tokens", type=int, default=131072)
+    ap.add_argument("--batch", type=int, default=1,
+                    help="canvases of different users stepped together (model workloads; 256 x batch <= 1024)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="finish with device copies of BYTES bytes (scale for HBM traffic counters)")
@@ -484,6 +503,8 @@ def main():
         args.steps = 2 if args.workload == "prefill" else 96
     if args.warmup is None:
         args.warmup = 1 if args.workload == "prefill" else 4
+    if args.batch != 1 and args.workload in ("sampler", "prefill"):
+        ap.error("--batch applies to the model workloads")
     if args.gpus != 1:
         print("bench.py measures one GPU: the denoising step here is built for a single MI355X "
               "and has no multi-GPU path", file=sys.stderr)
