@@ -75,7 +75,8 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     embed = wl.embedding(cfg, device=dev)
     fnorm = wl.final_norm(cfg, device=dev)
     layers = [wl.layer_weights(cfg, l, device=dev) for l in range(cfg.n_layers)]
-    model = B.Model(cfg, embed, fnorm, layers, max_canvas=cfg.canvas * nb)
+    lm8 = wl.lm_head_e4m3(cfg, device=dev) if args.fp8_lm_head else (None, None)
+    model = B.Model(cfg, embed, fnorm, layers, max_canvas=cfg.canvas * nb, lm_head_e4m3=lm8[0], lm_head_scale=lm8[1])
     torch.cuda.synchronize()
     t_weights = time.perf_counter() - t0
     n = cfg.canvas
@@ -144,7 +145,7 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
         torch.cuda.synchronize()
         tot_ms, launches = B.timing_read()
         B.timing_enable(B.TIME_OFF)
-        nbytes, flops = _algorithmic(cfg, name, rec, nb)
+        nbytes, flops = _algorithmic(cfg, name, rec, nb, args.fp8_lm_head)
         kernels[name] = {"launches": launches, "ms_total": tot_ms, "bytes": nbytes, "flops": flops,
                          "us_per_launch": round(tot_ms / max(launches, 1) * 1e3, 2),
                          "ms_per_step": round(tot_ms / max(len(rec), 1), 4),
@@ -173,7 +174,7 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     return res, (model, kv, ws, canvas, stats)
 
 
-def _algorithmic(cfg, name, rec, nbat=1):
+def _algorithmic(cfg, name, rec, nbat=1, lm8=False):
     """Algorithmic HBM bytes and flops of every launch of kernel ``name`` over
     the recorded steps [(prefix length P, experts hit per layer)] of nbat
     canvases in lockstep (each with a cache of P rows): each weight byte of
@@ -204,7 +205,7 @@ def _algorithmic(cfg, name, rec, nbat=1):
                 nb += nbat * keys * Hkv * hd * 2 * ab + 2 * n * Hq * hd * ab
                 fl += 4.0 * n * Hq * keys * hd
         if name == "lm_head":
-            nb += V * d * ab + n * d * ab + n * V * ab
+            nb += V * d * (1 if lm8 else ab) + n * d * ab + n * V * ab
             fl += 2.0 * n * V * d
     return nb, fl
 
@@ -241,12 +242,14 @@ def bench_stack(args, torch, B, which):
     cfg = {"stack30": wl.STACK30, "one_layer": wl.FULL_LAYER, "tiny": wl.TINY, "longctx": wl.STACK30_FP8}[which]
     plen = {"stack30": 8192, "one_layer": 4096, "tiny": wl.TINY_PREFIX, "longctx": 131072}[which]
     res, handles = _model_workload(args, torch, B, cfg, plen, 8)
-    wname = f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}" + (f"_batch{args.batch}" if args.batch > 1 else "")
+    wname = (f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}" + (f"_batch{args.batch}" if args.batch > 1 else "")
+             + ("_e4m3head" if args.fp8_lm_head else ""))
     res["config"] = {"workload": wname, "layers": cfg.n_layers,
                      "d_model": cfg.d_model, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                      "experts": f"{cfg.n_experts} top-{cfg.top_k} + 1 shared, F={cfg.ffn_hidden}",
                      "vocab": cfg.vocab, "canvas": cfg.canvas, "batch": args.batch, "window": cfg.window,
-                     "global_every": cfg.global_every, "prompt": plen, "weights": cfg.weight_dtype}
+                     "global_every": cfg.global_every, "prompt": plen, "weights": cfg.weight_dtype,
+                     "lm_head": "e4m3" if args.fp8_lm_head else cfg.act_dtype}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_model_step(cfg, handles, torch, B, plen, args.batch)
     return res
@@ -493,6 +496,8 @@ def main():
     ap.add_argument("--workload", default="stack30", choices=["stack30", "one_layer", "sampler", "tiny", "prefill",
                                                                  "longctx"])
     ap.add_argument("--prefill-tokens", type=int, default=131072)
+    ap.add_argument("--fp8-lm-head", action="store_true",
+                    help="the LM head reads an e4m3 copy of the tied matrix (model workloads)")
     ap.add_argument("--batch", type=int, default=1,
                     help="canvases of different users stepped together (model workloads; 256 x batch <= 1024)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -503,8 +508,8 @@ def main():
         args.steps = 2 if args.workload == "prefill" else 96
     if args.warmup is None:
         args.warmup = 1 if args.workload == "prefill" else 4
-    if args.batch != 1 and args.workload in ("sampler", "prefill"):
-        ap.error("--batch applies to the model workloads")
+    if (args.batch != 1 or args.fp8_lm_head) and args.workload in ("sampler", "prefill", "tiny"):
+        ap.error("--batch and --fp8-lm-head apply to the bf16 model workloads")
     if args.gpus != 1:
         print("bench.py measures one GPU: the denoising step here is built for a single MI355X "
               "and has no multi-GPU path", file=sys.stderr)

@@ -61,7 +61,8 @@ class LayerStruct(C.Structure):
 
 
 class WeightsStruct(C.Structure):
-    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerStruct))]
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("layers", C.POINTER(LayerStruct)),
+                ("lm_head_e4m3", C.c_void_p), ("lm_head_scale", C.c_void_p)]
 
 
 class KVStruct(C.Structure):
@@ -239,11 +240,17 @@ class Model:
     """Borrowed device weights plus the library's model handle.
 
     ``cfg`` is a geometry object with the fields of synth.workloads.ModelConfig;
-    ``layers`` a list of dicts of device tensors (names as in dg_layer_weights).
+    ``layers`` a list of dicts of device tensors (names as in dg_layer_weights);
+    ``max_canvas`` the most canvas rows of one step (default cfg.canvas; a
+    batch needs their sum); ``lm_head_e4m3``/``lm_head_scale`` an optional
+    e4m3 copy of the tied matrix (uint8 [vocab][d], bf16 [vocab]) that the
+    LM head then reads.
     """
 
-    def __init__(self, cfg, embed, final_norm, layers, max_canvas: int | None = None):
+    def __init__(self, cfg, embed, final_norm, layers, max_canvas: int | None = None, lm_head_e4m3=None,
+                 lm_head_scale=None):
         self.cfg = cfg
+        self.lm_head_e4m3, self.lm_head_scale = lm_head_e4m3, lm_head_scale
         self.embed, self.final_norm, self.layers = embed, final_norm, layers
         self._cs = ConfigStruct(
             n_layers=cfg.n_layers, d_model=cfg.d_model, n_q_heads=cfg.n_q_heads,
@@ -259,7 +266,7 @@ class Model:
                                            .replace("up_scale", "w_up_scale")
                                            .replace("down_scale", "w_down_scale"))))
         self._layers = arr
-        self._ws = WeightsStruct(_ptr(embed), _ptr(final_norm), arr)
+        self._ws = WeightsStruct(_ptr(embed), _ptr(final_norm), arr, _ptr(lm_head_e4m3), _ptr(lm_head_scale))
         h = C.c_void_p()
         check(lib.dg_model_create(C.byref(self._cs), C.byref(self._ws), C.byref(h)))
         self.handle = h

@@ -662,7 +662,7 @@ static hipError_t launch_tile_t(const GemmArgs& g, int groups, int max_rows, hip
 
 bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
     if (act_f32 || (w_fp8 != 0) != (g.w_scale != nullptr) || (w_fp8 && !DG_TILE_FP8)) return false;
-    if (w_fp8 && (epi == EPI_LMHEAD || (epi == EPI_SWIGLU && !g.w2_scale))) return false;
+    if (w_fp8 && epi == EPI_SWIGLU && !g.w2_scale) return false;
     if (g.K % TBK || g.lda % 8 || g.ldw % 8) return false;
     switch (epi) {
         case EPI_SWIGLU: return !g.c_f32 && g.ldc % 8 == 0 && (g.N / 2) % 8 == 0;
@@ -716,15 +716,16 @@ static hipError_t tile_gemm_launch_w(const GemmArgs& g, int epi, int groups, int
 }
 
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
-    if (g.w_scale) {
-        if (epi == EPI_LMHEAD || (epi == EPI_SWIGLU && !g.w2_scale)) return hipErrorInvalidValue;
+    if (epi != EPI_LMHEAD) {
+        if (!g.w_scale) return tile_gemm_launch_w<false>(g, epi, groups, max_rows, st);
+        if (epi == EPI_SWIGLU && !g.w2_scale) return hipErrorInvalidValue;
         return tile_gemm_launch_w<true>(g, epi, groups, max_rows, st);
     }
-    if (epi != EPI_LMHEAD) return tile_gemm_launch_w<false>(g, epi, groups, max_rows, st);
     // 256-row blocks (the blocks of one vocabulary tile run on one XCD, so
     // the tile's weight rows come from its L2 after the first); statistics
-    // partials per 128 vocabulary rows
+    // partials per 128 vocabulary rows; bf16 or e4m3 vocabulary rows
     if (g.ksplit > 1 || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
+    if (g.w_scale) return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM, TBM, true>(g, 1, g.M, st);
     return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM>(g, 1, g.M, st);
 }
 

@@ -24,6 +24,8 @@ using namespace dgapi;
 struct dg_model {
     dg_config cfg;
     const void* embed;
+    const void* lm8 = nullptr;        // optional e4m3 LM head [vocab][d]
+    const uint16_t* lm8_scale = nullptr;
     const float* final_norm;
     std::vector<dg_layer_weights> layers;
 };
@@ -397,15 +399,18 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
     if (!normed_in)
         DG_TRY(dg::launch_rmsnorm(w.X, n, c.d_model, m->final_norm, c.norm_eps, w.A, f32, state, st), "final norm");
     dg::GemmArgs g = gargs();
-    g.A = w.A; g.lda = c.d_model; g.W = m->embed; g.ldw = c.d_model;
+    g.A = w.A; g.lda = c.d_model; g.W = m->lm8 ? m->lm8 : m->embed; g.ldw = c.d_model;
+    g.w_scale = m->lm8_scale;
     g.M = n; g.N = c.vocab; g.K = c.d_model;
     g.C = stats->logits; g.ldc = stats->logits_ld; g.c_f32 = f32;
     g.parts = w.parts; g.nsplit = lm_nsplit(c);
     g.state = state; g.step_override = step_override; g.sp = sp; g.mask_id = c.mask_id;
     g.bias_tok = bias_tok; g.bias_val = bias_val;
     int slot = timing_begin(st, DG_TIME_LM_HEAD);
-    if (dg::tile_gemm_supported(g, f32, 0, dg::EPI_LMHEAD))
+    if (dg::tile_gemm_supported(g, f32, m->lm8 != nullptr, dg::EPI_LMHEAD))
         DG_TRY(dg::tile_gemm_launch(g, dg::EPI_LMHEAD, 1, n, st), "lm head");
+    else if (m->lm8)
+        return fail(DG_E_UNSUPPORTED, "e4m3 LM head: shape outside the tile kernel");
     else
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
     timing_end(slot, st);
@@ -481,6 +486,10 @@ dg_status dg_model_create(const dg_config* c, const dg_weights* w, dg_model** ou
     if (!w->embed || !w->final_norm || !w->layers) return fail(DG_E_INVALID, "weight pointer is NULL");
     auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
     if (!a16(w->embed) || !a16(w->final_norm)) return fail(DG_E_INVALID, "weights must be 16-byte aligned");
+    if ((w->lm_head_e4m3 == nullptr) != (w->lm_head_scale == nullptr))
+        return fail(DG_E_INVALID, "lm_head_e4m3 and lm_head_scale must both be set or both NULL");
+    if (w->lm_head_e4m3 && (c->act_dtype != DG_BF16 || !a16(w->lm_head_e4m3)))
+        return fail(DG_E_UNSUPPORTED, "an e4m3 LM head needs bf16 activations and 16-byte alignment");
     const bool fp8 = c->weight_dtype == DG_FP8_E4M3;
     for (int l = 0; l < c->n_layers; ++l) {
         const dg_layer_weights& L = w->layers[l];
@@ -497,6 +506,8 @@ dg_status dg_model_create(const dg_config* c, const dg_weights* w, dg_model** ou
     if (!m) return fail(DG_E_INVALID, "out of host memory");
     m->cfg = *c;
     m->embed = w->embed;
+    m->lm8 = w->lm_head_e4m3;
+    m->lm8_scale = (const uint16_t*)w->lm_head_scale;
     m->final_norm = w->final_norm;
     m->layers.assign(w->layers, w->layers + c->n_layers);
     *out = m;

@@ -252,11 +252,18 @@ typedef struct dg_layer_weights {
 
 /* Whole-model weights: the tied embedding / LM-head matrix [vocab][d] (act
  * dtype), the final RMSNorm weight [d] f32, and n_layers layer records
- * (host array, copied by dg_model_create). */
+ * (host array, copied by dg_model_create).
+ * lm_head_e4m3 / lm_head_scale (optional, both NULL or both set; bf16
+ * activations only): an OCP e4m3 copy of the tied matrix, [vocab][d] codes
+ * with one bf16 scale per vocabulary row. When set, the LM head reads it (half
+ * the bytes of the largest single weight read); the input embedding still
+ * reads `embed`. */
 typedef struct dg_weights {
     const void* embed;
     const float* final_norm;
     const dg_layer_weights* layers;
+    const void* lm_head_e4m3;
+    const void* lm_head_scale;
 } dg_weights;
 
 /* KV cache: per layer (host arrays of n_layers device pointers) K of

@@ -245,12 +245,21 @@ class Weights:
     """Float64 view of a model: embedding, final norm and lazily widened layers.
 
     ``layer_fn(l)`` returns layer l's weights as torch tensors; layers are
-    widened on first use and can be dropped with ``release``.
+    widened on first use and can be dropped with ``release``. ``lm_head``
+    (optional): (e4m3 codes [V][d], per-row scales [V]) of an e4m3 copy of the
+    tied matrix that the LM head reads instead of the embedding; ``LM`` is the
+    matrix the LM head uses.
     """
 
-    def __init__(self, cfg, embed, final_norm, layer_fn):
+    def __init__(self, cfg, embed, final_norm, layer_fn, lm_head=None):
         self.cfg = cfg
         self.E = widen(embed)
+        if lm_head is None:
+            self.LM = self.E
+        else:
+            codes, scale = lm_head
+            codes = codes.detach().to("cpu").numpy() if hasattr(codes, "detach") else np.asarray(codes)
+            self.LM = fp8.dequantize(codes, widen(scale))
         self.final_norm = widen(final_norm)
         self._fn = layer_fn
         self._cache: dict[int, dict] = {}
@@ -272,7 +281,7 @@ def canvas_logits(W: Weights, tokens, kv: KVCache, boost=None, keep_layers=True)
         X = decoder_layer(X, W.layer(l), kv.K[l], kv.V[l], l, cfg)
         if not keep_layers:
             W.release(l)
-    return lm_logits(X, W.final_norm, W.E, cfg.norm_eps, boost)
+    return lm_logits(X, W.final_norm, W.LM, cfg.norm_eps, boost)
 
 
 # ---------------------------------------------------------------------------

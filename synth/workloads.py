@@ -144,6 +144,11 @@ def embedding(cfg: ModelConfig, device="cpu") -> torch.Tensor:
                      WEIGHT_STD, dtype=dt, device=device)
 
 
+def lm_head_e4m3(cfg: ModelConfig, device="cpu"):
+    """An e4m3 copy of the tied embedding for the LM head: (codes, scales)."""
+    return quantize_e4m3(embedding(cfg, device=device))
+
+
 def final_norm(cfg: ModelConfig, device="cpu") -> torch.Tensor:
     return torch.ones(cfg.d_model, dtype=torch.float32, device=device)
 

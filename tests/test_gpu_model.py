@@ -3,6 +3,7 @@ one decoder layer (windowed and global, f32 and bf16), the LM head with its
 fused statistics, the encoder prefill/append, and full canvas trajectories
 on the tiny f32 workload (per step, decomposed, and as whole trajectories)."""
 import numpy as np
+import scipy.special
 import pytest
 import torch
 
@@ -125,6 +126,64 @@ def test_decoder_layer(B, name, layer):
     g_o = np.take_along_axis(tr["gates"], np.argsort(tr["ids"], 1), 1)
     g_g = np.take_along_axis(gates.cpu().numpy(), np.argsort(ids_g, 1), 1)
     assert np.abs(g_o[same] - g_g[same]).max() < (2e-2 if name != "tiny_f32" else 1e-5)
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "full_width"])
+def test_e4m3_lm_head_logits_and_statistics(B, name):
+    """The LM head reading an e4m3 copy of the tied matrix (bf16 scale per
+    vocabulary row): logits within the e4m3 bound of the oracle on the
+    dequantised matrix, statistics and argmax on the logits it wrote, and
+    end-to-end entropies within the first-order bound that the logit gap
+    sets (both heads are limited by the bf16 activations and logits of
+    record, not by the weight format)."""
+    cfg = SMALL_BF16 if name == "small_bf16" else wl.FULL_LAYER
+    embed = wl.embedding(cfg, device="cuda")
+    codes, scale = wl.lm_head_e4m3(cfg, device="cuda")
+    fnorm = wl.final_norm(cfg, device="cuda")
+    layers = [wl.layer_weights(cfg, l, device="cuda") for l in range(cfg.n_layers)]
+    m8 = B.Model(cfg, embed, fnorm, layers, lm_head_e4m3=codes, lm_head_scale=scale)
+    mb = B.Model(cfg, embed, fnorm, layers)
+    n = cfg.canvas
+    g = torch.Generator().manual_seed(6)
+    X = torch.randn(n, cfg.d_model, generator=g).cuda()
+    bt, bv = wl.canvas_boost(cfg, 1)
+    bt, bv = bt.cuda(), bv.cuda()
+    ws = m8.workspace(n)
+    scfg = B.sampler_default()
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    Xn = X.cpu().numpy().astype(np.float64)
+    W8 = M.Weights(cfg, embed.cpu(), fnorm.cpu(), lambda l: {}, lm_head=(codes.cpu(), scale.cpu()))
+    Lo8 = M.lm_logits(Xn, W8.final_norm, W8.LM, cfg.norm_eps)
+    Lob = M.lm_logits(Xn, W8.final_norm, W8.E, cfg.norm_eps)
+    btn, bvn = bt.cpu().numpy(), bv.cpu().numpy().astype(np.float64)
+    for t in (0, 47):
+        tau = S.temperature(t, ocfg)
+        res = {}
+        for key, model, Lo in (("e4m3", m8, Lo8), ("bf16", mb, Lob)):
+            stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=model.act_dtype)
+            B.lm_head(model, X, scfg, t, stats, ws, bt, bv)
+            torch.cuda.synchronize()
+            Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+            Lb = Lg.copy()
+            Lb[np.arange(n), btn] += bvn
+            H, a, Mx, Ss = S.row_stats(Lb, tau, cfg.mask_id)
+            Hg = stats.entropy.cpu().numpy()
+            assert np.abs(Hg - H).max() < ENT_TOL
+            assert np.array_equal(stats.argmax.cpu().numpy(), a)
+            Lo_b = Lo.copy()
+            Lo_b[np.arange(n), btn] += bvn
+            Ho, _, _, _ = S.row_stats(Lo_b, tau, cfg.mask_id)
+            # |dH| <= max_v |dz_v| * sum_v p_v |log p_v + H| to first order
+            zo = S.tempered(Lo_b, tau, cfg.mask_id)
+            lp = zo - scipy.special.logsumexp(zo, axis=1, keepdims=True)
+            p = np.exp(lp)
+            spread = np.nansum(p * np.abs(np.where(p > 0, lp, 0.0) + Ho[:, None]), axis=1)
+            keep = np.arange(cfg.vocab) != cfg.mask_id
+            dz = np.abs(Lb - Lo_b)[:, keep].max(axis=1) / tau
+            assert np.all(np.abs(Hg - Ho) <= 1.5 * spread * dz + 1e-5), (key, t)
+            res[key] = rel_l2_rows(Lg, Lo).max()
+        assert res["e4m3"] < 5e-2, res
+        assert res["e4m3"] < 1.5 * res["bf16"] + 1e-4, res
 
 
 @pytest.mark.parametrize("name", list(CFGS))

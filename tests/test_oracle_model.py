@@ -320,3 +320,51 @@ def test_decoder_attention_is_one_joint_softmax():
         p = np.exp(s - s.max(1, keepdims=True))
         p /= p.sum(1, keepdims=True)
         assert np.allclose(tr["attn"][:, h], p @ vals, atol=1e-13)
+
+
+# ------------------------------------------------------ e4m3 LM head -------
+
+def test_e4m3_lm_head_logits_by_brute_force():
+    """The LM head on an e4m3 copy of the tied matrix: each logit is the sum
+    over d of the normalised activation times the code's value (the scalar
+    e4m3 decoder) times its vocabulary row's scale; the embedding lookup is
+    untouched."""
+    from oracle import fp8
+    cfg = SMALL.replace(vocab=24, d_model=32)
+    codes, scale = wl.lm_head_e4m3(cfg)
+    W8 = M.Weights(cfg, wl.embedding(cfg), wl.final_norm(cfg), lambda l: wl.layer_weights(cfg, l),
+                   lm_head=(codes, scale))
+    Wb = _tiny_model(cfg)
+    assert np.array_equal(W8.E, Wb.E)
+    rng = np.random.default_rng(4)
+    X = rng.normal(size=(3, cfg.d_model))
+    L8 = M.lm_logits(X, W8.final_norm, W8.LM, cfg.norm_eps)
+    a = M.rmsnorm(X, W8.final_norm, cfg.norm_eps)
+    c = codes.numpy()
+    s = scale.float().numpy()
+    for i in range(3):
+        for v in range(cfg.vocab):
+            want = sum(a[i, k] * fp8.e4m3_value(int(c[v, k])) for k in range(cfg.d_model)) * float(s[v])
+            assert abs(L8[i, v] - want) <= 1e-12 * max(1.0, abs(want))
+    # close to, but not the same as, the bf16 head
+    Lb = M.lm_logits(X, Wb.final_norm, Wb.LM, cfg.norm_eps)
+    r = np.linalg.norm(L8 - Lb) / np.linalg.norm(Lb)
+    assert 1e-4 < r < 0.1, r
+
+
+def test_canvas_logits_read_the_e4m3_head():
+    cfg = SMALL
+    codes, scale = wl.lm_head_e4m3(cfg)
+    W8 = M.Weights(cfg, wl.embedding(cfg), wl.final_norm(cfg), lambda l: wl.layer_weights(cfg, l),
+                   lm_head=(codes, scale))
+    Wb = _tiny_model(cfg)
+    kv = M.KVCache.empty(cfg)
+    M.encoder_append(Wb, kv, wl.prefix_tokens(cfg, 10).numpy())
+    toks = np.full(cfg.canvas, cfg.mask_id)
+    L8 = M.canvas_logits(W8, toks, kv)
+    Lb = M.canvas_logits(Wb, toks, kv)
+    assert not np.allclose(L8, Lb)
+    X = W8.E[toks].copy()
+    for l in range(cfg.n_layers):
+        X = M.decoder_layer(X, W8.layer(l), kv.K[l], kv.V[l], l, cfg)
+    assert np.allclose(L8, M.lm_logits(X, W8.final_norm, W8.LM, cfg.norm_eps), rtol=0, atol=1e-12)
