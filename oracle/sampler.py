@@ -23,7 +23,10 @@ Readings taken where the pages are silent:
   with the MASK id excluded;
 * tau_t = tau0 + (tau1 - tau0) * t / (max_steps - 1), indexed by step;
 * a committed token is a categorical draw by inverse CDF in vocabulary order
-  with one Philox4x32-10 uniform per (position, step, canvas);
+  with one Philox4x32-10 uniform per (position, step, canvas); the optional
+  "gumbel_max" draw takes instead the argmax over v of z_v - log(-log u_v)
+  (the Gumbel-max identity: an exact draw from softmax(z)), one Philox
+  uniform per (position, step, canvas, vocabulary id);
 * ties: argmax -> lowest id; selection order -> lower position first;
 * stop is tested after the commit; on stop, at the last step, or when every
   position is committed, the remaining positions take their argmax.
@@ -55,6 +58,7 @@ class SamplerConfig:
     stable_steps: int = 2
     bound_mode: str = "sum"           # "sum" | "sum_minus_max"
     commit_mode: str = "keep"         # "keep" | "reselect_all"
+    draw_mode: str = "inverse_cdf"    # "inverse_cdf" | "gumbel_max"
     mask_id: int = -1                 # excluded vocabulary id (-1: none)
 
 
@@ -183,6 +187,48 @@ def draw_uniform(seed: int, pos: int, step: int, canvas_idx: int) -> float:
     return (x0 >> 8) * 2.0 ** -24
 
 
+def philox4x32_10_many(c0, c1, c2, c3, key):
+    """Philox4x32-10 over numpy arrays of counters (uint64 holding 32-bit
+    words), the same rounds as philox4x32_10; returns 4 arrays of words."""
+    c = [np.asarray(x, dtype=np.uint64) & _U32 for x in np.broadcast_arrays(c0, c1, c2, c3)]
+    k0, k1 = (int(k) & _U32 for k in key)
+    m = np.uint64(_U32)
+    for r in range(10):
+        if r:
+            k0 = (k0 + _PHILOX_W0) & _U32
+            k1 = (k1 + _PHILOX_W1) & _U32
+        p0 = np.uint64(_PHILOX_M0) * c[0]
+        p1 = np.uint64(_PHILOX_M1) * c[2]
+        hi0, lo0 = p0 >> np.uint64(32), p0 & m
+        hi1, lo1 = p1 >> np.uint64(32), p1 & m
+        c = [hi1 ^ c[1] ^ np.uint64(k0), lo1, hi0 ^ c[3] ^ np.uint64(k1), lo0]
+    return c
+
+
+def gumbel_uniforms(seed: int, pos: int, step: int, canvas_idx: int, V: int) -> np.ndarray:
+    """u_v in (0,1) for v < V: counter = (pos, step, canvas, 1 + v // 4),
+    output word v % 4, (top 24 bits + 1/2) * 2**-24 (never 0 or 1)."""
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    blocks = np.arange((V + 3) // 4, dtype=np.uint64) + np.uint64(1)
+    w = philox4x32_10_many(pos, step, canvas_idx, blocks, (seed & _U32, seed >> 32))
+    words = np.stack(w, axis=1).reshape(-1)[:V]
+    return ((words >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+
+
+def gumbel_perturbed(logits_row, tau: float, mask_id: int, seed: int, pos: int, step: int,
+                     canvas_idx: int) -> np.ndarray:
+    """z_v - log(-log u_v) with z = softmax's argument (MASK at -inf)."""
+    z = tempered(logits_row, tau, mask_id)
+    u = gumbel_uniforms(seed, pos, step, canvas_idx, z.shape[0])
+    return z - np.log(-np.log(u))
+
+
+def draw_token_gumbel(logits_row, tau: float, mask_id: int, seed: int, pos: int, step: int,
+                      canvas_idx: int) -> int:
+    """Gumbel-max draw: the lowest v maximising z_v - log(-log u_v)."""
+    return int(np.argmax(gumbel_perturbed(logits_row, tau, mask_id, seed, pos, step, canvas_idx)))
+
+
 def draw_token(logits_row, tau: float, mask_id: int, u: float) -> int:
     """Inverse-CDF categorical draw from softmax(L/tau) in vocabulary order.
 
@@ -275,8 +321,13 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
     sel = eb_select(H32, ~cand, cfg.bound, cfg.bound_mode)
     drawn = {}
     for i in np.nonzero(sel)[0]:
-        u = draw_uniform(seed, int(i), t, state.canvas_idx)
-        tok = draw_token(L[i], tau, cfg.mask_id, u)
+        if cfg.draw_mode == "gumbel_max":
+            tok = draw_token_gumbel(L[i], tau, cfg.mask_id, seed, int(i), t, state.canvas_idx)
+        elif cfg.draw_mode == "inverse_cdf":
+            u = draw_uniform(seed, int(i), t, state.canvas_idx)
+            tok = draw_token(L[i], tau, cfg.mask_id, u)
+        else:
+            raise ValueError("unknown draw mode")
         state.tokens[i] = tok
         state.committed[i] = True
         drawn[int(i)] = tok

@@ -497,3 +497,80 @@ def test_unknown_commit_mode_is_rejected():
     with pytest.raises(ValueError):
         S.sampler_step(S.CanvasState.fresh(4, 3), np.zeros((4, 4)), 0,
                        S.SamplerConfig(mask_id=3, commit_mode="nope"), 1)
+
+
+# ------------------------------------------------------------- Gumbel-max ---
+
+def test_vector_philox_equals_the_scalar_engine():
+    rng = np.random.default_rng(17)
+    ctr = rng.integers(0, 2 ** 32, size=(4, 300), dtype=np.uint64)
+    key = (int(rng.integers(0, 2 ** 32)), int(rng.integers(0, 2 ** 32)))
+    got = S.philox4x32_10_many(*ctr, key)
+    for j in range(300):
+        want = S.philox4x32_10([int(c[j]) for c in ctr], key)
+        assert tuple(int(w[j]) for w in got) == want
+
+
+def test_gumbel_draw_by_brute_force():
+    """Token = lowest argmax of z_v - log(-log u_v), u_v from the scalar
+    engine at counter (pos, step, canvas, 1 + v // 4), word v % 4."""
+    rng = np.random.default_rng(18)
+    seed = 0x1234_5678_9ABC_DEF0
+    for trial in range(20):
+        V = int(rng.integers(2, 40))
+        L = rng.normal(size=V) * 2
+        mask = int(rng.integers(0, V))
+        tau, pos, step, cv = 0.7, int(rng.integers(0, 256)), int(rng.integers(0, 48)), trial
+        best, tok = -math.inf, -1
+        for v in range(V):
+            if v == mask:
+                continue
+            w = S.philox4x32_10((pos, step, cv, 1 + v // 4), (seed & 0xFFFFFFFF, seed >> 32))[v % 4]
+            u = ((w >> 8) + 0.5) * 2.0 ** -24
+            val = L[v] / tau - math.log(-math.log(u))
+            if val > best:
+                best, tok = val, v
+        assert S.draw_token_gumbel(L, tau, mask, seed, pos, step, cv) == tok
+
+
+def test_gumbel_draw_special_rows():
+    L = np.full(64, -np.inf)
+    L[9] = 3.0
+    for pos in range(20):
+        assert S.draw_token_gumbel(L, 0.4, 63, 5, pos, 0, 0) == 9       # one finite logit
+    L = np.zeros(8)
+    L[7] = 100.0                                                          # MASK largest
+    toks = {S.draw_token_gumbel(L, 0.8, 7, 5, pos, 1, 0) for pos in range(200)}
+    assert 7 not in toks and len(toks) > 3
+    u = S.gumbel_uniforms(3, 0, 0, 0, 4096)
+    assert u.min() > 0 and u.max() < 1
+
+
+def test_gumbel_draw_frequencies_follow_softmax():
+    rng = np.random.default_rng(19)
+    V = 10
+    L = rng.normal(size=V) * 1.5
+    tau = 0.8
+    p = scipy.special.softmax(np.where(np.arange(V) == V - 1, -np.inf, L / tau))
+    n = 20000
+    counts = np.zeros(V)
+    for i in range(n):
+        counts[S.draw_token_gumbel(L, tau, V - 1, 99, i % 256, (i // 256) % 48, i // (256 * 48))] += 1
+    assert counts[V - 1] == 0
+    expected = n * p[:V - 1]
+    chi2 = ((counts[:V - 1] - expected) ** 2 / expected).sum()
+    assert chi2 < scipy.stats.chi2.ppf(0.999, V - 2)
+
+
+def test_sampler_step_in_gumbel_mode_draws_the_gumbel_token():
+    rng = np.random.default_rng(20)
+    n, V = 24, 300
+    cfg = S.SamplerConfig(mask_id=V - 1, draw_mode="gumbel_max")
+    st = S.CanvasState.fresh(n, V - 1, canvas_idx=2)
+    L = rng.normal(size=(n, V)) * rng.uniform(1, 40, size=(n, 1))
+    rec = S.sampler_step(st, L, 3, cfg, 77, )
+    tau = S.temperature(3, cfg)
+    for i in np.nonzero(rec.selected)[0]:
+        assert st.tokens[i] == S.draw_token_gumbel(L[i], tau, V - 1, 77, int(i), 3, 2)
+    with pytest.raises(ValueError):
+        S.sampler_step(S.CanvasState.fresh(n, V - 1), L, 0, S.SamplerConfig(mask_id=V - 1, draw_mode="x"), 1)
