@@ -207,12 +207,13 @@ def philox4x32_10_many(c0, c1, c2, c3, key):
 
 def gumbel_uniforms(seed: int, pos: int, step: int, canvas_idx: int, V: int) -> np.ndarray:
     """u_v in (0,1) for v < V: counter = (pos, step, canvas, 1 + v // 4),
-    output word v % 4, (top 24 bits + 1/2) * 2**-24 (never 0 or 1)."""
+    output word v % 4, (top 23 bits + 1/2) * 2**-23: never 0 or 1, and every
+    value exact in float32, so both precisions take the same u."""
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     blocks = np.arange((V + 3) // 4, dtype=np.uint64) + np.uint64(1)
     w = philox4x32_10_many(pos, step, canvas_idx, blocks, (seed & _U32, seed >> 32))
     words = np.stack(w, axis=1).reshape(-1)[:V]
-    return ((words >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+    return ((words >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
 
 
 def gumbel_perturbed(logits_row, tau: float, mask_id: int, seed: int, pos: int, step: int,

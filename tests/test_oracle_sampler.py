@@ -526,7 +526,7 @@ def test_gumbel_draw_by_brute_force():
             if v == mask:
                 continue
             w = S.philox4x32_10((pos, step, cv, 1 + v // 4), (seed & 0xFFFFFFFF, seed >> 32))[v % 4]
-            u = ((w >> 8) + 0.5) * 2.0 ** -24
+            u = ((w >> 9) + 0.5) * 2.0 ** -23
             val = L[v] / tau - math.log(-math.log(u))
             if val > best:
                 best, tok = val, v
