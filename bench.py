@@ -92,6 +92,7 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     stats = B.StepStats(n * nb, device=dev, vocab=cfg.vocab, logits_dtype=model.act_dtype, n_layers=cfg.n_layers,
                         n_canvases=nb)
     scfg = B.sampler_default()
+    scfg.draw_mode = B.DG_DRAW_GUMBEL_MAX if args.gumbel else B.DG_DRAW_INVERSE_CDF
     sched = {"t": 0, "canvas": 0, "committed": 0}
 
     def run(K, record=None, use_graph=False):
@@ -243,13 +244,14 @@ def bench_stack(args, torch, B, which):
     plen = {"stack30": 8192, "one_layer": 4096, "tiny": wl.TINY_PREFIX, "longctx": 131072}[which]
     res, handles = _model_workload(args, torch, B, cfg, plen, 8)
     wname = (f"{cfg.name}_canvas{cfg.canvas}_prompt{plen}" + (f"_batch{args.batch}" if args.batch > 1 else "")
-             + ("_e4m3head" if args.fp8_lm_head else ""))
+             + ("_e4m3head" if args.fp8_lm_head else "") + ("_gumbel" if args.gumbel else ""))
     res["config"] = {"workload": wname, "layers": cfg.n_layers,
                      "d_model": cfg.d_model, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv x {cfg.head_dim}",
                      "experts": f"{cfg.n_experts} top-{cfg.top_k} + 1 shared, F={cfg.ffn_hidden}",
                      "vocab": cfg.vocab, "canvas": cfg.canvas, "batch": args.batch, "window": cfg.window,
                      "global_every": cfg.global_every, "prompt": plen, "weights": cfg.weight_dtype,
-                     "lm_head": "e4m3" if args.fp8_lm_head else cfg.act_dtype}
+                     "lm_head": "e4m3" if args.fp8_lm_head else cfg.act_dtype,
+                     "draw": "gumbel_max" if args.gumbel else "inverse_cdf"}
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_model_step(cfg, handles, torch, B, plen, args.batch)
     return res
@@ -435,6 +437,7 @@ def bench_sampler(args, torch, B):
     stats = B.StepStats(n, dev)
     ws = torch.empty(B.sampler_workspace_bytes(n, V), dtype=torch.uint8, device=dev)
     cfg = B.sampler_default()
+    cfg.draw_mode = B.DG_DRAW_GUMBEL_MAX if args.gumbel else B.DG_DRAW_INVERSE_CDF
 
     def run(k0, K):
         for k in range(k0, k0 + K):
@@ -461,14 +464,15 @@ def bench_sampler(args, torch, B):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "logit_stats_kernel", "kernel_ms": round(kern_ms, 5),
                      "algorithmic_bytes_per_launch": bytes_per_launch},
-        "config": {"workload": "sampler_only_256x262144_bf16", "canvas": n, "vocab": V, "batch": 1,
+        "config": {"workload": "sampler_only_256x262144_bf16" + ("_gumbel" if args.gumbel else ""), "canvas": n,
+                   "vocab": V, "batch": 1, "draw": "gumbel_max" if args.gumbel else "inverse_cdf",
                    "logit_buffers": 4},
         "dtype": "bf16",
     }
     if not args.no_cpu:
         import numpy as np
         from oracle import sampler as S
-        ocfg = S.SamplerConfig(mask_id=mask)
+        ocfg = S.SamplerConfig(mask_id=mask, draw_mode="gumbel_max" if args.gumbel else "inverse_cdf")
         Ls = [b.float().cpu().numpy() for b in bufs[:2]]
         st = S.CanvasState.fresh(n, mask)
         times = []
@@ -498,6 +502,7 @@ def main():
     ap.add_argument("--prefill-tokens", type=int, default=131072)
     ap.add_argument("--fp8-lm-head", action="store_true",
                     help="the LM head reads an e4m3 copy of the tied matrix (model workloads)")
+    ap.add_argument("--gumbel", action="store_true", help="Gumbel-max draws fused into the statistics pass")
     ap.add_argument("--batch", type=int, default=1,
                     help="canvases of different users stepped together (model workloads; 256 x batch <= 1024)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -510,6 +515,8 @@ def main():
         args.warmup = 1 if args.workload == "prefill" else 4
     if (args.batch != 1 or args.fp8_lm_head) and args.workload in ("sampler", "prefill", "tiny"):
         ap.error("--batch and --fp8-lm-head apply to the bf16 model workloads")
+    if args.gumbel and (args.batch != 1 or args.workload in ("prefill", "tiny")):
+        ap.error("--gumbel applies to single-canvas bf16 steps and the sampler workload")
     if args.gpus != 1:
         print("bench.py measures one GPU: the denoising step here is built for a single MI355X "
               "and has no multi-GPU path", file=sys.stderr)

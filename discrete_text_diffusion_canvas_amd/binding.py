@@ -19,6 +19,7 @@ DG_OK = 0
 DG_F32, DG_BF16, DG_FP8_E4M3 = 0, 1, 2
 DG_BOUND_SUM, DG_BOUND_SUM_MINUS_MAX = 0, 1
 DG_COMMIT_KEEP, DG_COMMIT_RESELECT_ALL = 0, 1
+DG_DRAW_INVERSE_CDF, DG_DRAW_GUMBEL_MAX = 0, 1
 STATE_WORDS = 8
 ST_DONE, ST_STEP, ST_COMMITTED, ST_STABLE, ST_SELECTED, ST_STOP, ST_FINISHED = range(7)
 
@@ -32,7 +33,7 @@ class DgError(RuntimeError):
 class SamplerCfg(C.Structure):
     _fields_ = [("max_steps", C.c_int32), ("temp_start", C.c_float), ("temp_end", C.c_float),
                 ("bound", C.c_float), ("stop_entropy", C.c_float), ("stable_steps", C.c_int32),
-                ("bound_mode", C.c_int32), ("commit_mode", C.c_int32)]
+                ("bound_mode", C.c_int32), ("commit_mode", C.c_int32), ("draw_mode", C.c_int32)]
 
 
 class CanvasStruct(C.Structure):

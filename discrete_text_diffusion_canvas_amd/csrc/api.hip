@@ -40,6 +40,8 @@ dg_status check_sampler_cfg(const dg_sampler_cfg* s) {
         return fail(DG_E_INVALID, "unknown bound_mode");
     if (s->commit_mode != DG_COMMIT_KEEP && s->commit_mode != DG_COMMIT_RESELECT_ALL)
         return fail(DG_E_INVALID, "unknown commit_mode");
+    if (s->draw_mode != DG_DRAW_INVERSE_CDF && s->draw_mode != DG_DRAW_GUMBEL_MAX)
+        return fail(DG_E_INVALID, "unknown draw_mode");
     return DG_OK;
 }
 
@@ -53,6 +55,9 @@ dg::SamplerParams to_params(const dg_sampler_cfg* s) {
     p.stable_steps = s->stable_steps;
     p.bound_mode = s->bound_mode;
     p.commit_mode = s->commit_mode;
+    p.draw_mode = s->draw_mode;
+    p.seed_lo = p.seed_hi = 0;
+    p.canvas_idx = 0;
     return p;
 }
 
@@ -116,7 +121,8 @@ using namespace dgapi;
 
 size_t sampler_ws(int n, int V) {
     return align256((size_t)n * dg::sampler_nsplit(V) * sizeof(dg::RowPart)) +
-           align256((size_t)n * sizeof(int32_t)) + align256((size_t)n * dg::draw_nchunk(V) * sizeof(double));
+           align256((size_t)n * sizeof(int32_t)) + align256((size_t)n * dg::draw_nchunk(V) * sizeof(double)) +
+           align256((size_t)n * sizeof(int32_t));
 }
 
 }  // namespace
@@ -137,6 +143,7 @@ dg_sampler_cfg dg_sampler_default(void) {
     c.stable_steps = 2;
     c.bound_mode = DG_BOUND_SUM;
     c.commit_mode = DG_COMMIT_KEEP;
+    c.draw_mode = DG_DRAW_INVERSE_CDF;
     return c;
 }
 
@@ -203,10 +210,14 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
     if (!ws || ws_bytes < sampler_ws(n, vocab)) return fail(DG_E_CAPACITY, "workspace too small");
     hipStream_t st = (hipStream_t)stream;
     dg::SamplerParams sp = to_params(scfg);
+    sp.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    sp.seed_hi = (uint32_t)(seed >> 32);
+    sp.canvas_idx = canvas->canvas_idx;
     Carve cv(ws);
     dg::RowPart* parts = cv.take<dg::RowPart>((size_t)n * dg::sampler_nsplit(vocab));
     int32_t* sel_list = cv.take<int32_t>(n);
     double* chunk_sum = cv.take<double>((size_t)n * dg::draw_nchunk(vocab));
+    int32_t* gtok = sp.draw_mode ? cv.take<int32_t>(n) : nullptr;
     int f32 = logits_dtype == DG_F32;
     int slot = timing_begin(st, DG_TIME_LM_HEAD);
     if (dg_status s = hip_check(dg::launch_logit_stats(logits, f32, ld, n, vocab, canvas->state, step_idx, sp, mask_id,
@@ -215,14 +226,14 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
         return s;
     timing_end(slot, st);
     if (dg_status s = hip_check(dg::launch_merge_rows(parts, n, dg::sampler_nsplit(vocab), canvas->state,
-                                                      stats->entropy, stats->lse, stats->argmax, st),
+                                                      stats->entropy, stats->lse, stats->argmax, gtok, st),
                                 "merge_rows"))
         return s;
     return hip_check(dg::launch_sampler_tail(logits, f32, ld, n, vocab, mask_id, canvas->bias_tok,
                                              canvas->bias_val, stats->entropy, stats->argmax, canvas->state,
                                              step_idx, sp, seed, canvas->canvas_idx, canvas->tokens,
                                              canvas->committed, canvas->prev_argmax, stats->selected, sel_list,
-                                             chunk_sum, stats->mean_entropy, st),
+                                             chunk_sum, gtok, stats->mean_entropy, st),
                      "sampler tail");
 }
 

@@ -159,7 +159,35 @@ struct RowPart {
     float t;     // sum 2^(z2 - m2) (z2 - m2)
     float lmax;  // max raw (biased) logit over the tile
     int amax;    // its lowest column index (-1 if empty)
-    int pad[3];
+    int pad[3];  // Gumbel-max draws: [0] best z - log(-log u) (float bits), [1] its column (-1: none)
 };
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC'11), written from the paper's description: ten rounds, each
+// multiplying words 0 and 2 by fixed odd constants, swapping the high halves
+// into the other words xor the round key; the key advances by two Weyl
+// constants.
+__device__ __forceinline__ u32x4 philox10(u32x4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
+        uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
+        u32x4 o;
+        o[0] = hi1 ^ c[1] ^ k0;
+        o[1] = lo1;
+        o[2] = hi0 ^ c[3] ^ k1;
+        o[3] = lo0;
+        c = o;
+    }
+    return c;
+}
+
+// Gumbel noise -log(-log u) of one Philox word: u = (top 23 bits + 1/2) *
+// 2^-23, exact in float32 and inside (0, 1).
+__device__ __forceinline__ float gumbel_of(uint32_t w) {
+    const float u = ((float)(w >> 9) + 0.5f) * 1.1920928955078125e-7f;
+    return -logf(-logf(u));
+}
 
 }  // namespace dg

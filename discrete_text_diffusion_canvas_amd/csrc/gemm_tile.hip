@@ -285,11 +285,45 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T
         __syncthreads();
         if (act && part == 0) { sum += row[BN]; tt += row[BN + 1]; }
     }
+    // Gumbel-max draws: this tile's lowest column maximising z - log(-log u),
+    // z = (L + bias) / tau, u from Philox at (row, step, canvas, 1 + v / 4)
+    float gv = -INFINITY;
+    int gi = 0x7fffffff;
+    if (g.sp.draw_mode) {
+        const float inv_tau = (float)(1.0 / lm_tau_at(g.sp, step));
+        if (act) {
+            for (int c = c0; c < c0 + CW && n0 + c < N; c += 4) {
+                const int v0 = n0 + c;
+                const u32x4 wd = philox10(u32x4{(uint32_t)(rbase + r), (uint32_t)step, (uint32_t)g.sp.canvas_idx,
+                                                (uint32_t)(1 + v0 / 4)},
+                                          g.sp.seed_lo, g.sp.seed_hi);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int v = v0 + u;
+                    if (v >= N || v == g.mask_id) continue;
+                    const float val = (row[c + u] + (v == bt ? bv : 0.f)) * inv_tau + gumbel_of(wd[u]);
+                    if (val > gv) { gv = val; gi = v; }
+                }
+            }
+        }
+        if constexpr (TPR == 2) {
+            __syncthreads();  // part 0 has read the sums
+            if (act && part == 1) { row[BN + 2] = gv; row[BN + 3] = __int_as_float(gi); }
+            __syncthreads();
+            if (act && part == 0) {
+                const float ov = row[BN + 2];
+                const int oi = __float_as_int(row[BN + 3]);
+                if (ov > gv || (ov == gv && oi < gi)) { gv = ov; gi = oi; }
+            }
+        }
+    }
     if (act && part == 0) {
         RowPart p;
         p.m2 = rawm == -INFINITY ? -INFINITY : vm; p.s = sum; p.t = tt; p.lmax = rawm;
         p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
-        p.pad[0] = p.pad[1] = p.pad[2] = 0;
+        p.pad[0] = __float_as_int(gv);
+        p.pad[1] = gi == 0x7fffffff ? -1 : gi;
+        p.pad[2] = 0;
         g.parts[(int64_t)(rbase + r) * g.nsplit + tile] = p;
     }
 }

@@ -73,6 +73,7 @@ struct Work {
     dg::RowPart* parts;  // [min(T, canvas)][nsplit]
     int32_t* sel_list;
     double* chunk_sum;
+    int32_t* gtok;      // [Nc]: Gumbel-max candidates of the rows
     int32_t* bias_tok;  // [T]: a batch's per-row bias tokens (-1: none)
     float* bias_val;    // [T]
     size_t bytes;
@@ -149,6 +150,7 @@ Work carve(const dg_model* m, void* base, int T) {
     w.parts = cv.take<dg::RowPart>((size_t)Nc * lm_nsplit(c));
     w.sel_list = cv.take<int32_t>(Nc);
     w.chunk_sum = cv.take<double>((size_t)Nc * dg::draw_nchunk(c.vocab));
+    w.gtok = cv.take<int32_t>(Nc);
     w.bias_tok = cv.take<int32_t>(T);
     w.bias_val = cv.take<float>(T);
     w.bytes = cv.off;
@@ -393,7 +395,7 @@ dg_status encoder_chunk(const dg_model* m, const Work& w, int n, const dg_kv* kv
 
 dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerParams& sp, int step_override,
                   const int32_t* state, const int32_t* bias_tok, const float* bias_val, dg_step_stats* stats,
-                  bool normed_in, hipStream_t st) {
+                  bool normed_in, hipStream_t st, int32_t* gtok = nullptr) {
     const dg_config& c = m->cfg;
     const int f32 = c.act_dtype == DG_F32;
     if (!normed_in)
@@ -409,12 +411,13 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
     int slot = timing_begin(st, DG_TIME_LM_HEAD);
     if (dg::tile_gemm_supported(g, f32, m->lm8 != nullptr, dg::EPI_LMHEAD))
         DG_TRY(dg::tile_gemm_launch(g, dg::EPI_LMHEAD, 1, n, st), "lm head");
-    else if (m->lm8)
-        return fail(DG_E_UNSUPPORTED, "e4m3 LM head: shape outside the tile kernel");
+    else if (m->lm8 || sp.draw_mode)
+        return fail(DG_E_UNSUPPORTED, "e4m3 LM head or Gumbel-max draws: shape outside the tile kernel");
     else
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
     timing_end(slot, st);
-    DG_TRY(dg::launch_merge_rows(w.parts, n, lm_nsplit(c), state, stats->entropy, stats->lse, stats->argmax, st),
+    DG_TRY(dg::launch_merge_rows(w.parts, n, lm_nsplit(c), state, stats->entropy, stats->lse, stats->argmax,
+                                 sp.draw_mode ? gtok : nullptr, st),
            "merge rows");
     return DG_OK;
 }
@@ -611,11 +614,16 @@ dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, 
     if (dg_status s = check_kv(m, kv)) return s;
     if (dg_status s = check_logits(m, stats, n)) return s;
     if (step_idx < -1 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
+    if (scfg->draw_mode == DG_DRAW_GUMBEL_MAX && m->cfg.act_dtype != DG_BF16)
+        return fail(DG_E_UNSUPPORTED, "Gumbel-max draws need bf16 activations");
     Work w;
     if (dg_status s = ws_for(m, ws, ws_bytes, n, &w)) return s;
     w.experts_hit = stats->experts_hit;
     hipStream_t st = (hipStream_t)stream;
-    const dg::SamplerParams sp = to_params(scfg);
+    dg::SamplerParams sp = to_params(scfg);
+    sp.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    sp.seed_hi = (uint32_t)(seed >> 32);
+    sp.canvas_idx = canvas->canvas_idx;
     const dg_config& c = m->cfg;
     DG_TRY(dg::launch_embed(m->embed, c.act_dtype == DG_F32, c.d_model, c.vocab, canvas->tokens, n, w.X, canvas->state, st),
            "embed");
@@ -626,13 +634,13 @@ dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, 
         if (dg_status s = decoder_layer(m, l, w, n, &seg, 1, canvas->state, l > 0, next, st)) return s;
     }
     if (dg_status s = lm_head(m, w, n, sp, step_idx, canvas->state, canvas->bias_tok, canvas->bias_val, stats, true,
-                              st))
+                              st, w.gtok))
         return s;
     return hip_check(dg::launch_sampler_tail(stats->logits, c.act_dtype == DG_F32, stats->logits_ld, n, c.vocab,
                                              c.mask_id, canvas->bias_tok, canvas->bias_val, stats->entropy,
                                              stats->argmax, canvas->state, step_idx, sp, seed, canvas->canvas_idx,
                                              canvas->tokens, canvas->committed, canvas->prev_argmax, stats->selected,
-                                             w.sel_list, w.chunk_sum, stats->mean_entropy, st),
+                                             w.sel_list, w.chunk_sum, w.gtok, stats->mean_entropy, st),
                      "sampler tail");
 }
 
@@ -672,6 +680,7 @@ dg_status dg_canvas_step_batch(const dg_model* m, dg_canvas* canvases, const dg_
     if (nb < 1 || nb > 64) return fail(DG_E_SHAPE, "batch of %d canvases outside 1..64", nb);
     if (dg_status s = check_sampler_cfg(scfg)) return s;
     if (step_idx < 0 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
+    if (scfg->draw_mode != DG_DRAW_INVERSE_CDF) return fail(DG_E_UNSUPPORTED, "batches draw by inverse CDF");
     const dg_config& c = m->cfg;
     Seg segs[64];
     int rows = 0;
@@ -733,7 +742,7 @@ dg_status dg_canvas_step_batch(const dg_model* m, dg_canvas* canvases, const dg_
                                        c.mask_id, cv.bias_tok, cv.bias_val, stats->entropy + sg.row0,
                                        stats->argmax + sg.row0, cv.state, step_idx, sp, seed, cv.canvas_idx,
                                        cv.tokens, cv.committed, cv.prev_argmax, stats->selected + sg.row0,
-                                       w.sel_list, w.chunk_sum, stats->mean_entropy + b, st),
+                                       w.sel_list, w.chunk_sum, nullptr, stats->mean_entropy + b, st),
                "sampler tail");
     }
     return DG_OK;

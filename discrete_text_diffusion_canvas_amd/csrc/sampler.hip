@@ -66,8 +66,11 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
 // for bf16 logits z2 preserves the order and the equalities of x exactly (two
 // distinct bf16 values differ by at least 2^-8 relative), for f32 logits the
 // raw values are compared instead.
+// GUMBEL: the same pass also keeps the Gumbel-max candidate of the split, the
+// lowest column maximising z_v - log(-log u_v) with z = (L + bias) / tau and
+// u_v from Philox at counter (row, step, canvas, 1 + v / 4), word v % 4.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool GUMBEL>
 __global__ void __launch_bounds__(256) logit_stats_kernel(
     const T* __restrict__ logits, int64_t ld, int V, int split_cols,
     const int32_t* __restrict__ state, int step_override, SamplerParams sp, int mask_id,
@@ -88,6 +91,8 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
 
     EntPart e{-INFINITY, 0.f, 0.f};
     ArgMax am{-INFINITY, 0x7fffffff};
+    ArgMax gm{-INFINITY, 0x7fffffff};
+    const float inv_tau = (float)(1.0 / tau_at(sp, t));
     for (int base = c0; base < c1; base += 256 * 8 * PER) {
         float x[PER][8];
 #pragma unroll
@@ -137,6 +142,27 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
                     }
                 }
         }
+        if constexpr (GUMBEL) {
+            // z = z2 / log2(e) and the bias / MASK handling of z2 above
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int v0 = base + (j * 256 + tid) * 8;
+                if (v0 >= c1) continue;
+                u32x4 w[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    w[h] = philox10(u32x4{(uint32_t)row, (uint32_t)t, (uint32_t)sp.canvas_idx,
+                                          (uint32_t)(1 + v0 / 4 + h)},
+                                    sp.seed_lo, sp.seed_hi);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float zn = z[j][q] * 0.6931471805599453f;
+                    if (zn == -INFINITY || v0 + q >= c1) continue;
+                    const float val = zn + gumbel_of(w[q >> 2][q & 3]);
+                    if (val > gm.v) { gm.v = val; gm.i = v0 + q; }
+                }
+            }
+        }
         if (vm == -INFINITY) continue;
         float ls = 0.f, lt = 0.f;
 #pragma unroll
@@ -154,16 +180,23 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
     }
     e = wave_ent(e);
     am = wave_argmax(am);
+    if constexpr (GUMBEL) gm = wave_argmax(gm);
     __shared__ EntPart se[4];
-    __shared__ ArgMax sa[4];
+    __shared__ ArgMax sa[4], sg[4];
     const int w = tid >> 6;
-    if ((tid & 63) == 0) { se[w] = e; sa[w] = am; }
+    if ((tid & 63) == 0) { se[w] = e; sa[w] = am; sg[w] = gm; }
     __syncthreads();
     if (tid == 0) {
-        for (int i = 1; i < 4; ++i) { e = ent_merge(e, se[i]); am = argmax_merge(am, sa[i]); }
+        for (int i = 1; i < 4; ++i) {
+            e = ent_merge(e, se[i]);
+            am = argmax_merge(am, sa[i]);
+            if constexpr (GUMBEL) gm = argmax_merge(gm, sg[i]);
+        }
         RowPart p;
         p.m2 = e.m; p.s = e.s; p.t = e.t; p.lmax = am.v; p.amax = am.i == 0x7fffffff ? -1 : am.i;
-        p.pad[0] = p.pad[1] = p.pad[2] = 0;
+        p.pad[0] = __float_as_int(gm.v);
+        p.pad[1] = gm.i == 0x7fffffff ? -1 : gm.i;
+        p.pad[2] = 0;
         parts[(int64_t)row * nsplit + sp_i] = p;
     }
 }
@@ -174,13 +207,13 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) merge_rows_kernel(
     const RowPart* __restrict__ parts, int n, int nsplit, const int32_t* __restrict__ state,
-    float* __restrict__ H, float* __restrict__ lse, int32_t* __restrict__ amax) {
+    float* __restrict__ H, float* __restrict__ lse, int32_t* __restrict__ amax, int32_t* __restrict__ gtok) {
     if (state && state[0]) return;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= n) return;
     EntPart e{-INFINITY, 0.f, 0.f};
-    ArgMax am{-INFINITY, 0x7fffffff};
+    ArgMax am{-INFINITY, 0x7fffffff}, gm{-INFINITY, 0x7fffffff};
     const RowPart* p = parts + (int64_t)row * nsplit;
     for (int i = lane; i < nsplit; i += 64) {
         RowPart q = p[i];
@@ -188,9 +221,11 @@ __global__ void __launch_bounds__(256) merge_rows_kernel(
             e = ent_merge(e, EntPart{q.m2, q.s, q.t});
             am = argmax_merge(am, ArgMax{q.lmax, q.amax});
         }
+        if (gtok && q.pad[1] >= 0) gm = argmax_merge(gm, ArgMax{__int_as_float(q.pad[0]), q.pad[1]});
     }
     e = wave_ent(e);
     am = wave_argmax(am);
+    if (gtok) gm = wave_argmax(gm);
     if (lane == 0) {
         const float LN2 = 0.6931471805599453f;
         float l2s = log2f(e.s);
@@ -198,6 +233,7 @@ __global__ void __launch_bounds__(256) merge_rows_kernel(
         H[row] = fmaxf(h, 0.f);
         lse[row] = LN2 * (e.m + l2s);
         amax[row] = am.i == 0x7fffffff ? 0 : am.i;  // no finite logit (NaN input): id 0
+        if (gtok) gtok[row] = gm.i == 0x7fffffff ? amax[row] : gm.i;
     }
 }
 
@@ -271,28 +307,6 @@ __global__ void __launch_bounds__(1024) eb_select_kernel(
         selected[pos] = 1;
         sel_list[i] = pos;
     }
-}
-
-// ---------------------------------------------------------------------------
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), written from the paper's
-// definition: ten rounds; each multiplies words 0 and 2 by fixed constants,
-// the high halves are xored with words 1/3 and the round key, and the key is
-// advanced by two Weyl increments between rounds.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 philox10(u32x4 c, uint32_t k0, uint32_t k1) {
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-        uint32_t lo0 = 0xD2511F53u * c[0], hi0 = __umulhi(0xD2511F53u, c[0]);
-        uint32_t lo1 = 0xCD9E8D57u * c[2], hi1 = __umulhi(0xCD9E8D57u, c[2]);
-        u32x4 o;
-        o[0] = hi1 ^ c[1] ^ k0;
-        o[1] = lo1;
-        o[2] = hi0 ^ c[3] ^ k1;
-        o[3] = lo0;
-        c = o;
-    }
-    return c;
 }
 
 // ---------------------------------------------------------------------------
@@ -526,19 +540,41 @@ hipError_t launch_logit_stats(const void* logits, int dtype_f32, int64_t ld, int
     int cols = (V + ns - 1) / ns;
     cols = ((cols + 2047) / 2048) * 2048;
     dim3 grid(ns, n);
-    if (dtype_f32)
-        logit_stats_kernel<float><<<grid, 256, 0, st>>>((const float*)logits, ld, V, cols, state, step_override,
-                                                        sp, mask_id, bias_tok, bias_val, parts, ns);
-    else
-        logit_stats_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)logits, ld, V, cols, state,
-                                                           step_override, sp, mask_id, bias_tok, bias_val,
-                                                           parts, ns);
+#define DG_STATS(T, G)                                                                                          \
+    logit_stats_kernel<T, G><<<grid, 256, 0, st>>>((const T*)logits, ld, V, cols, state, step_override, sp, \
+                                                   mask_id, bias_tok, bias_val, parts, ns)
+    if (dtype_f32) {
+        if (sp.draw_mode) DG_STATS(float, true);
+        else DG_STATS(float, false);
+    } else {
+        if (sp.draw_mode) DG_STATS(uint16_t, true);
+        else DG_STATS(uint16_t, false);
+    }
+#undef DG_STATS
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Gumbel-max draws: the selected rows sel_list[0 .. state[4]) take the
+// candidate the statistics pass kept for them.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) gumbel_commit_kernel(const int32_t* __restrict__ sel_list,
+                                                            const int32_t* __restrict__ gtok,
+                                                            const int32_t* __restrict__ state,
+                                                            int32_t* __restrict__ tokens,
+                                                            uint8_t* __restrict__ committed) {
+    if (state[0]) return;
+    const int k = state[4];
+    for (int i = threadIdx.x; i < k; i += 256) {
+        const int row = sel_list[i];
+        tokens[row] = gtok[row];
+        committed[row] = 1;
+    }
+}
+
 hipError_t launch_merge_rows(const RowPart* parts, int n, int nsplit, const int32_t* state, float* H,
-                             float* lse, int32_t* amax, hipStream_t st) {
-    merge_rows_kernel<<<(n + 3) / 4, 256, 0, st>>>(parts, n, nsplit, state, H, lse, amax);
+                             float* lse, int32_t* amax, int32_t* gtok, hipStream_t st) {
+    merge_rows_kernel<<<(n + 3) / 4, 256, 0, st>>>(parts, n, nsplit, state, H, lse, amax, gtok);
     return hipGetLastError();
 }
 
@@ -547,11 +583,14 @@ hipError_t launch_sampler_tail(const void* logits, int dtype_f32, int64_t ld, in
                                const int32_t* amax, int32_t* state, int step_override, const SamplerParams& sp,
                                uint64_t seed, int canvas_idx, int32_t* tokens, uint8_t* committed,
                                int32_t* prev_amax, uint8_t* selected, int32_t* sel_list, double* chunk_sum,
-                               double* mean_out, hipStream_t st) {
+                               const int32_t* gtok, double* mean_out, hipStream_t st) {
     eb_select_kernel<<<1, 1024, 0, st>>>(H, committed, n, state, sp, selected, sel_list);
     uint32_t lo = (uint32_t)(seed & 0xffffffffu), hi = (uint32_t)(seed >> 32);
     const int grid = 512;
-    if (dtype_f32) {
+    if (sp.draw_mode) {
+        if (!gtok) return hipErrorInvalidValue;
+        gumbel_commit_kernel<<<1, 256, 0, st>>>(sel_list, gtok, state, tokens, committed);
+    } else if (dtype_f32) {
         draw_chunks_kernel<float><<<grid, 256, 0, st>>>((const float*)logits, ld, V, mask_id, bias_tok, bias_val,
                                                         sel_list, amax, state, step_override, sp, chunk_sum);
         draw_pick_kernel<float><<<n, 256, 0, st>>>((const float*)logits, ld, V, mask_id, bias_tok, bias_val,

@@ -65,6 +65,18 @@ typedef int32_t dg_status;
 #define DG_COMMIT_KEEP 0
 #define DG_COMMIT_RESELECT_ALL 1
 
+/* Draw modes of a committed token, both exact draws from softmax((L + bias) /
+ * tau) without the MASK id. INVERSE_CDF: one Philox4x32-10 uniform per
+ * (position, step, canvas) through the cumulative sum in vocabulary order, in
+ * float64, by kernels that re-read the selected rows' logits.
+ * GUMBEL_MAX: the lowest v maximising z_v - log(-log u_v), u_v = (top 23 bits
+ * of Philox word v % 4 at counter (position, step, canvas, 1 + v / 4) + 1/2)
+ * * 2^-23, float32, evaluated inside the statistics pass (the LM head
+ * epilogue or the logit statistics), so no pass re-reads the logits. Model
+ * steps support it with bf16 activations and one canvas per step. */
+#define DG_DRAW_INVERSE_CDF 0
+#define DG_DRAW_GUMBEL_MAX 1
+
 /* Canvas state words (int32 device array of DG_STATE_WORDS). */
 #define DG_STATE_WORDS 8
 #define DG_ST_DONE 0        /* 1 once the canvas is finished */
@@ -77,7 +89,7 @@ typedef int32_t dg_status;
 
 /* Sampler settings. dg_sampler_default() returns the model card's values
  * (best practice 1): 48 steps, 0.8 -> 0.4, bound 0.1, stop entropy 0.005,
- * 2 stable steps, DG_BOUND_SUM, DG_COMMIT_KEEP. */
+ * 2 stable steps, DG_BOUND_SUM, DG_COMMIT_KEEP, DG_DRAW_INVERSE_CDF. */
 typedef struct dg_sampler_cfg {
     int32_t max_steps;
     float temp_start;
@@ -87,6 +99,7 @@ typedef struct dg_sampler_cfg {
     int32_t stable_steps; /* argmax vector unchanged over this many consecutive steps */
     int32_t bound_mode;   /* DG_BOUND_SUM or DG_BOUND_SUM_MINUS_MAX */
     int32_t commit_mode;  /* DG_COMMIT_KEEP or DG_COMMIT_RESELECT_ALL */
+    int32_t draw_mode;    /* DG_DRAW_INVERSE_CDF or DG_DRAW_GUMBEL_MAX */
 } dg_sampler_cfg;
 
 /* One canvas. All pointers are device memory of n elements (state: 8).

@@ -145,3 +145,17 @@ def test_batch_step_validates_before_launch(lib):
         assert call([64, 64], step=48) == -1
     finally:
         L.dg_model_destroy(h)
+
+
+def test_draw_mode_is_validated(lib):
+    from discrete_text_diffusion_canvas_amd import binding as B
+    L = B.lib
+    assert B.sampler_default().draw_mode == B.DG_DRAW_INVERSE_CDF
+    fake = C.c_void_p(0x1000)
+    canvas = B.CanvasStruct(0x1000, 0x1000, 0x1000, 0x1000, None, None, 16, 0)
+    stats = B.StepStatsStruct(0x1000, 0x1000, 0x1000, 0x1000, None)
+    bad = B.sampler_default()
+    bad.draw_mode = 3
+    code = L.dg_sampler_step(C.byref(bad), fake, B.DG_BF16, 16, 64, 64, 63, C.byref(canvas), 0, 1,
+                             C.byref(stats), fake, 1 << 20, None)
+    assert code == -1 and b"draw_mode" in L.dg_last_error()

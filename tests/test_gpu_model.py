@@ -301,6 +301,45 @@ def test_tiny_canvas_steps_decomposed(B, commit_mode):
         assert rel_l2(kv.k[l][:, :kv.length].cpu().numpy(), okv.K[l]) < 1e-4
 
 
+def test_small_bf16_canvas_steps_with_gumbel_max_draws(B):
+    """Canvas steps whose draws are the Gumbel-max candidates kept by the LM
+    head epilogue: the sampler's decisions on the logits the step wrote
+    against the oracle's Gumbel-max draws (near ties of the perturbed values
+    excused), and the logits themselves against the oracle decoder."""
+    cfg = SMALL_BF16
+    model = device_model(B, cfg)
+    P, n = 160, cfg.canvas
+    prompt = wl.prefix_tokens(cfg, P)
+    kv = B.KVCache(model, P + n)
+    ws = model.workspace(n)
+    B.prefill_append(model, kv, prompt.cuda(), ws)
+    W = oracle_weights(model)
+    okv = M.KVCache.empty(cfg)
+    M.encoder_append(W, okv, prompt.numpy())
+    bt, bv = wl.canvas_boost(cfg, 0)
+    canvas = B.Canvas(n, cfg.mask_id, 4, "cuda", bt.cuda(), bv.cuda())
+    stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=torch.bfloat16)
+    scfg = B.sampler_default()
+    scfg.draw_mode = B.DG_DRAW_GUMBEL_MAX
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id, draw_mode="gumbel_max")
+    st = S.CanvasState.fresh(n, cfg.mask_id, 4)
+    drawn = 0
+    for t in range(10):
+        before = canvas.tokens.cpu().numpy()
+        assert np.array_equal(before, st.tokens)
+        B.canvas_step(model, canvas, kv, t, SEED, scfg, stats, ws)
+        torch.cuda.synchronize()
+        Lo = M.canvas_logits(W, before, okv, (bt.numpy(), bv.numpy()))
+        Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+        Lg[np.arange(n), bt.numpy()] += bv.numpy().astype(np.float64)
+        assert np.quantile(rel_l2_rows(Lg, Lo), 0.9) < 2e-2
+        rec = check_sampler_step(B, st, ocfg, Lg, t, SEED, 4, stats, canvas)
+        drawn += int(rec.selected.sum())
+        if st.done:
+            break
+    assert drawn >= 2
+
+
 def test_tiny_generation_matches_the_oracle_trajectory(B):
     """Two canvases generated end to end on the GPU (dg_generate_canvas with
     the append) against the oracle's own independent generation."""
