@@ -46,6 +46,20 @@
 
 namespace dg {
 
+// Split-KV partial outputs of the bf16 kernels are stored as bf16 (half the
+// bytes written by the splits and read by the merge; the merge sums them in
+// f32); f32 models keep f32 partials.
+#ifndef DG_ATTN_PART_BF16
+#define DG_ATTN_PART_BF16 1
+#endif
+template <typename TL>
+constexpr bool part_bf16() { return DG_ATTN_PART_BF16 && sizeof(TL) == 2; }
+template <typename TL>
+__device__ __forceinline__ void store_part(float* base, int64_t idx, float v) {
+    if constexpr (part_bf16<TL>()) reinterpret_cast<uint16_t*>(base)[idx] = f2bf(v);
+    else base[idx] = v;
+}
+
 template <typename TL> struct AFrag;
 template <> struct AFrag<uint16_t> { typedef u16x8 type; };
 template <> struct AFrag<float> { struct type { f32x4 lo, hi; }; };
@@ -275,9 +289,9 @@ __global__ void __launch_bounds__(256) attention_kernel(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < NT_D; ++j) from_f(out + j * 16 + lr, o[j][i] * inv);
         } else {
-            float* po = a.part_o + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + h) * HD;
+            const int64_t po = (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + h) * HD;
 #pragma unroll
-            for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[j][i];
+            for (int j = 0; j < NT_D; ++j) store_part<TL>(a.part_o, po + j * 16 + lr, o[j][i]);
             if (lr == 0) {
                 float* pm = a.part_ml + (((int64_t)blockIdx.z * a.nq + qr) * a.Hq + h) * 2;
                 pm[0] = m_run[i];
@@ -562,9 +576,9 @@ __global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
 #pragma unroll
                 for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[t][j][i] * inv);
             } else {
-                float* po = a.part_o + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
+                const int64_t po = (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
 #pragma unroll
-                for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[t][j][i];
+                for (int j = 0; j < NT_D; ++j) store_part<uint16_t>(a.part_o, po + j * 16 + lr, o[t][j][i]);
                 if (lr == 0) {
                     float* pm = a.part_ml + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * 2;
                     pm[0] = m_run[t][i];
@@ -894,9 +908,9 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
 #pragma unroll
                 for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[t][j][i] * inv);
             } else {
-                float* po = a.part_o + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
+                const int64_t po = (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
 #pragma unroll
-                for (int j = 0; j < NT_D; ++j) po[j * 16 + lr] = o[t][j][i];
+                for (int j = 0; j < NT_D; ++j) store_part<uint16_t>(a.part_o, po + j * 16 + lr, o[t][j][i]);
                 if (lr == 0) {
                     float* pm = a.part_ml + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * 2;
                     pm[0] = mi * LN2;  // natural-log units, as the merge expects
@@ -930,7 +944,16 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int hd) {
     for (int s = 0; s < MS; ++s) {
         if (s < a.splits) {
             ml[s] = *reinterpret_cast<const float2*>(a.part_ml + (s * rs + pair) * 2);
-            if (has) po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * rs + pair) * hd + c);
+            if (has) {
+                if constexpr (part_bf16<TL>()) {
+                    const uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.part_o) +
+                                                                     (s * rs + pair) * hd + c);
+                    po[s] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                                        __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+                } else {
+                    po[s] = *reinterpret_cast<const float4*>(a.part_o + (s * rs + pair) * hd + c);
+                }
+            }
         }
     }
     float M = -INFINITY;
