@@ -87,12 +87,13 @@ def _route_margins(W, tokens, okv):
     return gap
 
 
-def _run_decomposed(B, cfg, model, W, users, ws, logit_tol, max_steps=48, route_tie=ROUTE_TIE):
+def _run_decomposed(B, cfg, model, W, users, ws, logit_tol, max_steps=48, route_tie=ROUTE_TIE, commit_mode=0):
     n = cfg.canvas
     nb = len(users)
-    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id, commit_mode=["keep", "reselect_all"][commit_mode])
     stats = B.StepStats(n * nb, vocab=cfg.vocab, logits_dtype=model.act_dtype, n_canvases=nb)
     scfg = B.sampler_default()
+    scfg.commit_mode = commit_mode
     finished_at = [None] * nb
     for t in range(max_steps):
         before = [u.canvas.tokens.cpu().numpy() for u in users]
@@ -128,12 +129,29 @@ def _run_decomposed(B, cfg, model, W, users, ws, logit_tol, max_steps=48, route_
     return finished_at
 
 
-def test_tiny_f32_batch_of_three_users(B):
+@pytest.mark.parametrize("commit_mode", [0, 1])
+def test_tiny_f32_batch_of_three_users(B, commit_mode):
     cfg = wl.TINY.replace(canvas=64)
     model = _model(B, cfg, 3 * 64)
     ws = model.workspace(3 * 64)
     W, users = _users(B, cfg, model, [128, 200, 64], ws)
-    _run_decomposed(B, cfg, model, W, users, ws, 1e-4)
+    _run_decomposed(B, cfg, model, W, users, ws, 1e-4, commit_mode=commit_mode)
+
+
+def test_small_bf16_batch_with_an_e4m3_lm_head(B):
+    """Two users' canvases through the e4m3 LM head over two 128-row canvases:
+    logits against the oracle decoder with the dequantised head."""
+    cfg = SMALL_BF16.replace(canvas=128)
+    codes, scale = wl.lm_head_e4m3(cfg, device="cuda")
+    embed = wl.embedding(cfg, device="cuda")
+    fnorm = wl.final_norm(cfg, device="cuda")
+    layers = [wl.layer_weights(cfg, l, device="cuda") for l in range(cfg.n_layers)]
+    model = B.Model(cfg, embed, fnorm, layers, max_canvas=256, lm_head_e4m3=codes, lm_head_scale=scale)
+    ws = model.workspace(256)
+    _, users = _users(B, cfg, model, [150, 300], ws)
+    host = [{k: v.cpu() for k, v in L.items()} for L in layers]
+    W8 = M.Weights(cfg, embed.cpu(), fnorm.cpu(), lambda l: host[l], lm_head=(codes.cpu(), scale.cpu()))
+    _run_decomposed(B, cfg, model, W8, users, ws, 2e-2, max_steps=3, route_tie=ROUTE_TIE_BF16)
 
 
 def test_small_bf16_batch_of_two_users(B):

@@ -394,11 +394,14 @@ def test_experts_hit_counts_the_routed_experts(B, name):
     assert stats.experts_hit.cpu().tolist() == want
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "small_bf16_gumbel"])
 def test_step_graph_replays_match_eager_steps(B, name):
     """A captured step replayed with eager work and synchronisation between the
     replays gives, at every step, bit-for-bit the eager step's canvas, state,
-    statistics and logits."""
+    statistics and logits (inverse-CDF draws, and Gumbel-max draws whose
+    step index the replay reads from the canvas state)."""
+    gumbel = name.endswith("_gumbel")
+    name = name.replace("_gumbel", "")
     cfg = CFGS[name]
     model = device_model(B, cfg)
     P = 300 if name != "tiny_f32" else wl.TINY_PREFIX
@@ -413,6 +416,8 @@ def test_step_graph_replays_match_eager_steps(B, name):
     sb = B.StepStats(n, vocab=cfg.vocab, logits_dtype=dt)
     ws_a, ws_b = model.workspace(n), model.workspace(n)
     scfg = B.sampler_default()
+    if gumbel:
+        scfg.draw_mode = B.DG_DRAW_GUMBEL_MAX
     graph = B.StepGraph(model, cb, kv, scfg, SEED, sb, ws_b)
     for t in range(6):
         B.canvas_step(model, ca, kv, t, SEED, scfg, sa, ws_a)
