@@ -34,6 +34,11 @@
 #ifndef DG_ATTN_MIN_BLOCKS
 #define DG_ATTN_MIN_BLOCKS 3
 #endif
+// workgroups the KV splits aim for (one per CU; 512 and 1024 measured slower
+// on the decode step, the long-context decode and the long prefill)
+#ifndef DG_ATTN_TARGET_WGS
+#define DG_ATTN_TARGET_WGS 256
+#endif
 // 1: scores formed transposed, P kept in registers (attn_t_kernel);
 // 0: scores as Q K^T, P through LDS (attn_reg_kernel)
 #ifndef DG_ATTN_TRANSPOSED
@@ -1044,7 +1049,8 @@ int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32,
         // about one workgroup per CU, each with at least DG_ATTN_MIN_BLOCKS key blocks
         const int64_t wgs = (int64_t)((nq + 128 / (Hq / Hkv) - 1) / (128 / (Hq / Hkv))) * Hkv;
         const int64_t blocks = (keys + KB - 1) / KB + 1;
-        s = (int)std::min<int64_t>((256 + wgs - 1) / wgs, std::max<int64_t>(1, blocks / DG_ATTN_MIN_BLOCKS));
+        s = (int)std::min<int64_t>((DG_ATTN_TARGET_WGS + wgs - 1) / wgs,
+                                   std::max<int64_t>(1, blocks / DG_ATTN_MIN_BLOCKS));
     } else {
         const int qtiles = (nq + 63) / 64;
         s = (int)std::min<int64_t>(max_splits, std::max<int64_t>(1, (keys + 511) / 512));
