@@ -155,16 +155,24 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
                          "mean_experts_hit": round(sum(sum(h) for _, h in rec) / max(len(rec), 1) / cfg.n_layers, 2)}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
-    achieved = kd["achieved_gbs"]
+    # the bound is the roof the kernel's algorithmic work reaches first: HBM
+    # bytes at 8 TB/s or flops at the bf16 MFMA peak
+    hbm_bound = kd["bytes"] / (HBM_PEAK_GBS * 1e9) >= kd["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": kd["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kd["achieved_gbs"] / HBM_PEAK_GBS, 4), "traffic": _traffic(dom, kd)}
+    else:
+        roof = {"bound": "mfma", "achieved": kd["achieved_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": _traffic(dom, kd)}
     res = {
         "ms_per_step": ms / args.steps,
         "committed_tokens": committed,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic(dom, kd),
-                     "kernel": dom, "us_per_launch": kd["us_per_launch"],
-                     "algorithmic_bytes_per_launch": round(kd["bytes"] / max(kd["launches"], 1)),
-                     "mfma_tflops": kd["achieved_tflops"],
-                     "mfma_frac": round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4)},
+        "roofline": dict(roof, kernel=dom, us_per_launch=kd["us_per_launch"],
+                         algorithmic_bytes_per_launch=round(kd["bytes"] / max(kd["launches"], 1)),
+                         algorithmic_flops_per_launch=round(kd["flops"] / max(kd["launches"], 1)),
+                         hbm_gbs=kd["achieved_gbs"], hbm_frac=round(kd["achieved_gbs"] / HBM_PEAK_GBS, 4),
+                         mfma_tflops=kd["achieved_tflops"],
+                         mfma_frac=round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4)),
         "kernels": {k: {kk: vv for kk, vv in v.items() if kk not in ("ms_total", "bytes", "flops")}
                     for k, v in kernels.items()},
         "extra": {"prefill_tokens": prompt_len, "prefill_ms": round(ms_prefill, 2),
