@@ -352,30 +352,54 @@ __global__ void __launch_bounds__(256) tile_reduce_kernel(GemmArgs g) {
 // and up summed over the K slices in slice order, then h = silu(gate) * up to
 // bf16. Groups of at least big_min rows were cut into ks_big slices, the
 // others into ks_small; a count of 1 means that GEMM stored h itself. The
-// group of a slot is found by bisection of g.group_offsets.
+// group of a slot is found by bisection of g.group_offsets (copied to LDS
+// first when there are at most SWR_LDS_OFF of them, so the bisection does not
+// wait on a chain of global loads); the loads of up to 8 slices go out before
+// the first add.
+constexpr int SWR_LDS_OFF = 1024;
 __global__ void __launch_bounds__(256) tile_swiglu_reduce_kernel(GemmArgs g, int groups, int big_min, int ks_big,
                                                                  int ks_small) {
     if (g.state && g.state[0]) return;
+    __shared__ int off_s[SWR_LDS_OFF];
+    const bool in_lds = groups + 1 <= SWR_LDS_OFF;
+    if (in_lds) {
+        for (int q = threadIdx.x; q <= groups; q += 256) off_s[q] = g.group_offsets[q];
+        __syncthreads();
+    }
+    const int* off = in_lds ? off_s : g.group_offsets;
     const int F = g.N / 2, f4 = F / 4;
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int total = g.group_offsets[groups];
+    const int total = off[groups];
     if (e >= (int64_t)total * f4) return;
     const int slot = (int)(e / f4), f = (int)(e % f4) * 4;
     int lo = 0, hi = groups;  // group gr with off[gr] <= slot < off[gr + 1]
     while (hi - lo > 1) {
         const int mid = (lo + hi) / 2;
-        if (g.group_offsets[mid] <= slot) lo = mid; else hi = mid;
+        if (off[mid] <= slot) lo = mid; else hi = mid;
     }
-    const int ks = g.group_offsets[lo + 1] - g.group_offsets[lo] >= big_min ? ks_big : ks_small;
+    const int ks = off[lo + 1] - off[lo] >= big_min ? ks_big : ks_small;
     if (ks <= 1) return;
-    float4 ga = *reinterpret_cast<const float4*>(g.part + (int64_t)slot * g.N + f);
-    float4 ua = *reinterpret_cast<const float4*>(g.part + (int64_t)slot * g.N + F + f);
-    for (int s = 1; s < ks; ++s) {
+    float4 gp[8], up[8];  // slices past ks load slice ks - 1 again (unused)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        const float* P = g.part + ((int64_t)min(s, ks - 1) * g.M + slot) * g.N;
+        gp[s] = *reinterpret_cast<const float4*>(P + f);
+        up[s] = *reinterpret_cast<const float4*>(P + F + f);
+    }
+    float4 ga = gp[0], ua = up[0];
+#pragma unroll
+    for (int s = 1; s < 8; ++s) {
+        if (s < ks) {
+            ga.x += gp[s].x; ga.y += gp[s].y; ga.z += gp[s].z; ga.w += gp[s].w;
+            ua.x += up[s].x; ua.y += up[s].y; ua.z += up[s].z; ua.w += up[s].w;
+        }
+    }
+    for (int s = 8; s < ks; ++s) {
         const float* P = g.part + ((int64_t)s * g.M + slot) * g.N;
-        const float4 gp = *reinterpret_cast<const float4*>(P + f);
-        const float4 up = *reinterpret_cast<const float4*>(P + F + f);
-        ga.x += gp.x; ga.y += gp.y; ga.z += gp.z; ga.w += gp.w;
-        ua.x += up.x; ua.y += up.y; ua.z += up.z; ua.w += up.w;
+        const float4 gq = *reinterpret_cast<const float4*>(P + f);
+        const float4 uq = *reinterpret_cast<const float4*>(P + F + f);
+        ga.x += gq.x; ga.y += gq.y; ga.z += gq.z; ga.w += gq.w;
+        ua.x += uq.x; ua.y += uq.y; ua.z += uq.z; ua.w += uq.w;
     }
     uint2 o;
     o.x = f2bf2(tsilu(ga.x) * ua.x, tsilu(ga.y) * ua.y);
