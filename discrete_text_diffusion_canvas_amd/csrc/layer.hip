@@ -518,15 +518,13 @@ __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __res
 // is also normalised (the next layer's pre-attention RMSNorm, or the final
 // norm) into A, from the registers that hold it.
 // ---------------------------------------------------------------------------
-// KT > 0: k == KT known at compile time (no branch between the row loads).
-template <typename TO, int KT>
+template <typename TO>
 __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int d, const float* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_of,
-                                                      const float* __restrict__ gates, int k_arg, int shared_off,
+                                                      const float* __restrict__ gates, int k, int shared_off,
                                                       const float* __restrict__ nw, float eps, TO* __restrict__ A,
                                                       const int32_t* __restrict__ state) {
     if (state && state[0]) return;
-    const int k = KT > 0 ? KT : k_arg;
     const int i = blockIdx.x, nv = d / 4;
     __shared__ int sl[16];
     __shared__ float gt[16];
@@ -537,44 +535,20 @@ __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int
     __syncthreads();
     const float4* ysh = reinterpret_cast<const float4*>(Y + (int64_t)(shared_off + i) * d);
     float4* xr = reinterpret_cast<float4*>(X + (int64_t)i * d);
-    // the loads of the shared row, the residual and 8 experts' rows for all of
-    // the thread's float4s go out before the first sum (clamped addresses, so
-    // no branch separates them; the clamped duplicates are not used)
-    int cc[NORM_V4];
-    float4 acc[NORM_V4], xo[NORM_V4];
-#pragma unroll
-    for (int j = 0; j < NORM_V4; ++j) {
-        cc[j] = min(threadIdx.x + 256 * j, nv - 1);
-        acc[j] = ysh[cc[j]];
-        xo[j] = xr[cc[j]];
-    }
-    for (int e0 = 0; e0 < k; e0 += 8) {
-        float4 y[8][NORM_V4];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4* yr = reinterpret_cast<const float4*>(Y + (int64_t)sl[min(e0 + q, k - 1)] * d);
-#pragma unroll
-            for (int j = 0; j < NORM_V4; ++j) y[q][j] = yr[cc[j]];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            if (e0 + q >= k) break;
-            const float g = gt[e0 + q];
-#pragma unroll
-            for (int j = 0; j < NORM_V4; ++j) {
-                acc[j].x += g * y[q][j].x; acc[j].y += g * y[q][j].y;
-                acc[j].z += g * y[q][j].z; acc[j].w += g * y[q][j].w;
-            }
-        }
-    }
     float4 x[NORM_V4];
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
         const int c = threadIdx.x + 256 * j;
         x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (c >= nv) continue;
-        float4 v = xo[j];
-        v.x += acc[j].x; v.y += acc[j].y; v.z += acc[j].z; v.w += acc[j].w;
+        float4 acc = ysh[c];
+        for (int e = 0; e < k; ++e) {
+            const float4 y = reinterpret_cast<const float4*>(Y + (int64_t)sl[e] * d)[c];
+            const float g = gt[e];
+            acc.x += g * y.x; acc.y += g * y.y; acc.z += g * y.z; acc.w += g * y.w;
+        }
+        float4 v = xr[c];
+        v.x += acc.x; v.y += acc.y; v.z += acc.z; v.w += acc.w;
         xr[c] = v;
         x[j] = v;
     }
@@ -671,18 +645,12 @@ hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t*
                           int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
                           hipStream_t st) {
     if (d % 4 || d > 4 * 256 * NORM_V4 || k > 16) return hipErrorInvalidValue;
-    if (act_f32 && k == 8)
-        combine_kernel<float, 8><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
-                                                    state);
-    else if (act_f32)
-        combine_kernel<float, 0><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
-                                                    state);
-    else if (k == 8)
-        combine_kernel<uint16_t, 8><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
-                                                       (uint16_t*)A, state);
+    if (act_f32)
+        combine_kernel<float><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
+                                                 state);
     else
-        combine_kernel<uint16_t, 0><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
-                                                       (uint16_t*)A, state);
+        combine_kernel<uint16_t><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
+                                                    (uint16_t*)A, state);
     return hipGetLastError();
 }
 
