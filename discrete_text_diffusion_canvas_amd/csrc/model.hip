@@ -30,7 +30,9 @@ struct dg_model {
     std::vector<dg_layer_weights> layers;
 };
 
-// expert groups with at least this many rows take the LDS-staged GEMM (bf16)
+// expert groups with at least this many rows take the LDS-staged GEMM (bf16);
+// on the 256-row decode step 33 and 49 measured the same as 65, 97 and 129
+// 4% and 6% slower per step
 #ifndef DG_TILE_MIN_ROWS
 #define DG_TILE_MIN_ROWS 65
 #endif
