@@ -47,8 +47,6 @@
 #ifndef DG_TILE_BN_GU
 #define DG_TILE_BN_GU 128
 #endif
-// (down and dense products at 64 measured slower on the 256-row decode step:
-// down 39.4 -> 43.9 us; QKV 26.3 -> 30.1 us, output projection 20.8 -> 23.4 us)
 #ifndef DG_TILE_BN_DN
 #define DG_TILE_BN_DN 128
 #endif
