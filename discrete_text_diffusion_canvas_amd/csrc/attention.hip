@@ -16,13 +16,8 @@
 // merge kernel combines. V is stored transposed ([d][key]) so that the B
 // operand of P V reads contiguous keys.
 //
-// bf16 (attn_reg_kernel): a workgroup's 128 query rows are the 128/R
-// positions of all R query heads of one KV group, so every K/V tile is shared
-// by the whole group; Q sits in LDS; the K tile [64 keys][hd] and V^T tile
-// [hd][64 keys] of the next block are loaded into registers while the current
-// block is computed and written into the XOR-swizzled LDS slot after it. Key
-// blocks are aligned to multiples of 64 in each segment and masked outside
-// the visible range.
+// bf16 (attn_t_kernel): the query heads of one KV group share every K/V
+// tile, scores are formed transposed and P stays in registers (below).
 #include "common.hpp"
 #include "layer.hpp"
 
@@ -38,11 +33,6 @@
 // on the decode step, the long-context decode and the long prefill)
 #ifndef DG_ATTN_TARGET_WGS
 #define DG_ATTN_TARGET_WGS 256
-#endif
-// 1: scores formed transposed, P kept in registers (attn_t_kernel);
-// 0: scores as Q K^T, P through LDS (attn_reg_kernel)
-#ifndef DG_ATTN_TRANSPOSED
-#define DG_ATTN_TRANSPOSED 1
 #endif
 // 1: the transposed kernel keeps each wave's Q fragments in registers
 #ifndef DG_ATTN_QREG
@@ -334,268 +324,15 @@ __device__ __forceinline__ void attn_ids(int nqt, int& qt, int& gs) {
     gs = (rest / nqt) * 8 + lane8;                // (group, split) pair; past the last: no work
 }
 
-template <int HD, int NW>
-__global__ void __launch_bounds__(NW * 64) attn_reg_kernel(AttnArgs a, int R) {
-    if (a.state && a.state[0]) return;
-    const int QP = 128 / R;                       // positions per workgroup
-    const int nqt = (a.nq + QP - 1) / QP;
-    int qt, gs;
-    attn_ids(nqt, qt, gs);
-    if (gs >= a.Hkv * a.splits) return;
-    const int g = gs % a.Hkv, sp = gs / a.Hkv;
-    constexpr int KROWB = HD * 2;                 // bytes per K row
-    constexpr int K_BYTES = KB * KROWB;           // K tile
-    constexpr int V_BYTES = HD * KB * 2;          // V^T tile (rows of 128 bytes)
-    constexpr int STAGE = K_BYTES + V_BYTES;
-    constexpr int K_LD = K_BYTES / 1024 / NW;     // 16-byte loads per lane and block
-    constexpr int V_LD = V_BYTES / 1024 / NW;
-    constexpr int TPW = 128 / (16 * NW);          // 16-row tiles per wave
-    constexpr int RPW = 16 * TPW;                 // rows per wave
-    constexpr int KRPI = 1024 / KROWB;            // K rows per 1 KB piece
-    constexpr int KCPR = KROWB / 16;              // chunks per K row
-    constexpr int NT_D = HD / 16;
-    constexpr int KS = HD / 32;
-    constexpr int SP = KB + 8;
-    extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* Qs = smem + STAGE;                                  // [128 rows][HD], swizzled
-    uint16_t* Ps = reinterpret_cast<uint16_t*>(smem + STAGE + 128 * KROWB);  // [128 rows][SP]
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int qx0 = qt * QP;
-    // workgroup row rho in [0, 128) = (head g*R + rho / QP, position qx0 + rho % QP);
-    // wave w owns rows [RPW w, RPW (w + 1)) as TPW 16-row tiles
-    auto row_head = [&](int rho) { return g * R + rho / QP; };
-    auto row_pos = [&](int rho) { return qx0 + rho % QP; };
-
-    // ---- the key blocks of this workgroup ----
-    const int64_t qlo = a.qpos0 + qx0, qhi = a.qpos0 + min(qx0 + QP, a.nq) - 1;
-    int64_t b1lo, b1hi;                           // segment-1 blocks [b1lo, b1hi)
-    if (a.causal) {
-        int64_t kmin = a.s1, kmax = min<int64_t>(a.e1 - 1, qhi);
-        if (a.window > 0) kmin = max<int64_t>(kmin, qlo - a.window + 1);
-        b1lo = kmin / KB;
-        b1hi = kmax >= kmin ? kmax / KB + 1 : b1lo;
-    } else {
-        b1lo = a.s1 / KB;
-        b1hi = a.e1 > a.s1 ? (a.e1 - 1) / KB + 1 : b1lo;
-    }
-    const int64_t nb1 = b1hi - b1lo;
-    const int64_t nb2 = a.n2 > 0 ? (a.n2 + KB - 1) / KB : 0;
-    const int64_t nb = nb1 + nb2;
-    const int64_t per = (nb + a.splits - 1) / a.splits;
-    const int64_t bb0 = per * sp, bb1 = min<int64_t>(nb, bb0 + per);
-
-    const uint16_t* K1 = reinterpret_cast<const uint16_t*>(a.K1) + (int64_t)g * a.ld1 * HD;
-    const uint16_t* V1 = reinterpret_cast<const uint16_t*>(a.V1) + (int64_t)g * HD * a.ld1;
-    const uint16_t* K2 = a.K2 ? reinterpret_cast<const uint16_t*>(a.K2) + (int64_t)g * a.ld2 * HD : nullptr;
-    const uint16_t* V2 = a.V2 ? reinterpret_cast<const uint16_t*>(a.V2) + (int64_t)g * HD * a.ld2 : nullptr;
-
-    // register loads of virtual block vb (clamped to this workgroup's last
-    // block, so the loop stays branch-free); the LDS layout written by store()
-    // is K [64 keys][HD] and V^T [HD][64 keys], XOR-swizzled by 16-byte chunk
-    u32x4 kr[K_LD], vr[V_LD];
-    auto load = [&](int64_t vb) {
-        vb = min<int64_t>(vb, bb1 - 1);
-        const bool seg1 = vb < nb1;
-        const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
-        const int64_t rlim = seg1 ? a.e1 : a.n2;   // rows >= rlim: any valid row (masked)
-        const uint16_t* Kb = seg1 ? K1 : K2;
-        const uint16_t* Vb = seg1 ? V1 : V2;
-        const int64_t vld = seg1 ? a.ld1 : a.ld2;
-#pragma unroll
-        for (int j = 0; j < K_LD; ++j) {
-            const int r = (wave * K_LD + j) * KRPI + lane / KCPR;
-            const int pos = lane % KCPR;
-            int64_t kr_row = row0 + r;
-            if (kr_row >= rlim) kr_row = rlim - 1;
-            if (kr_row < 0) kr_row = 0;
-            kr[j] = *reinterpret_cast<const u32x4*>(Kb + kr_row * HD + 8 * kswz(r, pos));
-        }
-#pragma unroll
-        for (int j = 0; j < V_LD; ++j) {
-            const int d = (wave * V_LD + j) * 8 + lane / 8;
-            const int pos = lane % 8;
-            vr[j] = *reinterpret_cast<const u32x4*>(Vb + (int64_t)d * vld + row0 + 8 * vswz(d, pos));
-        }
-    };
-    auto store = [&]() {
-        unsigned char* base = smem;
-#pragma unroll
-        for (int j = 0; j < K_LD; ++j) *reinterpret_cast<u32x4*>(base + (wave * K_LD + j) * 1024 + lane * 16) = kr[j];
-#pragma unroll
-        for (int j = 0; j < V_LD; ++j)
-            *reinterpret_cast<u32x4*>(base + K_BYTES + (wave * V_LD + j) * 1024 + lane * 16) = vr[j];
-    };
-
-    // ---- Q rows of the workgroup into LDS (row rho, 16-byte chunk c at kswz):
-    // all loads first (rows past nq read row 0 and are zeroed), then the writes
-    {
-        constexpr int QL = 128 * KCPR / (NW * 64);  // 16-byte pieces per thread
-        u16x8 qv[QL];
-#pragma unroll
-        for (int j = 0; j < QL; ++j) {
-            const int e = tid + NW * 64 * j, rho = e / KCPR, c = e % KCPR;
-            const int qp = row_pos(rho);
-            qv[j] = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(a.Q) +
-                                                    ((int64_t)row_head(rho) * a.ldq + (qp < a.nq ? qp : 0)) * HD +
-                                                    c * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < QL; ++j) {
-            const int e = tid + NW * 64 * j, rho = e / KCPR, c = e % KCPR;
-            const u16x8 z = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            *reinterpret_cast<u16x8*>(Qs + rho * KROWB + kswz(rho, c) * 16) = row_pos(rho) < a.nq ? qv[j] : z;
-        }
-    }
-    f32x4 o[TPW][NT_D];
-    float m_run[TPW][4], l_run[TPW][4];
-    int qpos[TPW][4];  // absolute positions (< 2^31)
-    bool qok[TPW][4];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-        for (int j = 0; j < NT_D; ++j) o[t][j] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            m_run[t][i] = -INFINITY;
-            l_run[t][i] = 0.f;
-            const int rho = wave * RPW + t * 16 + lg * 4 + i;
-            qpos[t][i] = (int)(a.qpos0 + row_pos(rho));
-            qok[t][i] = row_pos(rho) < a.nq;
-        }
-    }
-    const float scale = 1.f / sqrtf((float)HD);
-
-    // pipeline: block vb is computed from the LDS slot while block vb + 1 sits
-    // in registers; after a barrier vb + 1 replaces it and vb + 2 is loaded
-    if (bb0 < bb1) {
-        load(bb0);
-        store();
-        load(bb0 + 1);
-    }
-    attn_lds_barrier();
-    for (int64_t vb = bb0; vb < bb1; ++vb) {
-        const unsigned char* Kt = smem;
-        const unsigned char* Vt = Kt + K_BYTES;
-        const bool seg1 = vb < nb1;
-        const int64_t row0 = seg1 ? (b1lo + vb) * KB : (vb - nb1) * KB;
-        // ---- S = Q K^T (each K fragment feeds both row tiles); the fragments
-        // of k-step ks + 1 are read while the MFMAs of ks run ----
-        f32x4 s[TPW][4];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) s[t][nt] = f32x4{0, 0, 0, 0};
-        u16x8 qf[2][TPW], kf[2][4];
-        auto ld_s = [&](int bsel, int ks) {
-            const int c = ks * 4 + lg;
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int q = wave * RPW + t * 16 + lr;
-                qf[bsel][t] = *reinterpret_cast<const u16x8*>(Qs + q * KROWB + kswz(q, c) * 16);
-            }
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int r = nt * 16 + lr;
-                kf[bsel][nt] = *reinterpret_cast<const u16x8*>(Kt + r * KROWB + kswz(r, c) * 16);
-            }
-        };
-        ld_s(0, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) ld_s((ks + 1) & 1, ks + 1);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) s[t][nt] = amfma(qf[ks & 1][t], kf[ks & 1][nt], s[t][nt]);
-        }
-        // ---- mask (branch-free, 32-bit positions), online softmax, P to LDS ----
-        int kp[4];
-        bool kin[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int row = (int)(row0 + nt * 16 + lr);
-            kin[nt] = seg1 ? (row >= (int)a.s1) & (row < (int)a.e1) : (row < a.n2);
-            kp[nt] = seg1 ? row : (int)a.pos2_0 + row;
-        }
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bool ok = kin[nt] & qok[t][i];
-                    if (a.causal) {  // uniform
-                        const int dq = qpos[t][i] - kp[nt];
-                        ok = ok & (dq >= 0) & ((a.window <= 0) | (dq < a.window));
-                    }
-                    s[t][nt][i] = ok ? s[t][nt][i] * scale : -INFINITY;
-                }
-            softmax_block<uint16_t, NT_D, SP>(s[t], m_run[t], l_run[t], o[t], Ps + (wave * RPW + t * 16) * SP, lr, lg);
-        }
-        // ---- O += P V (each V^T fragment feeds both row tiles); V fragments in
-        // groups of 4, the next group read during the current MFMAs ----
-        const uint16_t* pw = Ps + wave * RPW * SP;
-#pragma unroll
-        for (int ks2 = 0; ks2 < KB / 32; ++ks2) {
-            u16x8 pf[TPW];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                pf[t] = *reinterpret_cast<const u16x8*>(pw + (t * 16 + lr) * SP + ks2 * 32 + lg * 8);
-            u16x8 vf[2][4];
-            auto ld_v = [&](int bsel, int jg) {
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int d = (jg * 4 + jj) * 16 + lr;
-                    vf[bsel][jj] = *reinterpret_cast<const u16x8*>(Vt + d * 128 + vswz(d, ks2 * 4 + lg) * 16);
-                }
-            };
-            ld_v(0, 0);
-#pragma unroll
-            for (int jg = 0; jg < NT_D / 4; ++jg) {
-                if (jg + 1 < NT_D / 4) ld_v((jg + 1) & 1, jg + 1);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-                    for (int t = 0; t < TPW; ++t) o[t][jg * 4 + jj] = amfma(pf[t], vf[jg & 1][jj], o[t][jg * 4 + jj]);
-            }
-        }
-        __builtin_amdgcn_s_barrier();  // every wave done with the slot
-        store();
-        load(vb + 2);
-        attn_lds_barrier();
-    }
-    __syncthreads();  // retire the tail loads
-    // ---- write out ----
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (!qok[t][i]) continue;
-            const int rho = wave * RPW + t * 16 + lg * 4 + i;
-            const int hq = row_head(rho), qr = row_pos(rho);
-            if (a.splits == 1) {
-                const float inv = l_run[t][i] > 0.f ? 1.f / l_run[t][i] : 0.f;
-                uint16_t* out = reinterpret_cast<uint16_t*>(a.O) + (int64_t)qr * a.Hq * HD + (int64_t)hq * HD;
-#pragma unroll
-                for (int j = 0; j < NT_D; ++j) out[j * 16 + lr] = f2bf(o[t][j][i] * inv);
-            } else {
-                const int64_t po = (((int64_t)sp * a.nq + qr) * a.Hq + hq) * HD;
-#pragma unroll
-                for (int j = 0; j < NT_D; ++j) store_part<uint16_t>(a.part_o, po + j * 16 + lr, o[t][j][i]);
-                if (lr == 0) {
-                    float* pm = a.part_ml + (((int64_t)sp * a.nq + qr) * a.Hq + hq) * 2;
-                    pm[0] = m_run[t][i];
-                    pm[1] = l_run[t][i];
-                }
-            }
-        }
-    }
-}
-
-// bf16 kernel with transposed scores. The same work as attn_reg_kernel, but S
-// is formed as K Q^T: a lane then holds, for query row lr of its wave's tile,
+// bf16 kernel with transposed scores. A workgroup's 128 query rows are the
+// 128/R positions of all R query heads of one KV group, so every K/V tile is
+// shared by the whole group; the K tile [64 keys][hd] and V^T tile [hd][64
+// keys] of the next block are loaded into registers while the current block
+// is computed and written into the XOR-swizzled LDS slot after it. Key blocks
+// are aligned to multiples of 64 in each segment; keys outside the visible
+// range are masked in the scores, and V^T values of keys at or past the end
+// of a segment are read as zero, so whatever the buffers hold there cannot
+// reach the output. S is formed as K Q^T: a lane then holds, for query row lr of its wave's tile,
 // 16 scores of keys nt*16 + 4*lg + q (nt, q < 4). That layout is already the
 // A operand of the P V product if the keys of each 32-key k-step are taken in
 // the order (first run: 32*ks2 + 4*lg + q, second: 32*ks2 + 16 + 4*lg + q),
@@ -678,10 +415,16 @@ __global__ void __launch_bounds__(NW * 64) attn_t_kernel(AttnArgs a, int R) {
             if (kr_row < 0) kr_row = 0;
             kr[j] = *reinterpret_cast<const u32x4*>(Kb + kr_row * HD + 8 * kswz(r, pos));
         }
+        const int64_t vk0 = row0 + 8 * (lane % 8);  // first of this lane's 8 keys
 #pragma unroll
         for (int j = 0; j < V_LD; ++j) {
             const int d = (wave * V_LD + j) * 8 + lane / 8;
-            vr[j] = *reinterpret_cast<const u32x4*>(Vb + (int64_t)d * vld + row0 + 8 * (lane % 8));
+            vr[j] = *reinterpret_cast<const u32x4*>(Vb + (int64_t)d * vld + vk0);
+            if (vk0 + 8 > rlim) {  // keys at or past the segment's end read as zero
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (vk0 + e >= rlim) vr[j][e / 2] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
         }
     };
     // V^T row d: 16-byte slot L = 4*ks2 + l4 holds keys 32*ks2 + 4*l4 + (0..3)
@@ -1018,12 +761,12 @@ static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
 }
 
 template <int HD>
-static hipError_t launch_attn_reg(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_attn_grouped(const AttnArgs& a, hipStream_t st) {
     constexpr int NW = DG_ATTN_WAVES;
     const int R = a.Hq / a.Hkv;
     constexpr int STAGE = 64 * HD * 2 * 2;
-    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2 + (DG_ATTN_TRANSPOSED ? 0 : (size_t)128 * (KB + 8) * 2);
-    auto kern = DG_ATTN_TRANSPOSED ? attn_t_kernel<HD, NW> : attn_reg_kernel<HD, NW>;
+    const size_t lds = (size_t)STAGE + (size_t)128 * HD * 2;
+    auto kern = attn_t_kernel<HD, NW>;
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -1064,8 +807,8 @@ int attention_splits(int nq, int64_t keys, int Hq, int Hkv, int hd, int act_f32,
 hipError_t launch_attention(const AttnArgs& a, int act_f32, hipStream_t st) {
     if (a.splits > MERGE_MAX_SPLITS || a.hd % 4 || a.hd > 256) return hipErrorInvalidValue;
     if (attention_uses_grouped(a.Hq, a.Hkv, a.hd, act_f32) && a.ld1 % 64 == 0 && (a.n2 == 0 || a.ld2 % 64 == 0)) {
-        if (a.hd == 256) return launch_attn_reg<256>(a, st);
-        return launch_attn_reg<128>(a, st);
+        if (a.hd == 256) return launch_attn_grouped<256>(a, st);
+        return launch_attn_grouped<128>(a, st);
     }
     if (act_f32) {
         if (a.hd == 64) return launch_attn_t<float, 64>(a, st);

@@ -363,8 +363,10 @@ hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int g
     DG_DISPATCH(EPI_SWIGLU)
 #undef DG_DISPATCH
     if (epi == EPI_LMHEAD) {
+        // f32 models, and bf16 shapes outside the tiled kernel (d_model not a
+        // multiple of 64, or a logits row stride not a multiple of 8)
         if (act_f32) return launch_cfg<2, 2, 4, 4, 32, float, WK_SAME, EPI_LMHEAD>(g, 0, st);
-        return launch_lmhead_bf16(g, st);
+        return launch_cfg<2, 2, 4, 4, 32, uint16_t, WK_SAME, EPI_LMHEAD>(g, 0, st);
     }
     return hipErrorInvalidValue;
 }

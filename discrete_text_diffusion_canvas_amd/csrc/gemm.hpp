@@ -53,7 +53,6 @@ struct GemmArgs {
 
 hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int shape,
                        hipStream_t st);
-hipError_t launch_lmhead_bf16(const GemmArgs& g, hipStream_t st);
 hipError_t stream_gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int max_rows,
                               hipStream_t st);
 // LDS-staged GEMM (bf16 activations and weights, K % 64 == 0): grouped over
@@ -71,10 +70,11 @@ int tile_grouped_ksplit(int rows);
 hipError_t swiglu_reduce_launch(const GemmArgs& g, int groups, int big_min, int ks_big, int ks_small, hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// LM-head epilogue: logits of record (accumulator rounded to the storage
-// type), stored; then per row over this tile's columns, the base-2 entropy
-// partials of z2 = (logit + bias) * log2(e) / tau with the MASK column
-// removed, and the argmax of (logit + bias), lowest column on ties.
+// LM-head epilogue: the logits of record (the accumulator in the storage
+// type) are stored; then per row over this tile's columns, from the f32
+// accumulators, the base-2 entropy partials of z2 = (logit + bias) *
+// log2(e) / tau with the MASK column removed, and the argmax of
+// (logit + bias), lowest column on ties.
 // ---------------------------------------------------------------------------
 template <int WM, int WN, int TM, int TN>
 constexpr size_t lmhead_epilogue_lds() {
@@ -115,8 +115,7 @@ __device__ __forceinline__ void lmhead_epilogue(const GemmArgs& g, f32x4 (&acc)[
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int n = n0 + wn * TN * 16 + j * 16 + lr;
-                float l = acc[i][j][q];
-                if (!g.c_f32) l = round_bf(l);
+                const float l = acc[i][j][q];
                 if (rok && n < g.N) {
                     if (g.c_f32)
                         reinterpret_cast<float*>(g.C)[(int64_t)row * g.ldc + n] = l;

@@ -175,13 +175,14 @@ __device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int 
     }
 }
 
-// LM-head epilogue on the tile T[r][c] (logits of record, bf16-rounded) of
-// vocabulary rows [tile*BN, +BN): (1) the bf16 logits leave in 16-byte
-// coalesced stores; (2) per canvas row, the tile's partial statistics: the
-// max and the 2^x partition sum and entropy partial of the tempered logits
-// (log2 units), and the raw argmax (first index among equal values), with
-// the row's bias token added and the mask token excluded. merge_rows
-// combines the partials.
+// LM-head epilogue on the tile T[r][c] (the f32 accumulators) of vocabulary
+// rows [tile*BN, +BN): (1) the logits of record leave as bf16 in 16-byte
+// coalesced stores; (2) per canvas row, the tile's partial statistics from
+// the f32 values: the max and the 2^x partition sum and entropy partial of
+// the tempered logits (log2 units), and the raw argmax (first index among
+// equal values), with the row's bias token added and the mask token
+// excluded. merge_rows combines the partials. Draws sample the logits of
+// record, so the Gumbel-max candidate is taken from the bf16-rounded values.
 //
 // The statistics use TPR = NT / BM threads per row (1 or 2), each over a
 // contiguous 1/TPR of the columns, in two passes: the raw max and its index,
@@ -304,7 +305,7 @@ __device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T
                 for (int u = 0; u < 4; ++u) {
                     const int v = v0 + u;
                     if (v >= N || v == g.mask_id) continue;
-                    const float val = (row[c + u] + (v == bt ? bv : 0.f)) * inv_tau + gumbel_of(wd[u]);
+                    const float val = (round_bf(row[c + u]) + (v == bt ? bv : 0.f)) * inv_tau + gumbel_of(wd[u]);
                     if (val > gv) { gv = val; gi = v; }
                 }
             }
@@ -621,8 +622,7 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        T[(wm * 64 + i * 16 + lg * 4 + q) * TS + c + lr] =
-                            EPI == EPI_LMHEAD ? round_bf(acc[i][j][q]) : acc[i][j][q];
+                        T[(wm * 64 + i * 16 + lg * 4 + q) * TS + c + lr] = acc[i][j][q];
             }
         }
         __syncthreads();

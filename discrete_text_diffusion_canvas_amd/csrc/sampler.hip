@@ -419,9 +419,17 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
         s_chunk = owner_c;
         owner = 0x7fffffff;
         last_owner = -1;
+        if (owner_c < 0) {
+            // no chunk holds finite positive mass (a NaN row, or a +inf logit
+            // whose exp(z - M) is NaN): the argmax is committed and no chunk
+            // is scanned
+            tokens[row] = amax[row];
+            committed[row] = 1;
+        }
     }
     __syncthreads();
     const int c = s_chunk;
+    if (c < 0) return;  // uniform over the workgroup
     const double target = s_target;
     const int v0 = c * DRAW_CHUNK + tid * 16;
     const double s = thread_chunk_sum(rowp, v0, V, mask_id, btok, bval, tau, M);

@@ -120,7 +120,11 @@ typedef struct dg_canvas {
 
 /* Per-step outputs (device memory, n elements each unless stated). */
 typedef struct dg_step_stats {
-    float* entropy;        /* nats, of softmax((L + bias) / tau_t), MASK excluded */
+    float* entropy;        /* nats, of softmax((L + bias) / tau_t), MASK excluded. dg_canvas_step and
+                              dg_lm_head take entropy, lse and argmax from the LM head's f32
+                              accumulators (the logits of record are those values rounded to the act
+                              dtype; draws sample the logits of record); dg_sampler_step from the
+                              given logits */
     float* lse;            /* log-sum-exp of (L + bias) / tau_t */
     int32_t* argmax;       /* lowest id on ties, MASK excluded */
     uint8_t* selected;     /* 1 where the EB selection committed (or, under
@@ -283,9 +287,10 @@ typedef struct dg_weights {
  * [n_kv_heads][capacity][head_dim] and V transposed, [n_kv_heads][head_dim]
  * [capacity], in the act dtype; keys after RoPE. Positions [0, len) are
  * filled; dg_prefill_append advances len on the host. capacity must be a
- * multiple of 64, at most 2^30 rows (DG_E_SHAPE otherwise), and the cache must hold finite values beyond len (allocate
- * it zero-filled): attention reads whole 64-key blocks and masks the keys
- * outside the visible range. */
+ * multiple of 64 and at most 2^30 rows (DG_E_SHAPE otherwise). Rows at or
+ * beyond len may hold anything (a reused cache, NaN): attention reads whole
+ * 64-key blocks, masks the scores of keys outside the visible range and
+ * reads the values of keys at or beyond len as zero. */
 typedef struct dg_kv {
     void* const* k;
     void* const* v;

@@ -31,14 +31,15 @@ Readings taken where the pages are silent:
 * stop is tested after the commit; on stop, at the last step, or when every
   position is committed, the remaining positions take their argmax.
 
-Decisions that floating point turns into integers are taken in float32 where
-the kernel takes them in float32 (the selection prefix sum, in sorted order)
-and in float64 where the kernel uses float64 (the canvas-mean entropy, the
-draw CDF).
+Sums that decide an integer outcome are taken by their plain definition in
+float64: the selection's prefix sums and the canvas-mean entropy with
+``math.fsum`` (the correctly rounded sum, independent of the order), the draw
+CDF with numpy's cumulative sum.
 """
 from __future__ import annotations
 
 import dataclasses
+import math
 
 import numpy as np
 
@@ -111,41 +112,56 @@ def row_stats(logits, tau: float, mask_id: int):
 # ---------------------------------------------------------------------------
 
 
-def eb_select(H32, committed, bound: float, mode: str = "sum") -> np.ndarray:
+def eb_select(H, committed, bound: float, mode: str = "sum") -> np.ndarray:
     """Positions committed this step ([MC-zh] BP1 token selection).
 
     Candidates are uncommitted positions, ordered by (entropy, position)
-    ascending. With S_k the float32 running sum of the first k sorted
-    entropies (added in sorted order), the step commits the first k*
-    candidates where
+    ascending. With S_k the sum of the first k sorted entropies (float64,
+    ``math.fsum``), the step commits the first k* candidates where
       mode "sum":           k* = max{k >= 1 : S_k <= bound}, or 1 if none;
       mode "sum_minus_max": k* = max{k >= 1 : S_{k-1} <= bound}
                             (the bound on the k-1 smallest, S_0 = 0).
-    Returns a bool mask over all positions.
+    The entropies are non-negative, so S_k grows with k and the first k whose
+    sum breaks the bound ends the prefix. Returns a bool mask over all
+    positions.
     """
-    H32 = np.asarray(H32, dtype=np.float32)
+    H = np.asarray(H, dtype=np.float64)
     committed = np.asarray(committed).astype(bool)
-    n = H32.shape[0]
+    n = H.shape[0]
     sel = np.zeros(n, dtype=bool)
     cand = [i for i in range(n) if not committed[i]]
     if not cand:
         return sel
-    order = sorted(cand, key=lambda i: (float(H32[i]), i))
-    b = np.float32(bound)
-    run = np.float32(0.0)
+    order = sorted(cand, key=lambda i: (float(H[i]), i))
     k_star = 0
-    for k, i in enumerate(order, start=1):
-        prev = run
-        run = np.float32(run + H32[i])
-        ok = (run <= b) if mode == "sum" else (prev <= b)
-        if ok:
-            k_star = k
-        else:
+    for k in range(1, len(order) + 1):
+        s_k = math.fsum(float(H[i]) for i in order[:k])
+        s_prev = math.fsum(float(H[i]) for i in order[:k - 1])
+        ok = (s_k <= bound) if mode == "sum" else (s_prev <= bound)
+        if not ok:
             break
+        k_star = k
     k_star = max(k_star, 1)
     for i in order[:k_star]:
         sel[i] = True
     return sel
+
+
+def selection_cut(H, committed, bound: float, mode: str = "sum"):
+    """The two sums the selection compared with the bound around its cut, for
+    judging near-ties: (the sum at the last accepted k*, the sum at k* + 1),
+    i.e. (S_{k*}, S_{k*+1}) in mode "sum" and (S_{k*-1}, S_{k*}) in mode
+    "sum_minus_max" (float64, math.fsum; inf past the last candidate)."""
+    H = np.asarray(H, dtype=np.float64)
+    committed = np.asarray(committed).astype(bool)
+    sel = eb_select(H, committed, bound, mode)
+    cand = [i for i in range(H.shape[0]) if not committed[i]]
+    order = sorted(cand, key=lambda i: (float(H[i]), i))
+    k = int(sel.sum()) - (1 if mode == "sum_minus_max" else 0)
+
+    def prefix(j):
+        return math.fsum(float(H[i]) for i in order[:j]) if j <= len(order) else math.inf
+    return prefix(k), prefix(k + 1)
 
 
 # ---------------------------------------------------------------------------
@@ -277,7 +293,7 @@ class StepRecord:
     t: int
     tau: float
     H: np.ndarray          # float64 [N]
-    H32: np.ndarray        # float32 [N] (the values the decisions use)
+    H_dec: np.ndarray      # float64 [N]: the entropies the decisions use (H, or those fed in)
     argmax: np.ndarray     # int64 [N]
     selected: np.ndarray   # bool [N]
     drawn: dict            # pos -> token
@@ -286,22 +302,24 @@ class StepRecord:
     finished: bool
 
 
-def mean_entropy(H32) -> float:
-    """Canvas-mean entropy over all N positions: float64 sum in position order."""
-    acc = 0.0
-    for h in np.asarray(H32, dtype=np.float32):
-        acc += float(h)
-    return acc / len(H32)
+def mean_entropy(H) -> float:
+    """Canvas-mean entropy over all N positions ([MC-zh] BP1: the mean model
+    entropy of the whole canvas): math.fsum of the entropies over N."""
+    H = np.asarray(H, dtype=np.float64)
+    return math.fsum(float(h) for h in H) / len(H)
 
 
 def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: int,
-                 H32_override=None, argmax_override=None) -> StepRecord:
+                 H_override=None, argmax_override=None, selected_override=None,
+                 stop_override=None) -> StepRecord:
     """Advance ``state`` by one denoising step on logits [N][V] (in place).
 
-    ``H32_override`` / ``argmax_override`` let a parity test feed the
+    ``H_override`` / ``argmax_override`` let a parity test feed the
     entropies and argmaxes another implementation computed (after checking
     them against this oracle's), so that selection, draws, stop and fill are
-    compared on identical inputs.
+    compared on identical inputs. ``selected_override`` / ``stop_override``
+    let it adopt the other implementation's selection or stop decision where
+    it has judged the two within a stated distance of a tie.
     """
     if state.done:
         raise ValueError("canvas already finished")
@@ -310,7 +328,7 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
     tau = temperature(t, cfg)
     L = np.asarray(logits, dtype=np.float64)
     H, a, _, _ = row_stats(L, tau, cfg.mask_id)
-    H32 = H.astype(np.float32) if H32_override is None else np.asarray(H32_override, np.float32)
+    H_dec = H if H_override is None else np.asarray(H_override, np.float64)
     if argmax_override is not None:
         a = np.asarray(argmax_override, dtype=np.int64)
     if cfg.commit_mode == "keep":
@@ -319,7 +337,9 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
         cand = np.ones_like(state.committed)
     else:
         raise ValueError("unknown commit mode")
-    sel = eb_select(H32, ~cand, cfg.bound, cfg.bound_mode)
+    sel = eb_select(H_dec, ~cand, cfg.bound, cfg.bound_mode)
+    if selected_override is not None:
+        sel = np.asarray(selected_override).astype(bool) & cand
     drawn = {}
     for i in np.nonzero(sel)[0]:
         if cfg.draw_mode == "gumbel_max":
@@ -336,10 +356,12 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
     # "reselect_all" this also takes back earlier commits left unselected
     state.tokens[cand & ~sel] = cfg.mask_id
     state.committed[cand & ~sel] = False
-    mH = mean_entropy(H32)
+    mH = mean_entropy(H_dec)
     same = bool(np.array_equal(a, state.prev_argmax))
     state.stable = state.stable + 1 if (t > 0 and same) else 1
     stop = (state.stable >= cfg.stable_steps) and (mH < cfg.stop_entropy)
+    if stop_override is not None:
+        stop = bool(stop_override)
     state.prev_argmax = a.astype(np.int64).copy()
     finished = stop or t == cfg.max_steps - 1 or bool(state.committed.all())
     if finished:
@@ -348,5 +370,5 @@ def sampler_step(state: CanvasState, logits, t: int, cfg: SamplerConfig, seed: i
         state.committed[:] = True
         state.done = True
     state.steps = t + 1
-    return StepRecord(t=t, tau=tau, H=H, H32=H32, argmax=a.astype(np.int64), selected=sel,
+    return StepRecord(t=t, tau=tau, H=H, H_dec=H_dec, argmax=a.astype(np.int64), selected=sel,
                       drawn=drawn, mean_H=mH, stop=stop, finished=finished)

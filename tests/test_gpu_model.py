@@ -12,9 +12,10 @@ from oracle import model as M
 from oracle import sampler as S
 from synth import workloads as wl
 
-from model_fixtures import (SMALL_BF16, device_model, device_v, fill_synthetic_kv, oracle_kv_from_device,
-                            oracle_weights, rel_l2, rel_l2_rows, routing_near_tie_ok)
-from parity import ENT_TOL, check_sampler_step
+from model_fixtures import (SMALL_BF16, check_logit_rows, device_model, device_v, fill_synthetic_kv,
+                            oracle_kv_from_device, oracle_weights, rel_l2, rel_l2_rows, route_margins,
+                            routing_near_tie_ok)
+from parity import ENT_TOL_NORTH, check_sampler_step, check_statistics
 
 pytestmark = pytest.mark.gpu
 
@@ -93,6 +94,45 @@ def test_router_ids_stay_valid_and_distinct_on_nan_activations(B):
     assert all(len(set(r.tolist())) == cfg.top_k for r in g)
 
 
+def test_stale_values_beyond_the_visible_rows_never_reach_the_output(B):
+    """Cache rows at or past len hold NaN (a reused cache), and the canvas
+    K/V rows past a 40-row canvas in the workspace hold NaN left by an
+    earlier 64-row call: the decoder layers (windowed and global) and the
+    encoder give bit-for-bit the results of zero-filled buffers, since
+    attention masks those keys' scores and reads their values as zero."""
+    cfg = SMALL_BF16
+    model = device_model(B, cfg)
+    P, n = 300, 40                      # 40 canvas rows: a partial 64-row key block
+    tok = _canvas_tokens(cfg, 20)[:n].contiguous()
+    outs = []
+    for poison in (False, True):
+        kv = B.KVCache(model, P + 200)
+        fill_synthetic_kv(kv, cfg, P)
+        ws = torch.zeros_like(model.workspace(cfg.canvas))
+        if poison:
+            # an earlier call over 64 rows whose last 24 are NaN leaves NaN
+            # canvas K/V rows 40..63 in the workspace
+            X64 = torch.randn(64, cfg.d_model, dtype=torch.float32, device="cuda")
+            X64[n:] = float("nan")
+            for l in range(cfg.n_layers):
+                B.decoder_layer(model, l, X64, kv, ws)
+            for l in range(cfg.n_layers):
+                kv.k[l][:, P:] = float("nan")
+                kv.v[l][:, :, P:] = float("nan")
+        X = torch.empty(n, cfg.d_model, dtype=torch.float32, device="cuda")
+        B.embed(model, tok, X)
+        for l in range(cfg.n_layers):
+            B.decoder_layer(model, l, X, kv, ws)
+        B.prefill_append(model, kv, tok, ws)
+        torch.cuda.synchronize()
+        outs.append((X.clone(), [kv.k[l][:, :P + n].clone() for l in range(cfg.n_layers)],
+                     [kv.v[l][:, :, :P + n].clone() for l in range(cfg.n_layers)]))
+    assert torch.isfinite(outs[1][0]).all()
+    assert torch.equal(outs[0][0], outs[1][0])
+    for l in range(cfg.n_layers):
+        assert torch.equal(outs[0][1][l], outs[1][1][l]) and torch.equal(outs[0][2][l], outs[1][2][l]), l
+
+
 @pytest.mark.parametrize("name", list(LAYER_CFGS))
 @pytest.mark.parametrize("layer", [0, 1])
 def test_decoder_layer(B, name, layer):
@@ -166,10 +206,8 @@ def test_e4m3_lm_head_logits_and_statistics(B, name):
             Lg = stats.logits.float().cpu().numpy().astype(np.float64)
             Lb = Lg.copy()
             Lb[np.arange(n), btn] += bvn
-            H, a, Mx, Ss = S.row_stats(Lb, tau, cfg.mask_id)
+            check_statistics(stats, ocfg, Lb, t, rounded_from_f32=True)
             Hg = stats.entropy.cpu().numpy()
-            assert np.abs(Hg - H).max() < ENT_TOL
-            assert np.array_equal(stats.argmax.cpu().numpy(), a)
             Lo_b = Lo.copy()
             Lo_b[np.arange(n), btn] += bvn
             Ho, _, _, _ = S.row_stats(Lo_b, tau, cfg.mask_id)
@@ -208,10 +246,38 @@ def test_lm_head_logits_and_statistics(B, name):
         assert rel_l2_rows(Lg, Lo).max() < LOGIT_TOL[name], rel_l2_rows(Lg, Lo).max()
         Lb = Lg.astype(np.float64)
         Lb[np.arange(n), bt.cpu().numpy()] += bv.cpu().numpy().astype(np.float64)
-        H, a, Mx, Ss = S.row_stats(Lb, S.temperature(t, ocfg), cfg.mask_id)
-        assert np.abs(stats.entropy.cpu().numpy() - H).max() < ENT_TOL
-        assert np.array_equal(stats.argmax.cpu().numpy(), a)
-        assert np.abs(stats.lse.cpu().numpy() - (Mx + np.log(Ss))).max() < 1e-4 * max(1, np.abs(Mx).max())
+        # the reduction against the logits it stored (their f32 originals:
+        # within the first-order effect of the bf16 rounding)
+        check_statistics(stats, ocfg, Lb, t, rounded_from_f32=name != "tiny_f32")
+        # and against the oracle's own logits of the same activations
+        Lob = Lo.copy()
+        Lob[np.arange(n), bt.cpu().numpy()] += bv.cpu().numpy().astype(np.float64)
+        Ho, _, _, _ = S.row_stats(Lob, S.temperature(t, ocfg), cfg.mask_id)
+        assert np.abs(stats.entropy.cpu().numpy() - Ho).max() < ENT_TOL_NORTH
+
+
+def test_lm_head_outside_the_tiled_kernel(B):
+    """A bf16 model whose width is not a multiple of 64 (d_model 96): the LM
+    head takes the generic LDS GEMM with the same statistics epilogue."""
+    cfg = SMALL_BF16.replace(name="odd_bf16", n_layers=1, d_model=96, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                             vocab=1000)
+    model = device_model(B, cfg)
+    n = cfg.canvas
+    g = torch.Generator().manual_seed(7)
+    X = torch.randn(n, cfg.d_model, generator=g).cuda()
+    ws = model.workspace(n)
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    for t in (0, 47):
+        stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=torch.bfloat16)
+        B.lm_head(model, X, B.sampler_default(), t, stats, ws)
+        torch.cuda.synchronize()
+        Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+        Lo = M.lm_logits(X.cpu().numpy().astype(np.float64), model.final_norm.cpu().numpy().astype(np.float64),
+                         model.embed.float().cpu().numpy().astype(np.float64), cfg.norm_eps)
+        assert rel_l2_rows(Lg, Lo).max() < 1e-2, rel_l2_rows(Lg, Lo).max()
+        check_statistics(stats, ocfg, Lg, t, rounded_from_f32=True)
+        Ho, _, _, _ = S.row_stats(Lo, S.temperature(t, ocfg), cfg.mask_id)
+        assert np.abs(stats.entropy.cpu().numpy() - Ho).max() < ENT_TOL_NORTH
 
 
 @pytest.mark.parametrize("name", list(CFGS))
@@ -332,8 +398,8 @@ def test_small_bf16_canvas_steps_with_gumbel_max_draws(B):
         Lo = M.canvas_logits(W, before, okv, (bt.numpy(), bv.numpy()))
         Lg = stats.logits.float().cpu().numpy().astype(np.float64)
         Lg[np.arange(n), bt.numpy()] += bv.numpy().astype(np.float64)
-        assert np.quantile(rel_l2_rows(Lg, Lo), 0.9) < 2e-2
-        rec = check_sampler_step(B, st, ocfg, Lg, t, SEED, 4, stats, canvas)
+        check_logit_rows(rel_l2_rows(Lg, Lo), 2e-2, lambda: route_margins(W, before, okv), 3e-2)
+        rec = check_sampler_step(B, st, ocfg, Lg, t, SEED, 4, stats, canvas, rounded_from_f32=True)
         drawn += int(rec.selected.sum())
         if st.done:
             break
@@ -359,7 +425,7 @@ def test_tiny_generation_matches_the_oracle_trajectory(B):
             # only allowed when the oracle's own run met a near tie somewhere
             gaps = []
             for r in recs:
-                h = np.sort(r.H32[~np.isnan(r.H32)])
+                h = np.sort(r.H_dec[~np.isnan(r.H_dec)])
                 gaps.append(np.min(np.diff(h)) if h.size > 1 else 1.0)
             assert min(gaps) < 1e-3, (c, toks, ost.tokens)
         else:

@@ -70,7 +70,7 @@ def test_tiny_canvas_steps_follow_the_selection_rule():
                                    0x5EED, 0, on_step)
     prev_com = np.zeros(cfg.canvas, bool)
     for rec, com, toks in log:
-        sel = S.eb_select(rec.H32, prev_com, scfg.bound)
+        sel = S.eb_select(rec.H_dec, prev_com, scfg.bound)
         assert np.array_equal(sel, rec.selected)
         assert sel.sum() >= 1
         for i, tok in rec.drawn.items():

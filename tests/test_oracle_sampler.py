@@ -112,24 +112,28 @@ def test_temperature_lowers_entropy():
 
 # ------------------------------------------------------------- EB select ---
 
-def _brute_force(H32, committed, bound, mode):
-    n = len(H32)
+def _brute_force(H, committed, bound, mode):
+    """The largest subset of candidates whose summed entropies (minus the
+    largest, in sum_minus_max mode) stay within the bound, then the smallest
+    sum, then the lexicographically smallest positions; one argmin position
+    when no non-empty subset qualifies. Sums are exact (math.fsum)."""
+    n = len(H)
     cand = [i for i in range(n) if not committed[i]]
     if not cand:
         return set()
     best = None
     for r in range(len(cand), 0, -1):
         for U in itertools.combinations(cand, r):
-            hs = sorted(float(H32[i]) for i in U)
+            hs = sorted(float(H[i]) for i in U)
             tot = math.fsum(hs)
-            lim = tot - hs[-1] if mode == "sum_minus_max" else tot
-            if lim <= float(np.float32(bound)):
+            lim = math.fsum(hs[:-1]) if mode == "sum_minus_max" else tot
+            if lim <= bound:
                 key = (tot, sorted(U))
                 if best is None or key < best:
                     best = key
         if best is not None:
             return set(best[1])
-    i = min(cand, key=lambda i: (float(H32[i]), i))
+    i = min(cand, key=lambda i: (float(H[i]), i))
     return {i}
 
 
@@ -140,24 +144,38 @@ def test_eb_select_equals_brute_force(mode):
     for trial in range(400):
         n = int(rng.integers(1, 11))
         scale = float(rng.choice([0.005, 0.02, 0.05, 0.2]))
-        H = rng.exponential(scale, size=n).astype(np.float32)
+        H = rng.exponential(scale, size=n)
         if trial % 5 == 0:                     # exact ties
             H[rng.integers(0, n, size=n // 2)] = H[0]
         com = rng.random(n) < 0.3
-        # skip cases whose float32 running sums land within 1e-6 of the bound
-        order = sorted([i for i in range(n) if not com[i]], key=lambda i: (H[i], i))
-        sums = np.cumsum([float(H[i]) for i in order]) if order else []
-        if any(abs(s - 0.1) < 1e-6 for s in sums):
-            continue
         got = set(np.nonzero(S.eb_select(H, com, 0.1, mode))[0].tolist())
         assert got == _brute_force(H, com, 0.1, mode), (H, com)
         checked += 1
-    assert checked > 300
+    assert checked == 400
+
+
+def test_selection_and_mean_use_exact_sums():
+    """Prefix sums and the canvas mean are the correctly rounded float64 sums
+    (math.fsum), so neither the summation order nor cancellation moves a
+    decision: a cut that lands exactly on the bound is inclusive, and many
+    tiny entropies after a large one still count in the mean."""
+    H = np.array([0.05, 0.05, 0.3])
+    assert 0.05 + 0.05 == 0.1
+    sel = S.eb_select(H, np.zeros(3, bool), 0.1)
+    assert sel.tolist() == [True, True, False]
+    s_k, s_next = S.selection_cut(H, np.zeros(3, bool), 0.1)
+    assert s_k == 0.1 and s_next == math.fsum(H)
+    Hm = np.array([1.0] + [1e-16] * 10)
+    naive = 0.0
+    for h in Hm:
+        naive += h
+    assert naive == 1.0 and math.fsum(Hm) > 1.0
+    assert S.mean_entropy(Hm) == math.fsum(Hm) / len(Hm) != naive / len(Hm)
 
 
 def test_eb_select_special_cases():
     n = 16
-    H = np.zeros(n, np.float32)
+    H = np.zeros(n)
     com = np.zeros(n, bool)
     com[3] = True
     sel = S.eb_select(H, com, 0.1)
@@ -167,11 +185,11 @@ def test_eb_select_special_cases():
     assert sel.sum() == 1 and sel[n - 1]                  # all > bound -> exactly one (min H)
     sel = S.eb_select(H, np.ones(n, bool), 0.1)
     assert sel.sum() == 0                                 # no candidates
-    H = np.full(n, 0.04, np.float32)
+    H = np.full(n, 0.04)
     assert S.eb_select(H, np.zeros(n, bool), 0.1).sum() == 2          # 0.08 <= 0.1 < 0.12
     assert S.eb_select(H, np.zeros(n, bool), 0.1, "sum_minus_max").sum() == 3
     # tie at the cut: lower position first
-    H = np.array([0.06, 0.05, 0.05, 0.05], np.float32)
+    H = np.array([0.06, 0.05, 0.05, 0.05])
     sel = S.eb_select(H, np.zeros(4, bool), 0.1)
     assert list(np.nonzero(sel)[0]) == [1, 2]
 
@@ -335,8 +353,8 @@ def test_stop_threshold_is_strict():
         assert (float(h) < 0.005) == want
         st = S.CanvasState.fresh(256, 63)
         Hs = np.full(256, h, np.float32)
-        S.sampler_step(st, L, 0, cfg, 1, H32_override=Hs)
-        rec = S.sampler_step(st, L, 1, cfg, 1, H32_override=Hs)
+        S.sampler_step(st, L, 0, cfg, 1, H_override=Hs)
+        rec = S.sampler_step(st, L, 1, cfg, 1, H_override=Hs)
         assert rec.stop == want
 
 
@@ -415,7 +433,7 @@ def test_reselect_all_step_equals_brute_force_over_every_position(mode):
         st.tokens[st.committed] = rng.integers(0, mask, size=int(st.committed.sum()))
         L = rng.normal(size=(n, V)) * 3.0
         t = int(rng.integers(0, 47))
-        rec = S.sampler_step(st, L, t, cfg, seed, H32_override=H)
+        rec = S.sampler_step(st, L, t, cfg, seed, H_override=H)
         want = _brute_force(H, np.zeros(n, bool), 0.1, mode)
         assert set(np.nonzero(rec.selected)[0].tolist()) == want
         tau = S.temperature(t, cfg)
