@@ -86,6 +86,10 @@ def _load() -> C.CDLL:
     lib.dg_sampler_step.argtypes = [C.POINTER(SamplerCfg), vp, i32, i32, i32, i64, i32,
                                     C.POINTER(CanvasStruct), i32, u64, C.POINTER(StepStatsStruct),
                                     vp, sz, vp]
+    lib.dg_sampler_step_noalloc.argtypes = [C.POINTER(SamplerCfg), vp, i32, i32, i32, i64, i32,
+                                            C.POINTER(CanvasStruct), i32, u64, C.POINTER(StepStatsStruct), vp]
+    lib.dg_sampler_static_scratch_bytes.argtypes = []
+    lib.dg_sampler_static_scratch_bytes.restype = sz
     P = C.POINTER
     lib.dg_model_create.argtypes = [P(ConfigStruct), P(WeightsStruct), P(C.c_void_p)]
     lib.dg_model_destroy.argtypes = [vp]
@@ -109,7 +113,7 @@ def _load() -> C.CDLL:
     lib.dg_step_graph_launch.argtypes = [vp, vp]
     lib.dg_step_graph_destroy.argtypes = [vp]
     lib.dg_step_graph_destroy.restype = None
-    for name in ("dg_canvas_reset", "dg_sampler_step", "dg_model_create", "dg_prefill_append",
+    for name in ("dg_canvas_reset", "dg_sampler_step", "dg_sampler_step_noalloc", "dg_model_create", "dg_prefill_append",
                  "dg_canvas_step", "dg_generate_canvas", "dg_canvas_step_batch", "dg_generate_batch",
                  "dg_embed", "dg_decoder_layer", "dg_lm_head",
                  "dg_step_graph_create", "dg_step_graph_launch"):
@@ -206,6 +210,21 @@ def sampler_step(scfg: SamplerCfg, logits: torch.Tensor, mask_id: int, canvas: C
     check(lib.dg_sampler_step(C.byref(scfg), _ptr(logits), dtype_code(logits), n, V, logits.stride(0),
                               mask_id, C.byref(c), step_idx, seed, C.byref(s), _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sampler_step_noalloc(scfg: SamplerCfg, logits: torch.Tensor, mask_id: int, canvas: Canvas, step_idx: int,
+                         seed: int, stats: StepStats, stream=None) -> None:
+    """dg_sampler_step_noalloc: the sampler step on the library's static
+    per-GPU scratch (no workspace argument, no device allocation)."""
+    n, V = logits.shape
+    c = canvas.struct()
+    s = stats.struct()
+    check(lib.dg_sampler_step_noalloc(C.byref(scfg), _ptr(logits), dtype_code(logits), n, V, logits.stride(0),
+                                      mask_id, C.byref(c), step_idx, seed, C.byref(s), _stream(stream)))
+
+
+def sampler_static_scratch_bytes() -> int:
+    return int(lib.dg_sampler_static_scratch_bytes())
 
 
 lib.dg_timing_enable.argtypes = [C.c_int32]

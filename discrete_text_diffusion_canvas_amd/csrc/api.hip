@@ -3,6 +3,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/dg.h"
@@ -193,9 +194,21 @@ size_t dg_sampler_workspace_bytes(int32_t n, int32_t vocab) {
     return sampler_ws(n, vocab);
 }
 
-dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_t logits_dtype, int32_t n,
-                          int32_t vocab, int64_t ld, int32_t mask_id, dg_canvas* canvas, int32_t step_idx,
-                          uint64_t seed, dg_step_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Scratch memory of dg_sampler_step_noalloc: one copy per GPU, held until the
+// process ends. Every call on a GPU shares it; the kernels write each part
+// (row partials, selected-row list, draw chunk sums, Gumbel candidates)
+// before reading it, so nothing needs to start at zero.
+static __device__ __align__(256) unsigned char scratch[DG_SAMPLER_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Argument checks shared by dg_sampler_step and dg_sampler_step_noalloc
+// (everything but the workspace).
+dg_status check_sampler_args(const dg_sampler_cfg* scfg, const void* logits, int32_t logits_dtype, int32_t n,
+                             int32_t vocab, int64_t ld, int32_t mask_id, const dg_canvas* canvas, int32_t step_idx,
+                             const dg_step_stats* stats) {
     if (dg_status s = check_sampler_cfg(scfg)) return s;
     if (!logits) return fail(DG_E_INVALID, "logits is NULL");
     if (logits_dtype != DG_F32 && logits_dtype != DG_BF16) return fail(DG_E_UNSUPPORTED, "logits dtype");
@@ -207,8 +220,14 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
     if (dg_status s = check_canvas(canvas, n)) return s;
     if (dg_status s = check_stats(stats)) return s;
     if (step_idx < -1 || step_idx >= scfg->max_steps) return fail(DG_E_INVALID, "step_idx out of range");
-    if (!ws || ws_bytes < sampler_ws(n, vocab)) return fail(DG_E_CAPACITY, "workspace too small");
-    hipStream_t st = (hipStream_t)stream;
+    return DG_OK;
+}
+
+// The sampler step's launches over scratch memory `ws` (device address, at
+// least sampler_ws(n, vocab) bytes); arguments already checked.
+dg_status sampler_step_launch(const dg_sampler_cfg* scfg, const void* logits, int32_t logits_dtype, int32_t n,
+                              int32_t vocab, int64_t ld, int32_t mask_id, dg_canvas* canvas, int32_t step_idx,
+                              uint64_t seed, dg_step_stats* stats, void* ws, hipStream_t st) {
     dg::SamplerParams sp = to_params(scfg);
     sp.seed_lo = (uint32_t)(seed & 0xffffffffu);
     sp.seed_hi = (uint32_t)(seed >> 32);
@@ -235,6 +254,61 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
                                              canvas->committed, canvas->prev_argmax, stats->selected, sel_list,
                                              chunk_sum, gtok, stats->mean_entropy, st),
                      "sampler tail");
+}
+
+constexpr size_t kStaticScratchBytes = (size_t)DG_SAMPLER_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's scratch array, looked up once per device
+// (with that device current). The array's host-side name is not a device
+// address and is never passed to a kernel.
+dg_status static_scratch(void** out) {
+    int dev = -1;
+    if (dg_status s = hip_check(hipGetDevice(&dev), "hipGetDevice")) return s;
+    if (dev < 0 || dev >= kMaxDevices) return fail(DG_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (dg_status s = hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+            return s;
+        if (!p) return fail(DG_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_t logits_dtype, int32_t n,
+                          int32_t vocab, int64_t ld, int32_t mask_id, dg_canvas* canvas, int32_t step_idx,
+                          uint64_t seed, dg_step_stats* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (dg_status s = check_sampler_args(scfg, logits, logits_dtype, n, vocab, ld, mask_id, canvas, step_idx, stats))
+        return s;
+    if (!ws || ws_bytes < sampler_ws(n, vocab)) return fail(DG_E_CAPACITY, "workspace too small");
+    return sampler_step_launch(scfg, logits, logits_dtype, n, vocab, ld, mask_id, canvas, step_idx, seed, stats, ws,
+                               (hipStream_t)stream);
+}
+
+size_t dg_sampler_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+dg_status dg_sampler_step_noalloc(const dg_sampler_cfg* scfg, const void* logits, int32_t logits_dtype, int32_t n,
+                                  int32_t vocab, int64_t ld, int32_t mask_id, dg_canvas* canvas, int32_t step_idx,
+                                  uint64_t seed, dg_step_stats* stats, void* stream) {
+    if (dg_status s = check_sampler_args(scfg, logits, logits_dtype, n, vocab, ld, mask_id, canvas, step_idx, stats))
+        return s;
+    const size_t need = sampler_ws(n, vocab);
+    if (need > kStaticScratchBytes)
+        return fail(DG_E_CAPACITY, "n=%d x vocab=%d needs %zu bytes of scratch, above the static %zu", n, vocab, need,
+                    kStaticScratchBytes);
+    void* ws = nullptr;
+    if (dg_status s = static_scratch(&ws)) return s;
+    return sampler_step_launch(scfg, logits, logits_dtype, n, vocab, ld, mask_id, canvas, step_idx, seed, stats, ws,
+                               (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -215,6 +215,29 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
                           size_t ws_bytes, void* stream);
 
 
+/*
+ * dg_sampler_step_noalloc - dg_sampler_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, checks and results as
+ * dg_sampler_step, without ws / ws_bytes: its scratch is a static device
+ * array of DG_SAMPLER_STATIC_SCRATCH_BYTES bytes per GPU (also returned by
+ * dg_sampler_static_scratch_bytes()), which each GPU the library runs on
+ * holds until the process ends. The call allocates nothing and calls no
+ * allocating routine; the array's device address is looked up on the first
+ * call on each device (call it with that device current).
+ *   Limit: DG_E_CAPACITY when dg_sampler_workspace_bytes(n, vocab) exceeds
+ *   the array (n = 1024 rows fit up to a vocabulary of about 500K; 256 rows
+ *   up to about 2M).
+ *   Every call on a GPU shares that GPU's array, which keeps the last call's
+ *   contents: calls that overlap on one GPU (different streams or threads)
+ *   race; serialise them.
+ */
+#define DG_SAMPLER_STATIC_SCRATCH_BYTES (2u << 20)
+size_t dg_sampler_static_scratch_bytes(void);
+dg_status dg_sampler_step_noalloc(const dg_sampler_cfg* scfg, const void* logits, int32_t logits_dtype, int32_t n,
+                                  int32_t vocab, int64_t ld, int32_t mask_id, dg_canvas* canvas,
+                                  int32_t step_idx, uint64_t seed, dg_step_stats* stats, void* stream);
+
 /* ------------------------------------------------------------------------
  * Model geometry. The spec table of the model card fixes the counts (30
  * layers, 1024-token window, 128 experts with 8 active plus 1 shared, 262K
