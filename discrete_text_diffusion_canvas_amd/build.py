@@ -34,7 +34,10 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    # DG_HIPCC_FLAGS: extra -D settings of the build-time tunables (kernel
+    # shape sweeps); empty for the normal build
+    extra = os.environ.get("DG_HIPCC_FLAGS", "").split()
+    cmd = [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-4000:]}")

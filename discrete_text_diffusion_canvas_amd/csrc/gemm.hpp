@@ -14,6 +14,7 @@ enum { SHAPE_PROJ = 0, SHAPE_SMALL_M = 1, SHAPE_LDS = 2 };
 struct GemmArgs {
     // A: activations [rows][K] (f32 or bf16), row stride lda; optional gather
     const void* A;
+    const void* A2;                 // LM head: the bf16 residual x - bf16(x) of A, same layout
     int64_t lda;
     const int32_t* a_rows;          // A row of output row r is a_rows[r] (grouped gathers)
     // W: weights [N][K] per group, row stride ldw (elements); fp8 codes or same type as A
@@ -55,6 +56,11 @@ hipError_t gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int g
                        hipStream_t st);
 hipError_t stream_gemm_launch(const GemmArgs& g, int act_f32, int w_fp8, int epi, int groups, int max_rows,
                               hipStream_t st);
+// The LM head with bf16 activations given as hi + lo pairs (A, A2), bf16 or
+// e4m3 (w_scale) vocabulary rows, f32 statistics partials per 128 columns
+// (lmhead.hip): K % 64 == 0, N % 8 == 0, ldc % 8 == 0, nsplit = N / 128.
+bool lmhead_supported(const GemmArgs& g);
+hipError_t lmhead_launch(const GemmArgs& g, hipStream_t st);
 // LDS-staged GEMM (bf16 activations and weights, K % 64 == 0): grouped over
 // the big-group list in g.hit / g.hit_mb (SwiGLU or f32 store), or dense
 // (g.group_offsets NULL) with optional split-K through g.part.

@@ -70,18 +70,9 @@
 #ifndef DG_GU_KSPLIT
 #define DG_GU_KSPLIT 2
 #endif
-// LM head tile width (128 or 256; statistics partials stay per 128 rows).
-// 256 halves the activation bytes per weight byte; its registers allow only
-// one stage loaded ahead (measured 421 vs 455 us on 256 x 262144 x 2816)
-#ifndef DG_TILE_BN_LM
-#define DG_TILE_BN_LM 256
-#endif
-// stages the operand registers are loaded ahead (dense/grouped; LM head)
+// stages the operand registers are loaded ahead
 #ifndef DG_TILE_DEPTH
 #define DG_TILE_DEPTH 2
-#endif
-#ifndef DG_TILE_DEPTH_LM
-#define DG_TILE_DEPTH_LM (DG_TILE_BN_LM > 128 ? 1 : DG_TILE_DEPTH)
 #endif
 // e4m3 -> bf16 widening of the weight tiles: 1 = the gfx950 scaled pack
 // conversion at scale 1, 0 = bit manipulation
@@ -172,163 +163,6 @@ __device__ __forceinline__ void tile_store4(const GemmArgs& g, int64_t row, int 
         } else {
             for (int q = 0; q < 4 && n + q < g.N; ++q) dst[q] += vv[q];
         }
-    }
-}
-
-// LM-head epilogue on the tile T[r][c] (the f32 accumulators) of vocabulary
-// rows [tile*BN, +BN): (1) the logits of record leave as bf16 in 16-byte
-// coalesced stores; (2) per canvas row, the tile's partial statistics from
-// the f32 values: the max and the 2^x partition sum and entropy partial of
-// the tempered logits (log2 units), and the raw argmax (first index among
-// equal values), with the row's bias token added and the mask token
-// excluded. merge_rows combines the partials. Draws sample the logits of
-// record, so the Gumbel-max candidate is taken from the bf16-rounded values.
-//
-// The statistics use TPR = NT / BM threads per row (1 or 2), each over a
-// contiguous 1/TPR of the columns, in two passes: the raw max and its index,
-// exchanged between the row's threads through the 4 padding floats of its T
-// row; then the sums against the merged max (tempering by 1/tau > 0 keeps the
-// order, so the tempered max is the raw max times the factor), added across
-// the row's threads. A thread whose columns hold no bias or mask token and
-// no column past N runs a loop free of per-column tests.
-template <int BN, int NT, int BM>
-__device__ __forceinline__ void tile_lmhead_epilogue(const GemmArgs& g, float* T, int mcount, int tile, int rbase) {
-    constexpr int TS = BN + 4;
-    constexpr int TPR = NT / BM;
-    static_assert(TPR == 1 || TPR == 2, "one or two threads per row");
-    constexpr int CW = BN / TPR;  // columns per thread
-    const int tid = threadIdx.x, N = g.N, n0 = tile * BN;
-    uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
-    for (int e = tid; e < mcount * (BN / 8); e += NT) {
-        const int r = e / (BN / 8), c0 = (e % (BN / 8)) * 8;
-        const int n = n0 + c0;
-        const float* t = T + r * TS + c0;
-        uint16_t* dst = C + (int64_t)(rbase + r) * g.ldc + n;
-        if (n + 8 <= N) {
-            uint4 w;
-            w.x = f2bf2(t[0], t[1]);
-            w.y = f2bf2(t[2], t[3]);
-            w.z = f2bf2(t[4], t[5]);
-            w.w = f2bf2(t[6], t[7]);
-            *reinterpret_cast<uint4*>(dst) = w;
-        } else {
-            for (int u = 0; u < 8 && n + u < N; ++u) dst[u] = f2bf(t[u]);
-        }
-    }
-    const int r = tid % BM, part = tid / BM;
-    const bool act = r < mcount;
-    const int c0 = part * CW, cn0 = n0 + c0;  // this thread's first column / vocabulary row
-    float* row = T + r * TS;
-    const int step = g.step_override >= 0 ? g.step_override : (g.state ? g.state[1] : 0);
-    const float c2 = (float)(1.4426950408889634 / lm_tau_at(g.sp, step));
-    const int bt = act && g.bias_tok ? g.bias_tok[rbase + r] : -1;
-    const float bv = act && g.bias_tok ? g.bias_val[rbase + r] : 0.f;
-    const bool special = (bt >= cn0 && bt < cn0 + CW) || (g.mask_id >= cn0 && g.mask_id < cn0 + CW) || cn0 + CW > N;
-    // pass 1: raw max and its first index
-    float rawm = -INFINITY;
-    int vi = 0x7fffffff;
-    if (act && !special) {
-#pragma unroll 4
-        for (int c = c0; c < c0 + CW; c += 4) {
-            const float4 v4 = *reinterpret_cast<const float4*>(row + c);
-            const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (e4[u] > rawm) { rawm = e4[u]; vi = n0 + c + u; }
-        }
-    } else if (act) {
-        for (int c = c0; c < c0 + CW; ++c) {
-            const int n = n0 + c;
-            float lb = row[c] + (n == bt ? bv : 0.f);
-            if (n >= N || n == g.mask_id) lb = -INFINITY;
-            if (lb > rawm) { rawm = lb; vi = n; }
-        }
-    }
-    if constexpr (TPR == 2) {
-        __syncthreads();  // every thread done reading T's values
-        if (act) { row[BN + 2 * part] = rawm; row[BN + 2 * part + 1] = __int_as_float(vi); }
-        __syncthreads();
-        if (act) {
-            const float om = row[BN + 2 * (1 - part)];
-            const int oi = __float_as_int(row[BN + 2 * (1 - part) + 1]);
-            if (om > rawm || (om == rawm && oi < vi)) { rawm = om; vi = oi; }
-        }
-    }
-    // pass 2: partition sum and entropy partial against the merged max
-    const float vm = rawm * c2;
-    float sum = 0.f, tt = 0.f;
-    if (act && rawm != -INFINITY) {
-        if (!special) {
-#pragma unroll 4
-            for (int c = c0; c < c0 + CW; c += 4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(row + c);
-                const float e4[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float d = e4[u] * c2 - vm;
-                    const float w = exp2f(d);
-                    sum += w;
-                    tt += w * d;
-                }
-            }
-        } else {
-            for (int c = c0; c < c0 + CW; ++c) {
-                const int n = n0 + c;
-                float lb = row[c] + (n == bt ? bv : 0.f);
-                if (n >= N || n == g.mask_id) lb = -INFINITY;
-                const float d = lb * c2 - vm;
-                const float w = exp2f(d);
-                sum += w;
-                tt += w > 0.f ? w * d : 0.f;
-            }
-        }
-    }
-    if constexpr (TPR == 2) {
-        __syncthreads();  // both halves' maxima read
-        if (act && part == 1) { row[BN] = sum; row[BN + 1] = tt; }
-        __syncthreads();
-        if (act && part == 0) { sum += row[BN]; tt += row[BN + 1]; }
-    }
-    // Gumbel-max draws: this tile's lowest column maximising z - log(-log u),
-    // z = (L + bias) / tau, u from Philox at (row, step, canvas, 1 + v / 4)
-    float gv = -INFINITY;
-    int gi = 0x7fffffff;
-    if (g.sp.draw_mode) {
-        const float inv_tau = (float)(1.0 / lm_tau_at(g.sp, step));
-        if (act) {
-            for (int c = c0; c < c0 + CW && n0 + c < N; c += 4) {
-                const int v0 = n0 + c;
-                const u32x4 wd = philox10(u32x4{(uint32_t)(rbase + r), (uint32_t)step, (uint32_t)g.sp.canvas_idx,
-                                                (uint32_t)(1 + v0 / 4)},
-                                          g.sp.seed_lo, g.sp.seed_hi);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int v = v0 + u;
-                    if (v >= N || v == g.mask_id) continue;
-                    const float val = (round_bf(row[c + u]) + (v == bt ? bv : 0.f)) * inv_tau + gumbel_of(wd[u]);
-                    if (val > gv) { gv = val; gi = v; }
-                }
-            }
-        }
-        if constexpr (TPR == 2) {
-            __syncthreads();  // part 0 has read the sums
-            if (act && part == 1) { row[BN + 2] = gv; row[BN + 3] = __int_as_float(gi); }
-            __syncthreads();
-            if (act && part == 0) {
-                const float ov = row[BN + 2];
-                const int oi = __float_as_int(row[BN + 3]);
-                if (ov > gv || (ov == gv && oi < gi)) { gv = ov; gi = oi; }
-            }
-        }
-    }
-    if (act && part == 0) {
-        RowPart p;
-        p.m2 = rawm == -INFINITY ? -INFINITY : vm; p.s = sum; p.t = tt; p.lmax = rawm;
-        p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
-        p.pad[0] = __float_as_int(gv);
-        p.pad[1] = gi == 0x7fffffff ? -1 : gi;
-        p.pad[2] = 0;
-        g.parts[(int64_t)(rbase + r) * g.nsplit + tile] = p;
     }
 }
 
@@ -645,8 +479,6 @@ __global__ void __launch_bounds__((tile_waves<BN, BM>() * 64)) tile_gemm_kernel(
                 const float4 v = *reinterpret_cast<const float4*>(T + r * TS + c0);
                 *reinterpret_cast<float4*>(P + (int64_t)(row0 + m0 + r) * g.N + n) = v;  // N % 8 == 0
             }
-        } else if constexpr (EPI == EPI_LMHEAD) {
-            if (ptile < g.nsplit) tile_lmhead_epilogue<EP, NT, BM>(g, T, mcount, ptile, m0);  // past N: no columns
         } else if constexpr (EPI == EPI_SWIGLU) {
             constexpr int CH = EP / 2 / 8;  // 8-column chunks of hidden units per row
             uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
@@ -730,7 +562,6 @@ bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
         case EPI_STORE_F32: return g.ldc % 4 == 0 && g.N % 4 == 0;
         case EPI_STORE_BF16: return g.ldc % 4 == 0 && g.N % 4 == 0;
         case EPI_RESIDUAL: return g.ldx % 4 == 0 && g.N % 4 == 0;
-        case EPI_LMHEAD: return !g.c_f32 && g.ldc % 8 == 0;
         default: return false;
     }
 }
@@ -777,17 +608,9 @@ static hipError_t tile_gemm_launch_w(const GemmArgs& g, int epi, int groups, int
 }
 
 hipError_t tile_gemm_launch(const GemmArgs& g, int epi, int groups, int max_rows, hipStream_t st) {
-    if (epi != EPI_LMHEAD) {
-        if (!g.w_scale) return tile_gemm_launch_w<false>(g, epi, groups, max_rows, st);
-        if (epi == EPI_SWIGLU && !g.w2_scale) return hipErrorInvalidValue;
-        return tile_gemm_launch_w<true>(g, epi, groups, max_rows, st);
-    }
-    // 256-row blocks (the blocks of one vocabulary tile run on one XCD, so
-    // the tile's weight rows come from its L2 after the first); statistics
-    // partials per 128 vocabulary rows; bf16 or e4m3 vocabulary rows
-    if (g.ksplit > 1 || g.c_f32 || g.nsplit != (g.N + 127) / 128) return hipErrorInvalidValue;
-    if (g.w_scale) return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM, TBM, true>(g, 1, g.M, st);
-    return launch_tile_t<DG_TILE_BN_LM, EPI_LMHEAD, DG_TILE_DEPTH_LM>(g, 1, g.M, st);
+    if (!g.w_scale) return tile_gemm_launch_w<false>(g, epi, groups, max_rows, st);
+    if (epi == EPI_SWIGLU && !g.w2_scale) return hipErrorInvalidValue;
+    return tile_gemm_launch_w<true>(g, epi, groups, max_rows, st);
 }
 
 }  // namespace dg

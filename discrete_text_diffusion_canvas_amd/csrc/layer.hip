@@ -38,9 +38,12 @@ __global__ void __launch_bounds__(256) embed_kernel(const TE* __restrict__ E, in
 // ---------------------------------------------------------------------------
 constexpr int NORM_V4 = 4;  // float4 per thread: d <= 4096
 
+// With ylo (bf16 outputs only) the row is also left as a pair: y = bf16(v)
+// and ylo = bf16(v - y), which carries v to ~16 significant bits (the LM
+// head's activation operand).
 template <typename TO>
 __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int nv, const float* __restrict__ w,
-                                               float eps, int d, TO* __restrict__ y) {
+                                               float eps, int d, TO* __restrict__ y, TO* __restrict__ ylo) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
@@ -65,6 +68,12 @@ __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int n
             o.x = f2bf2(v[0], v[1]);
             o.y = f2bf2(v[2], v[3]);
             reinterpret_cast<uint2*>(y)[c] = o;
+            if (ylo) {
+                uint2 r;
+                r.x = f2bf2(v[0] - __uint_as_float(o.x << 16), v[1] - __uint_as_float(o.x & 0xffff0000u));
+                r.y = f2bf2(v[2] - __uint_as_float(o.y << 16), v[3] - __uint_as_float(o.y & 0xffff0000u));
+                reinterpret_cast<uint2*>(ylo)[c] = r;
+            }
         } else {
             reinterpret_cast<float4*>(y)[c] = make_float4(v[0], v[1], v[2], v[3]);
         }
@@ -77,7 +86,8 @@ __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int n
 template <typename TO>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(float* __restrict__ X, const float* __restrict__ part, int nparts,
                                                       int n, int d, const float* __restrict__ w, float eps,
-                                                      TO* __restrict__ Y, const int32_t* __restrict__ state) {
+                                                      TO* __restrict__ Y, TO* __restrict__ Ylo,
+                                                      const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     const int i = blockIdx.x, nv = d / 4;
     float4* x4 = reinterpret_cast<float4*>(X + (int64_t)i * d);
@@ -119,7 +129,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(float* __restrict__ X, con
             x4[c] = x[j];
         }
     }
-    norm_row_store<TO>(x, nv, w, eps, d, Y + (int64_t)i * d);
+    norm_row_store<TO>(x, nv, w, eps, d, Y + (int64_t)i * d, Ylo ? Ylo + (int64_t)i * d : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -523,7 +533,7 @@ __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gates, int k, int shared_off,
                                                       const float* __restrict__ nw, float eps, TO* __restrict__ A,
-                                                      const int32_t* __restrict__ state) {
+                                                      TO* __restrict__ Alo, const int32_t* __restrict__ state) {
     if (state && state[0]) return;
     const int i = blockIdx.x, nv = d / 4;
     __shared__ int sl[16];
@@ -552,7 +562,7 @@ __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int
         xr[c] = v;
         x[j] = v;
     }
-    if (nw) norm_row_store<TO>(x, nv, nw, eps, d, A + (int64_t)i * d);
+    if (nw) norm_row_store<TO>(x, nv, nw, eps, d, A + (int64_t)i * d, Alo ? Alo + (int64_t)i * d : nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -566,15 +576,17 @@ hipError_t launch_embed(const void* E, int act_f32, int d, int V, const int32_t*
 }
 
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
-                          const int32_t* state, hipStream_t st) {
-    return launch_residual_rmsnorm(const_cast<float*>(X), nullptr, 0, n, d, w, eps, Y, act_f32, state, st);
+                          const int32_t* state, hipStream_t st, void* Ylo) {
+    return launch_residual_rmsnorm(const_cast<float*>(X), nullptr, 0, n, d, w, eps, Y, act_f32, state, st, Ylo);
 }
 
 hipError_t launch_residual_rmsnorm(float* X, const float* part, int nparts, int n, int d, const float* w, float eps,
-                                   void* Y, int act_f32, const int32_t* state, hipStream_t st) {
-    if (d % 4 || d > 4 * 256 * NORM_V4 || (nparts > 0 && !part)) return hipErrorInvalidValue;
-    if (act_f32) rmsnorm_kernel<float><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (float*)Y, state);
-    else rmsnorm_kernel<uint16_t><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (uint16_t*)Y, state);
+                                   void* Y, int act_f32, const int32_t* state, hipStream_t st, void* Ylo) {
+    if (d % 4 || d > 4 * 256 * NORM_V4 || (nparts > 0 && !part) || (Ylo && act_f32)) return hipErrorInvalidValue;
+    if (act_f32) rmsnorm_kernel<float><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (float*)Y, nullptr, state);
+    else
+        rmsnorm_kernel<uint16_t><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (uint16_t*)Y, (uint16_t*)Ylo,
+                                                     state);
     return hipGetLastError();
 }
 
@@ -643,14 +655,14 @@ hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t*
 
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
                           int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
-                          hipStream_t st) {
-    if (d % 4 || d > 4 * 256 * NORM_V4 || k > 16) return hipErrorInvalidValue;
+                          hipStream_t st, void* Alo) {
+    if (d % 4 || d > 4 * 256 * NORM_V4 || k > 16 || (Alo && act_f32)) return hipErrorInvalidValue;
     if (act_f32)
         combine_kernel<float><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
-                                                 state);
+                                                 nullptr, state);
     else
         combine_kernel<uint16_t><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
-                                                    (uint16_t*)A, state);
+                                                    (uint16_t*)A, (uint16_t*)Alo, state);
     return hipGetLastError();
 }
 

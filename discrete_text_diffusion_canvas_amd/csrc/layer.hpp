@@ -8,12 +8,13 @@ namespace dg {
 
 hipError_t launch_embed(const void* E, int act_f32, int d, int V, const int32_t* tok, int n, float* X,
                         const int32_t* state, hipStream_t st);
+// Y = rmsnorm(X); with Ylo (bf16 only) also Ylo = bf16(rmsnorm(X) - Y)
 hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float eps, void* Y, int act_f32,
-                          const int32_t* state, hipStream_t st);
+                          const int32_t* state, hipStream_t st, void* Ylo = nullptr);
 // X += sum over the nparts K-slice partials part[s][n][d] (slice order), then
 // Y = rmsnorm(X); nparts = 0: the plain norm
 hipError_t launch_residual_rmsnorm(float* X, const float* part, int nparts, int n, int d, const float* w, float eps,
-                                   void* Y, int act_f32, const int32_t* state, hipStream_t st);
+                                   void* Y, int act_f32, const int32_t* state, hipStream_t st, void* Ylo = nullptr);
 hipError_t launch_rope_table(int n, int hd, int64_t pos0, double base, float* cs, const int32_t* state,
                              hipStream_t st);
 // qkv, or (nparts > 1) its K-slice f32 partials part[nparts][n][width]
@@ -29,17 +30,19 @@ int hist_permute_max_rows(int k, int E);
 hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t* offsets, int32_t* perm,
                                int32_t* slot_of, int32_t* hit, int32_t* hit_mb, int32_t* hitB, int32_t* hitB_mb,
                                int big_min, int32_t* hit_out, const int32_t* state, hipStream_t st);
+// X += shared + gated expert rows; with norm_w, A = rmsnorm(X) (and, with Alo,
+// bf16 only, Alo = bf16(rmsnorm(X) - A))
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
                           int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
-                          hipStream_t st);
+                          hipStream_t st, void* Alo = nullptr);
 
 // Attention over up to two key segments per KV head (V stored transposed):
 //   segment 1: K1 [Hkv][ld1][hd], V1^T [Hkv][hd][ld1], rows [s1, e1) (cache),
 //              positions = row index
 //   segment 2: K2 [Hkv][ld2][hd], V2^T [Hkv][hd][ld2], rows [0, n2) (canvas),
 //              positions pos2_0 + row
-// ld1 and ld2 are multiples of 64; V^T columns past e1 / n2 up to the next
-// multiple of 64 hold finite values.
+// ld1 and ld2 are multiples of 64; V^T columns past e1 / n2 may hold anything
+// (the bf16 kernel reads them as zero; the generic kernel never reads them).
 // Queries Q [Hq][ldq][hd] rows [0, nq) at positions qpos0 + row; output
 // O [nq][Hq*hd]. causal: key position <= query position; window > 0: and
 // query position - key position < window (per query). Softmax scale 1/sqrt(hd).

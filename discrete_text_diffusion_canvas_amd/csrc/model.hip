@@ -50,6 +50,7 @@ bool is_global(const dg_config& c, int l) { return c.global_every > 0 && l % c.g
 struct Work {
     float* X;          // [T][d] residual stream
     void* A;           // [T][d] normed activations (act dtype)
+    void* A_lo;        // [T][d] bf16 residual of the final-normed activations (LM head operand)
     void* QKV;         // [T][(Hq+2Hkv) hd]
     void* Q;           // [Hq][T][hd]
     void* Kc;          // [Hkv][T64][hd]
@@ -118,6 +119,7 @@ Work carve(const dg_model* m, void* base, int T) {
     Work w;
     w.X = cv.take<float>((size_t)T * d);
     w.A = cv.take<char>((size_t)T * d * ab);
+    w.A_lo = cv.take<char>((size_t)T * d * ab);
     w.QKV = cv.take<char>((size_t)T * (Hq + 2 * Hkv) * hd * ab);
     w.Q = cv.take<char>((size_t)T * Hq * hd * ab);
     const int T64 = (T + 63) / 64 * 64;
@@ -209,8 +211,10 @@ hipError_t dense_gemm(dg::GemmArgs g, const Work& w, int f32, int fp8, int epi, 
 // ---------------------------------------------------------------------------
 // resid_parts > 1: the output projection left that many K-slice partials in
 // w.gemm_part, added to X here before the norm.
+// next_lo: with the final norm as next_norm (bf16), the normed rows are also
+// left as hi + lo pairs for the LM head (w.A, w.A_lo).
 dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float* next_norm, const int32_t* state,
-                    hipStream_t st, int resid_parts = 1) {
+                    hipStream_t st, int resid_parts = 1, bool next_lo = false) {
     const dg_config& c = m->cfg;
     const dg_layer_weights& L = m->layers[l];
     const int d = c.d_model, E = c.n_experts, k = c.top_k, F = c.ffn_hidden;
@@ -275,7 +279,7 @@ dg_status moe_block(const dg_model* m, int l, const Work& w, int n, const float*
         timing_end(slot, st);
     }
     DG_TRY(dg::launch_combine(w.X, n, d, w.Y, w.slot_of, w.gates, k, n * k, next_norm, c.norm_eps, w.A, f32, state,
-                              st),
+                              st, next_lo && !f32 ? w.A_lo : nullptr),
            "combine");
     return DG_OK;
 }
@@ -298,7 +302,8 @@ struct Seg {
 };
 
 dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const Seg* segs, int nseg,
-                        const int32_t* state, bool normed_in, const float* next_norm, hipStream_t st) {
+                        const int32_t* state, bool normed_in, const float* next_norm, hipStream_t st,
+                        bool next_lo = false) {
     const dg_config& c = m->cfg;
     const dg_layer_weights& L = m->layers[l];
     const int d = c.d_model, hd = c.head_dim, Hq = c.n_q_heads, Hkv = c.n_kv_heads;
@@ -345,7 +350,7 @@ dg_status decoder_layer(const dg_model* m, int l, const Work& w, int n, const Se
         DG_TRY(dense_gemm(g, w, f32, fp8, dg::EPI_RESIDUAL, st, &o_parts), "o gemm");
         timing_end(slot, st);
     }
-    return moe_block(m, l, w, n, next_norm, state, st, o_parts);
+    return moe_block(m, l, w, n, next_norm, state, st, o_parts, next_lo);
 }
 
 // ---------------------------------------------------------------------------
@@ -400,10 +405,15 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
                   bool normed_in, hipStream_t st, int32_t* gtok = nullptr) {
     const dg_config& c = m->cfg;
     const int f32 = c.act_dtype == DG_F32;
+    // bf16: the final-normed rows as hi + lo pairs (w.A, w.A_lo), written by
+    // the last layer's combine when normed_in
     if (!normed_in)
-        DG_TRY(dg::launch_rmsnorm(w.X, n, c.d_model, m->final_norm, c.norm_eps, w.A, f32, state, st), "final norm");
+        DG_TRY(dg::launch_rmsnorm(w.X, n, c.d_model, m->final_norm, c.norm_eps, w.A, f32, state, st,
+                                  f32 ? nullptr : w.A_lo),
+               "final norm");
     dg::GemmArgs g = gargs();
-    g.A = w.A; g.lda = c.d_model; g.W = m->lm8 ? m->lm8 : m->embed; g.ldw = c.d_model;
+    g.A = w.A; g.A2 = f32 ? nullptr : w.A_lo; g.lda = c.d_model; g.W = m->lm8 ? m->lm8 : m->embed;
+    g.ldw = c.d_model;
     g.w_scale = m->lm8_scale;
     g.M = n; g.N = c.vocab; g.K = c.d_model;
     g.C = stats->logits; g.ldc = stats->logits_ld; g.c_f32 = f32;
@@ -411,10 +421,10 @@ dg_status lm_head(const dg_model* m, const Work& w, int n, const dg::SamplerPara
     g.state = state; g.step_override = step_override; g.sp = sp; g.mask_id = c.mask_id;
     g.bias_tok = bias_tok; g.bias_val = bias_val;
     int slot = timing_begin(st, DG_TIME_LM_HEAD);
-    if (dg::tile_gemm_supported(g, f32, m->lm8 != nullptr, dg::EPI_LMHEAD))
-        DG_TRY(dg::tile_gemm_launch(g, dg::EPI_LMHEAD, 1, n, st), "lm head");
+    if (!f32 && dg::lmhead_supported(g))
+        DG_TRY(dg::lmhead_launch(g, st), "lm head");
     else if (m->lm8 || sp.draw_mode)
-        return fail(DG_E_UNSUPPORTED, "e4m3 LM head or Gumbel-max draws: shape outside the tile kernel");
+        return fail(DG_E_UNSUPPORTED, "e4m3 LM head or Gumbel-max draws: shape outside the LM-head kernel");
     else
         DG_TRY(dg::gemm_launch(g, f32, 0, dg::EPI_LMHEAD, 0, dg::SHAPE_PROJ, st), "lm head");
     timing_end(slot, st);
@@ -633,7 +643,8 @@ dg_status dg_canvas_step(const dg_model* m, dg_canvas* canvas, const dg_kv* kv, 
     for (int l = 0; l < c.n_layers; ++l) {
         const float* next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
         const Seg seg{0, n, kv};
-        if (dg_status s = decoder_layer(m, l, w, n, &seg, 1, canvas->state, l > 0, next, st)) return s;
+        if (dg_status s = decoder_layer(m, l, w, n, &seg, 1, canvas->state, l > 0, next, st, l + 1 == c.n_layers))
+            return s;
     }
     if (dg_status s = lm_head(m, w, n, sp, step_idx, canvas->state, canvas->bias_tok, canvas->bias_val, stats, true,
                               st, w.gtok))
@@ -731,7 +742,8 @@ dg_status dg_canvas_step_batch(const dg_model* m, dg_canvas* canvases, const dg_
     }
     for (int l = 0; l < c.n_layers; ++l) {
         const float* next = l + 1 < c.n_layers ? m->layers[l + 1].attn_norm : m->final_norm;
-        if (dg_status s = decoder_layer(m, l, w, rows, segs, nb, nullptr, l > 0, next, st)) return s;
+        if (dg_status s = decoder_layer(m, l, w, rows, segs, nb, nullptr, l > 0, next, st, l + 1 == c.n_layers))
+            return s;
     }
     if (dg_status s = lm_head(m, w, rows, sp, step_idx, nullptr, any_bias ? w.bias_tok : nullptr,
                               any_bias ? w.bias_val : nullptr, stats, true, st))

@@ -12,7 +12,7 @@ from oracle import sampler as S
 from synth import workloads as wl
 
 from model_fixtures import device_model, device_v, oracle_weights, rel_l2, rel_l2_rows, routing_near_tie_ok
-from parity import check_sampler_step
+from parity import ENT_TOL_NORTH, check_sampler_step, check_statistics
 
 pytestmark = pytest.mark.gpu
 
@@ -100,3 +100,42 @@ def test_full_width_layer_and_lm_head_step(B, setup):
     # entropies against the oracle's own float64 logits: the stated 1e-2 nats
     Ho, _, _, _ = S.row_stats(Lo, S.temperature(5, ocfg), cfg.mask_id)
     assert np.abs(stats.entropy.cpu().numpy() - Ho).max() < 1e-2
+
+
+@pytest.mark.parametrize("head", ["bf16", "e4m3"])
+def test_full_width_lm_head_entropies_across_the_schedule(B, setup, head):
+    """The LM head on the full-width decoder layer's output (the GPU's
+    residual stream after one layer over a canvas with 128 committed
+    positions): at t = 0, 23 and 47 (tau 0.8, 0.6, 0.4) every row's entropy
+    is within the stated 1e-2 nats of the entropy of the oracle's own float64
+    logits of the same rows, for the bf16 head and the e4m3 head (against
+    the dequantised matrix); logits within 2e-2 (bf16) / 5e-2 (e4m3)."""
+    cfg, model, kv, ws, W, prompt = setup
+    n = cfg.canvas
+    toks, _ = wl.committed_canvas(cfg, 128)
+    X = torch.empty(n, cfg.d_model, dtype=torch.float32, device="cuda")
+    B.embed(model, toks.cuda(), X)
+    B.decoder_layer(model, 0, X, kv, ws)
+    torch.cuda.synchronize()
+    if head == "e4m3":
+        codes, scale = wl.lm_head_e4m3(cfg, device="cuda")
+        lm_model = B.Model(cfg, model.embed, model.final_norm, model.layers, lm_head_e4m3=codes,
+                           lm_head_scale=scale)
+        E = M.Weights(cfg, model.embed.cpu(), model.final_norm.cpu(), lambda l: {},
+                      lm_head=(codes.cpu(), scale.cpu())).LM
+    else:
+        lm_model, E = model, W.E
+    Lo = M.lm_logits(X.cpu().numpy().astype(np.float64), W.final_norm, E, cfg.norm_eps)
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    for t in (0, 23, 47):
+        stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=torch.bfloat16)
+        B.lm_head(lm_model, X, B.sampler_default(), t, stats, ws)
+        torch.cuda.synchronize()
+        Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+        assert rel_l2_rows(Lg, Lo).max() < (2e-2 if head == "bf16" else 5e-2), rel_l2_rows(Lg, Lo).max()
+        check_statistics(stats, ocfg, Lg, t, rounded_from_f32=True)
+        Ho, _, _, _ = S.row_stats(Lo, S.temperature(t, ocfg), cfg.mask_id)
+        dH = np.abs(stats.entropy.cpu().numpy() - Ho)
+        print(f"{head} t={t}: max |dH| {dH.max():.2e}, max row logit error {rel_l2_rows(Lg, Lo).max():.2e}")
+        assert dH.max() < ENT_TOL_NORTH, (head, t, float(dH.max()))
+        del Lg

@@ -171,11 +171,12 @@ def test_decoder_layer(B, name, layer):
 @pytest.mark.parametrize("name", ["small_bf16", "full_width"])
 def test_e4m3_lm_head_logits_and_statistics(B, name):
     """The LM head reading an e4m3 copy of the tied matrix (bf16 scale per
-    vocabulary row): logits within the e4m3 bound of the oracle on the
-    dequantised matrix, statistics and argmax on the logits it wrote, and
-    end-to-end entropies within the first-order bound that the logit gap
-    sets (both heads are limited by the bf16 activations and logits of
-    record, not by the weight format)."""
+    vocabulary row) and the bf16 head, on random activations with per-row
+    logit boosts U(0, 12), at the first, middle and last temperatures of the
+    schedule: logits within the bf16 / e4m3 bars of the oracle on the same
+    (dequantised) matrix, the statistics against the logits each stored, and
+    every row's entropy within the stated 1e-2 nats of the oracle's own
+    float64 logits."""
     cfg = SMALL_BF16 if name == "small_bf16" else wl.FULL_LAYER
     embed = wl.embedding(cfg, device="cuda")
     codes, scale = wl.lm_head_e4m3(cfg, device="cuda")
@@ -193,35 +194,26 @@ def test_e4m3_lm_head_logits_and_statistics(B, name):
     ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
     Xn = X.cpu().numpy().astype(np.float64)
     W8 = M.Weights(cfg, embed.cpu(), fnorm.cpu(), lambda l: {}, lm_head=(codes.cpu(), scale.cpu()))
-    Lo8 = M.lm_logits(Xn, W8.final_norm, W8.LM, cfg.norm_eps)
-    Lob = M.lm_logits(Xn, W8.final_norm, W8.E, cfg.norm_eps)
     btn, bvn = bt.cpu().numpy(), bv.cpu().numpy().astype(np.float64)
-    for t in (0, 47):
-        tau = S.temperature(t, ocfg)
-        res = {}
-        for key, model, Lo in (("e4m3", m8, Lo8), ("bf16", mb, Lob)):
+    for key, model in (("e4m3", m8), ("bf16", mb)):
+        Lo = M.lm_logits(Xn, W8.final_norm, W8.LM if key == "e4m3" else W8.E, cfg.norm_eps)
+        Lo_b = Lo.copy()
+        Lo_b[np.arange(n), btn] += bvn
+        for t in (0, 23, 47):
+            tau = S.temperature(t, ocfg)
             stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=model.act_dtype)
             B.lm_head(model, X, scfg, t, stats, ws, bt, bv)
             torch.cuda.synchronize()
             Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+            assert rel_l2_rows(Lg, Lo).max() < (5e-2 if key == "e4m3" else 1e-2), (key, rel_l2_rows(Lg, Lo).max())
             Lb = Lg.copy()
             Lb[np.arange(n), btn] += bvn
             check_statistics(stats, ocfg, Lb, t, rounded_from_f32=True)
-            Hg = stats.entropy.cpu().numpy()
-            Lo_b = Lo.copy()
-            Lo_b[np.arange(n), btn] += bvn
-            Ho, _, _, _ = S.row_stats(Lo_b, tau, cfg.mask_id)
-            # |dH| <= max_v |dz_v| * sum_v p_v |log p_v + H| to first order
-            zo = S.tempered(Lo_b, tau, cfg.mask_id)
-            lp = zo - scipy.special.logsumexp(zo, axis=1, keepdims=True)
-            p = np.exp(lp)
-            spread = np.nansum(p * np.abs(np.where(p > 0, lp, 0.0) + Ho[:, None]), axis=1)
-            keep = np.arange(cfg.vocab) != cfg.mask_id
-            dz = np.abs(Lb - Lo_b)[:, keep].max(axis=1) / tau
-            assert np.all(np.abs(Hg - Ho) <= 1.5 * spread * dz + 1e-5), (key, t)
-            res[key] = rel_l2_rows(Lg, Lo).max()
-        assert res["e4m3"] < 5e-2, res
-        assert res["e4m3"] < 1.5 * res["bf16"] + 1e-4, res
+            Ho, ao, _, _ = S.row_stats(Lo_b, tau, cfg.mask_id)
+            dH = np.abs(stats.entropy.cpu().numpy() - Ho)
+            assert dH.max() < ENT_TOL_NORTH, (key, t, float(dH.max()))
+            del Lg, Lb
+        del Lo, Lo_b
 
 
 @pytest.mark.parametrize("name", list(CFGS))
@@ -236,7 +228,7 @@ def test_lm_head_logits_and_statistics(B, name):
     ws = model.workspace(n)
     scfg = B.sampler_default()
     ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
-    for t in (0, 31, 47):
+    for t in (0, 23, 47):
         stats = B.StepStats(n, vocab=cfg.vocab, logits_dtype=model.act_dtype)
         B.lm_head(model, X, scfg, t, stats, ws, bt, bv)
         torch.cuda.synchronize()
