@@ -82,6 +82,7 @@ DIVERSE_COMMITTED = 128   # the headline canvas state of the one-layer workload:
 def _kernel_record(cfg, name, tot_ms, launches, rec, nb, lm8):
     nbytes, flops = _algorithmic(cfg, name, rec, nb, lm8)
     return {"launches": launches, "ms_total": tot_ms, "bytes": nbytes, "flops": flops,
+            "algorithmic_bytes_per_launch": round(nbytes / max(launches, 1)),
             "us_per_launch": round(tot_ms / max(launches, 1) * 1e3, 2),
             "ms_per_step": round(tot_ms / max(len(rec), 1), 4),
             "achieved_gbs": round(nbytes / (tot_ms * 1e-3) / 1e9, 1),
@@ -201,6 +202,15 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
         kernels[name] = _kernel_record(cfg, name, tot_ms, launches, rec, nb, args.fp8_lm_head)
     if nb == 1:
         eb_per_step = round(float(canvas.state[B.ST_COMMITTED].item()) / tsteps, 3) if tsteps < 48 else None
+    # counter evidence (same kernel sources only): measured HBM bytes per
+    # launch against the algorithmic ones, MFMA busy percentage
+    ctr = _counters(args.workload) if nb == 1 and not args.fp8_lm_head else {}
+    for name, k in kernels.items():
+        c = ctr.get(name)
+        per_launch = k["bytes"] / max(k["launches"], 1)
+        k["counter_hbm_bytes"] = round(c["hbm_bytes"]) if c else None
+        k["counter_vs_algorithmic"] = round(c["hbm_bytes"] / per_launch, 3) if c else None
+        k["mfma_busy_pct"] = c["mfma_busy_pct"] if c else None
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     kd = kernels[dom]
     # the bound is the roof the kernel's algorithmic work reaches first: HBM
@@ -208,10 +218,10 @@ def _model_workload(args, torch, B, cfg, prompt_len, n_canvases_cap):
     hbm_bound = kd["bytes"] / (HBM_PEAK_GBS * 1e9) >= kd["flops"] / (BF16_PEAK_TFLOPS * 1e12)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": kd["achieved_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(kd["achieved_gbs"] / HBM_PEAK_GBS, 4), "traffic": _traffic(dom, kd)}
+                "frac": round(kd["achieved_gbs"] / HBM_PEAK_GBS, 4), "traffic": kd["counter_hbm_bytes"]}
     else:
         roof = {"bound": "mfma", "achieved": kd["achieved_tflops"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": _traffic(dom, kd)}
+                "frac": round(kd["achieved_tflops"] / BF16_PEAK_TFLOPS, 4), "traffic": kd["counter_hbm_bytes"]}
     res = {
         "ms_per_step": ms / args.steps,
         "committed_tokens_per_s": round(canvas_tokens / (ms_canvas * 1e-3), 2),
@@ -270,6 +280,7 @@ def _diverse_canvas(args, torch, B, cfg, model, kv, ws, stats, scfg):
     del graph
     kernels = {}
     hits = None
+    ctr = _counters(args.workload + "_diverse") if not args.fp8_lm_head else {}
     for name, tgt in KERNELS:
         rec = []
         B.timing_enable(getattr(B, tgt))
@@ -281,6 +292,10 @@ def _diverse_canvas(args, torch, B, cfg, model, kv, ws, stats, scfg):
         tot_ms, launches = B.timing_read()
         B.timing_enable(B.TIME_OFF)
         r = _kernel_record(cfg, name, tot_ms, launches, rec, 1, args.fp8_lm_head)
+        c = ctr.get(name)
+        r["counter_hbm_bytes"] = round(c["hbm_bytes"]) if c else None
+        r["counter_vs_algorithmic"] = round(c["hbm_bytes"] / r["algorithmic_bytes_per_launch"], 3) if c else None
+        r["mfma_busy_pct"] = c["mfma_busy_pct"] if c else None
         kernels[name] = {kk: vv for kk, vv in r.items() if kk not in ("ms_total", "bytes", "flops")}
         hits = rec[-1][1]
     d, F = cfg.d_model, cfg.ffn_hidden
@@ -333,31 +348,39 @@ def _algorithmic(cfg, name, rec, nbat=1, lm8=False):
     return nb, fl
 
 
-def _traffic(kernel, kd):
-    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled
-    by the same counters on a copy of known size) from the summary committed
-    under profiles/, if it was taken on the kernel source as it is now."""
+COUNTERS_FILE = {"stack30": "stack30_decode_counters.txt", "stack30_diverse": "stack30_diverse_counters.txt"}
+
+
+def _counters(workload):
+    """Per-kernel rocprofv3 counters of the denoising steps (HBM bytes read +
+    written per launch, scaled by a copy of known size; MFMA busy percentage)
+    from the summary committed under profiles/, if it was taken on the kernel
+    sources as they are now; {} otherwise."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
+    name = COUNTERS_FILE.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else ""
+    if not path or not os.path.exists(path):
+        return {}
+    kv, rows = {}, {}
     for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            a, b = line.split(":", 1)
-            kv[a.strip()] = b.strip()
+        if line.startswith("#") or ":" not in line:
+            continue
+        a, b = line.split(":", 1)
+        a, b = a.strip(), b.strip()
+        if "=" in b:
+            rows[a] = dict(x.split("=", 1) for x in b.split())
+        else:
+            kv[a] = b
     srcs = [x for x in kv.get("kernel_source", "").split(",") if x]
     hashes = kv.get("kernel_source_sha256", "").split(",")
     if not srcs or len(srcs) != len(hashes):
-        return None
+        return {}
     for src, h in zip(srcs, hashes):
-        path = os.path.join(ROOT, src)
-        if not os.path.isfile(path) or hashlib.sha256(open(path, "rb").read()).hexdigest() != h:
-            return None
-    try:
-        return round(float(kv["hbm_bytes_per_launch"]))
-    except (KeyError, ValueError):
-        return None
+        f = os.path.join(ROOT, src)
+        if not os.path.isfile(f) or hashlib.sha256(open(f, "rb").read()).hexdigest() != h:
+            return {}
+    return {k: {"hbm_bytes": float(v["hbm_bytes"]), "mfma_busy_pct": float(v["mfma_busy_pct"])}
+            for k, v in rows.items() if "hbm_bytes" in v}
 
 
 def bench_stack(args, torch, B, which):
