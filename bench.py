@@ -292,10 +292,10 @@ def _diverse_canvas(args, torch, B, cfg, model, kv, ws, stats, scfg):
         tot_ms, launches = B.timing_read()
         B.timing_enable(B.TIME_OFF)
         r = _kernel_record(cfg, name, tot_ms, launches, rec, 1, args.fp8_lm_head)
-        c = ctr.get(name)
-        r["counter_hbm_bytes"] = round(c["hbm_bytes"]) if c else None
-        r["counter_vs_algorithmic"] = round(c["hbm_bytes"] / r["algorithmic_bytes_per_launch"], 3) if c else None
-        r["mfma_busy_pct"] = c["mfma_busy_pct"] if c else None
+        cr = ctr.get(name)
+        r["counter_hbm_bytes"] = round(cr["hbm_bytes"]) if cr else None
+        r["counter_vs_algorithmic"] = round(cr["hbm_bytes"] / r["algorithmic_bytes_per_launch"], 3) if cr else None
+        r["mfma_busy_pct"] = cr["mfma_busy_pct"] if cr else None
         kernels[name] = {kk: vv for kk, vv in r.items() if kk not in ("ms_total", "bytes", "flops")}
         hits = rec[-1][1]
     d, F = cfg.d_model, cfg.ffn_hidden

@@ -33,7 +33,11 @@ dg_status hip_check(hipError_t e, const char* what) {
 dg_status check_sampler_cfg(const dg_sampler_cfg* s) {
     if (!s) return fail(DG_E_INVALID, "sampler config is NULL");
     if (s->max_steps < 1 || s->max_steps > 1 << 20) return fail(DG_E_INVALID, "max_steps out of range");
-    if (!(s->temp_start > 0.f) || !(s->temp_end > 0.f)) return fail(DG_E_INVALID, "temperatures must be > 0");
+    // at least 1e-12: the statistics pass tempers its excluded-column value
+    // -2^64 by log2(e)/tau and needs the product finite
+    if (!(s->temp_start >= 1e-12f) || !(s->temp_end >= 1e-12f) || !(s->temp_start <= 3.0e38f) ||
+        !(s->temp_end <= 3.0e38f))
+        return fail(DG_E_INVALID, "temperatures must lie in [1e-12, 3e38]");
     if (!(s->bound >= 0.f)) return fail(DG_E_INVALID, "bound must be >= 0");
     if (!(s->stop_entropy >= 0.f)) return fail(DG_E_INVALID, "stop_entropy must be >= 0");
     if (s->stable_steps < 1) return fail(DG_E_INVALID, "stable_steps must be >= 1");

@@ -48,11 +48,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 }
 
 // ---- wavefront reductions ----
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-    return v;
-}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
@@ -90,6 +85,20 @@ __device__ __forceinline__ float xor32_sum(float v) {
     const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
+
+// Max over the wavefront, the result in every lane: DPP moves inside each row
+// of 16 lanes (swap neighbours, swap pairs, mirror halves of 8, mirror the
+// row), then the two permlane swaps across rows. VALU only.
+#define DG_MAX_DPP_STEP(v, ctrl) \
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false)))
+__device__ __forceinline__ float wave_max(float v) {
+    DG_MAX_DPP_STEP(v, 0xB1);
+    DG_MAX_DPP_STEP(v, 0x4E);
+    DG_MAX_DPP_STEP(v, 0x141);
+    DG_MAX_DPP_STEP(v, 0x140);
+    return xor32_max(xor16_max(v));
+}
+#undef DG_MAX_DPP_STEP
 
 // (value, index) argmax with lowest index on equal values
 struct ArgMax {
@@ -142,14 +151,35 @@ __device__ __forceinline__ EntPart ent_merge(EntPart a, EntPart b) {
     a.t += f * (b.t + d * b.s);
     return a;
 }
-__device__ __forceinline__ EntPart wave_ent(EntPart a) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        EntPart b{__shfl_xor(a.m, o, WAVE), __shfl_xor(a.s, o, WAVE), __shfl_xor(a.t, o, WAVE)};
-        a = ent_merge(a, b);
+// Merge over the wavefront, the result in every lane: the DPP and permlane
+// pairing of wave_max. The merge is commutative (bit for bit), so both lanes
+// of every pair hold the same partial after each step.
+#define DG_ENT_DPP_STEP(a, ctrl)                                                                              \
+    a = ent_merge(a, EntPart{__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                           \
+                                 0, __builtin_bit_cast(int, a.m), ctrl, 0xF, 0xF, false)),                    \
+                             __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                           \
+                                 0, __builtin_bit_cast(int, a.s), ctrl, 0xF, 0xF, false)),                    \
+                             __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                           \
+                                 0, __builtin_bit_cast(int, a.t), ctrl, 0xF, 0xF, false))})
+#define DG_ENT_PERM_STEP(a, swap)                                                                             \
+    {                                                                                                         \
+        const auto m = swap(__float_as_uint(a.m), __float_as_uint(a.m), false, false);                        \
+        const auto s = swap(__float_as_uint(a.s), __float_as_uint(a.s), false, false);                        \
+        const auto t = swap(__float_as_uint(a.t), __float_as_uint(a.t), false, false);                        \
+        a = ent_merge(EntPart{__uint_as_float(m[0]), __uint_as_float(s[0]), __uint_as_float(t[0])},           \
+                      EntPart{__uint_as_float(m[1]), __uint_as_float(s[1]), __uint_as_float(t[1])});          \
     }
+__device__ __forceinline__ EntPart wave_ent(EntPart a) {
+    DG_ENT_DPP_STEP(a, 0xB1);
+    DG_ENT_DPP_STEP(a, 0x4E);
+    DG_ENT_DPP_STEP(a, 0x141);
+    DG_ENT_DPP_STEP(a, 0x140);
+    DG_ENT_PERM_STEP(a, __builtin_amdgcn_permlane16_swap);
+    DG_ENT_PERM_STEP(a, __builtin_amdgcn_permlane32_swap);
     return a;
 }
+#undef DG_ENT_DPP_STEP
+#undef DG_ENT_PERM_STEP
 
 // Per-row partial written by the logit-statistics producers (LM-head epilogue
 // and the standalone statistics kernel) and merged by the merge kernel.

@@ -67,6 +67,8 @@ constexpr int LROWB = LKB * 2;                    // bytes of an LDS weight row
 constexpr int LB_BYTES = LBN * LROWB;             // one stage of the weight tile
 constexpr int LB_INSTR = LB_BYTES / 1024 / LNW;   // 1 KB pieces per wave and stage
 constexpr int TST = 129;                          // epilogue tile row stride (floats, odd)
+static_assert(LWR * LWC == LNW && LRT * 32 * LWR == LBM && LCT * 32 * LWC == LBN, "wave grid covers the tile");
+static_assert(LBN == 256 && (LWC == 1 || LWC == 2), "epilogue halves of 128 columns");
 constexpr size_t LM_LDS = std::max<size_t>(2 * (size_t)LB_BYTES, (size_t)LBM * TST * sizeof(float));
 
 __device__ __forceinline__ int lswz(int r, int c) { return c ^ ((r >> 1) & 7); }
@@ -237,7 +239,7 @@ __global__ void __launch_bounds__(LNW * 64) lmhead_kernel(GemmArgs g) {
 
         // ---- epilogue, per half of 128 columns ----
         // acc[t][j][q] is row wrow0 + 32 t + 8 (q / 4) + 4 hi + q % 4 of the
-        // item, column wcol0 + 32 j + l32 of the tile (half wc_g). The half goes through LDS as
+        // item, column wcol0 + 32 j + l32 of the tile. The half goes through LDS as
         // f32 (T[row][col], odd row stride: a thread per row reads without
         // bank conflicts); then the logits of record leave as bf16 in 16-byte
         // stores (16 threads per row) and thread r computes row r's partials.
@@ -253,17 +255,22 @@ __global__ void __launch_bounds__(LNW * 64) lmhead_kernel(GemmArgs g) {
             if (ptile >= g.nsplit) break;   // uniform: no columns in this half
             const int cb = n0 + 128 * h;    // first column of the half
             __syncthreads();                // the LDS is free (K loop, or the previous half)
-            if (live && wc_g == h) {        // the waves holding this half's columns
+            if (live) {
+                // the wave's column tiles that fall in this half (with one
+                // column group, tiles 4h .. 4h+3; with two, all tiles of the
+                // waves of group h)
 #pragma unroll
                 for (int jj = 0; jj < LCT; ++jj) {
+                    const int ct = wcol0 + 32 * jj - 128 * h;  // the tile's first column in the half
+                    if (ct < 0 || ct >= 128) continue;
                     float sc = 1.f;
-                    if constexpr (WF8) sc = bf2f(g.w_scale[min(cb + 32 * jj + l32, N - 1)]);
+                    if constexpr (WF8) sc = bf2f(g.w_scale[min(cb + ct + l32, N - 1)]);
 #pragma unroll
                     for (int t = 0; t < LRT; ++t)
 #pragma unroll
                         for (int q = 0; q < 16; ++q) {
                             const int row = wrow0 + 32 * t + 8 * (q / 4) + 4 * hi + (q % 4);
-                            T[row * TST + 32 * jj + l32] = acc[t][jj][q] * sc;
+                            T[row * TST + ct + l32] = acc[t][jj][q] * sc;
                         }
                 }
             }

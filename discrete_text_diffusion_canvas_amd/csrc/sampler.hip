@@ -40,44 +40,106 @@ __device__ __forceinline__ double tau_at(const SamplerParams& sp, int t) {
            ((double)sp.temp_end - (double)sp.temp_start) * (double)t / (double)(sp.max_steps - 1);
 }
 
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&x)[8]);
+// one logit of a row, widened to f32
+template <typename T> struct Raw8Elem;
+template <> struct Raw8Elem<uint16_t> {
+    static __device__ __forceinline__ float get(const uint16_t* p, int i) { return bf2f(p[i]); }
+};
+template <> struct Raw8Elem<float> {
+    static __device__ __forceinline__ float get(const float* p, int i) { return p[i]; }
+};
 
-template <>
-__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&x)[8]) {
-    u16x8 v = *reinterpret_cast<const u16x8*>(p);
+// Values at or below STATS_EXCLUDED take no part in the statistics (as -inf
+// would): the statistics pass writes it over MASK, over the bias token (whose
+// biased value joins the row once, after the loop) and over columns past the
+// end of a split, so the reduction over a chunk needs no per-column test.
+// Logits at or below -2^64 are thereby treated as -inf. The value stays
+// finite when tempered (|2^64 * log2(e) / tau| < 2^128 for tau > 2^-63), so
+// its 2^(z2 - m2) is 0 and its entropy term 0 * (z2 - m2) is 0, not NaN.
+constexpr float STATS_EXCLUDED = -0x1p64f;
+constexpr uint16_t STATS_EXCLUDED_BF16 = 0xDF80;  // -2^64
+
+// 8 consecutive logits as loaded (bf16: one 16-byte vector; f32: two),
+// widened to f32 only when used, so a load in flight does not stall the code
+// that issues the next ones.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+    u16x8 v;
+    __device__ __forceinline__ void load(const uint16_t* p) {
+        v = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(p));
+    }
+    __device__ __forceinline__ void fill_excluded() { v = STATS_EXCLUDED_BF16; }
+    // element q (0..7, may differ per lane) becomes STATS_EXCLUDED
+    __device__ __forceinline__ void exclude(int q) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = bf2f(v[j]);
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&x)[8]) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+        for (int k = 0; k < 8; ++k)
+            if (k == q) v[k] = STATS_EXCLUDED_BF16;
+    }
+    __device__ __forceinline__ float at(int j) const { return bf2f(v[j]); }
+    // makes the compiler treat the vector as rewritten, so values widened
+    // from it before this point are recomputed after it, not kept live
+    __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(v)); }
+};
+template <> struct Raw8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+    }
+    __device__ __forceinline__ void fill_excluded() { a = STATS_EXCLUDED; b = STATS_EXCLUDED; }
+    __device__ __forceinline__ void exclude(int q) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) { x[j] = a[j]; x[4 + j] = b[j]; }
-}
+        for (int k = 0; k < 4; ++k) {
+            if (k == q) a[k] = STATS_EXCLUDED;
+            if (k + 4 == q) b[k] = STATS_EXCLUDED;
+        }
+    }
+    __device__ __forceinline__ float at(int j) const { return j < 4 ? a[j] : b[j - 4]; }
+    __device__ __forceinline__ void refresh() {}
+};
 
 // ---------------------------------------------------------------------------
 // Row statistics over given logits (the sampler-only entry point). Grid
 // (nsplit, n), 256 threads; split i covers columns [i*split_cols, ...), a
-// multiple of 2048. Each thread loads its 64 columns (8 vectors of 8, wave
-// loads contiguous) before computing, so every thread keeps 8 loads in flight.
-// The max and its lowest column come from the tempered value z2 = x*log2(e)/tau;
-// for bf16 logits z2 preserves the order and the equalities of x exactly (two
-// distinct bf16 values differ by at least 2^-8 relative), for f32 logits the
-// raw values are compared instead.
-// GUMBEL: the same pass also keeps the Gumbel-max candidate of the split, the
-// lowest column maximising z_v - log(-log u_v) with z = (L + bias) / tau and
-// u_v from Philox at counter (row, step, canvas, 1 + v / 4), word v % 4.
+// multiple of 2048. The split is read in chunks of 16384 columns (256 threads
+// x 8 vectors x 8): a thread holds its 8 vectors of one chunk and already has
+// the next chunk's loads in flight while it reduces the current one, and the
+// kernel is held to 128 VGPRs so that four workgroups (and their loads) share
+// a CU. Per chunk, one pass over the values:
+//   sums    s = sum 2^d, t = sum 2^d d with d = x*c2 - r (one fma) against the
+//           lane's running reference r (its first chunk's tempered max; any
+//           reference gives the same entropy and log-sum-exp, and values below
+//           it by more than 126 are negligible next to the value at r), 2^d
+//           by the hardware exp; a chunk whose max lies more than 64 above r
+//           is summed again against that max, so 2^d never overflows;
+//   max     the lane's max of the raw values alongside (tempering by c2 > 0
+//           keeps the order);
+//   argmax  only when the wave's max beats the running one (wave-uniform, a
+//           few chunks per row) do the lanes holding it look for its lowest
+//           column.
+// The bias token's value L + bias joins the row's partial once, after the
+// loop. GUMBEL: the same pass also keeps the Gumbel-max candidate of the
+// split, the lowest column maximising z_v - log(-log u_v) with z =
+// (L + bias) / tau and u_v from Philox at counter (row, step, canvas,
+// 1 + v / 4), word v % 4.
 // ---------------------------------------------------------------------------
+// build-time tunable: waves per SIMD the statistics pass over bf16 logits is
+// compiled for (4: at most 128 VGPRs); f32 logits hold twice the registers
+// per chunk (2)
+#ifndef DG_STATS_WAVES_PER_EU
+#define DG_STATS_WAVES_PER_EU 4
+#endif
+constexpr int STATS_PER = 8;                      // vectors of 8 per thread and chunk
+constexpr int STATS_CHUNK = 256 * 8 * STATS_PER;  // columns per chunk
+
 template <typename T, bool GUMBEL>
-__global__ void __launch_bounds__(256) logit_stats_kernel(
-    const T* __restrict__ logits, int64_t ld, int V, int split_cols,
-    const int32_t* __restrict__ state, int step_override, SamplerParams sp, int mask_id,
-    const int32_t* __restrict__ bias_tok, const float* __restrict__ bias_val,
-    RowPart* __restrict__ parts, int nsplit) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? DG_STATS_WAVES_PER_EU : 2)))
+logit_stats_kernel(const T* __restrict__ logits, int64_t ld, int V, int split_cols,
+                   const int32_t* __restrict__ state, int step_override, SamplerParams sp, int mask_id,
+                   const int32_t* __restrict__ bias_tok, const float* __restrict__ bias_val,
+                   RowPart* __restrict__ parts, int nsplit) {
     if (state && state[0]) return;
-    constexpr int PER = 8;
+    constexpr int PER = STATS_PER;
     const int row = blockIdx.y;
     const int sp_i = blockIdx.x;
     const int t = step_override >= 0 ? step_override : state[1];
@@ -92,58 +154,103 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
     EntPart e{-INFINITY, 0.f, 0.f};
     ArgMax am{-INFINITY, 0x7fffffff};
     ArgMax gm{-INFINITY, 0x7fffffff};
-    const float inv_tau = (float)(1.0 / tau_at(sp, t));
-    for (int base = c0; base < c1; base += 256 * 8 * PER) {
-        float x[PER][8];
+    // cur: the chunk being reduced; nxt: the next one, its loads in flight
+    Raw8<T> cur[PER], nxt[PER];
+    // vector j of a chunk at `base`: columns base + (j*256 + tid)*8 .. +8
+    // (vocabulary and split bounds are multiples of 8). Every lane loads, a
+    // vector past c1 from c1 - 8 (set to STATS_EXCLUDED when its chunk is
+    // reduced): loads under a branch, even a uniform one, would make the
+    // compiler wait for all loads in flight, the next chunk's included,
+    // before using any
+    auto fetch = [&](Raw8<T> (&r)[PER], int base) {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            int v0 = base + (j * 256 + tid) * 8;
-            if (v0 < c1) {
-                load8<T>(rowp + v0, x[j]);
-            } else {
+        for (int j = 0; j < PER; ++j) r[j].load(rowp + min(base + (j * 256 + tid) * 8, c1 - 8));
+    };
+    if (c0 < c1) fetch(cur, c0);
+    for (int base = c0; base < c1; base += STATS_CHUNK) {
+        // unconditional as well (past the last chunk every lane reads c1 - 8,
+        // one line per wave, never used)
+        fetch(nxt, base + STATS_CHUNK);
+        // MASK, the bias token and columns past c1 leave the chunk's
+        // reduction (wave-uniform tests)
+        if (base + STATS_CHUNK > c1) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) x[j][q] = -INFINITY;
+            for (int j = 0; j < PER; ++j)
+                if (base + (j * 256 + tid) * 8 >= c1) cur[j].fill_excluded();
+        }
+        const bool has_mask = mask_id >= base && mask_id < base + STATS_CHUNK;
+        const bool has_bias = btok >= base && btok < base + STATS_CHUNK;
+        if (has_mask || has_bias) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int v0 = base + (j * 256 + tid) * 8;
+                if (has_mask && (unsigned)(mask_id - v0) < 8u) cur[j].exclude(mask_id - v0);
+                if (has_bias && (unsigned)(btok - v0) < 8u) cur[j].exclude(btok - v0);
             }
         }
-        const bool special = (btok >= base && btok < base + 256 * 8 * PER) ||
-                             (mask_id >= base && mask_id < base + 256 * 8 * PER);
-        float z[PER][8];
-        float vm = -INFINITY;
-        int vi = 0x7fffffff;
-        float rm = -INFINITY;  // raw max (f32 logits)
-        if (!special) {
+        // reference of the sums: the lane's running one; on its first chunk
+        // the lane's max (a max pass of its own)
+        float ref2 = e.m;
+        if (!(ref2 > -INFINITY)) {
+            float m0 = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+#pragma unroll
+                for (int q = 0; q < 8; ++q) m0 = fmaxf(m0, cur[j].at(q));
+#pragma unroll
+            for (int j = 0; j < PER; ++j) cur[j].refresh();
+            ref2 = m0 > STATS_EXCLUDED ? m0 * c2 : -INFINITY;
+        }
+        float lm = -INFINITY, ls = 0.f, lt = 0.f;
+        if (ref2 > -INFINITY) {
 #pragma unroll
             for (int j = 0; j < PER; ++j)
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    z[j][q] = x[j][q] * c2;
-                    const int col = base + (j * 256 + tid) * 8 + q;
-                    if constexpr (sizeof(T) == 2) {
-                        if (z[j][q] > vm) { vm = z[j][q]; vi = col; }
-                    } else {
-                        vm = fmaxf(vm, z[j][q]);
-                        if (x[j][q] > rm) { rm = x[j][q]; vi = col; }
-                    }
+                    const float x = cur[j].at(q);
+                    lm = fmaxf(lm, x);
+                    const float d = fmaf(x, c2, -ref2);
+                    const float w = __builtin_amdgcn_exp2f(d);
+                    ls += w;
+                    lt = fmaf(w, d, lt);
                 }
-        } else {
 #pragma unroll
-            for (int j = 0; j < PER; ++j)
+            for (int j = 0; j < PER; ++j) cur[j].refresh();
+            if (lm * c2 - ref2 > 64.f) {
+                // a value far above the reference (2^d up to 2^128 would
+                // overflow): the chunk again against its own max
+                ref2 = lm * c2;
+                ls = 0.f;
+                lt = 0.f;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int col = base + (j * 256 + tid) * 8 + q;
-                    float l = x[j][q] + (col == btok ? bval : 0.f);
-                    if (col == mask_id) l = -INFINITY;
-                    z[j][q] = l * c2;
-                    if constexpr (sizeof(T) == 2) {
-                        if (z[j][q] > vm) { vm = z[j][q]; vi = col; }
-                    } else {
-                        vm = fmaxf(vm, z[j][q]);
-                        if (l > rm) { rm = l; vi = col; }
+                for (int j = 0; j < PER; ++j)
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float d = fmaf(cur[j].at(q), c2, -ref2);
+                        const float w = __builtin_amdgcn_exp2f(d);
+                        ls += w;
+                        lt = fmaf(w, d, lt);
                     }
-                }
+#pragma unroll
+                for (int j = 0; j < PER; ++j) cur[j].refresh();
+            }
+            e = ent_merge(e, EntPart{ref2, ls, lt});
+        }
+        const float wm = wave_max(lm);
+        if (wm > am.v && wm > STATS_EXCLUDED) {
+            int li = 0x7fffffff;
+            if (lm == wm) {
+#pragma unroll
+                for (int j = PER - 1; j >= 0; --j)
+#pragma unroll
+                    for (int q = 7; q >= 0; --q)
+                        if (cur[j].at(q) == wm) li = base + (j * 256 + tid) * 8 + q;
+            }
+            am = ArgMax{wm, wave_min_i(li)};
         }
         if constexpr (GUMBEL) {
-            // z = z2 / log2(e) and the bias / MASK handling of z2 above
+#pragma unroll
+            for (int j = 0; j < PER; ++j) cur[j].refresh();
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const int v0 = base + (j * 256 + tid) * 8;
@@ -156,27 +263,15 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
                                     sp.seed_lo, sp.seed_hi);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const float zn = z[j][q] * 0.6931471805599453f;
-                    if (zn == -INFINITY || v0 + q >= c1) continue;
-                    const float val = zn + gumbel_of(w[q >> 2][q & 3]);
+                    const float xq = cur[j].at(q);
+                    if (!(xq > STATS_EXCLUDED)) continue;
+                    const float val = xq * c2 * 0.6931471805599453f + gumbel_of(w[q >> 2][q & 3]);
                     if (val > gm.v) { gm.v = val; gm.i = v0 + q; }
                 }
             }
         }
-        if (vm == -INFINITY) continue;
-        float ls = 0.f, lt = 0.f;
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                float d = z[j][q] - vm;
-                float w = exp2f(d);
-                ls += w;
-                lt += w > 0.f ? w * d : 0.f;
-            }
-        e = ent_merge(e, EntPart{vm, ls, lt});
-        ArgMax c{sizeof(T) == 2 ? vm : rm, vi};
-        am = argmax_merge(am, c);
+        for (int j = 0; j < PER; ++j) cur[j] = nxt[j];
     }
     e = wave_ent(e);
     am = wave_argmax(am);
@@ -191,6 +286,22 @@ __global__ void __launch_bounds__(256) logit_stats_kernel(
             e = ent_merge(e, se[i]);
             am = argmax_merge(am, sa[i]);
             if constexpr (GUMBEL) gm = argmax_merge(gm, sg[i]);
+        }
+        // the bias token, excluded from the loop: its biased value once
+        if (btok >= c0 && btok < c1 && btok != mask_id) {
+            const float xb = Raw8Elem<T>::get(rowp, btok) + bval;
+            if (!(xb <= STATS_EXCLUDED)) {  // NaN joins (and spoils the row, as a NaN logit does)
+                e = ent_merge(e, EntPart{xb * c2, 1.f, 0.f});
+                if (xb > STATS_EXCLUDED) am = argmax_merge(am, ArgMax{xb, btok});
+                if constexpr (GUMBEL) {
+                    const u32x4 u = philox10(u32x4{(uint32_t)row, (uint32_t)t, (uint32_t)sp.canvas_idx,
+                                                   (uint32_t)(1 + btok / 4)},
+                                             sp.seed_lo, sp.seed_hi);
+                    const uint32_t word = (btok & 3) == 0 ? u[0] : (btok & 3) == 1 ? u[1] : (btok & 3) == 2 ? u[2] : u[3];
+                    if (xb > STATS_EXCLUDED)
+                        gm = argmax_merge(gm, ArgMax{xb * c2 * 0.6931471805599453f + gumbel_of(word), btok});
+                }
+            }
         }
         RowPart p;
         p.m2 = e.m; p.s = e.s; p.t = e.t; p.lmax = am.v; p.amax = am.i == 0x7fffffff ? -1 : am.i;
@@ -316,8 +427,9 @@ __global__ void __launch_bounds__(1024) eb_select_kernel(
 // DRAW_CHUNK columns; each of the 256 threads of a chunk owns 16 consecutive
 // columns.
 //   draw_chunks: every (selected row, chunk) pair sums its w (chip-wide grid).
-//   draw_pick:   per selected row, the running sum over chunk totals finds the
-//                chunk where u * S falls, and a scan inside it the column.
+//   draw_pick:   per selected row, a workgroup scan of the chunk totals (256
+//                chunks at a time, in vocabulary order) finds the chunk where
+//                u * S falls, and a scan inside it the column.
 // ---------------------------------------------------------------------------
 constexpr int DRAW_CHUNK = 4096;
 
@@ -388,49 +500,63 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
     const double bval = bias_tok ? (double)bias_val[row] : 0.0;
     const double M = zval(rowp, amax[row], btok, bval, tau);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    __shared__ double s_target, s_cstart;
-    __shared__ int s_chunk, owner, last_owner;
+    __shared__ double s_cstart, s_last_start;
+    __shared__ int s_chunk, s_last_c, owner, last_owner;
     __shared__ double red[4];
-    if (tid == 0) {
-        u32x4 ctr;
-        ctr[0] = (uint32_t)row; ctr[1] = (uint32_t)t; ctr[2] = (uint32_t)canvas_idx; ctr[3] = 0u;
-        const uint32_t x0 = philox10(ctr, seed_lo, seed_hi)[0];
-        const double u = (double)(x0 >> 8) * (1.0 / 16777216.0);
-        const double* cs = chunk_sum + (int64_t)r * nchunk;
-        double tot = 0.0;
-        for (int c = 0; c < nchunk; ++c) tot += cs[c];
-        const double target = u * tot;
-        double run = 0.0;
-        int owner_c = -1;
-        double start = 0.0;
-        for (int c = 0; c < nchunk; ++c) {
-            if (cs[c] > 0.0 && run + cs[c] > target) { owner_c = c; start = run; break; }
-            run += cs[c];
+    const double* cs = chunk_sum + (int64_t)r * nchunk;
+    // the row's uniform and the target u * S, S the sum of the chunk totals
+    u32x4 ctr;
+    ctr[0] = (uint32_t)row; ctr[1] = (uint32_t)t; ctr[2] = (uint32_t)canvas_idx; ctr[3] = 0u;
+    const uint32_t x0 = philox10(ctr, seed_lo, seed_hi)[0];
+    const double u = (double)(x0 >> 8) * (1.0 / 16777216.0);
+    double part = 0.0;
+    for (int c = tid; c < nchunk; c += 256) part += cs[c];
+    part = wave_sum_d(part);
+    if (lane == 0) red[w] = part;
+    if (tid == 0) { s_chunk = 0x7fffffff; s_last_c = -1; owner = 0x7fffffff; last_owner = -1; }
+    __syncthreads();
+    const double target = u * ((red[0] + red[1]) + (red[2] + red[3]));
+    __syncthreads();
+    // the chunk where the running sum of the chunk totals (in vocabulary
+    // order, 256 chunks at a time) passes the target: the first with mass
+    // whose end exceeds it; if rounding leaves none, the last with mass
+    double run = 0.0;
+    for (int b = 0; b < nchunk; b += 256) {
+        const int c = b + tid;
+        const double v = c < nchunk ? cs[c] : 0.0;
+        double incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(incl, o, WAVE);
+            if (lane >= o) incl += y;
         }
-        if (owner_c < 0) {  // rounding at the very end: last chunk with mass
-            run = 0.0;
-            for (int c = 0; c < nchunk; ++c) {
-                if (cs[c] > 0.0) { owner_c = c; start = run; }
-                run += cs[c];
-            }
-        }
-        s_target = target;
-        s_cstart = start;
-        s_chunk = owner_c;
-        owner = 0x7fffffff;
-        last_owner = -1;
-        if (owner_c < 0) {
-            // no chunk holds finite positive mass (a NaN row, or a +inf logit
-            // whose exp(z - M) is NaN): the argmax is committed and no chunk
-            // is scanned
+        if (lane == 63) red[w] = incl;
+        __syncthreads();
+        double woff = 0.0;
+        for (int i = 0; i < w; ++i) woff += red[i];
+        const double start = run + woff + incl - v;
+        run += (red[0] + red[1]) + (red[2] + red[3]);
+        if (v > 0.0 && start + v > target) atomicMin(&s_chunk, c);
+        if (v > 0.0) atomicMax(&s_last_c, c);
+        __syncthreads();
+        if (c == s_chunk) s_cstart = start;
+        if (c == s_last_c) s_last_start = start;
+        __syncthreads();
+        if (s_chunk != 0x7fffffff) break;  // uniform
+    }
+    int c = s_chunk;
+    double cstart = s_cstart;
+    if (c == 0x7fffffff) { c = s_last_c; cstart = s_last_start; }
+    if (c < 0) {
+        // no chunk holds finite positive mass (a NaN row, or a +inf logit
+        // whose exp(z - M) is NaN): the argmax is committed and no chunk is
+        // scanned (uniform over the workgroup)
+        if (tid == 0) {
             tokens[row] = amax[row];
             committed[row] = 1;
         }
+        return;
     }
-    __syncthreads();
-    const int c = s_chunk;
-    if (c < 0) return;  // uniform over the workgroup
-    const double target = s_target;
     const int v0 = c * DRAW_CHUNK + tid * 16;
     const double s = thread_chunk_sum(rowp, v0, V, mask_id, btok, bval, tau, M);
     // exclusive scan of the thread sums inside the chunk
@@ -444,7 +570,7 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
     __syncthreads();
     double woff = 0.0;
     for (int i = 0; i < w; ++i) woff += red[i];
-    const double start = s_cstart + woff + incl - s;
+    const double start = cstart + woff + incl - s;
     if (s > 0.0 && start + s > target) atomicMin(&owner, tid);
     if (s > 0.0) atomicMax(&last_owner, tid);
     __syncthreads();
@@ -452,15 +578,15 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
     // leaves none, the last thread with mass in the chunk
     const int own = owner != 0x7fffffff ? owner : last_owner;
     if (tid == own) {
-        double run = start;
+        double acc = start;
         int pick = -1, last = -1;
         for (int q = 0; q < 16; ++q) {
             int v = v0 + q;
             if (v >= V || v == mask_id) continue;
             double wv = exp(zval(rowp, v, btok, bval, tau) - M);
             if (wv > 0.0) last = v;
-            run += wv;
-            if (run > target) { pick = v; break; }
+            acc += wv;
+            if (acc > target) { pick = v; break; }
         }
         if (pick < 0) pick = last >= 0 ? last : amax[row];  // no mass (NaN input): the argmax
         tokens[row] = pick;
@@ -530,9 +656,15 @@ __global__ void __launch_bounds__(1024) finalize_kernel(
 // ---------------------------------------------------------------------------
 // Host-side launchers.
 // ---------------------------------------------------------------------------
+// build-time tunable: chunks of 16384 columns per split of the statistics pass
+// (a workgroup streams its split with the next chunk's loads in flight)
+#ifndef DG_STATS_CHUNKS_PER_SPLIT
+#define DG_STATS_CHUNKS_PER_SPLIT 8
+#endif
 static int nsplit_for(int V) {
-    // 16384 columns per split (256 threads x 64), fewer for small vocabularies
-    int cols = 16384;
+    // DG_STATS_CHUNKS_PER_SPLIT x 16384 columns per split, fewer (a multiple
+    // of 2048) for small vocabularies
+    int cols = STATS_CHUNK * DG_STATS_CHUNKS_PER_SPLIT;
     if (V < cols) cols = ((V + 2047) / 2048) * 2048;
     return (V + cols - 1) / cols;
 }

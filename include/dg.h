@@ -92,7 +92,7 @@ typedef int32_t dg_status;
  * 2 stable steps, DG_BOUND_SUM, DG_COMMIT_KEEP, DG_DRAW_INVERSE_CDF. */
 typedef struct dg_sampler_cfg {
     int32_t max_steps;
-    float temp_start;
+    float temp_start;     /* temperatures in [1e-12, 3e38], else DG_E_INVALID */
     float temp_end;
     float bound;          /* nats */
     float stop_entropy;   /* nats, strict "<" */
@@ -226,8 +226,8 @@ dg_status dg_sampler_step(const dg_sampler_cfg* scfg, const void* logits, int32_
  * allocating routine; the array's device address is looked up on the first
  * call on each device (call it with that device current).
  *   Limit: DG_E_CAPACITY when dg_sampler_workspace_bytes(n, vocab) exceeds
- *   the array (n = 1024 rows fit up to a vocabulary of about 500K; 256 rows
- *   up to about 2M).
+ *   the array (n = 1024 rows fit up to a vocabulary of about 900K; 256 rows
+ *   up to about 3.7M).
  *   Every call on a GPU shares that GPU's array, which keeps the last call's
  *   contents: calls that overlap on one GPU (different streams or threads)
  *   race; serialise them.

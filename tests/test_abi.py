@@ -74,6 +74,10 @@ def test_sampler_step_validates_before_launch(lib):
     bad.temp_end = 0.0
     assert call(cfg=bad) == -1
     bad = B.sampler_default()
+    bad.temp_start = 1e-13       # its tempered excluded-column value would overflow
+    assert call(cfg=bad) == -1
+    assert b"temperatures" in L.dg_last_error()
+    bad = B.sampler_default()
     bad.bound_mode = 9
     assert call(cfg=bad) == -1
     assert b"bound_mode" in L.dg_last_error()

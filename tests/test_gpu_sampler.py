@@ -91,6 +91,45 @@ def test_ragged_vocab_f32_with_boost(B, V):
     run_and_compare(B, logits, n, V, 48, bias=(tok, mag), canvas_idx=3)
 
 
+@pytest.mark.parametrize("draw_mode", [0, 1])
+def test_bias_tokens_on_chunk_edges_bf16(B, draw_mode):
+    """bf16 logits over 40008 columns (three chunks of 16384 columns, the last
+    ragged) with the bias token at chunk and vector edges, on MASK, boosted
+    past the row's maximum, and banned with a -inf bias: the statistics pass
+    takes MASK and the bias token out of its per-chunk reduction and adds the
+    biased value once, which must give the oracle's statistics and draws."""
+    n, V = 32, 40008
+    edges = [0, 7, 8, 2047, 2048, 16383, 16384, 16385, 32767, 32768, 40000, V - 2, V - 1]
+    g = torch.Generator().manual_seed(77)
+    tok = torch.randint(0, V - 1, (n,), generator=g).numpy()
+    tok[:len(edges)] = edges
+    mag = (torch.rand(n, generator=g) * 12).numpy().astype(np.float32)
+    mag[1::3] = 40.0    # the bias token becomes the argmax
+    mag[5] = -np.inf    # token 16383 banned in row 5
+    mag[20] = -5.0
+
+    def logits(t):
+        return wl.sampler_logits(t + 11, shape=(n, V), device="cuda")
+    run_and_compare(B, logits, n, V, 48, bias=(tok, mag), canvas_idx=2, draw_mode=draw_mode)
+
+
+def test_peak_far_above_the_first_chunk(B):
+    """A row's maximum sits in its last chunk, 20 to 80 logits above the
+    rest: the statistics pass sums each chunk against a running reference
+    taken from the first chunk, and must sum such a chunk again against its
+    own maximum instead of overflowing 2^d."""
+    n, V = 16, 65536
+    g = torch.Generator().manual_seed(5)
+    cols = torch.randint(3 * 16384, V - 1, (n,), generator=g)
+    peaks = torch.linspace(20.0, 80.0, n)
+
+    def logits(t):
+        L = wl.sampler_logits(t + 21, shape=(n, V), max_peak=1.0, device="cuda")
+        L[torch.arange(n), cols.cuda()] = peaks.cuda().to(torch.bfloat16)
+        return L
+    run_and_compare(B, logits, n, V, None, step_ids=[0, 23, 47])
+
+
 def test_sum_minus_max_mode(B):
     n, V = 48, 1024
     run_and_compare(B, lambda t: wl.sampler_logits(t + 7, shape=(n, V), max_peak=30.0, device="cuda"),
