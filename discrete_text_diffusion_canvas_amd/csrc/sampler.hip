@@ -16,13 +16,15 @@
 // Kernels (one denoising step, in launch order):
 //   logit_stats   per (row, vocab split): base-2 entropy partials, raw argmax
 //   merge_rows    per row: entropy (nats), log-sum-exp, argmax
-//   eb_select     one workgroup: sort candidates by (entropy, position), float32
-//                 running sum in sorted order, cut at the bound (at least one)
+//   eb_select     one workgroup: rank candidates by (entropy, position), float32
+//                 running sum (a scan) in sorted order, cut at the bound (at
+//                 least one)
 //   draw_chunks   chip-wide: float64 sums of exp(z - M) per (selected row, chunk)
 //   draw_pick     per selected row: Philox4x32-10 uniform, float64 inverse CDF
 //                 in vocabulary order (chunk totals, then a scan in one chunk)
-//   finalize      one workgroup: re-mask, canvas-mean entropy (float64, position
-//                 order), stop test, argmax fill at the end, state update
+//   finalize      one workgroup: re-mask, canvas-mean entropy (float64, per
+//                 wave then the wave sums in order), stop test, argmax fill at
+//                 the end, state update
 // Every kernel reads the step index and the done flag from device memory so a
 // captured step can be replayed without host involvement.
 #include "common.hpp"
@@ -351,8 +353,11 @@ __global__ void __launch_bounds__(256) merge_rows_kernel(
 // ---------------------------------------------------------------------------
 // EB selection in one workgroup of 1024 threads (n <= 1024). Keys are
 // (entropy bits, position) as 64-bit integers: entropies are >= 0, so their
-// IEEE bit patterns order like the values. Non-candidates (committed rows,
-// unless every row is re-selected) sort last. Writes
+// IEEE bit patterns order like the values; with the position they are
+// unique, so thread i places its key at its rank (the count of smaller keys,
+// n LDS broadcasts) instead of a sorting network's log^2 n barriers.
+// Non-candidates (committed rows, unless every row is re-selected) rank last.
+// The running sum in sorted order is a workgroup scan in f32. Writes
 // the selection mask, the selected positions in sorted order (sel_list) and
 // their count (state word 4).
 // ---------------------------------------------------------------------------
@@ -361,62 +366,54 @@ __global__ void __launch_bounds__(1024) eb_select_kernel(
     int32_t* __restrict__ state, SamplerParams sp, uint8_t* __restrict__ selected,
     int32_t* __restrict__ sel_list) {
     if (state && state[0]) return;
-    __shared__ unsigned long long key[1024];
-    __shared__ float hs[1024];
-    __shared__ int kstar;
-    const int tid = threadIdx.x;
-    int npow = 1;
-    while (npow < n) npow <<= 1;
-    for (int i = tid; i < npow; i += 1024) {
-        unsigned long long k = ~0ull;
-        if (i < n && (sp.commit_mode != 0 || !committed[i]))
-            k = ((unsigned long long)__float_as_uint(H[i]) << 32) | (unsigned)i;
-        key[i] = k;
+    constexpr unsigned long long NONCAND = 0xffffffff00000000ull;
+    __shared__ unsigned long long key[1024], skey[1024];
+    __shared__ float wsum[16];
+    __shared__ int kcut, has_cand;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // keys (entropy bits, position): unique, so a key's rank is the number
+    // of smaller keys; non-candidates rank after every candidate
+    unsigned long long k = NONCAND | (unsigned)tid;
+    if (tid < n && (sp.commit_mode != 0 || !committed[tid]))
+        k = ((unsigned long long)__float_as_uint(H[tid]) << 32) | (unsigned)tid;
+    if (tid < n) key[tid] = k;
+    if (tid == 0) { kcut = 0x7fffffff; has_cand = 0; }
+    __syncthreads();
+    if (tid < n) {
+        int r = 0;
+        for (int j = 0; j < n; ++j) r += key[j] < k;  // one LDS broadcast per j
+        skey[r] = k;
+        selected[tid] = 0;
     }
     __syncthreads();
-    // bitonic sort ascending
-    for (int size = 2; size <= npow; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < npow; i += 1024) {
-                int j = i ^ stride;
-                if (j > i) {
-                    bool up = (i & size) == 0;
-                    unsigned long long a = key[i], b = key[j];
-                    if ((a > b) == up) { key[i] = b; key[j] = a; }
-                }
-            }
-            __syncthreads();
-        }
+    // running f32 sum of the sorted candidate entropies (a workgroup scan);
+    // mode 0 keeps position i while S_i <= bound, mode 1 while S_{i-1} <= bound
+    const unsigned long long sk = tid < n ? skey[tid] : NONCAND;
+    const bool cand = sk < NONCAND;
+    const float h = cand ? __uint_as_float((unsigned)(sk >> 32)) : 0.f;
+    float incl = h;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(incl, o, WAVE);
+        if (lane >= o) incl += y;
     }
-    for (int i = tid; i < n; i += 1024) {
-        unsigned long long kk = key[i];
-        hs[i] = kk == ~0ull ? -1.f : __uint_as_float((unsigned)(kk >> 32));
-        selected[i] = 0;
-    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    if (tid == 0) {
-        // float32 running sum in sorted order; mode 0: S_k <= bound,
-        // mode 1: S_{k-1} <= bound. At least one while candidates remain.
-        float run = 0.f;
-        int k = 0;
-        for (int i = 0; i < n; ++i) {
-            float h = hs[i];
-            if (h < 0.f) break;
-            float prev = run;
-            run = run + h;
-            bool ok = sp.bound_mode == 0 ? (run <= sp.bound) : (prev <= sp.bound);
-            if (!ok) break;
-            k = i + 1;
-        }
-        if (k == 0 && n > 0 && hs[0] >= 0.f) k = 1;
-        kstar = k;
-        state[4] = k;
-    }
+    float off = 0.f;
+    for (int i = 0; i < w; ++i) off += wsum[i];
+    incl += off;
+    const float excl = incl - h;
+    const bool ok = cand && (sp.bound_mode == 0 ? incl <= sp.bound : excl <= sp.bound);
+    if (tid < n && !ok) atomicMin(&kcut, tid);  // the first position not kept
+    if (tid == 0 && cand) has_cand = 1;
     __syncthreads();
-    for (int i = tid; i < kstar; i += 1024) {
-        int pos = (int)(key[i] & 0xffffffffu);
+    int kk = min(kcut, n);
+    if (kk == 0 && has_cand) kk = 1;  // at least one while candidates remain
+    if (tid == 0) state[4] = kk;
+    if (tid < kk) {
+        const int pos = (int)(sk & 0xffffffffu);
         selected[pos] = 1;
-        sel_list[i] = pos;
+        sel_list[tid] = pos;
     }
 }
 
@@ -425,7 +422,8 @@ __global__ void __launch_bounds__(1024) eb_select_kernel(
 // z = (L + bias) / tau and M' = z at the row's argmax (any offset cancels in
 // the comparison with u * sum w). The vocabulary is cut into chunks of
 // DRAW_CHUNK columns; each of the 256 threads of a chunk owns 16 consecutive
-// columns.
+// columns, loaded as two vectors before the first exp (one load round trip,
+// not one per column).
 //   draw_chunks: every (selected row, chunk) pair sums its w (chip-wide grid).
 //   draw_pick:   per selected row, a workgroup scan of the chunk totals (256
 //                chunks at a time, in vocabulary order) finds the chunk where
@@ -441,15 +439,39 @@ __device__ __forceinline__ double zval(const T* rowp, int v, int btok, double bv
     return L / tau;
 }
 
+// A thread's 16 consecutive logits v0 .. v0+15 (v0 a multiple of 16, V a
+// multiple of 8), loaded as whole vectors before any use; a vector at or
+// past V reads the row's last one and is marked absent.
 template <typename T>
-__device__ __forceinline__ double thread_chunk_sum(const T* rowp, int v0, int V, int mask_id, int btok,
-                                                   double bval, double tau, double M) {
-    double s = 0.0;
-    for (int q = 0; q < 16; ++q) {
-        int v = v0 + q;
-        if (v < V && v != mask_id) s += exp(zval(rowp, v, btok, bval, tau) - M);
+__device__ __forceinline__ void load16(const T* rowp, int v0, int V, float (&x)[16], bool (&in)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int vh = v0 + 8 * h;
+        in[h] = vh < V;
+        const int va = in[h] ? vh : V - 8;
+        if constexpr (sizeof(T) == 2) {
+            const u16x8 u = *reinterpret_cast<const u16x8*>(rowp + va);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x[8 * h + q] = bf2f(u[q]);
+        } else {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(rowp + va);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(rowp + va + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { x[8 * h + q] = a[q]; x[8 * h + 4 + q] = b[q]; }
+        }
     }
-    return s;
+}
+
+// w_v = exp(z_v - M) of the thread's 16 columns (0 for absent columns and
+// MASK), z = (L + bias) / tau in float64
+__device__ __forceinline__ void chunk_weights(const float (&x)[16], const bool (&in)[2], int v0, int mask_id,
+                                              int btok, double bval, double tau, double M, double (&w)[16]) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int v = v0 + q;
+        const double L = (double)x[q] + (v == btok ? bval : 0.0);
+        w[q] = (in[q / 8] && v != mask_id) ? exp(L / tau - M) : 0.0;
+    }
 }
 
 template <typename T>
@@ -471,7 +493,15 @@ __global__ void __launch_bounds__(256) draw_chunks_kernel(
         const int btok = bias_tok ? bias_tok[row] : -1;
         const double bval = bias_tok ? (double)bias_val[row] : 0.0;
         const double M = zval(rowp, amax[row], btok, bval, tau);
-        double s = thread_chunk_sum(rowp, c * DRAW_CHUNK + threadIdx.x * 16, V, mask_id, btok, bval, tau, M);
+        const int v0 = c * DRAW_CHUNK + threadIdx.x * 16;
+        float x[16];
+        bool in[2];
+        load16(rowp, v0, V, x, in);
+        double w[16];
+        chunk_weights(x, in, v0, mask_id, btok, bval, tau, M, w);
+        double s = 0.0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s += w[q];
         s = wave_sum_d(s);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
         __syncthreads();
@@ -558,7 +588,14 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
         return;
     }
     const int v0 = c * DRAW_CHUNK + tid * 16;
-    const double s = thread_chunk_sum(rowp, v0, V, mask_id, btok, bval, tau, M);
+    float x[16];
+    bool in[2];
+    load16(rowp, v0, V, x, in);
+    double wts[16];
+    chunk_weights(x, in, v0, mask_id, btok, bval, tau, M, wts);
+    double s = 0.0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s += wts[q];
     // exclusive scan of the thread sums inside the chunk
     double incl = s;
 #pragma unroll
@@ -580,13 +617,13 @@ __global__ void __launch_bounds__(256) draw_pick_kernel(
     if (tid == own) {
         double acc = start;
         int pick = -1, last = -1;
+#pragma unroll
         for (int q = 0; q < 16; ++q) {
-            int v = v0 + q;
-            if (v >= V || v == mask_id) continue;
-            double wv = exp(zval(rowp, v, btok, bval, tau) - M);
-            if (wv > 0.0) last = v;
+            if (pick >= 0) break;
+            const double wv = wts[q];
+            if (wv > 0.0) last = v0 + q;
             acc += wv;
-            if (acc > target) { pick = v; break; }
+            if (wv > 0.0 && acc > target) pick = v0 + q;
         }
         if (pick < 0) pick = last >= 0 ? last : amax[row];  // no mass (NaN input): the argmax
         tokens[row] = pick;
@@ -623,10 +660,18 @@ __global__ void __launch_bounds__(1024) finalize_kernel(
     if (d) atomicAdd(&diff, d);
     if (c) atomicAdd(&ncom, c);
     __syncthreads();
+    // canvas mean in float64: per wave, then the 16 wave sums in order
+    __shared__ double wmean[16];
     __shared__ double meanH;
+    {
+        const double v = tid < n ? (double)hs[tid] : 0.0;
+        const double ws = wave_sum_d(v);
+        if ((tid & 63) == 0) wmean[tid >> 6] = ws;
+    }
+    __syncthreads();
     if (tid == 0) {
-        double acc = 0.0;  // float64, position order
-        for (int i = 0; i < n; ++i) acc += (double)hs[i];
+        double acc = 0.0;
+        for (int i = 0; i < 16; ++i) acc += wmean[i];
         meanH = acc / (double)n;
     }
     __syncthreads();
