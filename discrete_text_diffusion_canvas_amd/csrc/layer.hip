@@ -32,11 +32,18 @@ __global__ void __launch_bounds__(256) embed_kernel(const TE* __restrict__ E, in
 }
 
 // ---------------------------------------------------------------------------
-// y = x / sqrt(mean(x^2) + eps) * w, f32 statistics. One workgroup of 256
-// threads per row; the row (d % 4 == 0, d <= 4096) stays in registers as up to
-// 4 float4 per thread between the sum of squares and the scaled store.
+// y = x / sqrt(mean(x^2) + eps) * w, f32 statistics. One workgroup of
+// NORM_NT threads per row; the row (d % 4 == 0, d <= 4096) stays in
+// registers as up to NORM_V4 float4 per thread between the sum of squares
+// and the scaled store.
 // ---------------------------------------------------------------------------
-constexpr int NORM_V4 = 4;  // float4 per thread: d <= 4096
+// build-time tunable: threads per row of the norm kernels (1024 measured
+// faster than 512 and 256: one row per CU, more loads in flight)
+#ifndef DG_NORM_THREADS
+#define DG_NORM_THREADS 1024
+#endif
+constexpr int NORM_NT = DG_NORM_THREADS;
+constexpr int NORM_V4 = 1024 / NORM_NT;  // float4 per thread: d <= 4096
 
 // With ylo (bf16 outputs only) the row is also left as a pair: y = bf16(v)
 // and ylo = bf16(v - y), which carries v to ~16 significant bits (the LM
@@ -47,19 +54,21 @@ __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int n
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
-        const int c = threadIdx.x + 256 * j;
+        const int c = threadIdx.x + NORM_NT * j;
         if (c < nv) ss += (x[j].x * x[j].x + x[j].y * x[j].y) + (x[j].z * x[j].z + x[j].w * x[j].w);
     }
     ss = wave_sum(ss);
-    __shared__ float red[4];
+    __shared__ float red[NORM_NT / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    float tot = 0.f;  // the wave sums in wave order
+#pragma unroll
+    for (int k = 0; k < NORM_NT / 64; ++k) tot += red[k];
     const float rs = 1.f / sqrtf(tot / (float)d + eps);
     const float4* w4 = reinterpret_cast<const float4*>(w);
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
-        const int c = threadIdx.x + 256 * j;
+        const int c = threadIdx.x + NORM_NT * j;
         if (c >= nv) continue;
         const float4 g = w4[c];
         const float v[4] = {x[j].x * rs * g.x, x[j].y * rs * g.y, x[j].z * rs * g.z, x[j].w * rs * g.w};
@@ -84,7 +93,7 @@ __device__ __forceinline__ void norm_row_store(const float4 (&x)[NORM_V4], int n
 // slice order, of the K-slice partials part[s][i][.] of the product that
 // produces it; the updated row is stored back to X and normalised.
 template <typename TO>
-__global__ void __launch_bounds__(256) rmsnorm_kernel(float* __restrict__ X, const float* __restrict__ part, int nparts,
+__global__ void __launch_bounds__(NORM_NT) rmsnorm_kernel(float* __restrict__ X, const float* __restrict__ part, int nparts,
                                                       int n, int d, const float* __restrict__ w, float eps,
                                                       TO* __restrict__ Y, TO* __restrict__ Ylo,
                                                       const int32_t* __restrict__ state) {
@@ -94,7 +103,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(float* __restrict__ X, con
     float4 x[NORM_V4];
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
-        const int c = threadIdx.x + 256 * j;
+        const int c = threadIdx.x + NORM_NT * j;
         x[j] = c < nv ? x4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (nparts > 0) {
@@ -106,13 +115,13 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(float* __restrict__ X, con
         float4 pv[NORM_V4][8];
 #pragma unroll
         for (int j = 0; j < NORM_V4; ++j) {
-            const int c = min(threadIdx.x + 256 * j, nv - 1);
+            const int c = min(threadIdx.x + NORM_NT * j, nv - 1);
 #pragma unroll
             for (int s = 0; s < 8; ++s) pv[j][s] = p4[min(s, nparts - 1) * ps + c];
         }
 #pragma unroll
         for (int j = 0; j < NORM_V4; ++j) {
-            const int c = threadIdx.x + 256 * j;
+            const int c = threadIdx.x + NORM_NT * j;
             if (c >= nv) continue;
             float4 acc = pv[j][0];
 #pragma unroll
@@ -529,7 +538,7 @@ __global__ void __launch_bounds__(1024) hist_permute_kernel(const int32_t* __res
 // norm) into A, from the registers that hold it.
 // ---------------------------------------------------------------------------
 template <typename TO>
-__global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int d, const float* __restrict__ Y,
+__global__ void __launch_bounds__(NORM_NT) combine_kernel(float* __restrict__ X, int d, const float* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_of,
                                                       const float* __restrict__ gates, int k, int shared_off,
                                                       const float* __restrict__ nw, float eps, TO* __restrict__ A,
@@ -548,7 +557,7 @@ __global__ void __launch_bounds__(256) combine_kernel(float* __restrict__ X, int
     float4 x[NORM_V4];
 #pragma unroll
     for (int j = 0; j < NORM_V4; ++j) {
-        const int c = threadIdx.x + 256 * j;
+        const int c = threadIdx.x + NORM_NT * j;
         x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (c >= nv) continue;
         float4 acc = ysh[c];
@@ -582,10 +591,10 @@ hipError_t launch_rmsnorm(const float* X, int n, int d, const float* w, float ep
 
 hipError_t launch_residual_rmsnorm(float* X, const float* part, int nparts, int n, int d, const float* w, float eps,
                                    void* Y, int act_f32, const int32_t* state, hipStream_t st, void* Ylo) {
-    if (d % 4 || d > 4 * 256 * NORM_V4 || (nparts > 0 && !part) || (Ylo && act_f32)) return hipErrorInvalidValue;
-    if (act_f32) rmsnorm_kernel<float><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (float*)Y, nullptr, state);
+    if (d % 4 || d > 4 * NORM_NT * NORM_V4 || (nparts > 0 && !part) || (Ylo && act_f32)) return hipErrorInvalidValue;
+    if (act_f32) rmsnorm_kernel<float><<<n, NORM_NT, 0, st>>>(X, part, nparts, n, d, w, eps, (float*)Y, nullptr, state);
     else
-        rmsnorm_kernel<uint16_t><<<n, 256, 0, st>>>(X, part, nparts, n, d, w, eps, (uint16_t*)Y, (uint16_t*)Ylo,
+        rmsnorm_kernel<uint16_t><<<n, NORM_NT, 0, st>>>(X, part, nparts, n, d, w, eps, (uint16_t*)Y, (uint16_t*)Ylo,
                                                      state);
     return hipGetLastError();
 }
@@ -656,12 +665,12 @@ hipError_t launch_hist_permute(const int32_t* ids, int n, int k, int E, int32_t*
 hipError_t launch_combine(float* X, int n, int d, const float* Y, const int32_t* slot_of, const float* gates, int k,
                           int shared_off, const float* norm_w, float eps, void* A, int act_f32, const int32_t* state,
                           hipStream_t st, void* Alo) {
-    if (d % 4 || d > 4 * 256 * NORM_V4 || k > 16 || (Alo && act_f32)) return hipErrorInvalidValue;
+    if (d % 4 || d > 4 * NORM_NT * NORM_V4 || k > 16 || (Alo && act_f32)) return hipErrorInvalidValue;
     if (act_f32)
-        combine_kernel<float><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
+        combine_kernel<float><<<n, NORM_NT, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps, (float*)A,
                                                  nullptr, state);
     else
-        combine_kernel<uint16_t><<<n, 256, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
+        combine_kernel<uint16_t><<<n, NORM_NT, 0, st>>>(X, d, Y, slot_of, gates, k, shared_off, norm_w, eps,
                                                     (uint16_t*)A, (uint16_t*)Alo, state);
     return hipGetLastError();
 }
