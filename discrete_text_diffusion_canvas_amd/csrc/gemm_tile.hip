@@ -566,17 +566,12 @@ bool tile_gemm_supported(const GemmArgs& g, int act_f32, int w_fp8, int epi) {
     }
 }
 
-// build-time tunable: dense products split over K until they have this many
-// work items
-#ifndef DG_TILE_SPLIT_TARGET
-#define DG_TILE_SPLIT_TARGET 160
-#endif
 int tile_dense_ksplit(int M, int N, int K) {
     // split until there are enough work items for most CUs (each slice keeps
     // at least 4 stages); every split adds M x N f32 partials to write and read
     const int items = (N + DG_TILE_BN_DENSE - 1) / DG_TILE_BN_DENSE * ((M + DG_TILE_BM_DENSE - 1) / DG_TILE_BM_DENSE);
     int ks = 1;
-    while (items * ks < DG_TILE_SPLIT_TARGET && (K / TBK) % (ks * 2) == 0 && K / TBK / (ks * 2) >= 4) ks *= 2;
+    while (items * ks < 160 && (K / TBK) % (ks * 2) == 0 && K / TBK / (ks * 2) >= 4) ks *= 2;
     return ks;
 }
 
