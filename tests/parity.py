@@ -128,7 +128,9 @@ def check_statistics(stats, ocfg, L, t, *, rounded_from_f32=False, ent_tol=ENT_T
     z = S.tempered(L, tau, ocfg.mask_id)
     if rounded_from_f32:
         bound = 1.5 * entropy_rounding_bound(L, tau, ocfg.mask_id) + ent_tol
-        slack = 2.0 * bf16_half_ulp(np.max(np.abs(L), axis=1)) / tau
+        # the rounding of the row's largest finite logit (a -inf from a
+        # banning bias is no rounding)
+        slack = 2.0 * bf16_half_ulp(np.max(np.where(np.isfinite(L), np.abs(L), 0.0), axis=1)) / tau
     else:
         bound = np.full(L.shape[0], ent_tol)
         slack = np.zeros(L.shape[0])

@@ -489,3 +489,52 @@ def test_step_graph_replays_match_eager_steps(B, name):
         assert torch.equal(sa.logits, sb.logits), t
         # eager work of the program between replays
         _ = (sb.entropy * 2).sum().item()
+
+
+@pytest.mark.parametrize("head", ["bf16", "e4m3"])
+def test_lm_head_bias_tokens_on_tile_edges(B, head):
+    """The LM head's epilogue takes each 128-column half tile with or without
+    per-column tests (bias token, MASK, vocabulary end): bias tokens placed on
+    half-tile and tile edges (0, 127, 128, 255, 256, MASK, V - 2, ...), some
+    boosted past the row's maximum, one banned with -inf. Statistics against
+    the oracle on the stored logits, and every row's entropy within 1e-2 nats
+    of the oracle's own float64 logits, at tau 0.8 and 0.4."""
+    cfg = SMALL_BF16
+    n, V = cfg.canvas, cfg.vocab
+    embed = wl.embedding(cfg, device="cuda")
+    fnorm = wl.final_norm(cfg, device="cuda")
+    layers = [wl.layer_weights(cfg, l, device="cuda") for l in range(cfg.n_layers)]
+    if head == "e4m3":
+        codes, scale = wl.lm_head_e4m3(cfg, device="cuda")
+        model = B.Model(cfg, embed, fnorm, layers, lm_head_e4m3=codes, lm_head_scale=scale)
+        W = M.Weights(cfg, embed.cpu(), fnorm.cpu(), lambda l: {}, lm_head=(codes.cpu(), scale.cpu()))
+        E = W.LM
+    else:
+        model = B.Model(cfg, embed, fnorm, layers)
+        W = M.Weights(cfg, embed.cpu(), fnorm.cpu(), lambda l: {})
+        E = W.E
+    edges = [0, 127, 128, 255, 256, 383, 384, 511, 512, V - 129, V - 128, V - 2, cfg.mask_id]
+    g = torch.Generator().manual_seed(21)
+    bt = torch.randint(0, V - 1, (n,), generator=g, dtype=torch.int32)
+    bt[:len(edges)] = torch.tensor(edges, dtype=torch.int32)
+    bv = torch.rand(n, generator=g) * 12
+    bv[1::4] = 30.0
+    bv[3] = float("-inf")
+    X = torch.randn(n, cfg.d_model, generator=g).cuda()
+    ws = model.workspace(n)
+    ocfg = S.SamplerConfig(mask_id=cfg.mask_id)
+    Lo = M.lm_logits(X.cpu().numpy().astype(np.float64), W.final_norm, E, cfg.norm_eps)
+    btn, bvn = bt.numpy().astype(np.int64), bv.numpy().astype(np.float64)
+    Lo_b = Lo.copy()
+    Lo_b[np.arange(n), btn] += bvn
+    for t in (0, 47):
+        stats = B.StepStats(n, vocab=V, logits_dtype=torch.bfloat16)
+        B.lm_head(model, X, B.sampler_default(), t, stats, ws, bt.cuda(), bv.cuda())
+        torch.cuda.synchronize()
+        Lg = stats.logits.float().cpu().numpy().astype(np.float64)
+        assert rel_l2_rows(Lg, Lo).max() < (5e-2 if head == "e4m3" else 1e-2)
+        Lb = Lg.copy()
+        Lb[np.arange(n), btn] += bvn
+        check_statistics(stats, ocfg, Lb, t, rounded_from_f32=True)
+        Ho, _, _, _ = S.row_stats(Lo_b, S.temperature(t, ocfg), cfg.mask_id)
+        assert np.abs(stats.entropy.cpu().numpy() - Ho).max() < ENT_TOL_NORTH, (head, t)

@@ -300,3 +300,25 @@ def test_row_without_finite_mass_commits_its_argmax(B, dtype, kind):
     assert int(canvas.committed[0]) == 1 and int(canvas.tokens[0]) == want
     tok = canvas.tokens.cpu().numpy()
     assert tok.min() >= 0 and tok.max() < V
+
+
+def test_full_vocabulary_f32_logits_with_bias_on_chunk_edges(B):
+    """f32 logits over the full 262144-column vocabulary (two splits of eight
+    16384-column chunks each, the f32 register layout of the statistics
+    pass), bias tokens on chunk and split edges, a peak 60 logits above the
+    rest in the last chunk of some rows."""
+    n, V = 32, 262144
+    edges = [0, 16383, 16384, 131071, 131072, 131073, 147456, V - 2, V - 1]
+    g = torch.Generator().manual_seed(31)
+    tok = torch.randint(0, V - 1, (n,), generator=g).numpy()
+    tok[:len(edges)] = edges
+    mag = (torch.rand(n, generator=g) * 12).numpy().astype(np.float32)
+    mag[2::5] = 40.0
+    peak_rows = torch.arange(16, 24)
+
+    def logits(t):
+        gg = torch.Generator().manual_seed(7000 + t)
+        L = torch.randn(n, V, generator=gg)
+        L[peak_rows, V - 3] = 60.0
+        return L.to("cuda")
+    run_and_compare(B, logits, n, V, None, step_ids=[0, 23, 47], bias=(tok, mag), canvas_idx=4)
