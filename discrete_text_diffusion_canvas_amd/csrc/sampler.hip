@@ -315,20 +315,21 @@ logit_stats_kernel(const T* __restrict__ logits, int64_t ld, int V, int split_co
 }
 
 // ---------------------------------------------------------------------------
-// Merge the per-split partials of each row. One wavefront per row.
+// Merge the per-split partials of each row. One workgroup of 256 threads
+// per row: each thread merges every 256th partial, then the waves, then the
+// wave results in order.
 // H = ln2 * (log2 S - T2 / S) (clamped at 0); lse = ln2 * (M2 + log2 S).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) merge_rows_kernel(
     const RowPart* __restrict__ parts, int n, int nsplit, const int32_t* __restrict__ state,
     float* __restrict__ H, float* __restrict__ lse, int32_t* __restrict__ amax, int32_t* __restrict__ gtok) {
     if (state && state[0]) return;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (row >= n) return;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     EntPart e{-INFINITY, 0.f, 0.f};
     ArgMax am{-INFINITY, 0x7fffffff}, gm{-INFINITY, 0x7fffffff};
     const RowPart* p = parts + (int64_t)row * nsplit;
-    for (int i = lane; i < nsplit; i += 64) {
+    for (int i = tid; i < nsplit; i += 256) {
         RowPart q = p[i];
         if (q.amax >= 0) {
             e = ent_merge(e, EntPart{q.m2, q.s, q.t});
@@ -339,7 +340,16 @@ __global__ void __launch_bounds__(256) merge_rows_kernel(
     e = wave_ent(e);
     am = wave_argmax(am);
     if (gtok) gm = wave_argmax(gm);
-    if (lane == 0) {
+    __shared__ EntPart se[4];
+    __shared__ ArgMax sa[4], sg[4];
+    if (lane == 0) { se[w] = e; sa[w] = am; sg[w] = gm; }
+    __syncthreads();
+    if (tid == 0) {
+        for (int i = 1; i < 4; ++i) {
+            e = ent_merge(e, se[i]);
+            am = argmax_merge(am, sa[i]);
+            if (gtok) gm = argmax_merge(gm, sg[i]);
+        }
         const float LN2 = 0.6931471805599453f;
         float l2s = log2f(e.s);
         float h = LN2 * (l2s - e.t / e.s);
@@ -759,7 +769,7 @@ __global__ void __launch_bounds__(256) gumbel_commit_kernel(const int32_t* __res
 
 hipError_t launch_merge_rows(const RowPart* parts, int n, int nsplit, const int32_t* state, float* H,
                              float* lse, int32_t* amax, int32_t* gtok, hipStream_t st) {
-    merge_rows_kernel<<<(n + 3) / 4, 256, 0, st>>>(parts, n, nsplit, state, H, lse, amax, gtok);
+    merge_rows_kernel<<<n, 256, 0, st>>>(parts, n, nsplit, state, H, lse, amax, gtok);
     return hipGetLastError();
 }
 
