@@ -245,7 +245,9 @@ __global__ void __launch_bounds__(LNW * 64) lmhead_kernel(GemmArgs g) {
         // stores (16 threads per row) and thread r computes row r's partials.
         float* T = reinterpret_cast<float*>(smem);
         uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
-        const int r_own = tid;                                  // this thread's row of the item
+        // statistics: two threads per row (lanes 2r' and 2r'+1 of a wave),
+        // each over 64 of the half's 128 columns, combined by a neighbour swap
+        const int r_own = tid >> 1, hf = tid & 1;               // this thread's row of the item, its 64 columns
         const bool own_ok = r_own < mcount;
         const int bt = own_ok && g.bias_tok ? g.bias_tok[m0 + r_own] : -1;
         const float bv = own_ok && g.bias_tok ? g.bias_val[m0 + r_own] : 0.f;
@@ -287,48 +289,72 @@ __global__ void __launch_bounds__(LNW * 64) lmhead_kernel(GemmArgs g) {
             }
             // (2) row r_own's partials over the half, from the f32 values:
             // raw max and its lowest column, then the base-2 partition sum
-            // and entropy partial against that max
-            if (own_ok) {
-                const float* tp = T + r_own * TST;
+            // and entropy partial against that max. Thread hf takes columns
+            // 64 hf + ((j + 32 hf) % 64), j = 0..63: the two threads of a row
+            // (and the 32 rows of a wave) read distinct LDS banks.
+            {
+                const float* tp = T + r_own * TST + 64 * hf;
                 const bool special = (bt >= cb && bt < cb + 128) || (g.mask_id >= cb && g.mask_id < cb + 128) ||
                                      cb + 128 > N;
+                auto colv = [&](int j) { return (j + 32 * hf) & 63; };
                 float rawm = -INFINITY;
                 int vi = 0x7fffffff;
                 if (!special) {
-                    for (int c = 0; c < 128; ++c) {
+#pragma unroll 4
+                    for (int j = 0; j < 64; ++j) {
+                        const int c = colv(j);
                         const float l = tp[c];
-                        if (l > rawm) { rawm = l; vi = cb + c; }
+                        const int col = cb + 64 * hf + c;
+                        if (l > rawm || (l == rawm && col < vi)) { rawm = l; vi = col; }
                     }
                 } else {
-                    for (int c = 0; c < 128; ++c) {
-                        const int col = cb + c;
+#pragma unroll 4
+                    for (int j = 0; j < 64; ++j) {
+                        const int c = colv(j);
+                        const int col = cb + 64 * hf + c;
                         float l = tp[c] + (col == bt ? bv : 0.f);
                         if (col >= N || col == g.mask_id) l = -INFINITY;
-                        if (l > rawm) { rawm = l; vi = col; }
+                        if (l > rawm || (l == rawm && col < vi)) { rawm = l; vi = col; }
                     }
+                }
+                // the row's max and lowest column over both threads
+                {
+                    const ArgMax o{__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, rawm), 0xB1, 0xF, 0xF, false)),
+                                   __builtin_amdgcn_update_dpp(0, vi, 0xB1, 0xF, 0xF, false)};
+                    const ArgMax m = argmax_merge(ArgMax{rawm, vi}, o);
+                    rawm = m.v;
+                    vi = m.i;
                 }
                 const float vm = rawm * c2;
                 float sa = 0.f, ta = 0.f;
                 if (rawm != -INFINITY) {
                     if (!special) {
-                        for (int c = 0; c < 128; ++c) {
-                            const float d = tp[c] * c2 - vm;
-                            const float w = exp2f(d);
+    #pragma unroll 4
+                    for (int j = 0; j < 64; ++j) {
+                            const float d = fmaf(tp[colv(j)], c2, -vm);
+                            const float w = __builtin_amdgcn_exp2f(d);
                             sa += w;
-                            ta += w * d;
+                            ta = fmaf(w, d, ta);
                         }
                     } else {
-                        for (int c = 0; c < 128; ++c) {
-                            const int col = cb + c;
+    #pragma unroll 4
+                    for (int j = 0; j < 64; ++j) {
+                            const int c = colv(j);
+                            const int col = cb + 64 * hf + c;
                             float l = tp[c] + (col == bt ? bv : 0.f);
                             if (col >= N || col == g.mask_id) l = -INFINITY;
                             const float d = l * c2 - vm;
-                            const float w = exp2f(d);
+                            const float w = __builtin_amdgcn_exp2f(d);
                             sa += w;
                             ta += w > 0.f ? w * d : 0.f;
                         }
                     }
                 }
+                sa += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, sa), 0xB1, 0xF,
+                                                                            0xF, false));
+                ta += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, ta), 0xB1, 0xF,
+                                                                            0xF, false));
                 // Gumbel-max candidate over the logits of record: the lowest
                 // column maximising z - log(-log u), u from Philox at (row,
                 // step, canvas, 1 + v / 4), word v % 4
@@ -336,7 +362,7 @@ __global__ void __launch_bounds__(LNW * 64) lmhead_kernel(GemmArgs g) {
                 int gi = 0x7fffffff;
                 if constexpr (GUMBEL) {
                     const int grow = m0 + r_own;
-                    for (int c = 0; c < 128 && cb + c < N; c += 4) {
+                    for (int c = 64 * hf; c < 64 * hf + 64 && cb + c < N; c += 4) {
                         const u32x4 wd = philox10(u32x4{(uint32_t)grow, (uint32_t)step, (uint32_t)g.sp.canvas_idx,
                                                         (uint32_t)(1 + (cb + c) / 4)},
                                                   g.sp.seed_lo, g.sp.seed_hi);
@@ -344,21 +370,30 @@ __global__ void __launch_bounds__(LNW * 64) lmhead_kernel(GemmArgs g) {
                         for (int u = 0; u < 4; ++u) {
                             const int col = cb + c + u;
                             if (col == g.mask_id) continue;
-                            const float val = (round_bf(tp[c + u]) + (col == bt ? bv : 0.f)) * inv_tau + gumbel_of(wd[u]);
+                            const float val =
+                                (round_bf(T[r_own * TST + c + u]) + (col == bt ? bv : 0.f)) * inv_tau + gumbel_of(wd[u]);
                             if (val > gv) { gv = val; gi = col; }
                         }
                     }
+                    const ArgMax o{__builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, gv), 0xB1, 0xF, 0xF, false)),
+                                   __builtin_amdgcn_update_dpp(0, gi, 0xB1, 0xF, 0xF, false)};
+                    const ArgMax m = argmax_merge(ArgMax{gv, gi}, o);
+                    gv = m.v;
+                    gi = m.i;
                 }
-                RowPart p;
-                p.m2 = rawm == -INFINITY ? -INFINITY : vm;
-                p.s = sa;
-                p.t = ta;
-                p.lmax = rawm;
-                p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
-                p.pad[0] = __float_as_int(gv);
-                p.pad[1] = gi == 0x7fffffff ? -1 : gi;
-                p.pad[2] = 0;
-                g.parts[(int64_t)(m0 + r_own) * g.nsplit + ptile] = p;
+                if (own_ok && hf == 0) {
+                    RowPart p;
+                    p.m2 = rawm == -INFINITY ? -INFINITY : vm;
+                    p.s = sa;
+                    p.t = ta;
+                    p.lmax = rawm;
+                    p.amax = (vi == 0x7fffffff || rawm == -INFINITY) ? -1 : vi;
+                    p.pad[0] = __float_as_int(gv);
+                    p.pad[1] = gi == 0x7fffffff ? -1 : gi;
+                    p.pad[2] = 0;
+                    g.parts[(int64_t)(m0 + r_own) * g.nsplit + ptile] = p;
+                }
             }
         }
         __syncthreads();  // the LDS is refilled by the next item
